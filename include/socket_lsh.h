@@ -1,0 +1,164 @@
+/*
+ * socket_lsh.h -- C ABI of the SOCKET sparse-attention decode path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "SOCKET: SOft Collision Kernel EsTimator for
+ * Sparse Attention" (paperpeel.com/paper/2602.06283), Section 4.1 "The Final
+ * Algorithm": keys are hashed into L tables at prefill and their bucket IDs
+ * are cached with the value-vector norms (Algorithm 1); at decode the query
+ * induces a probability distribution over the buckets of each table and each
+ * key is scored by the probability mass of its own buckets, weighted by its
+ * value norm (Algorithm 2, Section 1 "Key Idea"); the top-k keys are selected
+ * and exact attention runs over that subset only (Algorithm 3, Section 2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or retains them.  Work is enqueued on `stream`
+ *   (a hipStream_t, passed as void*; NULL means the default stream) and the
+ *   call returns right after enqueueing.  Nothing is synchronised.
+ * - No global state is kept between calls; calls on different streams with
+ *   disjoint outputs and workspaces may run concurrently.
+ * - Layouts are dense, row-major, with the last index contiguous:
+ *     K, V      [B][Hkv][n_cap][d]      dtype SOCKET_BF16 or SOCKET_F32
+ *     q         [B][Hq][d]              same dtype as K
+ *     W         [L*P][d]                same dtype as K; rows l*P..l*P+P-1 are
+ *                                       the P hyperplanes of table l
+ *     ids       [B][Hkv][n_cap][L]      uint8 (one bucket ID per table per key,
+ *                                       bit j = sign of plane j; P <= 8)
+ *     vnorm     [B][Hkv][n_cap]         float32
+ *     lens, ks  [B]                     int32, device
+ *     idx       [B][Hq][k_max]          int32
+ *     scores    [B][Hq][n_cap]          float32
+ *     out       [B][Hq][d]              float32
+ * - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
+ *   Hq must be a multiple of Hkv; socket_score_topk needs Hq / Hkv in
+ *   {1, 2, 4}.
+ * - d must be 128.  1 <= P <= 8, 1 <= L <= 256.
+ * - Errors are reported as negative return codes before anything is
+ *   enqueued (argument checks), or as SOCKET_EHIP when a launch fails.
+ *   Nothing throws or aborts.  socket_status_string() names a code.
+ */
+#ifndef SOCKET_LSH_H
+#define SOCKET_LSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SOCKET_OK = 0,
+  SOCKET_EINVAL = -1,       /* null pointer, bad size, bad shape            */
+  SOCKET_EUNSUPPORTED = -2, /* valid but not implemented (d != 128, P > 8)  */
+  SOCKET_ENOSPC = -3,       /* workspace smaller than the *_workspace size  */
+  SOCKET_EHIP = -4          /* a HIP launch failed                          */
+};
+
+enum { SOCKET_F32 = 0, SOCKET_BF16 = 1 };
+
+/* Name of a status code (static string). */
+const char* socket_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int socket_version(void);
+
+/*
+ * socket_hash_keys -- Algorithm 1 (SOCKET Sec. 4.1; bucket ID = sign pattern
+ * of W^(l) k, Appendix B.2) plus the value-norm cache (Sec. 1 "Key Idea").
+ *
+ * For every sequence b, KV head h and position i in [pos0[b], pos0[b]+count):
+ *   ids[b][h][i][l] = sum_j [ <W[l*P+j], K[b][h][i]> > 0 ] << j
+ *   vnorm[b][h][i]  = || V[b][h][i] ||_2
+ * The projection is accumulated in float32 (bf16 products are exact in
+ * float32).  A projection of exactly zero gives bit 0.  Positions at or past
+ * n_cap are skipped.  Prefill passes pos0 = 0 and count = n; the decode-time
+ * append passes pos0 = current length and count = 1 after the caller has
+ * written the new row of K and V.
+ *
+ * pos0 is a device int32 array [B].  Other rows of ids/vnorm are untouched.
+ */
+int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, int d,
+                     int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
+                     int P, uint8_t* ids, float* vnorm, void* stream);
+
+/* Workspace bytes needed by socket_score_topk for these sizes. */
+size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, int k_max);
+
+/*
+ * socket_score_topk -- Algorithms 2 and 3 of SOCKET Sec. 4.1.
+ *
+ * For each sequence b and query head g (KV head h = g / (Hq/Hkv)):
+ *   u[l][j]   = <W[l*P+j], q[b][g]>                         (float64)
+ *   p_l(c)    = softmax over buckets c of (sum_j s_j(c) u[l][j]) / tau,
+ *               s_j(c) = +1 if bit j of c is set else -1
+ *               (equivalently prod_j sigmoid(2 s_j(c) u[l][j] / tau))
+ *   s_i       = vnorm[b][h][i] * sum_l p_l(ids[b][h][i][l])   for i < lens[b]
+ *   idx[b][g] = the min(ks[b], lens[b]) keys with the largest s_i; among
+ *               equal scores the lower index wins.  The indices are written
+ *               in ascending order and the row is padded with -1 up to k_max.
+ * Scores are float32; the table entries are float32 roundings of float64
+ * values.  If `scores` is not NULL the scores of every i < lens[b] are
+ * written there (entries i >= lens[b] are left untouched).
+ *
+ * lens and ks are device int32 arrays [B] with 0 <= lens[b] <= n_cap and
+ * ks[b] <= k_max (a negative ks[b] is treated as 0).  tau > 0.
+ * ws must hold socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max) bytes
+ * and be 256-byte aligned; its contents need not be initialised.
+ */
+int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                      int L, int P, float tau, const uint8_t* ids, const float* vnorm,
+                      const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max,
+                      int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The three stages of socket_score_topk, for callers that schedule or time
+ * them separately.  All three take the same workspace (sized by
+ * socket_score_topk_workspace for the same B, Hq, n_cap, L) and must be
+ * enqueued in this order on one stream for one query batch:
+ *
+ * socket_soft_tables -- Algorithm 2, first half: the float64 projections of
+ *   q[b][g] and, per table, the float32 half-tables lo_l(c) (planes 0..3) and
+ *   hi_l(c) (planes 4..P-1) with p_l(c) = lo_l(c & 15) * hi_l(c >> 4).  Also
+ *   clears the selection histograms and counters held in the workspace.
+ * socket_score -- Algorithm 2, second half: s_i for every i < lens[b] of every
+ *   query head, written to `scores` (or into the workspace when scores is
+ *   NULL), plus a histogram of the top bits of each score in the workspace.
+ * socket_topk -- Algorithm 3: the top-k indices per query head, from the same
+ *   `scores` pointer (NULL = workspace) and the histogram left by
+ *   socket_score.  Output as in socket_score_topk.
+ */
+int socket_soft_tables(const void* q, int dtype, int B, int Hq, int d, const void* W, int L,
+                       int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes, void* stream);
+int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const float* vnorm,
+                 const int32_t* lens, int64_t n_cap, float* scores, void* ws, size_t ws_bytes,
+                 void* stream);
+int socket_topk(int B, int Hq, int L, const float* scores, const int32_t* lens, int64_t n_cap,
+                const int32_t* ks, int k_max, int32_t* idx, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Workspace bytes needed by socket_sparse_decode for these sizes. */
+size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max);
+
+/*
+ * socket_sparse_decode -- exact softmax attention over the selected keys
+ * (SOCKET Sec. 2 and Sec. 4.1, Algorithm 3):
+ *   a_i = exp(scale * <q, K_i>) / sum_{i' in S} exp(scale * <q, K_i'>)
+ *   out[b][g] = sum_{i in S} a_i V_i,   S = { idx[b][g][t] : t < k_max, idx >= 0 }
+ * with K, V of KV head g / (Hq/Hkv).  Accumulation is float32.  Entries of
+ * idx equal to -1 are skipped; every other entry must lie in [0, n_cap).
+ * A row with no selected key produces zeros.  `scale` is usually 1/sqrt(d).
+ * ws must hold socket_sparse_decode_workspace(B, Hq, d, k_max) bytes,
+ * 256-byte aligned; its contents need not be initialised.
+ */
+int socket_sparse_decode(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
+                         int Hkv, int d, int64_t n_cap, const int32_t* idx, int k_max,
+                         float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOCKET_LSH_H */

@@ -1,0 +1,14 @@
+"""SOCKET soft-LSH sparse-attention decode path for AMD MI355X (gfx950).
+
+The compute lives in the HIP library ``libsocket_lsh.so`` (C ABI in
+``include/socket_lsh.h``); this package only marshals torch tensors into
+its entry points.  Importing the package does not load the library; the
+first call does, and raises if the library has not been built.
+"""
+from ._lib import (  # noqa: F401
+    SOCKET_BF16, SOCKET_F32, SocketError, alloc_workspace, lib, socket_hash_keys,
+    socket_score_topk, socket_score_topk_workspace, socket_sparse_decode,
+    socket_sparse_decode_workspace,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,174 @@
+"""ctypes binding of ``libsocket_lsh.so`` (C ABI in include/socket_lsh.h).
+
+Argument marshalling only: every function checks the tensors' shapes,
+dtypes and devices, passes raw device pointers and the current HIP stream
+to the library, and raises :class:`SocketError` on a non-zero status.  All
+compute happens in the HIP kernels.  There is no fallback: if the library
+is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsocket_lsh.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "socket_lsh.h")
+
+SOCKET_F32, SOCKET_BF16 = 0, 1
+STATUS = {0: "SOCKET_OK", -1: "SOCKET_EINVAL", -2: "SOCKET_EUNSUPPORTED", -3: "SOCKET_ENOSPC",
+          -4: "SOCKET_EHIP"}
+
+_vp, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "socket_status_string": (ctypes.c_char_p, [_i]),
+    "socket_version": (_i, []),
+    "socket_hash_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp, _vp]),
+    "socket_score_topk_workspace": (_sz, [_i, _i, _i64, _i, _i, _i]),
+    "socket_score_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _i64, _vp,
+                               _i, _vp, _vp, _vp, _sz, _vp]),
+    "socket_sparse_decode_workspace": (_sz, [_i, _i, _i, _i]),
+    "socket_sparse_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i64, _vp, _i, _f, _vp, _vp,
+                                  _sz, _vp]),
+}
+
+_lib = None
+
+
+class SocketError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        name = STATUS.get(status, str(status))
+        super().__init__(f"{fn} failed with {name} ({lib().socket_status_string(status).decode()})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m "
+                               "soft_lsh_token_amd.build` (needs hipcc)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/socket_lsh.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(socket_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise SocketError(fn, rc)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SOCKET_BF16
+    if t.dtype == torch.float32:
+        return SOCKET_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
+                     vnorm: torch.Tensor, pos0: torch.Tensor, count: int, L: int, P: int,
+                     stream=None) -> None:
+    """Hash rows [pos0[b], pos0[b]+count) of K into ids and store ||V|| in vnorm."""
+    B, Hkv, n_cap, d = K.shape
+    dt = _dtype_code(K)
+    rc = lib().socket_hash_keys(
+        _dev(K, "K"), _dev(V, "V", K.dtype, K.shape), dt, B, Hkv, d, n_cap,
+        _dev(pos0, "pos0", torch.int32, (B,)), int(count), _dev(W, "W", K.dtype, (L * P, d)),
+        L, P, _dev(ids, "ids", torch.uint8, (B, Hkv, n_cap, L)),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _stream(K, stream))
+    _check("socket_hash_keys", rc)
+
+
+def socket_score_topk_workspace(B: int, Hq: int, n_cap: int, L: int, P: int, k_max: int) -> int:
+    return int(lib().socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max))
+
+
+def socket_sparse_decode_workspace(B: int, Hq: int, d: int, k_max: int) -> int:
+    return int(lib().socket_sparse_decode_workspace(B, Hq, d, k_max))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A device byte buffer whose data pointer is 256-byte aligned."""
+    return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+
+
+def _ws_ptr(ws: torch.Tensor, need: int) -> tuple[int, int]:
+    base = _dev(ws, "ws", torch.uint8)
+    off = (-base) % 256
+    return base + off, ws.numel() - off
+
+
+def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm: torch.Tensor,
+                      lens: torch.Tensor, ks: torch.Tensor, k_max: int, tau: float, L: int, P: int,
+                      idx: torch.Tensor, scores: torch.Tensor | None = None,
+                      ws: torch.Tensor | None = None, stream=None) -> None:
+    """Soft-LSH scores of every key and the top-k indices per query head."""
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = ids.shape
+    need = socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max)
+    if ws is None:
+        ws = alloc_workspace(need, q.device)
+    wptr, wbytes = _ws_ptr(ws, need)
+    sptr = None if scores is None else _dev(scores, "scores", torch.float32, (B, Hq, n_cap))
+    rc = lib().socket_score_topk(
+        _dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P,
+        float(tau), _dev(ids, "ids", torch.uint8, (B, Hkv, n_cap, L)),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
+        _dev(lens, "lens", torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)),
+        int(k_max), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr, wptr, wbytes,
+        _stream(q, stream))
+    _check("socket_score_topk", rc)
+
+
+def socket_sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
+                         scale: float, out: torch.Tensor, ws: torch.Tensor | None = None,
+                         stream=None) -> None:
+    """Exact attention of q over the keys listed in idx (-1 entries skipped)."""
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = K.shape
+    k_max = idx.shape[-1]
+    need = socket_sparse_decode_workspace(B, Hq, d, k_max)
+    if ws is None:
+        ws = alloc_workspace(need, q.device)
+    wptr, wbytes = _ws_ptr(ws, need)
+    rc = lib().socket_sparse_decode(
+        _dev(q, "q"), _dev(K, "K", q.dtype), _dev(V, "V", q.dtype, K.shape), _dtype_code(q), B, Hq,
+        Hkv, d, n_cap, _dev(idx, "idx", torch.int32, (B, Hq, k_max)), k_max, float(scale),
+        _dev(out, "out", torch.float32, (B, Hq, d)), wptr, wbytes, _stream(q, stream))
+    _check("socket_sparse_decode", rc)

@@ -1,0 +1,57 @@
+"""Build the HIP library ``libsocket_lsh.so`` for gfx950 with hipcc.
+
+The library is built in-tree next to this file.  ``python -m
+soft_lsh_token_amd.build`` rebuilds it; it always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsocket_lsh.so")
+SOURCES = ["api.hip", "hash.hip", "score_topk.hip", "sparse_decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP toolchain is required to build libsocket_lsh.so")
+
+
+def command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
+    return [
+        hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+        # keep the compiler away from packed fp32 instructions
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        "-o", out,
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        *(extra or []),
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
+            if "packed-fp32-ops" not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,161 @@
+// C ABI of the SOCKET decode path: argument checks, workspace sizing and
+// dispatch to the kernels.  Every check happens before anything is enqueued.
+#include "../../include/socket_lsh.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace socketlsh;
+
+namespace {
+
+constexpr int kMaxL = 256;
+constexpr int kMaxKmax = 1 << 20;
+
+bool group_ok(int Hq, int Hkv) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
+  const int G = Hq / Hkv;
+  return G == 1 || G == 2 || G == 4;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? SOCKET_OK : SOCKET_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* socket_status_string(int status) {
+  switch (status) {
+    case SOCKET_OK: return "ok";
+    case SOCKET_EINVAL: return "invalid argument";
+    case SOCKET_EUNSUPPORTED: return "unsupported configuration";
+    case SOCKET_ENOSPC: return "workspace too small";
+    case SOCKET_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int socket_version(void) { return 100; }
+
+int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, int d,
+                     int64_t n_cap, const int32_t* pos0, int count, const void* W, int L, int P,
+                     uint8_t* ids, float* vnorm, void* stream) {
+  if (!K || !V || !pos0 || !W || !ids || !vnorm) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (B <= 0 || Hkv <= 0 || n_cap <= 0 || count < 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
+  if (n_cap >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
+  if (d != kHead || P > 8 || L > kMaxL) return SOCKET_EUNSUPPORTED;
+  if ((int64_t)B * Hkv * count >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
+  if (count == 0) return SOCKET_OK;
+  return from_hip(launch_hash_keys(K, V, dtype, B, Hkv, n_cap, pos0, count, W, L, P, ids, vnorm,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, int k_max) {
+  (void)P;
+  (void)k_max;
+  if (B <= 0 || Hq <= 0 || n_cap <= 0 || L <= 0) return 0;
+  return score_ws_layout(B, Hq, n_cap, L, nullptr, nullptr);
+}
+
+static int score_ws(int B, int Hq, int64_t n_cap, int L, void* ws, size_t ws_bytes, ScoreWs* w) {
+  if (!ws) return SOCKET_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return SOCKET_EINVAL;
+  const size_t need = score_ws_layout(B, Hq, n_cap, L, w, ws);
+  return ws_bytes < need ? SOCKET_ENOSPC : SOCKET_OK;
+}
+
+static int check_sizes(int B, int Hq, int Hkv, int L, int P, int64_t n_cap) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
+  if (Hq % Hkv) return SOCKET_EINVAL;
+  if (!group_ok(Hq, Hkv)) return SOCKET_EUNSUPPORTED;
+  if (P > 8 || L > kMaxL) return SOCKET_EUNSUPPORTED;
+  if (n_cap >= ((int64_t)1 << 31) || (int64_t)B * Hq * n_cap >= ((int64_t)1 << 40))
+    return SOCKET_EUNSUPPORTED;
+  return SOCKET_OK;
+}
+
+int socket_soft_tables(const void* q, int dtype, int B, int Hq, int d, const void* W, int L,
+                       int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !W) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (!(tau > 0.f) || !(tau < INFINITY)) return SOCKET_EINVAL;
+  int rc = check_sizes(B, Hq, Hq, L, P, n_cap);
+  if (rc) return rc;
+  if (d != kHead) return SOCKET_EUNSUPPORTED;
+  ScoreWs w;
+  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  return from_hip(launch_soft_tables(q, dtype, B, Hq, W, L, P, tau, w,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const float* vnorm,
+                 const int32_t* lens, int64_t n_cap, float* scores, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (!ids || !vnorm || !lens) return SOCKET_EINVAL;
+  int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
+  if (rc) return rc;
+  ScoreWs w;
+  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  return from_hip(launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap,
+                               scores ? scores : w.scores, w, static_cast<hipStream_t>(stream)));
+}
+
+int socket_topk(int B, int Hq, int L, const float* scores, const int32_t* lens, int64_t n_cap,
+                const int32_t* ks, int k_max, int32_t* idx, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (!lens || !ks || !idx) return SOCKET_EINVAL;
+  if (k_max <= 0) return SOCKET_EINVAL;
+  if (k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
+  int rc = check_sizes(B, Hq, Hq, L, 1, n_cap);
+  if (rc) return rc;
+  ScoreWs w;
+  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  return from_hip(launch_topk(B, Hq, scores ? scores : w.scores, lens, n_cap, ks, k_max, idx, w,
+                              static_cast<hipStream_t>(stream)));
+}
+
+int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                      int L, int P, float tau, const uint8_t* ids, const float* vnorm,
+                      const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max,
+                      int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !W || !ids || !vnorm || !lens || !ks || !idx || !ws) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (k_max <= 0) return SOCKET_EINVAL;
+  if (!(tau > 0.f) || !(tau < INFINITY)) return SOCKET_EINVAL;
+  int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
+  if (rc) return rc;
+  if (d != kHead || k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
+  ScoreWs w;
+  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sc = scores ? scores : w.scores;
+  hipError_t e = launch_soft_tables(q, dtype, B, Hq, W, L, P, tau, w, s);
+  if (e == hipSuccess) e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sc, w, s);
+  if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, idx, w, s);
+  return from_hip(e);
+}
+
+size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max) {
+  if (B <= 0 || Hq <= 0 || d != kHead || k_max <= 0) return 0;
+  return decode_ws_layout(B, Hq, k_max, nullptr, nullptr);
+}
+
+int socket_sparse_decode(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
+                         int Hkv, int d, int64_t n_cap, const int32_t* idx, int k_max,
+                         float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !idx || !out || !ws) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || k_max <= 0) return SOCKET_EINVAL;
+  if (Hq % Hkv) return SOCKET_EINVAL;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return SOCKET_EINVAL;
+  if (d != kHead || k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
+  if (n_cap >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return SOCKET_EINVAL;
+  DecodeWs w;
+  const size_t need = decode_ws_layout(B, Hq, k_max, &w, ws);
+  if (ws_bytes < need) return SOCKET_ENOSPC;
+  return from_hip(launch_sparse_decode(q, K, V, dtype, B, Hq, Hkv, n_cap, idx, k_max, scale, out,
+                                       w, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

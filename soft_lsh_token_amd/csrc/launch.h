@@ -1,0 +1,51 @@
+// Host-side launchers of the SOCKET kernels.  Arguments have been validated
+// by the C ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace socketlsh {
+
+hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv,
+                            int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
+                            int P, uint8_t* ids, float* vnorm, hipStream_t s);
+
+struct ScoreWs {
+  float* sub;           // [B*Hq][L][32]  per-table half-tables (float32)
+  uint32_t* hist;       // [B*Hq][kHistBins]
+  uint32_t* counters;   // [B*Hq][4]  {candidates, done tickets, -, -}
+  uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/64)*2
+  uint2* cand;          // [B*Hq][n_cap]  (score bits, key index)
+  float* scores;        // [B*Hq][n_cap]  when the caller passes no score buffer
+  int64_t words;
+};
+
+size_t score_ws_layout(int B, int Hq, int64_t n_cap, int L, ScoreWs* ws, void* base);
+
+// Algorithm 2, part 1: per-table half-tables of every query head; clears the
+// histograms and counters the scorer and the selection use.
+hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, const void* W, int L,
+                              int P, float tau, const ScoreWs& ws, hipStream_t s);
+
+// Algorithm 2, part 2: scores of every key plus the first-digit histogram.
+hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,
+                        const float* vnorm, const int32_t* lens, int64_t n_cap, float* scores,
+                        const ScoreWs& ws, hipStream_t s);
+
+// Algorithm 3: top-k selection from the scores and their histogram.
+hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
+                       const int32_t* ks, int k_max, int32_t* idx, const ScoreWs& ws,
+                       hipStream_t s);
+
+struct DecodeWs {
+  float* part;          // [B*Hq][splits][kHead + 2]
+  int splits;
+};
+
+size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base);
+
+hipError_t launch_sparse_decode(const void* q, const void* K, const void* V, int dtype, int B,
+                                int Hq, int Hkv, int64_t n_cap, const int32_t* idx, int k_max,
+                                float scale, float* out, const DecodeWs& ws, hipStream_t s);
+
+}  // namespace socketlsh

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments before it
+enqueues anything (no GPU needed: every call here returns during argument
+checking)."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import soft_lsh_token_amd as S
+from soft_lsh_token_amd import _lib
+
+EINVAL, EUNSUP, ENOSPC = -1, -2, -3
+FAKE = 0x10000  # a non-null, 256-aligned stand-in pointer; never dereferenced
+
+
+def test_library_exports_every_header_function():
+    lib = S.lib()
+    names = _lib.header_functions()
+    assert {"socket_hash_keys", "socket_score_topk", "socket_sparse_decode",
+            "socket_score_topk_workspace", "socket_sparse_decode_workspace",
+            "socket_status_string", "socket_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    lib = S.lib()
+    for code in (0, EINVAL, EUNSUP, ENOSPC, -4):
+        assert lib.socket_status_string(code)
+    assert lib.socket_status_string(-99) == b"unknown status"
+    assert lib.socket_version() >= 100
+
+
+def test_workspace_sizes():
+    a = S.socket_score_topk_workspace(1, 32, 32768, 64, 8, 656)
+    b = S.socket_score_topk_workspace(1, 32, 131072, 64, 8, 1024)
+    assert 0 < a < b
+    assert a % 256 == 0
+    assert S.socket_score_topk_workspace(0, 32, 32768, 64, 8, 656) == 0
+    assert S.socket_sparse_decode_workspace(1, 32, 128, 1024) > 0
+    assert S.socket_sparse_decode_workspace(1, 32, 64, 1024) == 0
+
+
+def _hash(**kw):
+    args = dict(K=FAKE, V=FAKE, dtype=1, B=1, Hkv=8, d=128, n_cap=1024, pos0=FAKE, count=16,
+                W=FAKE, L=64, P=8, ids=FAKE, vnorm=FAKE, stream=None)
+    args.update(kw)
+    return S.lib().socket_hash_keys(*args.values())
+
+
+def test_hash_argument_checks():
+    assert _hash(K=None) == EINVAL
+    assert _hash(vnorm=None) == EINVAL
+    assert _hash(dtype=7) == EINVAL
+    assert _hash(B=0) == EINVAL
+    assert _hash(count=-1) == EINVAL
+    assert _hash(d=64) == EUNSUP
+    assert _hash(P=9) == EUNSUP
+    assert _hash(L=300) == EUNSUP
+    assert _hash(count=0) == 0  # nothing to do, nothing enqueued
+
+
+def _score(**kw):
+    B, Hq, n_cap, L, P, k_max = 1, 32, 1024, 64, 8, 32
+    need = S.socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max)
+    args = dict(q=FAKE, dtype=1, B=B, Hq=Hq, Hkv=8, d=128, W=FAKE, L=L, P=P, tau=0.5, ids=FAKE,
+                vnorm=FAKE, lens=FAKE, n_cap=n_cap, ks=FAKE, k_max=k_max, idx=FAKE, scores=None,
+                ws=FAKE, ws_bytes=need, stream=None)
+    args.update(kw)
+    return S.lib().socket_score_topk(*args.values())
+
+
+def test_score_argument_checks():
+    assert _score(q=None) == EINVAL
+    assert _score(ws=None) == EINVAL
+    assert _score(tau=0.0) == EINVAL
+    assert _score(tau=float("nan")) == EINVAL
+    assert _score(tau=float("inf")) == EINVAL
+    assert _score(Hkv=5) == EINVAL        # 32 % 5
+    assert _score(Hkv=4) == EUNSUP        # 8 query heads per KV head
+    assert _score(P=9) == EUNSUP
+    assert _score(d=96) == EUNSUP
+    assert _score(k_max=0) == EINVAL
+    assert _score(ws=FAKE + 8) == EINVAL  # misaligned workspace
+    assert _score(ws_bytes=1024) == ENOSPC
+
+
+def _decode(**kw):
+    B, Hq, k_max = 1, 32, 64
+    need = S.socket_sparse_decode_workspace(B, Hq, 128, k_max)
+    args = dict(q=FAKE, K=FAKE, V=FAKE, dtype=1, B=B, Hq=Hq, Hkv=8, d=128, n_cap=1024, idx=FAKE,
+                k_max=k_max, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=need, stream=None)
+    args.update(kw)
+    return S.lib().socket_sparse_decode(*args.values())
+
+
+def test_decode_argument_checks():
+    assert _decode(idx=None) == EINVAL
+    assert _decode(out=None) == EINVAL
+    assert _decode(dtype=3) == EINVAL
+    assert _decode(Hkv=3) == EINVAL
+    assert _decode(scale=float("nan")) == EINVAL
+    assert _decode(d=256) == EUNSUP
+    assert _decode(ws_bytes=16) == ENOSPC
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    K = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.socket_hash_keys(K, K, torch.zeros(8, 128, dtype=torch.bfloat16),
+                           torch.zeros(1, 1, 8, 1, dtype=torch.uint8),
+                           torch.zeros(1, 1, 8), torch.zeros(1, dtype=torch.int32), 8, 1, 8)

@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Per-kernel cases at small, ragged sizes; end-to-end
+cases at the full workload sizes (32K, 128K, the 16-sequence ragged batch and
+the prefill + 256-step decode loop), checked on every output or on sampled
+heads where the oracle would take too long."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_cases as GC
+from gpu_cases import DEV
+from oracle import socket_oracle as SO
+from soft_lsh_token_amd.inputs import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=2)
+def workload(name, **kw):
+    return make_workload(name, **dict(kw))
+
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- hashing
+
+@pytest.mark.parametrize("case", [
+    dict(name="c1"),                                   # fp32, generic path
+    dict(name="c2", n=1000),                           # bf16 MFMA, ragged tail
+    dict(name="c2", n=3000, L=32),                     # MFMA with 4 waves
+    dict(name="c2", n=40),                             # few keys: generic bf16 path
+    dict(name="c2", n=500, L=7, P=5, Hkv=2, Hq=4),     # odd shapes: generic path
+    dict(name="c2", n=300, L=3, P=8, Hkv=2, Hq=2),
+    dict(name="c4", n=(300, 900), B=3, Hkv=2, Hq=8),   # batch with different lengths
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_hash_parity(case):
+    print("case", case, flush=True)
+    w = make_workload(**case)
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    sync()
+    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    n_cap = w.n_cap
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            GC.check_ids(ids[b, h], w.K[b, h], w.W, w.L, w.P, n_cap)
+            ref = SO.value_norms(w.V[b, h])
+            np.testing.assert_allclose(vn[b, h], ref, rtol=2e-6)
+
+
+def test_hash_full_c2_mfma():
+    w = workload("c2")
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    sync()
+    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    band = 0
+    for h in range(w.Hkv):
+        band += GC.check_ids(ids[0, h], w.K[0, h], w.W, w.L, w.P, w.n_cap)
+        np.testing.assert_allclose(vn[0, h], SO.value_norms(w.V[0, h]), rtol=2e-6)
+    print("id bits inside the 1e-5 band:", band)
+
+
+def test_hash_append_rows_only():
+    """count=1 at pos0=lens hashes exactly one new row per (sequence, head)."""
+    w = make_workload("c4", n=(200, 600), B=2, Hkv=2, Hq=8)
+    d = GC.upload(w)
+    ids = torch.full((w.B, w.Hkv, w.n_cap, w.L), 0xAB, dtype=torch.uint8, device=DEV)
+    vn = torch.full((w.B, w.Hkv, w.n_cap), -1.0, dtype=torch.float32, device=DEV)
+    pos0 = d["lens"].clone()
+    GC.gpu_hash(w, d, pos0=pos0, count=1, ids=ids, vnorm=vn)
+    sync()
+    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    for b in range(w.B):
+        p = int(w.lens[b])
+        for h in range(w.Hkv):
+            if p < w.n_cap:
+                GC.check_ids(ids[b, h, p:p + 1], w.K[b, h, p:p + 1], w.W, w.L, w.P, 1)
+                np.testing.assert_allclose(vn[b, h, p], SO.value_norms(w.V[b, h, p]), rtol=2e-6)
+            mask = np.ones(w.n_cap, bool)
+            mask[p:p + 1] = False
+            assert (ids[b, h, mask] == 0xAB).all()
+            assert (vn[b, h, mask] == -1.0).all()
+
+
+# ----------------------------------------------------------------------------- scoring + top-k
+
+SCORE_CASES = [
+    dict(name="c1"),
+    dict(name="c2", n=5000),
+    dict(name="c2", n=4500, Hq=8, Hkv=8),          # one query head per KV head
+    dict(name="c2", n=4500, Hq=16, Hkv=8),         # two
+    dict(name="c2", n=3333, L=32),
+    dict(name="c2", n=2000, L=3, Hq=8, Hkv=2),     # L not a multiple of 4
+    dict(name="c2", n=2000, L=20, P=5, Hq=8, Hkv=2),
+    dict(name="c2", n=2000, tau=0.3),
+    dict(name="c4", n=(1000, 9000), B=4, k=0.02),  # ragged batch
+]
+
+
+def _oracle_ids(w):
+    ids = np.empty((w.B, w.Hkv, w.n_cap, w.L), np.uint8)
+    vn = np.empty((w.B, w.Hkv, w.n_cap), np.float32)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ids[b, h] = SO.hash_keys(w.K[b, h], w.W, w.L, w.P)[0].astype(np.uint8)
+            vn[b, h] = SO.value_norms(w.V[b, h]).astype(np.float32)
+    return ids, vn
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_score_topk_parity(case):
+    """Scorer fed the oracle's IDs and norms, so it is tested on its own."""
+    print("case", case, flush=True)
+    w = make_workload(**case)
+    d = GC.upload(w)
+    ids_np, vn_np = _oracle_ids(w)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    vn = torch.from_numpy(vn_np).to(DEV)
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn)
+    sync()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    s_ref = SO.scores(tables, ids_np, vn_np.astype(np.float64), w.lens)
+    for b in range(w.B):
+        n, k = int(w.lens[b]), int(w.ks[b])
+        for g in range(w.Hq):
+            GC.check_scores(sc[b, g, :n], s_ref[b, g, :n])
+            GC.check_exact_topk(idx[b, g], sc[b, g], k, n)
+            GC.check_set(idx[b, g], s_ref[b, g, :n], k)
+
+
+def test_topk_ties_lower_index_wins():
+    """All keys of a head share one bucket pattern and norm -> equal scores."""
+    w = make_workload("c2", n=3000, Hq=8, Hkv=2, k=100)
+    d = GC.upload(w)
+    ids = torch.zeros(w.B, w.Hkv, w.n_cap, w.L, dtype=torch.uint8, device=DEV)
+    vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+    # KV head 1: second half of the keys gets a larger norm -> they win, ties among them
+    vn[:, 1, 1500:] = 2.0
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn)
+    sync()
+    idx = idx.cpu().numpy()
+    for g in range(w.Hq):
+        h = g // (w.Hq // w.Hkv)
+        expect = np.arange(100) if h == 0 else np.arange(1500, 1600)
+        assert idx[0, g, :100].tolist() == expect.tolist()
+
+
+def test_topk_edge_lengths():
+    """Empty sequence, one key, k = n, k > n (clamped) in one batch."""
+    w = make_workload("c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 777, 300], n_cap=1000, k=5)
+    d = GC.upload(w)
+    ids_np, vn_np = _oracle_ids(w)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    vn = torch.from_numpy(vn_np).to(DEV)
+    ks = torch.tensor([5, 5, 777, 999], dtype=torch.int32, device=DEV)
+    k_max = 1000
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn, ks=ks, k_max=k_max)
+    out = GC.gpu_decode(w, d, idx)
+    sync()
+    idx, sc, out = idx.cpu().numpy(), sc.cpu().numpy(), out.cpu().numpy()
+    assert (idx[0] == -1).all()
+    assert (out[0] == 0).all()
+    assert (idx[1, :, 0] == 0).all() and (idx[1, :, 1:] == -1).all()
+    assert (idx[2, :, :777] == np.arange(777)).all() and (idx[2, :, 777:] == -1).all()
+    assert (idx[3, :, :300] == np.arange(300)).all() and (idx[3, :, 300:] == -1).all()
+    for b in (1, 2, 3):
+        for g in range(w.Hq):
+            GC.check_out(out[b, g], w.q[b, g], w.K[b, g // 4], w.V[b, g // 4], idx[b, g], w.scale)
+
+
+# ----------------------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("k_max", [1, 63, 200, 1024])
+def test_sparse_decode_parity(dtype, k_max):
+    w = make_workload("c2", n=4096, Hq=8, Hkv=2, dtype=dtype)
+    d = GC.upload(w)
+    rng = np.random.default_rng(k_max)
+    idx = np.full((w.B, w.Hq, k_max), -1, np.int32)
+    for g in range(w.Hq):
+        kk = rng.integers(0, k_max + 1) if g else k_max
+        idx[0, g, :kk] = rng.choice(4096, size=kk, replace=False)
+        rng.shuffle(idx[0, g])
+    out = GC.gpu_decode(w, d, torch.from_numpy(idx).to(DEV))
+    sync()
+    out = out.cpu().numpy()
+    for g in range(w.Hq):
+        GC.check_out(out[0, g], w.q[0, g], w.K[0, g // 4], w.V[0, g // 4], idx[0, g], w.scale)
+
+
+# ----------------------------------------------------------------------------- end to end
+
+def _e2e(w, heads=None):
+    """Hash -> score + top-k -> attention on the GPU, checked against the oracle."""
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn)
+    out = GC.gpu_decode(w, d, idx)
+    sync()
+    ids, vn, idx, sc, out = (t.cpu().numpy() for t in (ids, vn, idx, sc, out))
+    group = w.Hq // w.Hkv
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    stats = dict(band_bits=0, id_rows_differ=0, set_diff=0, max_out_err=0.0)
+    for b in range(w.B):
+        n, k = int(w.lens[b]), int(w.ks[b])
+        hs = sorted({g // group for g in (heads if heads is not None else range(w.Hq))})
+        for h in hs:
+            band, diff_rows, ids_ref = GC.check_ids(ids[b, h], w.K[b, h], w.W, w.L, w.P, n,
+                                                    detail=True)
+            stats["band_bits"] += band
+            stats["id_rows_differ"] += len(diff_rows)
+            vref = SO.value_norms(w.V[b, h, :n])
+            np.testing.assert_allclose(vn[b, h, :n], vref, rtol=2e-6)
+            for g in range(h * group, (h + 1) * group):
+                if heads is not None and g not in heads:
+                    continue
+                s_ref = GC.check_scores_both(sc[b, g, :n], tables[b, g], ids[b, h, :n], ids_ref,
+                                             vref, diff_rows)
+                GC.check_exact_topk(idx[b, g], sc[b, g], k, n)
+                stats["set_diff"] += GC.check_set(idx[b, g], s_ref, k)
+                e = GC.check_out(out[b, g], w.q[b, g], w.K[b, h], w.V[b, h], idx[b, g], w.scale)
+                stats["max_out_err"] = max(stats["max_out_err"], e)
+    print("e2e", w.name, stats, flush=True)
+    return stats
+
+
+def test_e2e_c1_full():
+    _e2e(workload("c1"))
+
+
+def test_e2e_c2_full():
+    _e2e(workload("c2"))
+
+
+def test_e2e_c3_full_sampled_heads():
+    _e2e(workload("c3"), heads=[0, 5, 14, 22, 31])
+
+
+def test_e2e_c4_full_sampled_heads():
+    _e2e(workload("c4"), heads=[0, 13, 30])
+
+
+def test_decode_loop_c5():
+    """Prefill 131072 keys, then 256 steps each appending one key/value per KV head;
+    steps 0, 1, 2, 127 and 255 are checked against the oracle on sampled heads."""
+    w = workload("c5")
+    d = GC.upload(w)
+    n0 = int(w.lens[0])
+    ids, vn = GC.gpu_hash(w, d, count=n0)
+    heads = [0, 9, 27]
+    check_steps = {0, 1, 2, 127, 255}
+    lens = d["lens"].clone()
+    ks = d["ks"]
+    keep = {}
+    for t in range(w.steps):
+        # the caller has written row n0+t of K/V (the inputs already hold it); hash it
+        GC.gpu_hash(w, d, pos0=lens, count=1, ids=ids, vnorm=vn)
+        lens += 1
+        q = torch.from_numpy(w.q_steps[t]).to(DEV).to(torch.bfloat16)
+        idx, sc = GC.gpu_score_topk(w, d, ids, vn, lens=lens, q=q)
+        out = GC.gpu_decode(w, d, idx, q=q)
+        if t in check_steps:
+            keep[t] = [x.cpu().numpy() for x in (idx, sc, out)]
+    sync()
+    ids_np, vn_np = ids.cpu().numpy(), vn.cpu().numpy()
+    group = w.Hq // w.Hkv
+    for h in sorted({g // group for g in heads}):
+        n_all = n0 + w.steps
+        band, diff_rows, ids_ref = GC.check_ids(ids_np[0, h], w.K[0, h], w.W, w.L, w.P, n_all,
+                                                detail=True)
+        print("kv head", h, "band bits", band, "rows whose ids differ", diff_rows.tolist(),
+              flush=True)
+        vref = SO.value_norms(w.V[0, h, :n_all])
+        np.testing.assert_allclose(vn_np[0, h, :n_all], vref, rtol=2e-6)
+        for t, (idx, sc, out) in keep.items():
+            n = n0 + t + 1
+            qt = w.q_steps[t]
+            tables = SO.soft_tables(qt, w.W, w.L, w.P, w.tau)
+            for g in heads:
+                if g // group != h:
+                    continue
+                s_ref = GC.check_scores_both(sc[0, g, :n], tables[0, g], ids_np[0, h, :n],
+                                             ids_ref[:n], vref[:n], diff_rows[diff_rows < n])
+                k = int(w.ks[0])
+                GC.check_exact_topk(idx[0, g], sc[0, g], k, n)
+                GC.check_set(idx[0, g], s_ref, k)
+                GC.check_out(out[0, g], qt[0, g], w.K[0, h], w.V[0, h], idx[0, g], w.scale)
+
+
+def test_run_twice_bitwise():
+    w = workload("c2")
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    r1 = [GC.gpu_score_topk(w, d, ids, vn)]
+    r1.append(GC.gpu_decode(w, d, r1[0][0]))
+    ids2, vn2 = GC.gpu_hash(w, d)
+    r2 = [GC.gpu_score_topk(w, d, ids2, vn2)]
+    r2.append(GC.gpu_decode(w, d, r2[0][0]))
+    sync()
+    assert torch.equal(ids, ids2) and torch.equal(vn, vn2)
+    assert torch.equal(r1[0][0], r2[0][0]) and torch.equal(r1[0][1], r2[0][1])
+    assert torch.equal(r1[1], r2[1])
