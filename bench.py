@@ -1,0 +1,387 @@
+"""Benchmark of the SOCKET decode hot path on one MI355X.
+
+One step = one decode step of the GQA 32/8 workload at n = 32768 cached keys
+(d = 128, L = 64 tables x P = 8 planes, tau = 0.5, k = 656 = ceil(2% of n)):
+
+  append  : hash the new key of every KV head and store its value norm
+  tables  : float64 query projections -> per-table soft-bucket half-tables
+  score   : soft-count score of all n + 1 keys for the 32 query heads
+  top-k   : top-656 keys per query head
+  attend  : exact attention of each query head over its selected keys
+
+`value` is keys scored+selected per second: 32 query heads x (n + 1) keys per
+step, divided by the wall time of K steps bracketed by device syncs.  Inputs
+are resident in HBM.  The cache is replicated `--replicas` times (one replica
+per step, round robin, like successive layers) so the 256 MiB Infinity Cache
+cannot serve a step from the previous one.
+
+Also reported: per-kernel GPU times from HIP events (taken in a second pass
+whose launches queue up behind a long matrix product, so launch gaps do not
+enter the event pairs), the 128K-key step latency, the prefill hashing rate
+against the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+SCORER_SRC = os.path.join(ROOT, "soft_lsh_token_amd", "csrc", "score_topk.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "scorer_c2_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=40)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-128k", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline")
+    return p.parse_args()
+
+
+class Case:
+    """Device buffers and pre-marshalled C calls of one decode workload."""
+
+    def __init__(self, name, replicas, lib, torch, S):
+        from soft_lsh_token_amd.inputs import make_workload
+        t0 = time.time()
+        self.w = w = make_workload(name, steps=1)   # one extra row: the appended key
+        log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s (n={int(w.lens[0])}, "
+            f"n_cap={w.n_cap}, replicas={replicas})")
+        dev = "cuda:0"
+        bf = torch.bfloat16
+        self.n = int(w.lens[0])
+        self.B, self.Hq, self.Hkv, self.L, self.P = w.B, w.Hq, w.Hkv, w.L, w.P
+        self.k = int(w.ks[0])
+        K0 = torch.from_numpy(w.K).to(dev).to(bf)
+        V0 = torch.from_numpy(w.V).to(dev).to(bf)
+        self.K = [K0] + [K0.clone() for _ in range(replicas - 1)]
+        self.V = [V0] + [V0.clone() for _ in range(replicas - 1)]
+        del K0, V0
+        self.W = torch.from_numpy(w.W).to(dev).to(bf)
+        self.q = torch.from_numpy(w.q).to(dev).to(bf)
+        self.pos_prefill = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        self.pos_append = torch.full((w.B,), self.n, dtype=torch.int32, device=dev)
+        self.lens = torch.full((w.B,), self.n + 1, dtype=torch.int32, device=dev)
+        self.ks = torch.from_numpy(w.ks).to(dev)
+        self.ids = [S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, dev) for _ in range(replicas)]
+        self.vn = [torch.empty(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
+                   for _ in range(replicas)]
+        self.idx = torch.empty(w.B, w.Hq, self.k, dtype=torch.int32, device=dev)
+        self.scores = torch.empty(w.B, w.Hq, w.n_cap, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+        sws = S.socket_score_topk_workspace(w.B, w.Hq, w.n_cap, w.L, w.P, self.k)
+        dws = S.socket_sparse_decode_workspace(w.B, w.Hq, w.d, self.k)
+        self.sws = S.alloc_workspace(sws, dev)
+        self.dws = S.alloc_workspace(dws, dev)
+        self.sws_p = self.sws.data_ptr() + (-self.sws.data_ptr()) % 256
+        self.dws_p = self.dws.data_ptr() + (-self.dws.data_ptr()) % 256
+        self.sws_n, self.dws_n = sws, dws
+        self.replicas = replicas
+        self.lib = lib
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self._prep()
+
+    def _prep(self):
+        w, lib = self.w, self.lib
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        st = vp(self.stream)
+        self.c_append, self.c_prefill, self.c_score, self.c_decode = [], [], [], []
+        for r in range(self.replicas):
+            K, V, ids, vn = self.K[r].data_ptr(), self.V[r].data_ptr(), self.ids[r].data_ptr(), \
+                self.vn[r].data_ptr()
+            common = (vp(K), vp(V), 1, w.B, w.Hkv, w.d, i64(w.n_cap))
+            self.c_prefill.append(common + (vp(self.pos_prefill.data_ptr()), self.n,
+                                             vp(self.W.data_ptr()), w.L, w.P, vp(ids), vp(vn), st))
+            self.c_append.append(common + (vp(self.pos_append.data_ptr()), 1,
+                                            vp(self.W.data_ptr()), w.L, w.P, vp(ids), vp(vn), st))
+            self.c_score.append((w.B, w.Hq, w.Hkv, w.L, w.P, vp(ids), vp(vn),
+                                 vp(self.lens.data_ptr()), i64(w.n_cap),
+                                 vp(self.scores.data_ptr()), vp(self.sws_p),
+                                 ctypes.c_size_t(self.sws_n), st))
+            self.c_decode.append((vp(self.q.data_ptr()), vp(K), vp(V), 1, w.B, w.Hq, w.Hkv, w.d,
+                                  i64(w.n_cap), vp(self.idx.data_ptr()), self.k,
+                                  ctypes.c_float(w.scale), vp(self.out.data_ptr()),
+                                  vp(self.dws_p), ctypes.c_size_t(self.dws_n), st))
+        self.c_tables = (vp(self.q.data_ptr()), 1, w.B, w.Hq, w.d, vp(self.W.data_ptr()), w.L,
+                         w.P, ctypes.c_float(w.tau), i64(w.n_cap), vp(self.sws_p),
+                         ctypes.c_size_t(self.sws_n), st)
+        self.c_topk = (w.B, w.Hq, w.L, vp(self.scores.data_ptr()), vp(self.lens.data_ptr()),
+                       i64(w.n_cap), vp(self.ks.data_ptr()), self.k, vp(self.idx.data_ptr()),
+                       vp(self.sws_p), ctypes.c_size_t(self.sws_n), st)
+
+    @staticmethod
+    def _ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} returned status {rc}")
+
+    def prefill(self, r):
+        self._ok(self.lib.socket_hash_keys(*self.c_prefill[r]), "socket_hash_keys")
+
+    def step(self, r, ev=None):
+        """One decode step on replica r; ev = list of 6 events to bracket the 5 stages."""
+        lib = self.lib
+        if ev: ev[0].record()
+        rc = lib.socket_hash_keys(*self.c_append[r])
+        if ev: ev[1].record()
+        rc |= lib.socket_soft_tables(*self.c_tables)
+        if ev: ev[2].record()
+        rc |= lib.socket_score(*self.c_score[r])
+        if ev: ev[3].record()
+        rc |= lib.socket_topk(*self.c_topk)
+        if ev: ev[4].record()
+        rc |= lib.socket_sparse_decode(*self.c_decode[r])
+        if ev: ev[5].record()
+        if rc:
+            raise RuntimeError(f"a decode-step call failed (status bits {rc})")
+
+    def free(self):
+        for a in ("K", "V", "ids", "vn"):
+            setattr(self, a, None)
+
+
+def busy_prologue(torch, ms_target=40.0):
+    """Queue ~ms_target of matrix products so the launches that follow pile up
+    behind them and then run back to back."""
+    a = torch.randn(8192, 8192, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda:0", dtype=torch.bfloat16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(); c = a @ b; e1.record(); torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 0.05)
+    reps = int(math.ceil(ms_target / one))
+    return lambda: [a @ b for _ in range(reps)], reps * one
+
+
+def timed_steps(case, torch, steps, warmup):
+    for i in range(warmup):
+        case.step(i % case.replicas)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        case.step(i % case.replicas)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def per_kernel(case, torch, steps):
+    """Mean GPU time of each stage from HIP events (launches queued behind a busy prologue)."""
+    run_busy, busy_ms = busy_prologue(torch)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    e_all0, e_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    run_busy()
+    t0 = time.perf_counter()
+    e_all0.record()
+    for i in range(steps):
+        case.step(i % case.replicas, evs[i])
+    e_all1.record()
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    if host_ms > busy_ms:
+        log(f"[bench] warning: host enqueue {host_ms:.1f} ms exceeded the busy prologue "
+            f"{busy_ms:.1f} ms; per-kernel times may include launch gaps")
+    names = ["append", "tables", "score", "topk", "attend"]
+    t = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            t[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    gpu_step_us = e_all0.elapsed_time(e_all1) * 1e3 / steps
+    return {n: float(np.mean(v)) for n, v in t.items()}, gpu_step_us, host_ms * 1e3 / steps
+
+
+def prefill_rate(case, torch, reps=5):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    case.prefill(0)
+    torch.cuda.synchronize()
+    times = []
+    for r in range(reps):
+        e0.record(); case.prefill(r % case.replicas); e1.record(); torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = float(np.median(times))
+    w = case.w
+    keys = w.B * w.Hkv * case.n
+    flops = 2.0 * keys * w.d * w.L * w.P
+    hbm = keys * (2 * w.d * 2 + w.L + 4)   # K and V rows read, ids and norm written
+    return dict(keys=keys, seconds=t, tflops=flops / t / 1e12,
+                mfma_frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, hbm_gbs=hbm / t / 1e9)
+
+
+def scorer_bytes(case):
+    """Algorithmic bytes of one scorer launch: per KV key its L one-byte IDs and
+    its float32 norm are read and G float32 scores are written."""
+    w = case.w
+    G = w.Hq // w.Hkv
+    kv_keys = w.B * w.Hkv * (case.n + 1)
+    return kv_keys * (w.L * w.P // 8 + 4 + 4 * G), kv_keys
+
+
+def counters_traffic(launch_bytes):
+    """HBM traffic of the scorer from committed rocprofv3 counters, if they were
+    taken on the current scorer source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+        with open(SCORER_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if c.get("source_sha256") != sha:
+            return None
+        return float(c["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the 32K decode step."""
+    from oracle import socket_oracle as SO
+    from soft_lsh_token_amd.inputs import make_workload
+    w = make_workload("c2", steps=1)
+    n = int(w.lens[0])
+    log("[bench] cpu baseline: oracle prefill hash (untimed)")
+    ids = np.empty((w.B, w.Hkv, w.n_cap, w.L), dtype=np.int64)
+    for h in range(w.Hkv):
+        ids[0, h, :n] = SO.hash_keys(w.K[0, h, :n], w.W, w.L, w.P)[0]
+    vn = np.zeros((w.B, w.Hkv, w.n_cap))
+    vn[0, :, :n] = SO.value_norms(w.V[0, :, :n])
+    lens = np.array([n + 1], dtype=np.int32)
+    # one step = append hash of the new key of every KV head + the decode step
+    # (tables, scores, top-k, attention); the sample is as many query heads of
+    # successive steps as fit in the time budget
+    heads_done, t_used, c_used = 0, 0.0, 0.0
+    group = w.Hq // w.Hkv
+    while t_used < seconds and heads_done < 4 * w.Hq:
+        g = heads_done % w.Hq
+        h = g // group
+        c0, t0 = time.process_time(), time.perf_counter()
+        ids[0, h, n] = SO.hash_keys(w.K[0, h, n:n + 1], w.W, w.L, w.P)[0][0]
+        vn[0, h, n] = SO.value_norms(w.V[0, h, n])
+        tab = SO.soft_tables(w.q[0, g], w.W, w.L, w.P, w.tau)
+        s = SO.scores(tab[None, None], ids[:, h:h + 1], vn[:, h:h + 1], lens)[0, 0]
+        sel = SO.topk(s, int(w.ks[0]), n + 1)
+        SO.sparse_attention(w.q[0, g], w.K[0, h], w.V[0, h], sel, w.scale)
+        t_used += time.perf_counter() - t0
+        c_used += time.process_time() - c0
+        heads_done += 1
+    keys = heads_done * (n + 1)
+    cores = max(1, int(round(c_used / max(t_used, 1e-9))))
+    return dict(value=keys / t_used, unit="keys/s", cores=cores, kind="oracle",
+                sample=f"{heads_done} query heads x {n + 1} keys of the 32K decode step "
+                       f"(append hash + tables + scores + top-k + attention per head), "
+                       f"{t_used:.1f}s wall; host affinity {len(os.sched_getaffinity(0))} cpus")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has "
+              f"no multi-GPU mode: every run uses exactly one GPU).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import soft_lsh_token_amd as S
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible; bench.py needs an MI355X")
+    lib = S.lib()
+    torch.cuda.set_device(0)
+
+    case = Case("c2", args.replicas, lib, torch, S)
+    for r in range(case.replicas):
+        case.prefill(r)
+    torch.cuda.synchronize()
+    pre32 = prefill_rate(case, torch)
+    log(f"[bench] prefill hash 32K: {pre32}")
+    sec = timed_steps(case, torch, args.steps, args.warmup)
+    log(f"[bench] 32K step wall {sec * 1e6:.1f} us")
+    stages, gpu_step_us, host_step_us = per_kernel(case, torch, min(args.steps, 200))
+    log(f"[bench] 32K per-kernel us {stages}; gpu step {gpu_step_us:.1f} us; "
+        f"host enqueue {host_step_us:.1f} us/step")
+    launch_bytes, kv_keys = scorer_bytes(case)
+    scorer_s = stages["score"] * 1e-6
+    achieved = launch_bytes / scorer_s / 1e9
+    traffic = counters_traffic(launch_bytes)
+    w = case.w
+    keys_per_step = w.B * w.Hq * (case.n + 1)
+    topk_bytes = keys_per_step * 4
+    extra32 = dict(
+        step_us_wall=sec * 1e6, step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
+        kernel_us=stages,
+        score_topk_us=stages["tables"] + stages["score"] + stages["topk"],
+        topk_gbs=topk_bytes / (stages["topk"] * 1e-6) / 1e9,
+        prefill=pre32)
+    case.free()
+    del case
+    torch.cuda.empty_cache()
+
+    extra128 = None
+    if not args.no_128k:
+        c3 = Case("c3", max(4, args.replicas // 5), lib, torch, S)
+        for r in range(c3.replicas):
+            c3.prefill(r)
+        torch.cuda.synchronize()
+        pre128 = prefill_rate(c3, torch)
+        log(f"[bench] prefill hash 128K (the decode-loop prefill): {pre128}")
+        sec3 = timed_steps(c3, torch, max(20, args.steps // 4), max(5, args.warmup // 4))
+        st3, gpu3, host3 = per_kernel(c3, torch, max(20, args.steps // 4))
+        lb3, _ = scorer_bytes(c3)
+        extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, kernel_us=st3,
+                        keys_per_s=c3.w.B * c3.w.Hq * (c3.n + 1) / sec3,
+                        scorer_gbs=lb3 / (st3["score"] * 1e-6) / 1e9,
+                        prefill=pre128)
+        log(f"[bench] 128K: {extra128}")
+        c3.free()
+        del c3
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    line = {
+        "metric": "keys scored+selected/s per GPU (32K-key GQA decode step)",
+        "value": keys_per_step / sec,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GQA 32/8 decode step, n=32768 (+1 appended key), d=128, L=64, "
+                               "P=8, tau=0.5, k=656, batch 1",
+                   "global_batch": 1, "seq_len": 32768, "parallelism": "single GPU",
+                   "replicas": args.replicas},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "scorer_kernel (soft-count scores + first-digit histogram)",
+                     "bytes_per_launch": launch_bytes, "kv_keys_per_launch": kv_keys},
+        "cpu_baseline": cpu,
+        "extra": {"ctx32k": extra32, "ctx128k": extra128},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

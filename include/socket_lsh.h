@@ -24,8 +24,7 @@
  *     q         [B][Hq][d]              same dtype as K
  *     W         [L*P][d]                same dtype as K; rows l*P..l*P+P-1 are
  *                                       the P hyperplanes of table l
- *     ids       [B][Hkv][n_cap][L]      uint8 (one bucket ID per table per key,
- *                                       bit j = sign of plane j; P <= 8)
+ *     ids       bucket-ID cache, socket_ids_bytes() bytes, tiled (below)
  *     vnorm     [B][Hkv][n_cap]         float32
  *     lens, ks  [B]                     int32, device
  *     idx       [B][Hq][k_max]          int32
@@ -34,7 +33,18 @@
  * - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
  *   Hq must be a multiple of Hkv; socket_score_topk needs Hq / Hkv in
  *   {1, 2, 4}.
- * - d must be 128.  1 <= P <= 8, 1 <= L <= 256.
+ * - d must be 128.  1 <= P <= 8, 1 <= L <= 128, 1 <= k_max <= 65536.
+ *
+ * Bucket-ID cache layout
+ * ----------------------
+ * The bucket ID of table l is one byte (bit j = sign of plane j).  The IDs of
+ * a key are cut into 16 words of TL bytes, TL = 1, 2, 4 or 8 the smallest
+ * power of two with 16*TL >= L; word w holds tables w*TL .. w*TL+TL-1 (byte
+ * b of the word = table w*TL + b; tables >= L read as 0).  Keys are tiled in
+ * groups of 64: key i of KV row r = b*Hkv + h lies in group i/64 at t = i%64,
+ * t = 16*kg + x, and its word w is stored at byte offset
+ *   ((r * ceil(n_cap/64) + i/64) * 1024 + ((x - w) mod 16) * 64 + 16*kg + w) * TL.
+ * This order lets the scorer read 64 consecutive words per load.
  * - Errors are reported as negative return codes before anything is
  *   enqueued (argument checks), or as SOCKET_EHIP when a launch fails.
  *   Nothing throws or aborts.  socket_status_string() names a code.
@@ -65,20 +75,26 @@ const char* socket_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int socket_version(void);
 
+/* Size in bytes of the bucket-ID cache for B x Hkv rows of n_cap keys
+ * (0 for invalid sizes). */
+size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L);
+
 /*
  * socket_hash_keys -- Algorithm 1 (SOCKET Sec. 4.1; bucket ID = sign pattern
  * of W^(l) k, Appendix B.2) plus the value-norm cache (Sec. 1 "Key Idea").
  *
  * For every sequence b, KV head h and position i in [pos0[b], pos0[b]+count):
- *   ids[b][h][i][l] = sum_j [ <W[l*P+j], K[b][h][i]> > 0 ] << j
- *   vnorm[b][h][i]  = || V[b][h][i] ||_2
+ *   ID of table l of key i = sum_j [ <W[l*P+j], K[b][h][i]> > 0 ] << j
+ *   vnorm[b][h][i]         = || V[b][h][i] ||_2
  * The projection is accumulated in float32 (bf16 products are exact in
  * float32).  A projection of exactly zero gives bit 0.  Positions at or past
  * n_cap are skipped.  Prefill passes pos0 = 0 and count = n; the decode-time
  * append passes pos0 = current length and count = 1 after the caller has
  * written the new row of K and V.
  *
- * pos0 is a device int32 array [B].  Other rows of ids/vnorm are untouched.
+ * pos0 is a device int32 array [B].  ids (socket_ids_bytes(B, Hkv, n_cap, L)
+ * bytes) receives all 16 words of every hashed key in the tiled layout;
+ * other keys and other rows of vnorm are untouched.
  */
 int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, int d,
                      int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
@@ -95,7 +111,7 @@ size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, i
  *   p_l(c)    = softmax over buckets c of (sum_j s_j(c) u[l][j]) / tau,
  *               s_j(c) = +1 if bit j of c is set else -1
  *               (equivalently prod_j sigmoid(2 s_j(c) u[l][j] / tau))
- *   s_i       = vnorm[b][h][i] * sum_l p_l(ids[b][h][i][l])   for i < lens[b]
+ *   s_i       = vnorm[b][h][i] * sum_l p_l(ID of table l of key i)   for i < lens[b]
  *   idx[b][g] = the min(ks[b], lens[b]) keys with the largest s_i; among
  *               equal scores the lower index wins.  The indices are written
  *               in ascending order and the row is padded with -1 up to k_max.

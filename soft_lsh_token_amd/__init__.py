@@ -5,10 +5,12 @@ The compute lives in the HIP library ``libsocket_lsh.so`` (C ABI in
 its entry points.  Importing the package does not load the library; the
 first call does, and raises if the library has not been built.
 """
+from . import layout  # noqa: F401
 from ._lib import (  # noqa: F401
-    SOCKET_BF16, SOCKET_F32, SocketError, alloc_workspace, lib, socket_hash_keys,
-    socket_score_topk, socket_score_topk_workspace, socket_sparse_decode,
-    socket_sparse_decode_workspace,
+    SOCKET_BF16, SOCKET_F32, SocketError, alloc_ids, alloc_workspace, lib, socket_hash_keys,
+    socket_ids_bytes, socket_score,
+    socket_score_topk, socket_score_topk_workspace, socket_soft_tables, socket_sparse_decode,
+    socket_sparse_decode_workspace, socket_topk,
 )
 
 __version__ = "0.1.0"

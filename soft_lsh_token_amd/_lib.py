@@ -26,10 +26,14 @@ _vp, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c
 _SIGS = {
     "socket_status_string": (ctypes.c_char_p, [_i]),
     "socket_version": (_i, []),
+    "socket_ids_bytes": (_sz, [_i, _i, _i64, _i]),
     "socket_hash_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp, _vp]),
     "socket_score_topk_workspace": (_sz, [_i, _i, _i64, _i, _i, _i]),
     "socket_score_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _i64, _vp,
                                _i, _vp, _vp, _vp, _sz, _vp]),
+    "socket_soft_tables": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _f, _i64, _vp, _sz, _vp]),
+    "socket_score": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "socket_topk": (_i, [_i, _i, _i, _vp, _vp, _i64, _vp, _i, _vp, _vp, _sz, _vp]),
     "socket_sparse_decode_workspace": (_sz, [_i, _i, _i, _i]),
     "socket_sparse_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i64, _vp, _i, _f, _vp, _vp,
                                   _sz, _vp]),
@@ -101,6 +105,23 @@ def _stream(t: torch.Tensor, stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def socket_ids_bytes(B: int, Hkv: int, n_cap: int, L: int) -> int:
+    return int(lib().socket_ids_bytes(B, Hkv, n_cap, L))
+
+
+def alloc_ids(B: int, Hkv: int, n_cap: int, L: int, device) -> torch.Tensor:
+    """A zeroed bucket-ID cache (tiled layout, see soft_lsh_token_amd.layout)."""
+    from .layout import ids_shape
+    t = torch.zeros(ids_shape(B, Hkv, n_cap, L), dtype=torch.uint8, device=device)
+    assert t.numel() == socket_ids_bytes(B, Hkv, n_cap, L)
+    return t
+
+
+def _ids(ids: torch.Tensor, B: int, Hkv: int, n_cap: int, L: int) -> int:
+    from .layout import ids_shape
+    return _dev(ids, "ids", torch.uint8, ids_shape(B, Hkv, n_cap, L))
+
+
 def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
                      vnorm: torch.Tensor, pos0: torch.Tensor, count: int, L: int, P: int,
                      stream=None) -> None:
@@ -110,7 +131,7 @@ def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: tor
     rc = lib().socket_hash_keys(
         _dev(K, "K"), _dev(V, "V", K.dtype, K.shape), dt, B, Hkv, d, n_cap,
         _dev(pos0, "pos0", torch.int32, (B,)), int(count), _dev(W, "W", K.dtype, (L * P, d)),
-        L, P, _dev(ids, "ids", torch.uint8, (B, Hkv, n_cap, L)),
+        L, P, _ids(ids, B, Hkv, n_cap, L),
         _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _stream(K, stream))
     _check("socket_hash_keys", rc)
 
@@ -140,7 +161,7 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
                       ws: torch.Tensor | None = None, stream=None) -> None:
     """Soft-LSH scores of every key and the top-k indices per query head."""
     B, Hq, d = q.shape
-    _, Hkv, n_cap, _ = ids.shape
+    Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
     need = socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max)
     if ws is None:
         ws = alloc_workspace(need, q.device)
@@ -148,12 +169,49 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
     sptr = None if scores is None else _dev(scores, "scores", torch.float32, (B, Hq, n_cap))
     rc = lib().socket_score_topk(
         _dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P,
-        float(tau), _dev(ids, "ids", torch.uint8, (B, Hkv, n_cap, L)),
+        float(tau), _ids(ids, B, Hkv, n_cap, L),
         _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
         _dev(lens, "lens", torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)),
         int(k_max), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr, wptr, wbytes,
         _stream(q, stream))
     _check("socket_score_topk", rc)
+
+
+def socket_soft_tables(q: torch.Tensor, W: torch.Tensor, L: int, P: int, tau: float, n_cap: int,
+                       ws: torch.Tensor, stream=None) -> None:
+    """Algorithm 2, first half: the per-table soft-bucket half-tables (into ws)."""
+    B, Hq, d = q.shape
+    wptr, wbytes = _ws_ptr(ws, 0)
+    rc = lib().socket_soft_tables(_dev(q, "q"), _dtype_code(q), B, Hq, d,
+                                  _dev(W, "W", q.dtype, (L * P, d)), L, P, float(tau), int(n_cap),
+                                  wptr, wbytes, _stream(q, stream))
+    _check("socket_soft_tables", rc)
+
+
+def socket_score(ids: torch.Tensor, vnorm: torch.Tensor, lens: torch.Tensor, Hq: int, L: int,
+                 P: int, scores: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """Algorithm 2, second half: soft-count scores (needs socket_soft_tables on ws first)."""
+    B, Hkv, n_cap = vnorm.shape
+    wptr, wbytes = _ws_ptr(ws, 0)
+    rc = lib().socket_score(B, Hq, Hkv, L, P, _ids(ids, B, Hkv, n_cap, L),
+                            _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
+                            _dev(lens, "lens", torch.int32, (B,)), n_cap,
+                            _dev(scores, "scores", torch.float32, (B, Hq, n_cap)), wptr, wbytes,
+                            _stream(ids, stream))
+    _check("socket_score", rc)
+
+
+def socket_topk(scores: torch.Tensor, lens: torch.Tensor, ks: torch.Tensor, L: int,
+                idx: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """Algorithm 3: top-k per query head from scores + the histogram socket_score left in ws."""
+    B, Hq, n_cap = scores.shape
+    k_max = idx.shape[-1]
+    wptr, wbytes = _ws_ptr(ws, 0)
+    rc = lib().socket_topk(B, Hq, L, _dev(scores, "scores", torch.float32), _dev(lens, "lens",
+                           torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)), k_max,
+                           _dev(idx, "idx", torch.int32, (B, Hq, k_max)), wptr, wbytes,
+                           _stream(scores, stream))
+    _check("socket_topk", rc)
 
 
 def socket_sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,

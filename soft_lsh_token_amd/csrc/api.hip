@@ -8,8 +8,9 @@ using namespace socketlsh;
 
 namespace {
 
-constexpr int kMaxL = 256;
-constexpr int kMaxKmax = 1 << 20;
+constexpr int kMaxL = 128;       // 16 ID words of at most 8 tables each
+constexpr int kMaxScoreL = 128;
+constexpr int kMaxKmax = 1 << 16;  // 1024 attention splits of 64 keys
 
 bool group_ok(int Hq, int Hkv) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
@@ -50,6 +51,11 @@ int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, in
                                    static_cast<hipStream_t>(stream)));
 }
 
+size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L) {
+  if (B <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || L > kMaxL) return 0;
+  return (size_t)B * Hkv * ids_groups(n_cap) * 64 * ids_key_bytes(L);
+}
+
 size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, int k_max) {
   (void)P;
   (void)k_max;
@@ -68,7 +74,7 @@ static int check_sizes(int B, int Hq, int Hkv, int L, int P, int64_t n_cap) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
   if (Hq % Hkv) return SOCKET_EINVAL;
   if (!group_ok(Hq, Hkv)) return SOCKET_EUNSUPPORTED;
-  if (P > 8 || L > kMaxL) return SOCKET_EUNSUPPORTED;
+  if (P > 8 || L > kMaxScoreL) return SOCKET_EUNSUPPORTED;
   if (n_cap >= ((int64_t)1 << 31) || (int64_t)B * Hq * n_cap >= ((int64_t)1 << 40))
     return SOCKET_EUNSUPPORTED;
   return SOCKET_OK;

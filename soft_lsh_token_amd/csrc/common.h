@@ -12,6 +12,29 @@ constexpr int kHistShift = 21;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Bucket-ID cache layout.  The IDs of one key are cut into 16 words of TL
+// bytes (word j = tables j*TL .. j*TL+TL-1; tables >= L read as 0), TL the
+// smallest power of two with 16*TL >= L.  Keys are tiled in groups of 64;
+// inside a group, key t = 16*kg + x stores word j at word slot
+// ((x - j) mod 16) * 64 + kg * 16 + j.  With this diagonal order the 64 lanes
+// of a scorer wave, lane (kg, j) taking word j of key 16*kg + (j + d) mod 16
+// in round d, read 64 consecutive words.
+__host__ __device__ constexpr int ids_word_bytes(int L) {
+  return L <= 16 ? 1 : L <= 32 ? 2 : L <= 64 ? 4 : 8;
+}
+__host__ __device__ constexpr int ids_key_bytes(int L) { return 16 * ids_word_bytes(L); }
+__host__ __device__ inline int64_t ids_groups(int64_t n_cap) { return (n_cap + 63) / 64; }
+
+// Byte offset of word j of key `key` of KV row bh.
+__host__ __device__ inline int64_t ids_word_offset(int64_t bh, int64_t n_cap, int L, int64_t key,
+                                                   int j) {
+  const int TL = ids_word_bytes(L);
+  const int64_t gi = key >> 6;
+  const int t = (int)(key & 63), kg = t >> 4, x = t & 15;
+  const int slot = (((x - j) & 15) << 6) | (kg << 4) | j;
+  return ((bh * ids_groups(n_cap) + gi) * 1024 + slot) * TL;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

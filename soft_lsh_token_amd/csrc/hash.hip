@@ -3,7 +3,7 @@
 // Appendix B.2: the bucket ID is the sign pattern of W^(l) k).
 //
 // Two projection paths:
-//  * hash_mfma_kernel: bf16 keys, P = 8, L in {8, 16, 32, 64}.  The projection
+//  * hash_mfma_kernel: bf16 keys, P = 8, L in {16, 32, 64}.  The projection
 //    Z = W K^T is a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
 //    accumulation).  W stays in registers for the whole workgroup (each wave
 //    owns 8 tables = 64 planes = two 32-row MFMA tiles); 32-key tiles of K
@@ -22,23 +22,29 @@ namespace socketlsh {
 // ---------------------------------------------------------------- generic path
 
 template <typename T>
-__device__ __forceinline__ float load_elem(const T* p, int64_t i);
+__device__ __forceinline__ void load8(const T* p, float* f);
 template <>
-__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* f) {
+  unpack_bf16x8(*reinterpret_cast<const uint4*>(p), f);
+}
 template <>
-__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
-  return __uint_as_float((uint32_t)p[i] << 16);
+__device__ __forceinline__ void load8<float>(const float* p, float* f) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// grid: B*Hkv*count blocks (block = one key), 256 threads.
+// grid: B*Hkv*count blocks (block = one key), kGenThreads threads; thread t
+// projects planes t, t + kGenThreads, ...  The 128-element plane row is read
+// with vector loads, all issued before the dot product.
+constexpr int kGenThreads = 512;
+
 template <typename T>
-__global__ __launch_bounds__(256) void hash_generic_kernel(const T* __restrict__ K,
-                                                           const T* __restrict__ V, int Hkv,
-                                                           int64_t n_cap,
-                                                           const int32_t* __restrict__ pos0,
-                                                           int count, const T* __restrict__ W,
-                                                           int L, int P, uint8_t* __restrict__ ids,
-                                                           float* __restrict__ vnorm) {
+__global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
+    const T* __restrict__ K, const T* __restrict__ V, int Hkv, int64_t n_cap,
+    const int32_t* __restrict__ pos0, int count, const T* __restrict__ W, int L, int P,
+    uint8_t* __restrict__ ids, float* __restrict__ vnorm) {
   const int c = blockIdx.x % count;
   const int bh = blockIdx.x / count;
   const int b = bh / Hkv;
@@ -48,25 +54,47 @@ __global__ __launch_bounds__(256) void hash_generic_kernel(const T* __restrict__
   __shared__ float kf[kHead];
   __shared__ uint32_t bits[256];
   const int tid = threadIdx.x;
-  if (tid < kHead) kf[tid] = load_elem<T>(K, row * kHead + tid);
-  bits[tid] = 0u;
+  if (tid < kHead / 8) load8<T>(K + row * kHead + 8 * tid, kf + 8 * tid);
+  if (tid < 256) bits[tid] = 0u;
   __syncthreads();
   const int planes = L * P;
-  for (int pl = tid; pl < planes; pl += blockDim.x) {
+  for (int pl = tid; pl < planes; pl += kGenThreads) {
+    const T* wr = W + (int64_t)pl * kHead;
     float z = 0.f;
-    const int64_t wrow = (int64_t)pl * kHead;
-#pragma unroll 8
-    for (int t = 0; t < kHead; ++t) z = fmaf(load_elem<T>(W, wrow + t), kf[t], z);
+#pragma unroll
+    for (int h0 = 0; h0 < kHead; h0 += kHead / 2) {
+      float wf[kHead / 2];
+#pragma unroll
+      for (int t = 0; t < kHead / 2; t += 8) load8<T>(wr + h0 + t, wf + t);
+#pragma unroll
+      for (int t = 0; t < kHead / 2; ++t) z = fmaf(wf[t], kf[h0 + t], z);
+    }
     if (z > 0.f) atomicOr(&bits[pl / P], 1u << (pl % P));
   }
-  if (tid < 64) {
-    const float a = load_elem<T>(V, row * kHead + tid);
-    const float b2 = load_elem<T>(V, row * kHead + 64 + tid);
-    const float ss = wave_sum(fmaf(a, a, b2 * b2));
+  if (tid < 16) {
+    float f[8];
+    load8<T>(V + row * kHead + 8 * tid, f);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    ss = row16_sum(ss);
     if (tid == 0) vnorm[row] = sqrtf(ss);
   }
   __syncthreads();
-  for (int t = tid; t < L; t += blockDim.x) ids[row * L + t] = (uint8_t)bits[t];
+  // word j of this key: tables j*TL .. j*TL+TL-1 (0 past L), in the tiled layout
+  const int TL = ids_word_bytes(L);
+  if (tid < 16) {
+    uint64_t w = 0;
+    for (int b8 = 0; b8 < TL; ++b8) {
+      const int l = tid * TL + b8;
+      if (l < L) w |= (uint64_t)(bits[l] & 255u) << (8 * b8);
+    }
+    uint8_t* dst = ids + ids_word_offset(bh, n_cap, L, pos, tid);
+    if (TL == 1) *dst = (uint8_t)w;
+    else if (TL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+    else if (TL == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w;
+    else *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w, (uint32_t)(w >> 32));
+  }
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -161,9 +189,24 @@ __global__ __launch_bounds__(NW * 64) void hash_mfma_kernel(const uint16_t* __re
       word |= (acc0[r] > 0.f ? 1u : 0u) << ((r >> 3) * 8 + (r & 7));
       word |= (acc1[r] > 0.f ? 1u : 0u) << (16 + (r >> 3) * 8 + (r & 7));
     }
+    // the 4 tables 8w + 4*half .. +3 of key pos, as IDs words of the tiled layout
     const int64_t pos = t0 + col;
-    if (pos < end)
-      *reinterpret_cast<uint32_t*>(ids + (rowbase + pos) * L + 8 * wave + 4 * half) = word;
+    if (pos < end) {
+      constexpr int TL = ids_word_bytes(L);
+      const int t0w = (8 * wave + 4 * half) / TL;  // first word index
+      if constexpr (TL == 4) {
+        *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) = word;
+      } else if constexpr (TL == 2) {
+        *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) =
+            (uint16_t)word;
+        *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w + 1)) =
+            (uint16_t)(word >> 16);
+      } else {
+#pragma unroll
+        for (int b8 = 0; b8 < 4; ++b8)
+          ids[ids_word_offset(bh, n_cap, L, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+      }
+    }
   }
 }
 
@@ -175,7 +218,8 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
   if (count <= 0 || B <= 0 || Hkv <= 0) return hipSuccess;
   const int64_t rows = (int64_t)B * Hkv * count;
   const bool bf16 = dtype == 1;
-  const bool mfma_ok = bf16 && P == 8 && (L == 8 || L == 16 || L == 32 || L == 64) && count >= 64;
+  // the MFMA path covers every ID word when L is 16, 32 or 64
+  const bool mfma_ok = bf16 && P == 8 && (L == 16 || L == 32 || L == 64) && count >= 64;
   if (mfma_ok) {
     const int kpb = 1024;
     const int nblk = (count + kpb - 1) / kpb;
@@ -184,7 +228,6 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     const uint16_t* Vb = static_cast<const uint16_t*>(V);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     switch (L) {
-      case 8: hash_mfma_kernel<1><<<grid, 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
       case 16: hash_mfma_kernel<2><<<grid, 128, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
       case 32: hash_mfma_kernel<4><<<grid, 256, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
       default: hash_mfma_kernel<8><<<grid, 512, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
@@ -193,11 +236,11 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
   }
   const dim3 grid((unsigned)rows);
   if (bf16)
-    hash_generic_kernel<uint16_t><<<grid, 256, 0, s>>>(
+    hash_generic_kernel<uint16_t><<<grid, kGenThreads, 0, s>>>(
         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), Hkv, n_cap, pos0, count,
         static_cast<const uint16_t*>(W), L, P, ids, vnorm);
   else
-    hash_generic_kernel<float><<<grid, 256, 0, s>>>(
+    hash_generic_kernel<float><<<grid, kGenThreads, 0, s>>>(
         static_cast<const float*>(K), static_cast<const float*>(V), Hkv, n_cap, pos0, count,
         static_cast<const float*>(W), L, P, ids, vnorm);
   return hipGetLastError();

@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   const int nt = t1 - t0;
 
   __shared__ float logit[kSplitKeys];
-  __shared__ int32_t rows[kSplitKeys];
   __shared__ float red[kDecWaves * 4][kHead];
   __shared__ float sh_m, sh_l;
 
@@ -76,22 +75,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   const int32_t* irow = idx + (int64_t)bg * k_max;
   const int64_t kvbase = ((int64_t)b * Hkv + h) * n_cap;
 
-  // logits: row (wave, kg) takes entries t0 + wave*4 + kg, +16, ...
-  for (int t = wave * 4 + kg; t < nt; t += kDecWaves * 4) {
-    int32_t i = irow[t0 + t];
-    if (i >= n_cap) i = -1;  // out-of-range entries are skipped like padding
-    float dot = 0.f;
-    if (i >= 0) {
-      float kf[8];
-      load_row8<T>(K + (kvbase + i) * kHead, j, kf);
+  // row (wave, kg) owns entries t = wave*4 + kg + 16*r, r < kRounds; every
+  // index, K row and V row it needs is requested before any is used
+  constexpr int kRounds = kSplitKeys / (kDecWaves * 4);
+  int32_t ii[kRounds];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[e], dot);
-    }
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = wave * 4 + kg + 16 * r;
+    int32_t i = t < nt ? irow[t0 + t] : -1;
+    if (i >= n_cap) i = -1;  // out-of-range entries are skipped like padding
+    ii[r] = i;
+  }
+  float kf[kRounds][8], vf[kRounds][8];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t row = kvbase + (ii[r] >= 0 ? ii[r] : 0);
+    load_row8<T>(K + row * kHead, j, kf[r]);
+    load_row8<T>(V + row * kHead, j, vf[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = wave * 4 + kg + 16 * r;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[r][e], dot);
     dot = row16_sum(dot);
-    if (j == 0) {
-      logit[t] = i >= 0 ? dot * scale : -INFINITY;
-      rows[t] = i;
-    }
+    if (j == 0 && t < nt) logit[t] = ii[r] >= 0 ? dot * scale : -INFINITY;
   }
   __syncthreads();
   if (wave == 0) {
@@ -111,14 +120,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int t = wave * 4 + kg; t < nt; t += kDecWaves * 4) {
-    const int32_t i = rows[t];
-    if (i >= 0) {
-      const float p = logit[t];
-      float vf[8];
-      load_row8<T>(V + (kvbase + i) * kHead, j, vf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = wave * 4 + kg + 16 * r;
+    if (t < nt && ii[r] >= 0) {
+      const float p = logit[t];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[r][e], acc[e]);
     }
   }
 #pragma unroll
@@ -137,28 +145,58 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   }
 }
 
-// grid: B*Hq blocks of 128 threads.  Merges the splits in index order.
+// grid: B*Hq blocks of kHead threads.  Merges the splits of one query head:
+// M = max_s m_s, w_s = exp(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s,
+// with the sums taken in split order.
+constexpr int kMaxSplits = 1024;
+
 __global__ __launch_bounds__(kHead) void decode_combine_kernel(const float* __restrict__ part,
                                                                int splits,
                                                                float* __restrict__ out) {
   const int bg = blockIdx.x;
   const int d = threadIdx.x;
   const float* p = part + (int64_t)bg * splits * kPartStride;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
+  __shared__ float wsh[kMaxSplits], lsh[kMaxSplits];
+  __shared__ float red[kHead / 64];
+  __shared__ float sh_M, sh_L;
+  float m = -INFINITY;
+  for (int s = d; s < splits; s += kHead) {
     const float* ps = p + (int64_t)s * kPartStride;
-    if (ps[kHead + 1] > 0.f) M = fmaxf(M, ps[kHead]);
+    const float ms = ps[kHead], ls = ps[kHead + 1];
+    wsh[s] = ls > 0.f ? ms : -INFINITY;
+    lsh[s] = ls;
+    m = fmaxf(m, wsh[s]);
   }
-  float L = 0.f, o = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* ps = p + (int64_t)s * kPartStride;
-    const float ls = ps[kHead + 1];
-    if (ls > 0.f) {
-      const float w = __expf(ps[kHead] - M);
-      L = fmaf(ls, w, L);
-      o = fmaf(ps[d], w, o);
-    }
+  m = wave_max(m);
+  if ((d & 63) == 0) red[d >> 6] = m;
+  __syncthreads();
+  if (d == 0) {
+    float M = red[0];
+    for (int w = 1; w < kHead / 64; ++w) M = fmaxf(M, red[w]);
+    sh_M = M;
   }
+  __syncthreads();
+  const float M = sh_M;
+  for (int s = d; s < splits; s += kHead)
+    wsh[s] = wsh[s] == -INFINITY ? 0.f : __expf(wsh[s] - M);
+  __syncthreads();
+  if (d == 0) {
+    float L = 0.f;
+    for (int s = 0; s < splits; ++s) L = fmaf(lsh[s], wsh[s], L);
+    sh_L = L;
+  }
+  float o = 0.f;
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(s + u) * kPartStride + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o = fmaf(v[u], wsh[s + u], o);
+  }
+  for (; s < splits; ++s) o = fmaf(p[(int64_t)s * kPartStride + d], wsh[s], o);
+  __syncthreads();
+  const float L = sh_L;
   out[(int64_t)bg * kHead + d] = L > 0.f ? o / L : 0.f;
 }
 

@@ -15,6 +15,7 @@ import torch
 
 import soft_lsh_token_amd as S
 from oracle import socket_oracle as SO
+from soft_lsh_token_amd import layout
 
 DEV = "cuda:0"
 ID_BAND = 1e-5
@@ -43,7 +44,7 @@ def upload(w):
 def gpu_hash(w, d, pos0=None, count=None, ids=None, vnorm=None):
     B, Hkv, n_cap = w.B, w.Hkv, w.n_cap
     if ids is None:
-        ids = torch.zeros(B, Hkv, n_cap, w.L, dtype=torch.uint8, device=DEV)
+        ids = S.alloc_ids(B, Hkv, n_cap, w.L, DEV)
     if vnorm is None:
         vnorm = torch.zeros(B, Hkv, n_cap, dtype=torch.float32, device=DEV)
     if pos0 is None:
@@ -70,6 +71,17 @@ def gpu_decode(w, d, idx, q=None):
     out = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device=DEV)
     S.socket_sparse_decode(q, d["K"], d["V"], idx, w.scale, out)
     return out
+
+
+def ids_np(ids_dev, L, n=None):
+    """Tiled device cache -> [B, Hkv, n, L] numpy bucket IDs."""
+    return layout.unpack(ids_dev.cpu().numpy(), L, n)
+
+
+def ids_dev(ids_plain, n_cap):
+    """[B, Hkv, n, L] numpy bucket IDs -> tiled device cache."""
+    return torch.from_numpy(layout.pack(np.ascontiguousarray(ids_plain, dtype=np.uint8),
+                                        n_cap)).to(DEV)
 
 
 def check_ids(ids_gpu, K, W, L, P, n, detail=False):

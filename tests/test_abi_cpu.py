@@ -114,3 +114,46 @@ def test_binding_rejects_host_tensors():
         S.socket_hash_keys(K, K, torch.zeros(8, 128, dtype=torch.bfloat16),
                            torch.zeros(1, 1, 8, 1, dtype=torch.uint8),
                            torch.zeros(1, 1, 8), torch.zeros(1, dtype=torch.int32), 8, 1, 8)
+
+
+def test_stage_argument_checks():
+    lib = S.lib()
+    need = S.socket_score_topk_workspace(1, 32, 1024, 64, 8, 32)
+    # socket_soft_tables(q, dtype, B, Hq, d, W, L, P, tau, n_cap, ws, ws_bytes, stream)
+    assert lib.socket_soft_tables(None, 1, 1, 32, 128, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EINVAL
+    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 128, FAKE, 64, 8, -1.0, 1024, FAKE, need, None) == EINVAL
+    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 64, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EUNSUP
+    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 128, FAKE, 64, 8, 0.5, 1024, FAKE, 64, None) == ENOSPC
+    # socket_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, scores, ws, ws_bytes, stream)
+    assert lib.socket_score(1, 32, 8, 64, 8, None, FAKE, FAKE, 1024, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_score(1, 32, 5, 64, 8, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_score(1, 32, 8, 64, 8, FAKE, FAKE, FAKE, 1024, FAKE, None, need, None) == EINVAL
+    # socket_topk(B, Hq, L, scores, lens, n_cap, ks, k_max, idx, ws, ws_bytes, stream)
+    assert lib.socket_topk(1, 32, 64, FAKE, FAKE, 1024, FAKE, 0, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_topk(1, 32, 64, FAKE, None, 1024, FAKE, 32, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_topk(1, 32, 64, FAKE, FAKE, 1024, FAKE, 32, FAKE, FAKE, 16, None) == ENOSPC
+
+
+@pytest.mark.parametrize("L", [3, 16, 20, 32, 60, 64, 100, 128])
+def test_ids_layout_roundtrip_and_formula(L):
+    """pack/unpack invert each other and place bytes where the header's formula says."""
+    import numpy as np
+    from soft_lsh_token_amd import layout
+    rng = np.random.default_rng(L)
+    B, Hkv, n, n_cap = 2, 3, 150, 200
+    ids = rng.integers(0, 256, size=(B, Hkv, n, L), dtype=np.uint8)
+    tiled = layout.pack(ids, n_cap)
+    assert tiled.shape == layout.ids_shape(B, Hkv, n_cap, L)
+    assert tiled.size == S.socket_ids_bytes(B, Hkv, n_cap, L)
+    np.testing.assert_array_equal(layout.unpack(tiled, L, n), ids)
+    TL = layout.word_bytes(L)
+    assert 16 * TL >= L and (TL == 1 or 8 * TL < L)
+    flat = tiled.reshape(-1)
+    G = (n_cap + 63) // 64
+    for (b, h, i, l) in [(0, 0, 0, 0), (1, 2, 149, L - 1), (0, 1, 77, L // 2), (1, 0, 64, 0)]:
+        r, w, byte = b * Hkv + h, l // TL, l % TL
+        t = i % 64
+        kg, x = t // 16, t % 16
+        off = ((r * G + i // 64) * 1024 + ((x - w) % 16) * 64 + 16 * kg + w) * TL + byte
+        assert flat[off] == ids[b, h, i, l]
+    assert S.socket_ids_bytes(1, 1, 10, 129) == 0

@@ -14,6 +14,7 @@ import torch
 import gpu_cases as GC
 from gpu_cases import DEV
 from oracle import socket_oracle as SO
+import soft_lsh_token_amd as S
 from soft_lsh_token_amd.inputs import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +47,7 @@ def test_hash_parity(case):
     d = GC.upload(w)
     ids, vn = GC.gpu_hash(w, d)
     sync()
-    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    ids, vn = GC.ids_np(ids, w.L), vn.cpu().numpy()
     n_cap = w.n_cap
     for b in range(w.B):
         for h in range(w.Hkv):
@@ -60,7 +61,7 @@ def test_hash_full_c2_mfma():
     d = GC.upload(w)
     ids, vn = GC.gpu_hash(w, d)
     sync()
-    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    ids, vn = GC.ids_np(ids, w.L), vn.cpu().numpy()
     band = 0
     for h in range(w.Hkv):
         band += GC.check_ids(ids[0, h], w.K[0, h], w.W, w.L, w.P, w.n_cap)
@@ -72,12 +73,12 @@ def test_hash_append_rows_only():
     """count=1 at pos0=lens hashes exactly one new row per (sequence, head)."""
     w = make_workload("c4", n=(200, 600), B=2, Hkv=2, Hq=8)
     d = GC.upload(w)
-    ids = torch.full((w.B, w.Hkv, w.n_cap, w.L), 0xAB, dtype=torch.uint8, device=DEV)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, DEV).fill_(0xAB)
     vn = torch.full((w.B, w.Hkv, w.n_cap), -1.0, dtype=torch.float32, device=DEV)
     pos0 = d["lens"].clone()
     GC.gpu_hash(w, d, pos0=pos0, count=1, ids=ids, vnorm=vn)
     sync()
-    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    ids, vn = GC.ids_np(ids, w.L, w.n_cap), vn.cpu().numpy()
     for b in range(w.B):
         p = int(w.lens[b])
         for h in range(w.Hkv):
@@ -122,7 +123,7 @@ def test_score_topk_parity(case):
     w = make_workload(**case)
     d = GC.upload(w)
     ids_np, vn_np = _oracle_ids(w)
-    ids = torch.from_numpy(ids_np).to(DEV)
+    ids = GC.ids_dev(ids_np, w.n_cap)
     vn = torch.from_numpy(vn_np).to(DEV)
     idx, sc = GC.gpu_score_topk(w, d, ids, vn)
     sync()
@@ -141,7 +142,7 @@ def test_topk_ties_lower_index_wins():
     """All keys of a head share one bucket pattern and norm -> equal scores."""
     w = make_workload("c2", n=3000, Hq=8, Hkv=2, k=100)
     d = GC.upload(w)
-    ids = torch.zeros(w.B, w.Hkv, w.n_cap, w.L, dtype=torch.uint8, device=DEV)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, DEV)
     vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
     # KV head 1: second half of the keys gets a larger norm -> they win, ties among them
     vn[:, 1, 1500:] = 2.0
@@ -159,7 +160,7 @@ def test_topk_edge_lengths():
     w = make_workload("c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 777, 300], n_cap=1000, k=5)
     d = GC.upload(w)
     ids_np, vn_np = _oracle_ids(w)
-    ids = torch.from_numpy(ids_np).to(DEV)
+    ids = GC.ids_dev(ids_np, w.n_cap)
     vn = torch.from_numpy(vn_np).to(DEV)
     ks = torch.tensor([5, 5, 777, 999], dtype=torch.int32, device=DEV)
     k_max = 1000
@@ -206,7 +207,8 @@ def _e2e(w, heads=None):
     idx, sc = GC.gpu_score_topk(w, d, ids, vn)
     out = GC.gpu_decode(w, d, idx)
     sync()
-    ids, vn, idx, sc, out = (t.cpu().numpy() for t in (ids, vn, idx, sc, out))
+    ids = GC.ids_np(ids, w.L, w.n_cap)
+    vn, idx, sc, out = (t.cpu().numpy() for t in (vn, idx, sc, out))
     group = w.Hq // w.Hkv
     tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
     stats = dict(band_bits=0, id_rows_differ=0, set_diff=0, max_out_err=0.0)
@@ -271,7 +273,7 @@ def test_decode_loop_c5():
         if t in check_steps:
             keep[t] = [x.cpu().numpy() for x in (idx, sc, out)]
     sync()
-    ids_np, vn_np = ids.cpu().numpy(), vn.cpu().numpy()
+    ids_np, vn_np = GC.ids_np(ids, w.L, w.n_cap), vn.cpu().numpy()
     group = w.Hq // w.Hkv
     for h in sorted({g // group for g in heads}):
         n_all = n0 + w.steps
@@ -309,3 +311,21 @@ def test_run_twice_bitwise():
     assert torch.equal(ids, ids2) and torch.equal(vn, vn2)
     assert torch.equal(r1[0][0], r2[0][0]) and torch.equal(r1[0][1], r2[0][1])
     assert torch.equal(r1[1], r2[1])
+
+
+def test_stage_entry_points_match_fused_call():
+    """socket_soft_tables + socket_score + socket_topk == socket_score_topk, bit for bit."""
+    w = make_workload("c4", n=(3000, 9000), B=3, k=0.02)
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    idx1, sc1 = GC.gpu_score_topk(w, d, ids, vn)
+    ws = S.alloc_workspace(S.socket_score_topk_workspace(w.B, w.Hq, w.n_cap, w.L, w.P, w.k_max),
+                           DEV)
+    sc2 = torch.zeros_like(sc1)
+    idx2 = torch.full_like(idx1, -7)
+    S.socket_soft_tables(d["q"], d["W"], w.L, w.P, w.tau, w.n_cap, ws)
+    S.socket_score(ids, vn, d["lens"], w.Hq, w.L, w.P, sc2, ws)
+    S.socket_topk(sc2, d["lens"], d["ks"], w.L, idx2, ws)
+    sync()
+    assert torch.equal(sc1, sc2)
+    assert torch.equal(idx1, idx2)
