@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--no-128k", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="also run one device-to-device copy of this many MiB (a known-size "
+                        "reference kernel for hardware byte counters)")
     return p.parse_args()
 
 
@@ -89,9 +92,10 @@ class Case:
         self.vn = [torch.empty(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
                    for _ in range(replicas)]
         self.idx = torch.empty(w.B, w.Hq, self.k, dtype=torch.int32, device=dev)
-        self.scores = torch.empty(w.B, w.Hq, w.n_cap, dtype=torch.float32, device=dev)
+        self.scores = torch.empty(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32,
+                                  device=dev)
         self.out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
-        sws = S.socket_score_topk_workspace(w.B, w.Hq, w.n_cap, w.L, w.P, self.k)
+        sws = S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, self.k)
         dws = S.socket_sparse_decode_workspace(w.B, w.Hq, w.d, self.k)
         self.sws = S.alloc_workspace(sws, dev)
         self.dws = S.alloc_workspace(dws, dev)
@@ -124,10 +128,10 @@ class Case:
                                   i64(w.n_cap), vp(self.idx.data_ptr()), self.k,
                                   ctypes.c_float(w.scale), vp(self.out.data_ptr()),
                                   vp(self.dws_p), ctypes.c_size_t(self.dws_n), st))
-        self.c_tables = (vp(self.q.data_ptr()), 1, w.B, w.Hq, w.d, vp(self.W.data_ptr()), w.L,
+        self.c_tables = (vp(self.q.data_ptr()), 1, w.B, w.Hq, w.Hkv, w.d, vp(self.W.data_ptr()), w.L,
                          w.P, ctypes.c_float(w.tau), i64(w.n_cap), vp(self.sws_p),
                          ctypes.c_size_t(self.sws_n), st)
-        self.c_topk = (w.B, w.Hq, w.L, vp(self.scores.data_ptr()), vp(self.lens.data_ptr()),
+        self.c_topk = (w.B, w.Hq, w.Hkv, w.L, vp(self.scores.data_ptr()), vp(self.lens.data_ptr()),
                        i64(w.n_cap), vp(self.ks.data_ptr()), self.k, vp(self.idx.data_ptr()),
                        vp(self.sws_p), ctypes.c_size_t(self.sws_n), st)
 
@@ -302,6 +306,15 @@ def main():
         raise RuntimeError("no GPU visible; bench.py needs an MI355X")
     lib = S.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration} MiB done")
+        del src, dst
 
     case = Case("c2", args.replicas, lib, torch, S)
     for r in range(case.replicas):

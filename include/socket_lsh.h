@@ -28,7 +28,7 @@
  *     vnorm     [B][Hkv][n_cap]         float32
  *     lens, ks  [B]                     int32, device
  *     idx       [B][Hq][k_max]          int32
- *     scores    [B][Hq][n_cap]          float32
+ *     scores    [B][Hq][ns]             float32, ns = n_cap rounded up to 64
  *     out       [B][Hq][d]              float32
  * - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
  *   Hq must be a multiple of Hkv; socket_score_topk needs Hq / Hkv in
@@ -42,9 +42,11 @@
  * power of two with 16*TL >= L; word w holds tables w*TL .. w*TL+TL-1 (byte
  * b of the word = table w*TL + b; tables >= L read as 0).  Keys are tiled in
  * groups of 64: key i of KV row r = b*Hkv + h lies in group i/64 at t = i%64,
- * t = 16*kg + x, and its word w is stored at byte offset
- *   ((r * ceil(n_cap/64) + i/64) * 1024 + ((x - w) mod 16) * 64 + 16*kg + w) * TL.
- * This order lets the scorer read 64 consecutive words per load.
+ * t = 16*kg + x; with u = (x - w) mod 16 and R = 16/TL its word w is stored at
+ * byte offset
+ *   ((r * ceil(n_cap/64) + i/64) * 1024 + (u/R)*64*R + (16*kg + w)*R + u%R) * TL.
+ * This order lets the scorer read its words with 16-byte loads, 1 KiB per
+ * wave and load.
  * - Errors are reported as negative return codes before anything is
  *   enqueued (argument checks), or as SOCKET_EHIP when a launch fails.
  *   Nothing throws or aborts.  socket_status_string() names a code.
@@ -100,8 +102,9 @@ int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, in
                      int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
                      int P, uint8_t* ids, float* vnorm, void* stream);
 
-/* Workspace bytes needed by socket_score_topk for these sizes. */
-size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, int k_max);
+/* Workspace bytes needed by socket_score_topk for these sizes (0 if unsupported). */
+size_t socket_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
+                                   int k_max);
 
 /*
  * socket_score_topk -- Algorithms 2 and 3 of SOCKET Sec. 4.1.
@@ -115,13 +118,15 @@ size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, i
  *   idx[b][g] = the min(ks[b], lens[b]) keys with the largest s_i; among
  *               equal scores the lower index wins.  The indices are written
  *               in ascending order and the row is padded with -1 up to k_max.
- * Scores are float32; the table entries are float32 roundings of float64
- * values.  If `scores` is not NULL the scores of every i < lens[b] are
+ * Scores are float32, score row stride ns = n_cap rounded up to a multiple of
+ * 64 (rows start 256-byte aligned).  A table entry is either the float32 rounding of the
+ * float64 p_l(c), or the float32 product lo * hi of the float32 roundings of
+ * its two factors (added with one fused multiply-add).  If `scores` is not NULL the scores of every i < lens[b] are
  * written there (entries i >= lens[b] are left untouched).
  *
  * lens and ks are device int32 arrays [B] with 0 <= lens[b] <= n_cap and
  * ks[b] <= k_max (a negative ks[b] is treated as 0).  tau > 0.
- * ws must hold socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max) bytes
+ * ws must hold socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max) bytes
  * and be 256-byte aligned; its contents need not be initialised.
  */
 int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
@@ -132,13 +137,15 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
 /*
  * The three stages of socket_score_topk, for callers that schedule or time
  * them separately.  All three take the same workspace (sized by
- * socket_score_topk_workspace for the same B, Hq, n_cap, L) and must be
+ * socket_score_topk_workspace for the same B, Hq, Hkv, n_cap, L) and must be
  * enqueued in this order on one stream for one query batch:
  *
  * socket_soft_tables -- Algorithm 2, first half: the float64 projections of
- *   q[b][g] and, per table, the float32 half-tables lo_l(c) (planes 0..3) and
- *   hi_l(c) (planes 4..P-1) with p_l(c) = lo_l(c & 15) * hi_l(c >> 4).  Also
- *   clears the selection histograms and counters held in the workspace.
+ *   q[b][g] and the bucket distribution of every table, stored in the
+ *   workspace either as the full table p_l(c) or as its two factors
+ *   lo_l(c & 15) (planes 0..3) and hi_l(c >> 4) (planes 4..P-1), each value
+ *   rounded once to float32.  Also clears the selection histograms and
+ *   counters held in the workspace.
  * socket_score -- Algorithm 2, second half: s_i for every i < lens[b] of every
  *   query head, written to `scores` (or into the workspace when scores is
  *   NULL), plus a histogram of the top bits of each score in the workspace.
@@ -146,14 +153,15 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
  *   `scores` pointer (NULL = workspace) and the histogram left by
  *   socket_score.  Output as in socket_score_topk.
  */
-int socket_soft_tables(const void* q, int dtype, int B, int Hq, int d, const void* W, int L,
-                       int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes, void* stream);
+int socket_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                       int L, int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes,
+                       void* stream);
 int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const float* vnorm,
                  const int32_t* lens, int64_t n_cap, float* scores, void* ws, size_t ws_bytes,
                  void* stream);
-int socket_topk(int B, int Hq, int L, const float* scores, const int32_t* lens, int64_t n_cap,
-                const int32_t* ks, int k_max, int32_t* idx, void* ws, size_t ws_bytes,
-                void* stream);
+int socket_topk(int B, int Hq, int Hkv, int L, const float* scores, const int32_t* lens,
+                int64_t n_cap, const int32_t* ks, int k_max, int32_t* idx, void* ws,
+                size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by socket_sparse_decode for these sizes. */
 size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max);

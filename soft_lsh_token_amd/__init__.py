@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     SOCKET_BF16, SOCKET_F32, SocketError, alloc_ids, alloc_workspace, lib, socket_hash_keys,
     socket_ids_bytes, socket_score,
     socket_score_topk, socket_score_topk_workspace, socket_soft_tables, socket_sparse_decode,
-    socket_sparse_decode_workspace, socket_topk,
+    socket_sparse_decode_workspace, socket_topk, score_stride,
 )
 
 __version__ = "0.1.0"

@@ -28,12 +28,12 @@ _SIGS = {
     "socket_version": (_i, []),
     "socket_ids_bytes": (_sz, [_i, _i, _i64, _i]),
     "socket_hash_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp, _vp]),
-    "socket_score_topk_workspace": (_sz, [_i, _i, _i64, _i, _i, _i]),
+    "socket_score_topk_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
     "socket_score_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _i64, _vp,
                                _i, _vp, _vp, _vp, _sz, _vp]),
-    "socket_soft_tables": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _f, _i64, _vp, _sz, _vp]),
+    "socket_soft_tables": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _i64, _vp, _sz, _vp]),
     "socket_score": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
-    "socket_topk": (_i, [_i, _i, _i, _vp, _vp, _i64, _vp, _i, _vp, _vp, _sz, _vp]),
+    "socket_topk": (_i, [_i, _i, _i, _i, _vp, _vp, _i64, _vp, _i, _vp, _vp, _sz, _vp]),
     "socket_sparse_decode_workspace": (_sz, [_i, _i, _i, _i]),
     "socket_sparse_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i64, _vp, _i, _f, _vp, _vp,
                                   _sz, _vp]),
@@ -136,8 +136,9 @@ def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: tor
     _check("socket_hash_keys", rc)
 
 
-def socket_score_topk_workspace(B: int, Hq: int, n_cap: int, L: int, P: int, k_max: int) -> int:
-    return int(lib().socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max))
+def socket_score_topk_workspace(B: int, Hq: int, Hkv: int, n_cap: int, L: int, P: int,
+                                k_max: int) -> int:
+    return int(lib().socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max))
 
 
 def socket_sparse_decode_workspace(B: int, Hq: int, d: int, k_max: int) -> int:
@@ -147,6 +148,11 @@ def socket_sparse_decode_workspace(B: int, Hq: int, d: int, k_max: int) -> int:
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     """A device byte buffer whose data pointer is 256-byte aligned."""
     return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+
+
+def score_stride(n_cap: int) -> int:
+    """Row stride of the score rows: n_cap rounded up to 64."""
+    return (n_cap + 63) // 64 * 64
 
 
 def _ws_ptr(ws: torch.Tensor, need: int) -> tuple[int, int]:
@@ -162,11 +168,12 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
     """Soft-LSH scores of every key and the top-k indices per query head."""
     B, Hq, d = q.shape
     Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
-    need = socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max)
+    need = socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
     if ws is None:
         ws = alloc_workspace(need, q.device)
     wptr, wbytes = _ws_ptr(ws, need)
-    sptr = None if scores is None else _dev(scores, "scores", torch.float32, (B, Hq, n_cap))
+    sptr = None if scores is None else _dev(scores, "scores", torch.float32,
+                                            (B, Hq, score_stride(n_cap)))
     rc = lib().socket_score_topk(
         _dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P,
         float(tau), _ids(ids, B, Hkv, n_cap, L),
@@ -177,12 +184,12 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
     _check("socket_score_topk", rc)
 
 
-def socket_soft_tables(q: torch.Tensor, W: torch.Tensor, L: int, P: int, tau: float, n_cap: int,
-                       ws: torch.Tensor, stream=None) -> None:
-    """Algorithm 2, first half: the per-table soft-bucket half-tables (into ws)."""
+def socket_soft_tables(q: torch.Tensor, W: torch.Tensor, Hkv: int, L: int, P: int, tau: float,
+                       n_cap: int, ws: torch.Tensor, stream=None) -> None:
+    """Algorithm 2, first half: every table's bucket distribution (into ws)."""
     B, Hq, d = q.shape
     wptr, wbytes = _ws_ptr(ws, 0)
-    rc = lib().socket_soft_tables(_dev(q, "q"), _dtype_code(q), B, Hq, d,
+    rc = lib().socket_soft_tables(_dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d,
                                   _dev(W, "W", q.dtype, (L * P, d)), L, P, float(tau), int(n_cap),
                                   wptr, wbytes, _stream(q, stream))
     _check("socket_soft_tables", rc)
@@ -196,18 +203,20 @@ def socket_score(ids: torch.Tensor, vnorm: torch.Tensor, lens: torch.Tensor, Hq:
     rc = lib().socket_score(B, Hq, Hkv, L, P, _ids(ids, B, Hkv, n_cap, L),
                             _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
                             _dev(lens, "lens", torch.int32, (B,)), n_cap,
-                            _dev(scores, "scores", torch.float32, (B, Hq, n_cap)), wptr, wbytes,
+                            _dev(scores, "scores", torch.float32, (B, Hq, score_stride(n_cap))),
+                            wptr, wbytes,
                             _stream(ids, stream))
     _check("socket_score", rc)
 
 
-def socket_topk(scores: torch.Tensor, lens: torch.Tensor, ks: torch.Tensor, L: int,
-                idx: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+def socket_topk(scores: torch.Tensor, lens: torch.Tensor, ks: torch.Tensor, Hkv: int, L: int,
+                n_cap: int, idx: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
     """Algorithm 3: top-k per query head from scores + the histogram socket_score left in ws."""
-    B, Hq, n_cap = scores.shape
+    B, Hq, _ = scores.shape
     k_max = idx.shape[-1]
     wptr, wbytes = _ws_ptr(ws, 0)
-    rc = lib().socket_topk(B, Hq, L, _dev(scores, "scores", torch.float32), _dev(lens, "lens",
+    rc = lib().socket_topk(B, Hq, Hkv, L, _dev(scores, "scores", torch.float32,
+                           (B, Hq, score_stride(n_cap))), _dev(lens, "lens",
                            torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)), k_max,
                            _dev(idx, "idx", torch.int32, (B, Hq, k_max)), wptr, wbytes,
                            _stream(scores, stream))

@@ -56,17 +56,20 @@ size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L) {
   return (size_t)B * Hkv * ids_groups(n_cap) * 64 * ids_key_bytes(L);
 }
 
-size_t socket_score_topk_workspace(int B, int Hq, int64_t n_cap, int L, int P, int k_max) {
-  (void)P;
+size_t socket_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
+                                   int k_max) {
   (void)k_max;
-  if (B <= 0 || Hq <= 0 || n_cap <= 0 || L <= 0) return 0;
-  return score_ws_layout(B, Hq, n_cap, L, nullptr, nullptr);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || L > kMaxScoreL || P <= 0 ||
+      P > 8 || !group_ok(Hq, Hkv))
+    return 0;
+  return score_ws_layout(B, Hq, Hkv, n_cap, L, nullptr, nullptr);
 }
 
-static int score_ws(int B, int Hq, int64_t n_cap, int L, void* ws, size_t ws_bytes, ScoreWs* w) {
+static int score_ws(int B, int Hq, int Hkv, int64_t n_cap, int L, void* ws, size_t ws_bytes,
+                    ScoreWs* w) {
   if (!ws) return SOCKET_EINVAL;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return SOCKET_EINVAL;
-  const size_t need = score_ws_layout(B, Hq, n_cap, L, w, ws);
+  const size_t need = score_ws_layout(B, Hq, Hkv, n_cap, L, w, ws);
   return ws_bytes < need ? SOCKET_ENOSPC : SOCKET_OK;
 }
 
@@ -80,17 +83,18 @@ static int check_sizes(int B, int Hq, int Hkv, int L, int P, int64_t n_cap) {
   return SOCKET_OK;
 }
 
-int socket_soft_tables(const void* q, int dtype, int B, int Hq, int d, const void* W, int L,
-                       int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes, void* stream) {
+int socket_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                       int L, int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!q || !W) return SOCKET_EINVAL;
   if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
   if (!(tau > 0.f) || !(tau < INFINITY)) return SOCKET_EINVAL;
-  int rc = check_sizes(B, Hq, Hq, L, P, n_cap);
+  int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
   if (rc) return rc;
   if (d != kHead) return SOCKET_EUNSUPPORTED;
   ScoreWs w;
-  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
-  return from_hip(launch_soft_tables(q, dtype, B, Hq, W, L, P, tau, w,
+  if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
+  return from_hip(launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -101,21 +105,21 @@ int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const
   int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
   if (rc) return rc;
   ScoreWs w;
-  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
   return from_hip(launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap,
                                scores ? scores : w.scores, w, static_cast<hipStream_t>(stream)));
 }
 
-int socket_topk(int B, int Hq, int L, const float* scores, const int32_t* lens, int64_t n_cap,
-                const int32_t* ks, int k_max, int32_t* idx, void* ws, size_t ws_bytes,
-                void* stream) {
+int socket_topk(int B, int Hq, int Hkv, int L, const float* scores, const int32_t* lens,
+                int64_t n_cap, const int32_t* ks, int k_max, int32_t* idx, void* ws,
+                size_t ws_bytes, void* stream) {
   if (!lens || !ks || !idx) return SOCKET_EINVAL;
   if (k_max <= 0) return SOCKET_EINVAL;
   if (k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
-  int rc = check_sizes(B, Hq, Hq, L, 1, n_cap);
+  int rc = check_sizes(B, Hq, Hkv, L, 1, n_cap);
   if (rc) return rc;
   ScoreWs w;
-  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
   return from_hip(launch_topk(B, Hq, scores ? scores : w.scores, lens, n_cap, ks, k_max, idx, w,
                               static_cast<hipStream_t>(stream)));
 }
@@ -132,10 +136,10 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
   if (rc) return rc;
   if (d != kHead || k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
   ScoreWs w;
-  if ((rc = score_ws(B, Hq, n_cap, L, ws, ws_bytes, &w))) return rc;
+  if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* sc = scores ? scores : w.scores;
-  hipError_t e = launch_soft_tables(q, dtype, B, Hq, W, L, P, tau, w, s);
+  hipError_t e = launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w, s);
   if (e == hipSuccess) e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sc, w, s);
   if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, idx, w, s);
   return from_hip(e);

@@ -14,11 +14,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Bucket-ID cache layout.  The IDs of one key are cut into 16 words of TL
 // bytes (word j = tables j*TL .. j*TL+TL-1; tables >= L read as 0), TL the
-// smallest power of two with 16*TL >= L.  Keys are tiled in groups of 64;
-// inside a group, key t = 16*kg + x stores word j at word slot
-// ((x - j) mod 16) * 64 + kg * 16 + j.  With this diagonal order the 64 lanes
-// of a scorer wave, lane (kg, j) taking word j of key 16*kg + (j + d) mod 16
-// in round d, read 64 consecutive words.
+// smallest power of two with 16*TL >= L.  Keys are tiled in groups of 64.
+// Inside a group, word j of key t = 16*kg + x belongs to scorer lane
+// 16*kg + j in round r = (x - j) mod 16 and is stored at word slot
+//   (r / R) * 64 * R + (16*kg + j) * R + r % R,   R = 16 / TL,
+// so that a lane's words of R consecutive rounds form one 16-byte vector and
+// a wave's 16-byte loads read 1 KiB contiguously.
 __host__ __device__ constexpr int ids_word_bytes(int L) {
   return L <= 16 ? 1 : L <= 32 ? 2 : L <= 64 ? 4 : 8;
 }
@@ -29,11 +30,17 @@ __host__ __device__ inline int64_t ids_groups(int64_t n_cap) { return (n_cap + 6
 __host__ __device__ inline int64_t ids_word_offset(int64_t bh, int64_t n_cap, int L, int64_t key,
                                                    int j) {
   const int TL = ids_word_bytes(L);
+  const int R = 16 / TL;
   const int64_t gi = key >> 6;
   const int t = (int)(key & 63), kg = t >> 4, x = t & 15;
-  const int slot = (((x - j) & 15) << 6) | (kg << 4) | j;
+  const int r = (x - j) & 15;
+  const int slot = (r / R) * 64 * R + ((kg << 4) | j) * R + (r % R);
   return ((bh * ids_groups(n_cap) + gi) * 1024 + slot) * TL;
 }
+
+// Row stride (floats) of the per-head score rows: n_cap rounded up to 64, so
+// every row starts 256-byte aligned.
+__host__ __device__ inline int64_t score_stride(int64_t n_cap) { return (n_cap + 63) & ~(int64_t)63; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -11,7 +11,8 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
                             int P, uint8_t* ids, float* vnorm, hipStream_t s);
 
 struct ScoreWs {
-  float* sub;           // [B*Hq][L][32]  per-table half-tables (float32)
+  float* img;           // [B*Hkv][img_floats]  LDS images of the soft tables
+  int img_floats;
   uint32_t* hist;       // [B*Hq][kHistBins]
   uint32_t* counters;   // [B*Hq][4]  {candidates, done tickets, -, -}
   uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/64)*2
@@ -20,12 +21,12 @@ struct ScoreWs {
   int64_t words;
 };
 
-size_t score_ws_layout(int B, int Hq, int64_t n_cap, int L, ScoreWs* ws, void* base);
+size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base);
 
-// Algorithm 2, part 1: per-table half-tables of every query head; clears the
-// histograms and counters the scorer and the selection use.
-hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, const void* W, int L,
-                              int P, float tau, const ScoreWs& ws, hipStream_t s);
+// Algorithm 2, part 1: the soft tables of every query head, written as the
+// scorer's LDS images; clears the histograms and counters of the selection.
+hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
+                              int L, int P, float tau, const ScoreWs& ws, hipStream_t s);
 
 // Algorithm 2, part 2: scores of every key plus the first-digit histogram.
 hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,

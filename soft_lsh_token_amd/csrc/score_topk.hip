@@ -32,28 +32,92 @@
 // candidates exactly (radix select on the remaining score bits, then on the
 // index so that the lower index wins a tie) and turns the bitmap into
 // ascending indices.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace socketlsh {
 
+// ---------------------------------------------------------------- table images
+
+// LDS image of the tables of one KV row (its G query heads).  Lane j of a
+// 16-lane scorer row owns tables j*TL .. j*TL+TL-1; the first NF of them are
+// kept as full tables, the other NS = TL - NF as their two factors:
+//   full slot (e*NF + m)*16 + j            e < 2^P, m < NF
+//   half slot FULL + ((hf*16 + c)*NS + m)*16 + j   hf = 0 (planes 0..3) or 1
+//                                            (planes 4..P-1), c < 16, m < NS
+// one slot = G floats (the G query heads).  Bank group of a slot = j, so the
+// 16 lookups of a row never collide.  NF is the largest count whose image
+// fits in LDS next to nothing else (the histogram reuses the image).
+template <int G, int TL>
+struct ImageShape {
+  static constexpr bool fit(int nf) {
+    return 256 * nf * 16 * G + 2 * 16 * (TL - nf) * 16 * G <= 38400;  // 150 KiB
+  }
+  static constexpr int pick() {
+    int nf = 0;
+    for (int c = 0; c <= TL; ++c)
+      if (fit(c)) nf = c;
+    return nf;
+  }
+  static constexpr int NF = pick();
+  static constexpr int NS = TL - NF;
+  static constexpr int FULL = 256 * NF * 16 * G;   // floats
+  static constexpr int HALF = 2 * 16 * NS * 16 * G;
+  static constexpr int FLOATS = FULL + HALF > G * kHistBins ? FULL + HALF : G * kHistBins;
+};
+
+struct ImageDims {
+  int G, TL, NF, NS, full, floats;
+};
+
+static ImageDims image_dims(int G, int L) {
+  const int TL = ids_word_bytes(L);
+  auto make = [](auto g, auto tl) {
+    using S = ImageShape<decltype(g)::value, decltype(tl)::value>;
+    return ImageDims{decltype(g)::value, decltype(tl)::value, S::NF, S::NS, S::FULL, S::FLOATS};
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  switch (G * 16 + TL) {
+    case 17: return make(I1{}, I1{});
+    case 18: return make(I1{}, I2{});
+    case 20: return make(I1{}, I4{});
+    case 24: return make(I1{}, I8{});
+    case 33: return make(I2{}, I1{});
+    case 34: return make(I2{}, I2{});
+    case 36: return make(I2{}, I4{});
+    case 40: return make(I2{}, I8{});
+    case 65: return make(I4{}, I1{});
+    case 66: return make(I4{}, I2{});
+    case 68: return make(I4{}, I4{});
+    default: return make(I4{}, I8{});
+  }
+}
+
 // ---------------------------------------------------------------- workspace
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t score_ws_layout(int B, int Hq, int64_t n_cap, int L, ScoreWs* ws, void* base) {
+size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
   const size_t heads = (size_t)B * Hq;
+  const int G = Hq / Hkv;
+  const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L);
   const int64_t words = ((n_cap + 63) / 64) * 2;
   size_t off = 0;
-  const size_t o_sub = off; off = align256(off + heads * L * 32 * sizeof(float));
+  const size_t o_img = off; off = align256(off + (size_t)B * Hkv * im.floats * sizeof(float));
   const size_t o_hist = off; off = align256(off + heads * kHistBins * sizeof(uint32_t));
   const size_t o_cnt = off; off = align256(off + heads * 4 * sizeof(uint32_t));
   const size_t o_bm = off; off = align256(off + heads * words * sizeof(uint32_t));
   const size_t o_cand = off; off = align256(off + heads * (size_t)n_cap * sizeof(uint2));
-  const size_t o_sc = off; off = align256(off + heads * (size_t)n_cap * sizeof(float));
+  const size_t o_sc = off; off = align256(off + heads * (size_t)score_stride(n_cap) * sizeof(float));
   if (ws) {
     char* p = static_cast<char*>(base);
-    ws->sub = reinterpret_cast<float*>(p + o_sub);
+    ws->img = reinterpret_cast<float*>(p + o_img);
+    ws->img_floats = im.floats;
     ws->hist = reinterpret_cast<uint32_t*>(p + o_hist);
     ws->counters = reinterpret_cast<uint32_t*>(p + o_cnt);
     ws->bitmap = reinterpret_cast<uint32_t*>(p + o_bm);
@@ -80,106 +144,121 @@ __device__ __forceinline__ void load_w8<float>(const float* p, float* f) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// grid: B*Hq blocks, 256 threads.  Also clears the head's histogram and counters.
+constexpr int kTabTables = 16;                 // tables per soft-table block
+constexpr int kTabThreads = kTabTables * 8;    // one plane per thread (P <= 8)
+
+// grid: B*Hq*ceil(L/16) blocks.  Block (bg, tb) computes the bucket
+// distributions of tables 16*tb .. 16*tb+15 of query head bg = b*Hq + g and
+// writes them into component g % G of the table image of KV row
+// b*Hkv + g / G.  Block tb = 0 also clears the head's histogram and counters.
 template <typename T>
-__global__ __launch_bounds__(256) void soft_tables_kernel(const T* __restrict__ q,
-                                                          const T* __restrict__ W, int L, int P,
-                                                          float tau, float* __restrict__ sub,
-                                                          uint32_t* __restrict__ hist,
-                                                          uint32_t* __restrict__ counters) {
-  const int bg = blockIdx.x;
+__global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
+    const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
+    int G, int TL, int NF, int NS, int FULL, int img_floats, int ntb, float* __restrict__ img,
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters) {
+  const int bg = blockIdx.x / ntb;
+  const int tb = blockIdx.x % ntb;
   const int tid = threadIdx.x;
-  __shared__ double qd[kHead];
-  __shared__ double sig[2048][2];  // [plane][bit] = sigmoid(-+2u/tau)
+  const int b = bg / Hq, g = bg % Hq;
+  const int comp = g % G;
+  float* im = img + ((int64_t)b * Hkv + g / G) * img_floats;
+  __shared__ float qf[kHead];                 // the query (exact in float32)
+  __shared__ double sig[kTabThreads][2];      // [plane][bit] = sigmoid(-+2u/tau)
+  __shared__ double half[kTabTables][32];     // [table][hf*16 + c]
   if (tid < kHead) {
     if constexpr (sizeof(T) == 2)
-      qd[tid] = (double)__uint_as_float((uint32_t)q[(int64_t)bg * kHead + tid] << 16);
+      qf[tid] = __uint_as_float((uint32_t)q[(int64_t)bg * kHead + tid] << 16);
     else
-      qd[tid] = (double)q[(int64_t)bg * kHead + tid];
+      qf[tid] = q[(int64_t)bg * kHead + tid];
   }
-  for (int i = tid; i < kHistBins; i += blockDim.x) hist[(int64_t)bg * kHistBins + i] = 0u;
-  if (tid < 4) counters[bg * 4 + tid] = 0u;
+  if (tb == 0) {
+    for (int i = tid; i < kHistBins; i += kTabThreads) hist[(int64_t)bg * kHistBins + i] = 0u;
+    if (tid < 4) counters[bg * 4 + tid] = 0u;
+  }
+  const int l0 = tb * kTabTables;
+  const int pl = l0 * P + tid;  // this thread's plane
+  const bool has_plane = tid < kTabTables * P && pl < L * P;
+  constexpr int NV = kHead * (int)sizeof(T) / 16;  // 16-byte vectors per plane row
+  uint4 raw[NV];
+  if (has_plane) {
+    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)pl * kHead);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) raw[v] = wr[v];
+  }
   __syncthreads();
-  const int planes = L * P;
-  const double inv_tau = 1.0 / (double)tau;
-  for (int pl = tid; pl < planes; pl += blockDim.x) {
-    const T* wr = W + (int64_t)pl * kHead;
-    float wf[kHead];
+  if (has_plane) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int t = 0; t < kHead; t += 8) load_w8<T>(wr + t, wf + t);
-    double u = 0.0;
+    for (int v = 0; v < NV; ++v) {
+      float f[8];
+      int cnt;
+      if constexpr (sizeof(T) == 2) {
+        unpack_bf16x8(raw[v], f);
+        cnt = 8;
+      } else {
+        f[0] = __uint_as_float(raw[v].x); f[1] = __uint_as_float(raw[v].y);
+        f[2] = __uint_as_float(raw[v].z); f[3] = __uint_as_float(raw[v].w);
+        cnt = 4;
+      }
 #pragma unroll
-    for (int t = 0; t < kHead; ++t) u = fma((double)wf[t], qd[t], u);
-    const double x = 2.0 * u * inv_tau;
-    sig[pl][1] = 1.0 / (1.0 + exp(-x));  // bit set: corner sign +1
-    sig[pl][0] = 1.0 / (1.0 + exp(x));   // bit clear: corner sign -1
+      for (int e = 0; e < cnt; ++e) acc[e & 3] = fma((double)f[e], (double)qf[v * cnt + e], acc[e & 3]);
+    }
+    const double u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const double x = 2.0 * u / (double)tau;
+    sig[tid][1] = 1.0 / (1.0 + exp(-x));  // bit set: corner sign +1
+    sig[tid][0] = 1.0 / (1.0 + exp(x));   // bit clear: corner sign -1
   }
   __syncthreads();
   const int plo = P < 4 ? P : 4;
   const int phi = P - plo;
-  for (int e = tid; e < L * 32; e += blockDim.x) {
-    const int l = e >> 5, r = e & 31, hf = r >> 4, c = r & 15;
+  for (int e = tid; e < kTabTables * 32; e += kTabThreads) {
+    const int lt = e >> 5, r = e & 31, hf = r >> 4, c = r & 15;
     const int nb = hf ? phi : plo;
     double prod = 0.0;
-    if (c < (1 << nb)) {
+    if (c < (1 << nb) && l0 + lt < L) {
       prod = 1.0;
-      const int p0 = l * P + (hf ? plo : 0);
+      const int p0 = lt * P + (hf ? plo : 0);
       for (int j = 0; j < nb; ++j) prod *= sig[p0 + j][(c >> j) & 1];
     }
-    sub[((int64_t)bg * L + l) * 32 + r] = (float)prod;
+    half[lt][r] = prod;
+  }
+  __syncthreads();
+  // this block's tables: table l = j*TL + m for lane j, member m
+  const int nent = 1 << P;
+  const int lomask = (1 << plo) - 1;
+  for (int i = tid; i < kTabTables * nent; i += kTabThreads) {
+    const int lt = i / nent, e = i % nent;
+    const int l = l0 + lt, j = l / TL, m = l % TL;
+    if (j >= 16 || m >= NF) continue;
+    const float v = l < L ? (float)(half[lt][e & lomask] * half[lt][16 + (e >> plo)]) : 0.f;
+    im[((int64_t)(e * NF + m) * 16 + j) * G + comp] = v;
+  }
+  for (int i = tid; i < kTabTables * 32; i += kTabThreads) {
+    const int lt = i >> 5, hc = i & 31;
+    const int l = l0 + lt, j = l / TL, m = l % TL;
+    if (j >= 16 || m < NF) continue;
+    const float v = l < L ? (float)half[lt][hc] : 0.f;
+    im[FULL + ((int64_t)(hc * NS + (m - NF)) * 16 + j) * G + comp] = v;
   }
 }
 
 // ---------------------------------------------------------------- scorer
 
 template <int G>
-__device__ __forceinline__ void lds_add(const float* lds, int slot, float* acc) {
+__device__ __forceinline__ void lds_get(const float* lds, int slot, float* v) {
   if constexpr (G == 1) {
-    acc[0] += lds[slot];
+    v[0] = lds[slot];
   } else if constexpr (G == 2) {
-    const float2 v = reinterpret_cast<const float2*>(lds)[slot];
-    acc[0] += v.x; acc[1] += v.y;
+    const float2 t = reinterpret_cast<const float2*>(lds)[slot];
+    v[0] = t.x; v[1] = t.y;
   } else {
-    const float4 v = reinterpret_cast<const float4*>(lds)[slot];
-    acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    const float4 t = reinterpret_cast<const float4*>(lds)[slot];
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
   }
-}
-
-// One TL-byte word of bucket IDs (TL <= 8) as two dwords.
-template <int TL>
-__device__ __forceinline__ uint2 load_ids(const uint8_t* p) {
-  uint2 w = make_uint2(0u, 0u);
-  if constexpr (TL == 1) w.x = p[0];
-  else if constexpr (TL == 2) w.x = *reinterpret_cast<const uint16_t*>(p);
-  else if constexpr (TL == 4) w.x = *reinterpret_cast<const uint32_t*>(p);
-  else w = *reinterpret_cast<const uint2*>(p);
-  return w;
-}
-
-template <int B8>
-__device__ __forceinline__ uint32_t id_byte(uint2 w) {
-  return ((B8 < 4 ? w.x : w.y) >> (8 * (B8 & 3))) & 255u;
 }
 
 constexpr int kScoreThreads = 512;
 constexpr int kScoreWaves = kScoreThreads / 64;
-constexpr int kTableFloats = 32768;  // 128 KiB of tables in LDS at a time
-// Half-tables of one chunk, one padded row of G*32 + 2 floats per table, so
-// that the 32 tables a wave reads from in the table build sit in distinct
-// LDS banks; later reused for the histogram (G*1024 <= 4096 words).
-constexpr int kStageFloats = 4352;
-template <int G>
-struct StageRow {
-  static constexpr int value = G * 32 + 2;
-};
-
-// Compile-time shape of the scorer.  G: query heads per KV head; TL: tables
-// (= ID bytes) per lane per key; S: 64-key groups per wave.
-template <int G, int TL, int S>
-struct ScorerShape {
-  static constexpr int MC = (TL < 8 / G) ? TL : 8 / G;  // tables per lane in LDS at a time
-  static constexpr int NCH = TL / MC;                    // chunks
-};
 
 // Reduce-scatter over a 16-lane row.  On entry lane j holds in u[x] its
 // contribution to key (j + x) mod 16 of the row; on exit u[0] of lane j is
@@ -204,19 +283,36 @@ __device__ __forceinline__ void row16_reduce_scatter(float (&u)[16][G]) {
   for (int g = 0; g < G; ++g) u[0][g] += dpp_f32<0x121>(u[1][g]);
 }
 
-// grid: B*Hkv*nblk, block = kScoreThreads threads.  Block blk of (b, h) owns
-// the 64-key groups [blk*gpb, (blk+1)*gpb) (gpb <= kScoreWaves*S); wave w
-// takes groups blk*gpb + w + kScoreWaves*s, s < S.
-template <int G, int TL, int S>
+// The TL-byte ID word of round x from the lane's TL 16-byte vectors.
+template <int TL>
+__device__ __forceinline__ uint2 round_word(const uint4 (&v)[TL], int x) {
+  constexpr int R = 16 / TL;
+  const uint4 q = v[x / R];
+  const int k = x % R;  // word index inside the vector
+  if constexpr (TL == 8) {
+    return k == 0 ? make_uint2(q.x, q.y) : make_uint2(q.z, q.w);
+  } else {
+    const int byte = k * TL;
+    const uint32_t d = byte < 4 ? q.x : byte < 8 ? q.y : byte < 12 ? q.z : q.w;
+    return make_uint2(TL == 4 ? d : (d >> (8 * (byte & 3))) & (TL == 2 ? 0xFFFFu : 0xFFu), 0u);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ uint32_t word_byte(uint2 w) {
+  return ((K < 4 ? w.x : w.y) >> (8 * (K & 3))) & 255u;
+}
+
+// grid: B*Hkv*nblk blocks of kScoreThreads.  Block blk of KV row bh owns the
+// 64-key groups [blk*gpb, (blk+1)*gpb); its waves take them round robin.
+template <int G, int TL>
 __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
-    const float* __restrict__ sub, const uint8_t* __restrict__ ids,
-    const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int L,
-    int P, int64_t n_cap, int nblk, int gpb, float* __restrict__ scores,
-    uint32_t* __restrict__ hist) {
-  using Sh = ScorerShape<G, TL, S>;
-  constexpr int MC = Sh::MC, NCH = Sh::NCH;
-  __shared__ __attribute__((aligned(16))) float tab[kTableFloats];
-  __shared__ __attribute__((aligned(16))) float stage[kStageFloats];
+    const float* __restrict__ img, const uint8_t* __restrict__ ids,
+    const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
+    int64_t n_cap, int nblk, int gpb, float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  using Sh = ImageShape<G, TL>;
+  constexpr int NF = Sh::NF, NS = Sh::NS, FULL = Sh::FULL;
+  __shared__ __attribute__((aligned(16))) float lds[Sh::FLOATS];
   const int blk = blockIdx.x % nblk;
   const int bh = blockIdx.x / nblk;
   const int b = bh / Hkv;
@@ -227,136 +323,106 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   int64_t g_end = (n + 63) >> 6;
   if (g_end > g_begin + gpb) g_end = g_begin + gpb;
   if (g_begin >= g_end) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kg = lane >> 4, j = lane & 15;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15;
   const int bg0 = b * Hq + h * G;
+  const int64_t sst = score_stride(n_cap);
   const int plo = P < 4 ? P : 4;
-  const int lomask = (1 << plo) - 1;
-  const int nent = 1 << P;
-  // first key of this wave's group s (groups past g_end hold no keys)
-  auto gkey = [&](int s) -> int64_t {
-    const int64_t gi = g_begin + wave + (int64_t)kScoreWaves * s;
-    return gi < g_end ? gi * 64 : n;
-  };
+  const uint32_t lomask = (1u << plo) - 1u;
 
-  // Row kg of the wave owns keys kg*16 .. kg*16+15 of each 64-key group; in
-  // round x lane j takes its ID word j of key kg*16 + (j + x) mod 16, which the
-  // tiled ID layout stores at word slot x*64 + lane of the group, so every
-  // load of the wave reads 64 consecutive words.  All bucket IDs, norms and
-  // half-tables this lane will need are requested before any table work.
+  // first group's IDs and norm, then the table image
   const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * TL;
-  uint2 idw[S][16];
-  float vnv[S];
+  const float* vrow = vnorm + (int64_t)bh * n_cap;
+  auto load_group = [&](int64_t gi, uint4 (&v)[TL], float& vn) {
+    if (gi < g_end) {
+      const uint4* src = reinterpret_cast<const uint4*>(idg + gi * 1024 * TL) + lane;
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int64_t k0 = gkey(s);
+      for (int qv = 0; qv < TL; ++qv) v[qv] = src[qv * 64];
+      const int64_t key = gi * 64 + lane;
+      vn = key < n ? vrow[key] : 0.f;
+    }
+  };
+  uint4 cur[TL], nxt[TL];
+  float vcur = 0.f, vnxt = 0.f;
+  int64_t gi = g_begin + wave;
+  load_group(gi, cur, vcur);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(img + (int64_t)bh * Sh::FLOATS);
+    uint4* dst = reinterpret_cast<uint4*>(lds);
+    constexpr int NV = (FULL + Sh::HALF) / 4;
+    for (int i = tid; i < NV; i += kScoreThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  for (; gi < g_end; gi += kScoreWaves) {
+    load_group(gi + kScoreWaves, nxt, vnxt);
+    float u[16][G];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      idw[s][x] = make_uint2(0u, 0u);
-      if (k0 < n) idw[s][x] = load_ids<TL>(idg + ((k0 >> 6) * 1024 + x * 64 + lane) * TL);
-    }
-    const int64_t key = k0 + lane;  // the key this lane finishes
-    vnv[s] = key < n ? vnorm[(int64_t)bh * n_cap + key] : 0.f;
-  }
-  constexpr int ROW = StageRow<G>::value;
-  constexpr int NSTAGE = 16 * MC * G * 32;             // half-table floats per chunk
-  constexpr int SPT = (NSTAGE + kScoreThreads - 1) / kScoreThreads;
-  float stv[NCH][SPT];
+      const uint2 w = round_word<TL>(cur, x);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)
-#pragma unroll
-    for (int q = 0; q < SPT; ++q) {
-      const int i = tid + q * kScoreThreads;
-      const int r = i & 31, rest = i >> 5;
-      const int g = rest % G, m = (rest / G) % MC, jj = rest / (G * MC);
-      const int l = jj * TL + c * MC + m;
-      stv[c][q] = (i < NSTAGE && l < L) ? sub[((int64_t)(bg0 + g) * L + l) * 32 + r] : 0.f;
-    }
-
-  float part[S][G];
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int g = 0; g < G; ++g) part[s][g] = 0.f;
-
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    __syncthreads();
-    // half-tables of this chunk: stage[(jj*MC + m)*ROW + g*32 + r] for table jj*TL + c*MC + m
-#pragma unroll
-    for (int q = 0; q < SPT; ++q) {
-      const int i = tid + q * kScoreThreads;
-      if (i < NSTAGE) {
-        const int r = i & 31, rest = i >> 5;
-        const int g = rest % G, t = rest / G;
-        stage[t * ROW + g * 32 + r] = stv[c][q];
-      }
-    }
-    __syncthreads();
-    // full tables: slot (e*MC + m)*16 + jj holds p_l(e) of the G heads
-    const int nslots = nent * MC * 16;
-    for (int slot = tid; slot < nslots; slot += kScoreThreads) {
-      const int jj = slot & 15;
-      const int m = (slot >> 4) % MC;
-      const int e = slot / (16 * MC);
-      const float* st = stage + (jj * MC + m) * ROW;
-      float v[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) v[g] = st[g * 32 + (e & lomask)] * st[g * 32 + 16 + (e >> plo)];
-      if constexpr (G == 4) {
-        reinterpret_cast<float4*>(tab)[slot] = make_float4(v[0], v[1], v[2], v[3]);
-      } else if constexpr (G == 2) {
-        reinterpret_cast<float2*>(tab)[slot] = make_float2(v[0], v[1]);
-      } else {
-        tab[slot] = v[0];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      float u[16][G];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) u[x][g] = 0.f;
-#pragma unroll
-        for (int m = 0; m < MC; ++m) {
-          uint32_t e;
-          switch (c * MC + m) {
-            case 0: e = id_byte<0>(idw[s][x]); break;
-            case 1: e = id_byte<1>(idw[s][x]); break;
-            case 2: e = id_byte<2>(idw[s][x]); break;
-            case 3: e = id_byte<3>(idw[s][x]); break;
-            case 4: e = id_byte<4>(idw[s][x]); break;
-            case 5: e = id_byte<5>(idw[s][x]); break;
-            case 6: e = id_byte<6>(idw[s][x]); break;
-            default: e = id_byte<7>(idw[s][x]); break;
-          }
-          lds_add<G>(tab, ((int)e * MC + m) * 16 + j, u[x]);
+      for (int m = 0; m < NF; ++m) {
+        uint32_t e;
+        switch (m) {
+          case 0: e = word_byte<0>(w); break;
+          case 1: e = word_byte<1>(w); break;
+          case 2: e = word_byte<2>(w); break;
+          case 3: e = word_byte<3>(w); break;
+          case 4: e = word_byte<4>(w); break;
+          case 5: e = word_byte<5>(w); break;
+          case 6: e = word_byte<6>(w); break;
+          default: e = word_byte<7>(w); break;
         }
+        float v[G];
+        lds_get<G>(lds, ((int)e * NF + m) * 16 + j, v);
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) u[x][gg] = m == 0 ? v[gg] : u[x][gg] + v[gg];
       }
-      row16_reduce_scatter<G>(u);
 #pragma unroll
-      for (int g = 0; g < G; ++g) part[s][g] += u[0][g];
+      for (int m = 0; m < NS; ++m) {
+        uint32_t e;
+        switch (NF + m) {
+          case 0: e = word_byte<0>(w); break;
+          case 1: e = word_byte<1>(w); break;
+          case 2: e = word_byte<2>(w); break;
+          case 3: e = word_byte<3>(w); break;
+          case 4: e = word_byte<4>(w); break;
+          case 5: e = word_byte<5>(w); break;
+          case 6: e = word_byte<6>(w); break;
+          default: e = word_byte<7>(w); break;
+        }
+        float lo[G], hi[G];
+        lds_get<G>(lds + FULL, ((int)(e & lomask) * NS + m) * 16 + j, lo);
+        lds_get<G>(lds + FULL, ((16 + (int)(e >> plo)) * NS + m) * 16 + j, hi);
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+          u[x][gg] = (NF == 0 && m == 0) ? lo[gg] * hi[gg] : fmaf(lo[gg], hi[gg], u[x][gg]);
+      }
     }
-  }
-
-  // scores and the first-digit histogram (in the staging buffer)
-  __syncthreads();
-  uint32_t* lhist = reinterpret_cast<uint32_t*>(stage);
-  for (int i = tid; i < G * kHistBins; i += kScoreThreads) lhist[i] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int64_t key = gkey(s) + lane;
+    row16_reduce_scatter<G>(u);
+    const int64_t key = gi * 64 + lane;
     if (key < n) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float sc = vnv[s] * part[s][g];
-        scores[(int64_t)(bg0 + g) * n_cap + key] = sc;
-        uint32_t dg = __float_as_uint(sc) >> kHistShift;
-        if (dg > kHistBins - 1) dg = kHistBins - 1;
-        atomicAdd(&lhist[g * kHistBins + dg], 1u);
-      }
+      for (int gg = 0; gg < G; ++gg) scores[(int64_t)(bg0 + gg) * sst + key] = vcur * u[0][gg];
+    }
+#pragma unroll
+    for (int qv = 0; qv < TL; ++qv) cur[qv] = nxt[qv];
+    vcur = vnxt;
+  }
+
+  // first-digit histogram of this block's scores (re-read from L2; the
+  // image is no longer needed, its LDS holds the counts)
+  __syncthreads();
+  uint32_t* lhist = reinterpret_cast<uint32_t*>(lds);
+  for (int i = tid; i < G * kHistBins; i += kScoreThreads) lhist[i] = 0u;
+  __syncthreads();
+  int64_t k1 = g_end * 64;
+  if (k1 > n) k1 = n;
+  for (int64_t key = g_begin * 64 + tid; key < k1; key += kScoreThreads) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      uint32_t dg = __float_as_uint(scores[(int64_t)(bg0 + gg) * sst + key]) >> kHistShift;
+      if (dg > kHistBins - 1) dg = kHistBins - 1;
+      atomicAdd(&lhist[gg * kHistBins + dg], 1u);
     }
   }
   __syncthreads();
@@ -425,8 +491,9 @@ __device__ __forceinline__ void clamp_nk(int64_t n_cap, int32_t len, int32_t kk,
 
 // grid: B*Hq*CH blocks of kSelThreads, CH = ceil(n_cap / kSelChunk).
 __global__ __launch_bounds__(kSelThreads) void topk_scan_kernel(
-    const float* __restrict__ scores, int64_t n_cap, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ ks, int k_max, int Hq, int CH, const uint32_t* __restrict__ hist,
+    const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq, int CH,
+    const uint32_t* __restrict__ hist,
     uint32_t* __restrict__ counters, uint32_t* __restrict__ bitmap, int64_t words,
     uint2* __restrict__ cand) {
   const int bg = blockIdx.x / CH;
@@ -441,7 +508,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_scan_kernel(
   if (c0 >= n64) return;
 
   // this lane's scores first (16 keys, one per 64-key group of the wave)
-  const float* srow = scores + (int64_t)bg * n_cap;
+  const float* srow = scores + (int64_t)bg * sstride;
   uint32_t bits[kSelGroups];
 #pragma unroll
   for (int i = 0; i < kSelGroups; ++i) {
@@ -643,14 +710,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_resolve_kernel(
 
 // ---------------------------------------------------------------- launchers
 
-template <int G, int TL, int S>
-static void launch_scorer(int B, int Hkv, int Hq, int L, int P, int64_t n_cap, int nblk, int gpb,
-                          const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
-                          const int32_t* lens, float* scores, hipStream_t s) {
-  scorer_kernel<G, TL, S><<<(unsigned)(B * Hkv * nblk), kScoreThreads, 0, s>>>(
-      ws.sub, ids, vnorm, lens, Hq, Hkv, L, P, n_cap, nblk, gpb, scores, ws.hist);
-}
-
 static int device_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -663,59 +722,49 @@ static int device_cus() {
   return cus;
 }
 
-// Split the 64-key groups of every (b, h) over blocks so that the grid fills
-// the CUs once (one scorer block fits per CU), within the S groups per wave
-// that the register budget allows.
 template <int G, int TL>
-static void launch_scorer_s(int B, int Hkv, int Hq, int L, int P, int64_t n_cap,
-                            const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
-                            const int32_t* lens, float* scores, hipStream_t s) {
-  constexpr int SMAX = G == 4 ? (TL == 8 ? 1 : 4) : (TL == 8 ? 2 : (G == 2 ? 4 : 8));
-  const int64_t ng = (n_cap + 63) / 64;
-  const int64_t heads = (int64_t)B * Hkv;
-  int64_t nblk = (device_cus() + heads - 1) / heads;
+static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, const ScoreWs& ws,
+                          const uint8_t* ids, const float* vnorm, const int32_t* lens,
+                          float* scores, hipStream_t s) {
+  // one block per CU: the 64-key groups of every KV row are split evenly
+  const int64_t ng = ids_groups(n_cap);
+  const int64_t rows = (int64_t)B * Hkv;
+  int64_t nblk = (device_cus() + rows - 1) / rows;
   if (nblk > ng) nblk = ng;
-  int64_t gpb = (ng + nblk - 1) / nblk;
-  if (gpb > (int64_t)kScoreWaves * SMAX) {
-    gpb = (int64_t)kScoreWaves * SMAX;
-    nblk = (ng + gpb - 1) / gpb;
-  }
-  const int need = (int)((gpb + kScoreWaves - 1) / kScoreWaves);
-  const int nb = (int)nblk, gp = (int)gpb;
-  if constexpr (SMAX >= 8) {
-    if (need > 4) return launch_scorer<G, TL, 8>(B, Hkv, Hq, L, P, n_cap, nb, gp, ws, ids, vnorm, lens, scores, s);
-  }
-  if constexpr (SMAX >= 4) {
-    if (need > 2) return launch_scorer<G, TL, 4>(B, Hkv, Hq, L, P, n_cap, nb, gp, ws, ids, vnorm, lens, scores, s);
-  }
-  if constexpr (SMAX >= 2) {
-    if (need > 1) return launch_scorer<G, TL, 2>(B, Hkv, Hq, L, P, n_cap, nb, gp, ws, ids, vnorm, lens, scores, s);
-  }
-  launch_scorer<G, TL, 1>(B, Hkv, Hq, L, P, n_cap, nb, gp, ws, ids, vnorm, lens, scores, s);
+  const int64_t gpb = (ng + nblk - 1) / nblk;
+  nblk = (ng + gpb - 1) / gpb;
+  scorer_kernel<G, TL><<<(unsigned)(rows * nblk), kScoreThreads, 0, s>>>(
+      ws.img, ids, vnorm, lens, Hq, Hkv, P, n_cap, (int)nblk, (int)gpb, scores, ws.hist);
 }
 
 template <int G>
 static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap,
                             const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
                             const int32_t* lens, float* scores, hipStream_t s) {
-  const int per_lane = ids_word_bytes(L);  // tables per lane
-  if (per_lane <= 1) launch_scorer_s<G, 1>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s);
-  else if (per_lane <= 2) launch_scorer_s<G, 2>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s);
-  else if (per_lane <= 4) launch_scorer_s<G, 4>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s);
-  else launch_scorer_s<G, 8>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s);
+  switch (ids_word_bytes(L)) {
+    case 1: launch_scorer<G, 1>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer<G, 2>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    case 4: launch_scorer<G, 4>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer<G, 8>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+  }
 }
 
-hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, const void* W, int L,
-                              int P, float tau, const ScoreWs& ws, hipStream_t s) {
+hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
+                              int L, int P, float tau, const ScoreWs& ws, hipStream_t s) {
+  const int G = Hq / Hkv;
+  const ImageDims im = image_dims(G, L);
   const int heads = B * Hq;
+  // tables of a padded lane word (l >= L) must be written too, so cover 16*TL
+  const int ntb = (16 * im.TL + kTabTables - 1) / kTabTables;
+  const unsigned grid = (unsigned)(heads * ntb);
   if (dtype == 1)
-    soft_tables_kernel<uint16_t><<<heads, 256, 0, s>>>(static_cast<const uint16_t*>(q),
-                                                       static_cast<const uint16_t*>(W), L, P,
-                                                       tau, ws.sub, ws.hist, ws.counters);
+    soft_tables_kernel<uint16_t><<<grid, kTabThreads, 0, s>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(W), Hq, Hkv, L, P, tau,
+        G, im.TL, im.NF, im.NS, im.full, im.floats, ntb, ws.img, ws.hist, ws.counters);
   else
-    soft_tables_kernel<float><<<heads, 256, 0, s>>>(static_cast<const float*>(q),
-                                                    static_cast<const float*>(W), L, P, tau,
-                                                    ws.sub, ws.hist, ws.counters);
+    soft_tables_kernel<float><<<grid, kTabThreads, 0, s>>>(
+        static_cast<const float*>(q), static_cast<const float*>(W), Hq, Hkv, L, P, tau, G,
+        im.TL, im.NF, im.NS, im.full, im.floats, ntb, ws.img, ws.hist, ws.counters);
   return hipGetLastError();
 }
 
@@ -735,7 +784,8 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
                        hipStream_t s) {
   const int CH = (int)((n_cap + kSelChunk - 1) / kSelChunk);
   topk_scan_kernel<<<(unsigned)(B * Hq * CH), kSelThreads, 0, s>>>(
-      scores, n_cap, lens, ks, k_max, Hq, CH, ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
+      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, CH, ws.hist, ws.counters,
+      ws.bitmap, ws.words, ws.cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_resolve_kernel<<<(unsigned)(B * Hq), kSelThreads, 0, s>>>(

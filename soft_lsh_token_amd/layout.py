@@ -35,7 +35,9 @@ def _perm(L: int):
     w = np.arange(16)[None, :, None]
     b = np.arange(TL)[None, None, :]
     kg, x = t // 16, t % 16
-    slot = ((x - w) % 16) * 64 + 16 * kg + w
+    R = 16 // TL
+    r = (x - w) % 16
+    slot = (r // R) * 64 * R + (16 * kg + w) * R + r % R
     return slot * TL + b          # [64, 16, TL]
 
 

@@ -61,7 +61,7 @@ def gpu_score_topk(w, d, ids, vnorm, lens=None, ks=None, k_max=None, q=None):
     k_max = w.k_max if k_max is None else k_max
     q = d["q"] if q is None else q
     idx = torch.full((w.B, w.Hq, k_max), -7, dtype=torch.int32, device=DEV)
-    scores = torch.zeros(w.B, w.Hq, w.n_cap, dtype=torch.float32, device=DEV)
+    scores = torch.zeros(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=DEV)
     S.socket_score_topk(q, d["W"], ids, vnorm, lens, ks, k_max, w.tau, w.L, w.P, idx, scores)
     return idx, scores
 

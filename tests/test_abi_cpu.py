@@ -35,11 +35,13 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    a = S.socket_score_topk_workspace(1, 32, 32768, 64, 8, 656)
-    b = S.socket_score_topk_workspace(1, 32, 131072, 64, 8, 1024)
+    a = S.socket_score_topk_workspace(1, 32, 8, 32768, 64, 8, 656)
+    b = S.socket_score_topk_workspace(1, 32, 8, 131072, 64, 8, 1024)
     assert 0 < a < b
     assert a % 256 == 0
-    assert S.socket_score_topk_workspace(0, 32, 32768, 64, 8, 656) == 0
+    assert S.socket_score_topk_workspace(0, 32, 8, 32768, 64, 8, 656) == 0
+    assert S.socket_score_topk_workspace(1, 32, 4, 32768, 64, 8, 656) == 0  # 8 heads per KV head
+    assert S.socket_score_topk_workspace(1, 32, 8, 32768, 129, 8, 656) == 0
     assert S.socket_sparse_decode_workspace(1, 32, 128, 1024) > 0
     assert S.socket_sparse_decode_workspace(1, 32, 64, 1024) == 0
 
@@ -65,7 +67,7 @@ def test_hash_argument_checks():
 
 def _score(**kw):
     B, Hq, n_cap, L, P, k_max = 1, 32, 1024, 64, 8, 32
-    need = S.socket_score_topk_workspace(B, Hq, n_cap, L, P, k_max)
+    need = S.socket_score_topk_workspace(B, Hq, 8, n_cap, L, P, k_max)
     args = dict(q=FAKE, dtype=1, B=B, Hq=Hq, Hkv=8, d=128, W=FAKE, L=L, P=P, tau=0.5, ids=FAKE,
                 vnorm=FAKE, lens=FAKE, n_cap=n_cap, ks=FAKE, k_max=k_max, idx=FAKE, scores=None,
                 ws=FAKE, ws_bytes=need, stream=None)
@@ -118,20 +120,20 @@ def test_binding_rejects_host_tensors():
 
 def test_stage_argument_checks():
     lib = S.lib()
-    need = S.socket_score_topk_workspace(1, 32, 1024, 64, 8, 32)
-    # socket_soft_tables(q, dtype, B, Hq, d, W, L, P, tau, n_cap, ws, ws_bytes, stream)
-    assert lib.socket_soft_tables(None, 1, 1, 32, 128, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EINVAL
-    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 128, FAKE, 64, 8, -1.0, 1024, FAKE, need, None) == EINVAL
-    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 64, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EUNSUP
-    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 128, FAKE, 64, 8, 0.5, 1024, FAKE, 64, None) == ENOSPC
+    need = S.socket_score_topk_workspace(1, 32, 8, 1024, 64, 8, 32)
+    # socket_soft_tables(q, dtype, B, Hq, Hkv, d, W, L, P, tau, n_cap, ws, ws_bytes, stream)
+    assert lib.socket_soft_tables(None, 1, 1, 32, 8, 128, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EINVAL
+    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 8, 128, FAKE, 64, 8, -1.0, 1024, FAKE, need, None) == EINVAL
+    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 8, 64, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EUNSUP
+    assert lib.socket_soft_tables(FAKE, 1, 1, 32, 8, 128, FAKE, 64, 8, 0.5, 1024, FAKE, 64, None) == ENOSPC
     # socket_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, scores, ws, ws_bytes, stream)
     assert lib.socket_score(1, 32, 8, 64, 8, None, FAKE, FAKE, 1024, FAKE, FAKE, need, None) == EINVAL
     assert lib.socket_score(1, 32, 5, 64, 8, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, need, None) == EINVAL
     assert lib.socket_score(1, 32, 8, 64, 8, FAKE, FAKE, FAKE, 1024, FAKE, None, need, None) == EINVAL
-    # socket_topk(B, Hq, L, scores, lens, n_cap, ks, k_max, idx, ws, ws_bytes, stream)
-    assert lib.socket_topk(1, 32, 64, FAKE, FAKE, 1024, FAKE, 0, FAKE, FAKE, need, None) == EINVAL
-    assert lib.socket_topk(1, 32, 64, FAKE, None, 1024, FAKE, 32, FAKE, FAKE, need, None) == EINVAL
-    assert lib.socket_topk(1, 32, 64, FAKE, FAKE, 1024, FAKE, 32, FAKE, FAKE, 16, None) == ENOSPC
+    # socket_topk(B, Hq, Hkv, L, scores, lens, n_cap, ks, k_max, idx, ws, ws_bytes, stream)
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 0, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, None, 1024, FAKE, 32, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 32, FAKE, FAKE, 16, None) == ENOSPC
 
 
 @pytest.mark.parametrize("L", [3, 16, 20, 32, 60, 64, 100, 128])
@@ -154,6 +156,7 @@ def test_ids_layout_roundtrip_and_formula(L):
         r, w, byte = b * Hkv + h, l // TL, l % TL
         t = i % 64
         kg, x = t // 16, t % 16
-        off = ((r * G + i // 64) * 1024 + ((x - w) % 16) * 64 + 16 * kg + w) * TL + byte
+        u, R = (x - w) % 16, 16 // TL
+        off = ((r * G + i // 64) * 1024 + (u // R) * 64 * R + (16 * kg + w) * R + u % R) * TL + byte
         assert flat[off] == ids[b, h, i, l]
     assert S.socket_ids_bytes(1, 1, 10, 129) == 0

@@ -319,13 +319,13 @@ def test_stage_entry_points_match_fused_call():
     d = GC.upload(w)
     ids, vn = GC.gpu_hash(w, d)
     idx1, sc1 = GC.gpu_score_topk(w, d, ids, vn)
-    ws = S.alloc_workspace(S.socket_score_topk_workspace(w.B, w.Hq, w.n_cap, w.L, w.P, w.k_max),
+    ws = S.alloc_workspace(S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, w.k_max),
                            DEV)
     sc2 = torch.zeros_like(sc1)
     idx2 = torch.full_like(idx1, -7)
-    S.socket_soft_tables(d["q"], d["W"], w.L, w.P, w.tau, w.n_cap, ws)
+    S.socket_soft_tables(d["q"], d["W"], w.Hkv, w.L, w.P, w.tau, w.n_cap, ws)
     S.socket_score(ids, vn, d["lens"], w.Hq, w.L, w.P, sc2, ws)
-    S.socket_topk(sc2, d["lens"], d["ks"], w.L, idx2, ws)
+    S.socket_topk(sc2, d["lens"], d["ks"], w.Hkv, w.L, w.n_cap, idx2, ws)
     sync()
     assert torch.equal(sc1, sc2)
     assert torch.equal(idx1, idx2)
