@@ -3,26 +3,26 @@
 //
 // Soft hashing: table l gives bucket c the probability
 //   p_l(c) = softmax_c( sum_j s_j(c) u_lj / tau ),  s_j(c) = +1 if bit j of c else -1,
-// which factorises over the planes as prod_j sigmoid(2 s_j(c) u_lj / tau).
-// Every table is therefore split into a low half (planes 0..3) and a high
-// half (planes 4..P-1) of at most 16 entries each; the scorer rebuilds
-// p_l(c) = lo_l(c & 15) * hi_l(c >> 4) in LDS.  The projections u = W q are
-// taken in float64.
+// which factorises over the planes as prod_j sigmoid(2 s_j(c) u_lj / tau), so
+// p_l(c) = lo_l(c & 15) * hi_l(c >> 4) with 16-entry halves over planes 0..3
+// and 4..P-1.  The projections u = W q are taken in float64.
+//
+// The soft-tables kernel writes, per KV head, an image of the tables of its G
+// query heads laid out for the scorer's LDS: as many tables as fit kept in
+// full (one lookup per key), the rest as their two halves (two lookups and a
+// multiply).  One image slot holds the G heads' values of one entry, so one
+// 16-byte LDS read serves all G query heads.
 //
 // Scorer (one pass per KV head for all of its GQA query heads): lane j of a
-// 16-lane row owns TL consecutive tables (j*TL .. j*TL+TL-1), so it reads one
-// TL-byte word of bucket IDs per key.  The tables of the G query heads are
-// interleaved in LDS as
-//   slot(c, m, j) = (c * MC + m) * 16 + j,   one slot = G floats,
-// for member m of the MC tables per lane held in LDS at a time.  A row works
-// on one key at a time, so its 16 lookups fall into 16 different 16-byte
-// bank groups whatever the bucket IDs are (gfx950 serves 16 lanes of a
-// ds_read_b128 per cycle).  Per-lane partial sums are reduced across the row
-// with DPP.  When the tables of the G heads do not fit in 128 KiB at once
-// (G = 4: 64 tables x 256 entries x 16 B = 256 KiB) they are rebuilt in
-// chunks; the IDs and value norms of all the workgroup's keys are loaded
-// into registers before the first chunk, so their HBM latency hides behind
-// the table build and no ID byte is read twice.
+// 16-lane row owns TL consecutive tables (j*TL .. j*TL+TL-1) and reads their
+// bucket IDs as TL-byte words out of the 16-byte per-lane vectors of the
+// tiled ID cache.  Each of the 16 rounds of a 64-key group gives lane j key
+// (j + x) mod 16 of its row, and the image slots of lane j sit in bank group
+// j, so the 16 lookups of a row never collide whatever the bucket IDs are
+// (gfx950 serves 16 lanes of a ds_read_b128 per cycle).  A rotated
+// reduce-scatter over the row (DPP row_ror) leaves each lane the full sum of
+// its own key.  Blocks of one KV head are placed on one XCD so that its image
+// is fetched from HBM into one L2 only.
 //
 // Top-k: the scorer also builds, per query head, a histogram of the top
 // digit of the float32 score bits (scores are non-negative, so their bit
@@ -49,11 +49,11 @@ namespace socketlsh {
 //                                            (planes 4..P-1), c < 16, m < NS
 // one slot = G floats (the G query heads).  Bank group of a slot = j, so the
 // 16 lookups of a row never collide.  NF is the largest count whose image
-// fits in LDS next to nothing else (the histogram reuses the image).
+// fits in the 160 KiB of LDS next to the G-head score histogram.
 template <int G, int TL>
 struct ImageShape {
   static constexpr bool fit(int nf) {
-    return 256 * nf * 16 * G + 2 * 16 * (TL - nf) * 16 * G <= 38400;  // 150 KiB
+    return 256 * nf * 16 * G + 2 * 16 * (TL - nf) * 16 * G <= 40960 - G * kHistBins;
   }
   static constexpr int pick() {
     int nf = 0;
@@ -65,7 +65,7 @@ struct ImageShape {
   static constexpr int NS = TL - NF;
   static constexpr int FULL = 256 * NF * 16 * G;   // floats
   static constexpr int HALF = 2 * 16 * NS * 16 * G;
-  static constexpr int FLOATS = FULL + HALF > G * kHistBins ? FULL + HALF : G * kHistBins;
+  static constexpr int FLOATS = FULL + HALF;
 };
 
 struct ImageDims {
@@ -260,28 +260,11 @@ __device__ __forceinline__ void lds_get(const float* lds, int slot, float* v) {
 constexpr int kScoreThreads = 512;
 constexpr int kScoreWaves = kScoreThreads / 64;
 
-// Reduce-scatter over a 16-lane row.  On entry lane j holds in u[x] its
-// contribution to key (j + x) mod 16 of the row; on exit u[0] of lane j is
-// the sum over the 16 lanes for key j.  Stage d adds, for x < d, the value
-// lane j - d holds for the same key (its slot x + d); row_ror:d gives lane j
-// the register of lane (j - d) mod 16.
-template <int G>
-__device__ __forceinline__ void row16_reduce_scatter(float (&u)[16][G]) {
-#pragma unroll
-  for (int x = 0; x < 8; ++x)
-#pragma unroll
-    for (int g = 0; g < G; ++g) u[x][g] += dpp_f32<0x128>(u[x + 8][g]);
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int g = 0; g < G; ++g) u[x][g] += dpp_f32<0x124>(u[x + 4][g]);
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int g = 0; g < G; ++g) u[x][g] += dpp_f32<0x122>(u[x + 2][g]);
-#pragma unroll
-  for (int g = 0; g < G; ++g) u[0][g] += dpp_f32<0x121>(u[1][g]);
-}
+// Reduce-scatter over a 16-lane row (see score_group): on entry lane j holds
+// in u[x] its contribution to key (j + x) mod 16 of the row; on exit u[0] of
+// lane j is the sum over the 16 lanes for key j.  Stage d adds, for x < d,
+// the value lane j - d holds for the same key (its slot x + d); row_ror:d
+// gives lane j the register of lane (j - d) mod 16.
 
 // The TL-byte ID word of round x from the lane's TL 16-byte vectors.
 template <int TL>
@@ -303,18 +286,130 @@ __device__ __forceinline__ uint32_t word_byte(uint2 w) {
   return ((K < 4 ? w.x : w.y) >> (8 * (K & 3))) & 255u;
 }
 
-// grid: B*Hkv*nblk blocks of kScoreThreads.  Block blk of KV row bh owns the
-// 64-key groups [blk*gpb, (blk+1)*gpb); its waves take them round robin.
+constexpr int kXcds = 8;      // workgroup i of a dispatch runs on XCD i mod 8
+constexpr int kPrefetch = 1;  // 64-key groups of IDs each wave keeps in flight
+
+// The lookups of one round: NF full-table slots and NS lo/hi half slots.
+template <int NF, int NS, int G>
+struct RoundVals {
+  float f[NF > 0 ? NF : 1][G];
+  float lo[NS > 0 ? NS : 1][G];
+  float hi[NS > 0 ? NS : 1][G];
+};
+
+template <int M>
+__device__ __forceinline__ uint32_t id_byte(uint2 w) {
+  if constexpr (M == 0) return word_byte<0>(w);
+  else if constexpr (M == 1) return word_byte<1>(w);
+  else if constexpr (M == 2) return word_byte<2>(w);
+  else if constexpr (M == 3) return word_byte<3>(w);
+  else if constexpr (M == 4) return word_byte<4>(w);
+  else if constexpr (M == 5) return word_byte<5>(w);
+  else if constexpr (M == 6) return word_byte<6>(w);
+  else return word_byte<7>(w);
+}
+
+template <int NF, int NS, int G, int M = 0>
+__device__ __forceinline__ void issue_full(const float* lds, uint2 w, int j, RoundVals<NF, NS, G>& r) {
+  if constexpr (M < NF) {
+    lds_get<G>(lds, ((int)id_byte<M>(w) * NF + M) * 16 + j, r.f[M]);
+    issue_full<NF, NS, G, M + 1>(lds, w, j, r);
+  }
+}
+
+template <int NF, int NS, int G, int M = 0>
+__device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, uint32_t lomask, int plo,
+                                           RoundVals<NF, NS, G>& r) {
+  if constexpr (M < NS) {
+    const uint32_t e = id_byte<NF + M>(w);
+    lds_get<G>(lds, ((int)(e & lomask) * NS + M) * 16 + j, r.lo[M]);
+    lds_get<G>(lds, ((16 + (int)(e >> plo)) * NS + M) * 16 + j, r.hi[M]);
+    issue_half<NF, NS, G, M + 1>(lds, w, j, lomask, plo, r);
+  }
+}
+
+template <int NF, int NS, int G>
+__device__ __forceinline__ void round_sum(const RoundVals<NF, NS, G>& r, float (&acc)[G]) {
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    float a = NF > 0 ? r.f[0][gg] : r.lo[0][gg] * r.hi[0][gg];
+#pragma unroll
+    for (int m = 1; m < NF; ++m) a += r.f[m][gg];
+#pragma unroll
+    for (int m = NF > 0 ? 0 : 1; m < NS; ++m) a = fmaf(r.lo[m][gg], r.hi[m][gg], a);
+    acc[gg] = a;
+  }
+}
+
+// Soft-count sums of one 64-key group: 16 rounds, round x giving lane j its
+// tables' share of key (j + x) mod 16 of its row; the LDS lookups of round
+// x + 1 are issued before round x is summed.  The first reduce-scatter stage
+// (row_ror 8) is applied as soon as round x + 8 is summed, so only 8 rounds of
+// partial sums stay live.  On exit u[0] of lane j holds the sums of its key.
+template <int NF, int NS, int G, int TL>
+__device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[TL], int j,
+                                            uint32_t lomask, int plo, float (&u)[8][G]) {
+  constexpr int FULL = 256 * NF * 16 * G;
+  RoundVals<NF, NS, G> cur, nxt;
+  {
+    const uint2 w = round_word<TL>(ids, 0);
+    issue_full<NF, NS, G>(lds, w, j, cur);
+    issue_half<NF, NS, G>(lds + FULL, w, j, lomask, plo, cur);
+  }
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    if (x < 15) {
+      const uint2 w = round_word<TL>(ids, x + 1);
+      issue_full<NF, NS, G>(lds, w, j, nxt);
+      issue_half<NF, NS, G>(lds + FULL, w, j, lomask, plo, nxt);
+    }
+    float acc[G];
+    round_sum<NF, NS, G>(cur, acc);
+    if (x < 8) {
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) u[x][gg] = acc[gg];
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) u[x - 8][gg] += dpp_f32<0x128>(acc[gg]);
+    }
+    cur = nxt;
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int g = 0; g < G; ++g) u[x][g] += dpp_f32<0x124>(u[x + 4][g]);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int g = 0; g < G; ++g) u[x][g] += dpp_f32<0x122>(u[x + 2][g]);
+#pragma unroll
+  for (int g = 0; g < G; ++g) u[0][g] += dpp_f32<0x121>(u[1][g]);
+}
+
+// grid: a multiple of kXcds blocks of kScoreThreads, at least B*Hkv*nblk.
+// Logical block lid = (blockIdx mod 8) * (grid / 8) + blockIdx / 8 keeps
+// consecutive logical blocks -- the blocks of one KV row -- on one XCD.
+// Logical block blk of KV row bh owns the 64-key groups
+// [blk*gpb, (blk+1)*gpb); its waves take them round robin, each keeping the
+// IDs of its next kPrefetch groups in flight (a ring of registers, indexed
+// by compile-time constants so no copy waits on a load).  Each score also
+// goes into an LDS histogram of its top digit, merged into the head's global
+// histogram at the end.
 template <int G, int TL>
 __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     const float* __restrict__ img, const uint8_t* __restrict__ ids,
     const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
-    int64_t n_cap, int nblk, int gpb, float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    int64_t n_cap, int rows, int nblk, int gpb, float* __restrict__ scores,
+    uint32_t* __restrict__ hist) {
   using Sh = ImageShape<G, TL>;
-  constexpr int NF = Sh::NF, NS = Sh::NS, FULL = Sh::FULL;
+  constexpr int NF = Sh::NF, NS = Sh::NS;
+  constexpr int D = kPrefetch;
   __shared__ __attribute__((aligned(16))) float lds[Sh::FLOATS];
-  const int blk = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
+  __shared__ uint32_t lhist[G * kHistBins];
+  const int lid = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  if (lid >= rows * nblk) return;
+  const int blk = lid % nblk;
+  const int bh = lid / nblk;
   const int b = bh / Hkv;
   const int h = bh % Hkv;
   int64_t n = lens[b];
@@ -323,106 +418,74 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   int64_t g_end = (n + 63) >> 6;
   if (g_end > g_begin + gpb) g_end = g_begin + gpb;
   if (g_begin >= g_end) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bg0 = b * Hq + h * G;
   const int64_t sst = score_stride(n_cap);
   const int plo = P < 4 ? P : 4;
   const uint32_t lomask = (1u << plo) - 1u;
 
-  // first group's IDs and norm, then the table image
+  // The first D groups' IDs and norms, then the table image.  Group loads
+  // are issued unconditionally (a group past the block's range re-reads its
+  // last group, keys past n_cap re-read the last norm) so that no branch sits
+  // between a load and its use and each wait covers only the group needed.
   const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * TL;
   const float* vrow = vnorm + (int64_t)bh * n_cap;
   auto load_group = [&](int64_t gi, uint4 (&v)[TL], float& vn) {
-    if (gi < g_end) {
-      const uint4* src = reinterpret_cast<const uint4*>(idg + gi * 1024 * TL) + lane;
+    const int64_t gl = gi < g_end ? gi : g_end - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * TL) + lane;
 #pragma unroll
-      for (int qv = 0; qv < TL; ++qv) v[qv] = src[qv * 64];
-      const int64_t key = gi * 64 + lane;
-      vn = key < n ? vrow[key] : 0.f;
-    }
+    for (int qv = 0; qv < TL; ++qv) v[qv] = src[qv * 64];
+    const int64_t key = gl * 64 + lane;
+    vn = vrow[key < n_cap ? key : n_cap - 1];
   };
-  uint4 cur[TL], nxt[TL];
-  float vcur = 0.f, vnxt = 0.f;
+  uint4 buf[D + 1][TL];
+  float vb[D + 1];
   int64_t gi = g_begin + wave;
-  load_group(gi, cur, vcur);
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_group(gi + (int64_t)d * kScoreWaves, buf[d], vb[d]);
   {
+    // The image goes straight from global memory into LDS (16 bytes per lane,
+    // no registers), every load of the block in flight at once.
     const uint4* src = reinterpret_cast<const uint4*>(img + (int64_t)bh * Sh::FLOATS);
     uint4* dst = reinterpret_cast<uint4*>(lds);
-    constexpr int NV = (FULL + Sh::HALF) / 4;
-    for (int i = tid; i < NV; i += kScoreThreads) dst[i] = src[i];
+    constexpr int NV = Sh::FLOATS / 4;
+    constexpr int PER = (NV + kScoreThreads - 1) / kScoreThreads;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int base = k * kScoreThreads + wave * 64;  // this wave's 64 vectors
+      if (NV % kScoreThreads == 0 || base + lane < NV)
+        __builtin_amdgcn_global_load_lds(src + base + lane, dst + base, 16, 0, 0);
+    }
+    for (int i = tid; i < G * kHistBins; i += kScoreThreads) lhist[i] = 0u;
+    __builtin_amdgcn_s_waitcnt(0);  // the LDS writes of those loads have landed
   }
   __syncthreads();
 
-  for (; gi < g_end; gi += kScoreWaves) {
-    load_group(gi + kScoreWaves, nxt, vnxt);
-    float u[16][G];
+  bool more = gi < g_end;
+  while (more) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const uint2 w = round_word<TL>(cur, x);
+    for (int s = 0; s <= D; ++s) {
+      if (more) {
+        load_group(gi + (int64_t)D * kScoreWaves, buf[(s + D) % (D + 1)], vb[(s + D) % (D + 1)]);
+        float u[8][G];
+        score_group<NF, NS, G, TL>(lds, buf[s], j, lomask, plo, u);
+        const int64_t key = gi * 64 + lane;
+        const bool valid = key < n;
 #pragma unroll
-      for (int m = 0; m < NF; ++m) {
-        uint32_t e;
-        switch (m) {
-          case 0: e = word_byte<0>(w); break;
-          case 1: e = word_byte<1>(w); break;
-          case 2: e = word_byte<2>(w); break;
-          case 3: e = word_byte<3>(w); break;
-          case 4: e = word_byte<4>(w); break;
-          case 5: e = word_byte<5>(w); break;
-          case 6: e = word_byte<6>(w); break;
-          default: e = word_byte<7>(w); break;
+        for (int gg = 0; gg < G; ++gg) {
+          const float sv = vb[s] * u[0][gg];
+          uint32_t dg = __float_as_uint(sv) >> kHistShift;
+          if (dg > kHistBins - 1) dg = kHistBins - 1;
+          atomicAdd(&lhist[gg * kHistBins + dg], valid ? 1u : 0u);
         }
-        float v[G];
-        lds_get<G>(lds, ((int)e * NF + m) * 16 + j, v);
+        if (valid) {
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) u[x][gg] = m == 0 ? v[gg] : u[x][gg] + v[gg];
-      }
-#pragma unroll
-      for (int m = 0; m < NS; ++m) {
-        uint32_t e;
-        switch (NF + m) {
-          case 0: e = word_byte<0>(w); break;
-          case 1: e = word_byte<1>(w); break;
-          case 2: e = word_byte<2>(w); break;
-          case 3: e = word_byte<3>(w); break;
-          case 4: e = word_byte<4>(w); break;
-          case 5: e = word_byte<5>(w); break;
-          case 6: e = word_byte<6>(w); break;
-          default: e = word_byte<7>(w); break;
+          for (int gg = 0; gg < G; ++gg) scores[(int64_t)(bg0 + gg) * sst + key] = vb[s] * u[0][gg];
         }
-        float lo[G], hi[G];
-        lds_get<G>(lds + FULL, ((int)(e & lomask) * NS + m) * 16 + j, lo);
-        lds_get<G>(lds + FULL, ((16 + (int)(e >> plo)) * NS + m) * 16 + j, hi);
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg)
-          u[x][gg] = (NF == 0 && m == 0) ? lo[gg] * hi[gg] : fmaf(lo[gg], hi[gg], u[x][gg]);
+        gi += kScoreWaves;
+        more = gi < g_end;
       }
-    }
-    row16_reduce_scatter<G>(u);
-    const int64_t key = gi * 64 + lane;
-    if (key < n) {
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) scores[(int64_t)(bg0 + gg) * sst + key] = vcur * u[0][gg];
-    }
-#pragma unroll
-    for (int qv = 0; qv < TL; ++qv) cur[qv] = nxt[qv];
-    vcur = vnxt;
-  }
-
-  // first-digit histogram of this block's scores (re-read from L2; the
-  // image is no longer needed, its LDS holds the counts)
-  __syncthreads();
-  uint32_t* lhist = reinterpret_cast<uint32_t*>(lds);
-  for (int i = tid; i < G * kHistBins; i += kScoreThreads) lhist[i] = 0u;
-  __syncthreads();
-  int64_t k1 = g_end * 64;
-  if (k1 > n) k1 = n;
-  for (int64_t key = g_begin * 64 + tid; key < k1; key += kScoreThreads) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      uint32_t dg = __float_as_uint(scores[(int64_t)(bg0 + gg) * sst + key]) >> kHistShift;
-      if (dg > kHistBins - 1) dg = kHistBins - 1;
-      atomicAdd(&lhist[gg * kHistBins + dg], 1u);
     }
   }
   __syncthreads();
@@ -733,8 +796,10 @@ static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, const Sc
   if (nblk > ng) nblk = ng;
   const int64_t gpb = (ng + nblk - 1) / nblk;
   nblk = (ng + gpb - 1) / gpb;
-  scorer_kernel<G, TL><<<(unsigned)(rows * nblk), kScoreThreads, 0, s>>>(
-      ws.img, ids, vnorm, lens, Hq, Hkv, P, n_cap, (int)nblk, (int)gpb, scores, ws.hist);
+  const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
+  scorer_kernel<G, TL><<<(unsigned)grid, kScoreThreads, 0, s>>>(
+      ws.img, ids, vnorm, lens, Hq, Hkv, P, n_cap, (int)rows, (int)nblk, (int)gpb, scores,
+      ws.hist);
 }
 
 template <int G>
