@@ -59,6 +59,20 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// OR over each group of 8 lanes (quad swaps, then the mirror inside each
+// half row, which pairs lane i with lane 7 - i of the other quad).
+__device__ __forceinline__ uint32_t or8_lanes(uint32_t x) {
+  x |= dpp_u32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x |= dpp_u32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x |= dpp_u32<0x141>(x);  // row_half_mirror
+  return x;
+}
+
 // Butterfly sum over each row of 16 lanes; every lane of the row gets the
 // same total (each level adds the same two operands in every lane).
 __device__ __forceinline__ float row16_sum(float x) {

@@ -14,17 +14,16 @@ struct ScoreWs {
   float* img;           // [B*Hkv][img_floats]  LDS images of the soft tables
   int img_floats;
   uint32_t* hist;       // [B*Hq][kHistBins]
-  uint32_t* counters;   // [B*Hq][4]  {candidates, done tickets, -, -}
-  uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/64)*2
-  uint2* cand;          // [B*Hq][n_cap]  (score bits, key index)
-  float* scores;        // [B*Hq][n_cap]  when the caller passes no score buffer
+  uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/4096)*128
+  uint2* cand;          // [B*Hq][n_cap]  candidates past the LDS capacity (score bits, key)
+  float* scores;        // [B*Hq][ns]  when the caller passes no score buffer
   int64_t words;
 };
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base);
 
 // Algorithm 2, part 1: the soft tables of every query head, written as the
-// scorer's LDS images; clears the histograms and counters of the selection.
+// scorer's LDS images; clears the selection histograms.
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
                               int L, int P, float tau, const ScoreWs& ws, hipStream_t s);
 

@@ -26,12 +26,11 @@
 //
 // Top-k: the scorer also builds, per query head, a histogram of the top
 // digit of the float32 score bits (scores are non-negative, so their bit
-// patterns order like the values).  The scan kernel finds the bin holding
-// the k-th largest score, marks every key above it in a bitmap and collects
-// the keys of that bin as candidates; the resolve kernel settles the
-// candidates exactly (radix select on the remaining score bits, then on the
-// index so that the lower index wins a tie) and turns the bitmap into
-// ascending indices.
+// patterns order like the values).  One select workgroup per query head then
+// finds the bin holding the k-th largest score, marks every key above it in
+// a bitmap, collects the keys of that bin as candidates, settles them exactly
+// (radix select on the remaining score bits, then on the index so that the
+// lower index wins a tie) and turns the bitmap into ascending indices.
 #include <type_traits>
 
 #include "common.h"
@@ -102,15 +101,19 @@ static ImageDims image_dims(int G, int L) {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kSelChunkKeys = 4096;  // keys per top-k chunk: its bitmap is a whole number of words
+constexpr int kSelRingChunks = 8;    // top-k chunks in flight; the bitmap covers whole rings
+
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
   const size_t heads = (size_t)B * Hq;
   const int G = Hq / Hkv;
   const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L);
-  const int64_t words = ((n_cap + 63) / 64) * 2;
+  const int64_t chunks = (n_cap + kSelChunkKeys - 1) / kSelChunkKeys;
+  const int64_t words = (chunks + kSelRingChunks - 1) / kSelRingChunks * kSelRingChunks *
+                        (kSelChunkKeys / 32);
   size_t off = 0;
   const size_t o_img = off; off = align256(off + (size_t)B * Hkv * im.floats * sizeof(float));
   const size_t o_hist = off; off = align256(off + heads * kHistBins * sizeof(uint32_t));
-  const size_t o_cnt = off; off = align256(off + heads * 4 * sizeof(uint32_t));
   const size_t o_bm = off; off = align256(off + heads * words * sizeof(uint32_t));
   const size_t o_cand = off; off = align256(off + heads * (size_t)n_cap * sizeof(uint2));
   const size_t o_sc = off; off = align256(off + heads * (size_t)score_stride(n_cap) * sizeof(float));
@@ -119,7 +122,6 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
     ws->img = reinterpret_cast<float*>(p + o_img);
     ws->img_floats = im.floats;
     ws->hist = reinterpret_cast<uint32_t*>(p + o_hist);
-    ws->counters = reinterpret_cast<uint32_t*>(p + o_cnt);
     ws->bitmap = reinterpret_cast<uint32_t*>(p + o_bm);
     ws->cand = reinterpret_cast<uint2*>(p + o_cand);
     ws->scores = reinterpret_cast<float*>(p + o_sc);
@@ -130,115 +132,117 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
 
 // ---------------------------------------------------------------- soft tables
 
-template <typename T>
-__device__ __forceinline__ void load_w8(const T* p, float* f);
-template <>
-__device__ __forceinline__ void load_w8<uint16_t>(const uint16_t* p, float* f) {
-  unpack_bf16x8(*reinterpret_cast<const uint4*>(p), f);
-}
-template <>
-__device__ __forceinline__ void load_w8<float>(const float* p, float* f) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+constexpr int kTabThreads = 256;  // >= TL * P * G projections (8 * 8 * 4)
+
+template <int G>
+__device__ __forceinline__ void store_slot(float* dst, const float* v) {
+  if constexpr (G == 4) *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  else if constexpr (G == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+  else dst[0] = v[0];
 }
 
-constexpr int kTabTables = 16;                 // tables per soft-table block
-constexpr int kTabThreads = kTabTables * 8;    // one plane per thread (P <= 8)
-
-// grid: B*Hq*ceil(L/16) blocks.  Block (bg, tb) computes the bucket
-// distributions of tables 16*tb .. 16*tb+15 of query head bg = b*Hq + g and
-// writes them into component g % G of the table image of KV row
-// b*Hkv + g / G.  Block tb = 0 also clears the head's histogram and counters.
-template <typename T>
+// grid: B*Hkv*16 blocks of kTabThreads.  Block (bh, j) computes the tables
+// j*TL .. j*TL+TL-1 (the tables of scorer lane j) for the G query heads of KV
+// row bh and writes their image slots whole (one slot = the G heads' values
+// of one entry).  It also clears a 1/16 share of those heads' histograms.
+// Tables l >= L (padding of the last lane word) get all-zero entries.
+template <typename T, int G>
 __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
-    int G, int TL, int NF, int NS, int FULL, int img_floats, int ntb, float* __restrict__ img,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters) {
-  const int bg = blockIdx.x / ntb;
-  const int tb = blockIdx.x % ntb;
+    int TL, int NF, int NS, int FULL, int img_floats, float* __restrict__ img,
+    uint32_t* __restrict__ hist) {
+  const int bh = blockIdx.x >> 4, j = blockIdx.x & 15;
+  const int b = bh / Hkv, h = bh % Hkv;
+  const int bg0 = b * Hq + h * G;
   const int tid = threadIdx.x;
-  const int b = bg / Hq, g = bg % Hq;
-  const int comp = g % G;
-  float* im = img + ((int64_t)b * Hkv + g / G) * img_floats;
-  __shared__ float qf[kHead];                 // the query (exact in float32)
-  __shared__ double sig[kTabThreads][2];      // [plane][bit] = sigmoid(-+2u/tau)
-  __shared__ double half[kTabTables][32];     // [table][hf*16 + c]
-  if (tid < kHead) {
-    if constexpr (sizeof(T) == 2)
-      qf[tid] = __uint_as_float((uint32_t)q[(int64_t)bg * kHead + tid] << 16);
-    else
-      qf[tid] = q[(int64_t)bg * kHead + tid];
+  float* im = img + (int64_t)bh * img_floats;
+  __shared__ float qf[G][kHead];         // the queries (exact in float32)
+  __shared__ double sig[kTabThreads][2];  // [(m*P + plane)*G + g][bit] = sigmoid(+-2u/tau)
+  __shared__ double half[8][G][32];       // [m][g][hf*16 + c]
+
+  constexpr int kHistShare = G * kHistBins / 16;
+  for (int i = tid; i < kHistShare; i += kTabThreads)
+    hist[(int64_t)bg0 * kHistBins + j * kHistShare + i] = 0u;
+  for (int i = tid; i < G * kHead; i += kTabThreads) {
+    const int64_t src = (int64_t)(bg0 + i / kHead) * kHead + i % kHead;
+    if constexpr (sizeof(T) == 2) qf[i / kHead][i % kHead] = __uint_as_float((uint32_t)q[src] << 16);
+    else qf[i / kHead][i % kHead] = q[src];
   }
-  if (tb == 0) {
-    for (int i = tid; i < kHistBins; i += kTabThreads) hist[(int64_t)bg * kHistBins + i] = 0u;
-    if (tid < 4) counters[bg * 4 + tid] = 0u;
-  }
-  const int l0 = tb * kTabTables;
-  const int pl = l0 * P + tid;  // this thread's plane
-  const bool has_plane = tid < kTabTables * P && pl < L * P;
+  // this thread's projection: table member m, plane pl, head g
+  const int m = tid / (P * G), pl = (tid / G) % P, g = tid % G;
+  const int l = j * TL + m;
+  const bool has = tid < TL * P * G;
+  const bool live = has && l < L;
   constexpr int NV = kHead * (int)sizeof(T) / 16;  // 16-byte vectors per plane row
   uint4 raw[NV];
-  if (has_plane) {
-    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)pl * kHead);
+  if (live) {
+    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + pl) * kHead);
 #pragma unroll
     for (int v = 0; v < NV; ++v) raw[v] = wr[v];
   }
   __syncthreads();
-  if (has_plane) {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  if (has) {
+    double u = 0.0;
+    if (live) {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      float f[8];
-      int cnt;
-      if constexpr (sizeof(T) == 2) {
-        unpack_bf16x8(raw[v], f);
-        cnt = 8;
-      } else {
-        f[0] = __uint_as_float(raw[v].x); f[1] = __uint_as_float(raw[v].y);
-        f[2] = __uint_as_float(raw[v].z); f[3] = __uint_as_float(raw[v].w);
-        cnt = 4;
+      for (int v = 0; v < NV; ++v) {
+        float f[8];
+        int cnt;
+        if constexpr (sizeof(T) == 2) {
+          unpack_bf16x8(raw[v], f);
+          cnt = 8;
+        } else {
+          f[0] = __uint_as_float(raw[v].x); f[1] = __uint_as_float(raw[v].y);
+          f[2] = __uint_as_float(raw[v].z); f[3] = __uint_as_float(raw[v].w);
+          cnt = 4;
+        }
+#pragma unroll
+        for (int e = 0; e < cnt; ++e)
+          acc[e & 3] = fma((double)f[e], (double)qf[g][v * cnt + e], acc[e & 3]);
       }
-#pragma unroll
-      for (int e = 0; e < cnt; ++e) acc[e & 3] = fma((double)f[e], (double)qf[v * cnt + e], acc[e & 3]);
+      u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
-    const double u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    // sigmoid(x) and sigmoid(-x) from one exponential of -|x|
     const double x = 2.0 * u / (double)tau;
-    sig[tid][1] = 1.0 / (1.0 + exp(-x));  // bit set: corner sign +1
-    sig[tid][0] = 1.0 / (1.0 + exp(x));   // bit clear: corner sign -1
+    const double e = exp(-fabs(x));
+    const double big = 1.0 / (1.0 + e), small = e * big;
+    sig[tid][1] = x >= 0.0 ? big : small;  // bit set: corner sign +1
+    sig[tid][0] = x >= 0.0 ? small : big;  // bit clear: corner sign -1
   }
   __syncthreads();
   const int plo = P < 4 ? P : 4;
   const int phi = P - plo;
-  for (int e = tid; e < kTabTables * 32; e += kTabThreads) {
-    const int lt = e >> 5, r = e & 31, hf = r >> 4, c = r & 15;
+  for (int i = tid; i < TL * G * 32; i += kTabThreads) {
+    const int mm = i / (G * 32), gg = (i / 32) % G, r = i & 31, hf = r >> 4, c = r & 15;
     const int nb = hf ? phi : plo;
     double prod = 0.0;
-    if (c < (1 << nb) && l0 + lt < L) {
+    if (c < (1 << nb) && j * TL + mm < L) {
       prod = 1.0;
-      const int p0 = lt * P + (hf ? plo : 0);
-      for (int j = 0; j < nb; ++j) prod *= sig[p0 + j][(c >> j) & 1];
+      const int p0 = hf ? plo : 0;
+      for (int jj = 0; jj < nb; ++jj) prod *= sig[(mm * P + p0 + jj) * G + gg][(c >> jj) & 1];
     }
-    half[lt][r] = prod;
+    half[mm][gg][r] = prod;
   }
   __syncthreads();
-  // this block's tables: table l = j*TL + m for lane j, member m
+  // full tables: slot (e*NF + m)*16 + j for entries e < 2^P
   const int nent = 1 << P;
   const int lomask = (1 << plo) - 1;
-  for (int i = tid; i < kTabTables * nent; i += kTabThreads) {
-    const int lt = i / nent, e = i % nent;
-    const int l = l0 + lt, j = l / TL, m = l % TL;
-    if (j >= 16 || m >= NF) continue;
-    const float v = l < L ? (float)(half[lt][e & lomask] * half[lt][16 + (e >> plo)]) : 0.f;
-    im[((int64_t)(e * NF + m) * 16 + j) * G + comp] = v;
+  for (int i = tid; i < NF * nent; i += kTabThreads) {
+    const int e = i / NF, mm = i % NF;
+    float v[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg)
+      v[gg] = (float)(half[mm][gg][e & lomask] * half[mm][gg][16 + (e >> plo)]);
+    store_slot<G>(im + ((int64_t)i * 16 + j) * G, v);
   }
-  for (int i = tid; i < kTabTables * 32; i += kTabThreads) {
-    const int lt = i >> 5, hc = i & 31;
-    const int l = l0 + lt, j = l / TL, m = l % TL;
-    if (j >= 16 || m < NF) continue;
-    const float v = l < L ? (float)half[lt][hc] : 0.f;
-    im[FULL + ((int64_t)(hc * NS + (m - NF)) * 16 + j) * G + comp] = v;
+  // factored tables: slot FULL/G + ((hc*NS + m - NF)*16 + j), hc = hf*16 + c
+  for (int i = tid; i < 32 * NS; i += kTabThreads) {
+    const int hc = i / NS, mm = NF + i % NS;
+    float v[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) v[gg] = (float)half[mm][gg][hc];
+    store_slot<G>(im + FULL + ((int64_t)i * 16 + j) * G, v);
   }
 }
 
@@ -495,15 +499,33 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   }
 }
 
-// ---------------------------------------------------------------- top-k: scan
+// ---------------------------------------------------------------- top-k
 
-constexpr int kSelThreads = 512;
+// One workgroup of kSelThreads per query head does the whole selection:
+//  1. the head's first-digit histogram (built by the scorer) gives the bin
+//     d1 holding the k-th largest score, the count `above` of keys in
+//     higher bins and the count C of keys in bin d1;
+//  2. one pass over the scores (4 consecutive keys per lane and chunk,
+//     kSelRing chunks in flight) writes a bitmap of the keys above d1 and
+//     gathers the keys of bin d1 as candidates in LDS (when the histogram
+//     shows more than kCandCap of them, a second pass gathers them into the
+//     workspace instead);
+//  3. a radix select on the remaining 21 score bits, then on the key index
+//     (the lower index wins a tie), picks the k - above candidates that
+//     complete the top-k;
+//  4. the bitmap plus those candidates become ascending indices.
+// Bitmap layout: 256-key block j (keys 256j + 4i + e, i < 64, e < 4) is 8
+// words; words 8j + 2e and 8j + 2e + 1 hold bit i = key 256j + 4i + e (the
+// wave ballot of the e-th of the 4 keys each lane loaded).
+constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelGroups = 16;                             // 64-key groups per wave
-constexpr int kSelChunk = kSelWaves * kSelGroups * 64;     // keys per scan workgroup (8192)
-constexpr int kCandLds = 4096;                             // candidates resolved in LDS
+constexpr int kSelChunk = kSelThreads * 4;   // keys per chunk (4 per thread)
+static_assert(kSelChunk == kSelChunkKeys, "bitmap sizing");
+constexpr int kSelRing = kSelRingChunks;     // chunks in flight per thread
+constexpr int kCandCap = 6144;               // candidates held in LDS
+constexpr int kSegBlocks = kSelThreads;      // 256-key bitmap blocks turned into indices per pass
 
-// Block-wide inclusive scan of one value per thread (kSelThreads threads).
+// Block-wide inclusive scan of one value per thread.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -520,105 +542,8 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) 
 }
 
 struct Boundary {
-  uint32_t d1, above;
+  uint32_t d1, above, count;
 };
-
-// Bin of the first digit that holds the k-th largest score, and how many keys
-// lie in higher bins.  Every thread of the block must call it.
-__device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum, Boundary* sh) {
-  const int tid = threadIdx.x;
-  const uint32_t c_hi = hh[kHistBins - 1 - 2 * tid];
-  const uint32_t c_lo = hh[kHistBins - 2 - 2 * tid];
-  const uint32_t inc = block_incl_scan(c_hi + c_lo, wsum);
-  const uint32_t prev = inc - c_hi - c_lo;
-  if (prev < k && k <= prev + c_hi) *sh = Boundary{(uint32_t)(kHistBins - 1 - 2 * tid), prev};
-  else if (prev + c_hi < k && k <= inc) *sh = Boundary{(uint32_t)(kHistBins - 2 - 2 * tid), prev + c_hi};
-  __syncthreads();
-  const Boundary r = *sh;
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ void clamp_nk(int64_t n_cap, int32_t len, int32_t kk, int k_max,
-                                         int64_t* n, int64_t* k) {
-  int64_t nn = len;
-  if (nn < 0) nn = 0;
-  if (nn > n_cap) nn = n_cap;
-  int64_t k2 = kk;
-  if (k2 < 0) k2 = 0;
-  if (k2 > nn) k2 = nn;
-  if (k2 > k_max) k2 = k_max;
-  *n = nn;
-  *k = k2;
-}
-
-// grid: B*Hq*CH blocks of kSelThreads, CH = ceil(n_cap / kSelChunk).
-__global__ __launch_bounds__(kSelThreads) void topk_scan_kernel(
-    const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
-    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq, int CH,
-    const uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ counters, uint32_t* __restrict__ bitmap, int64_t words,
-    uint2* __restrict__ cand) {
-  const int bg = blockIdx.x / CH;
-  const int c = blockIdx.x % CH;
-  const int b = bg / Hq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int64_t n, k;
-  clamp_nk(n_cap, lens[b], ks[b], k_max, &n, &k);
-  if (k == 0) return;
-  const int64_t n64 = (n + 63) & ~(int64_t)63;
-  const int64_t c0 = (int64_t)c * kSelChunk;
-  if (c0 >= n64) return;
-
-  // this lane's scores first (16 keys, one per 64-key group of the wave)
-  const float* srow = scores + (int64_t)bg * sstride;
-  uint32_t bits[kSelGroups];
-#pragma unroll
-  for (int i = 0; i < kSelGroups; ++i) {
-    const int64_t key = c0 + ((int64_t)i * kSelWaves + wave) * 64 + lane;
-    bits[i] = key < n ? __float_as_uint(srow[key]) : 0u;
-  }
-  __shared__ uint32_t wsum[kSelWaves];
-  __shared__ Boundary shb;
-  const Boundary bd = find_boundary(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
-
-  // candidates gather in LDS first; one global reservation per workgroup
-  __shared__ uint2 lc[kSelChunk];
-  __shared__ uint32_t lcount, gbase;
-  if (tid == 0) lcount = 0u;
-  __syncthreads();
-  uint32_t* bm = bitmap + (int64_t)bg * words;
-#pragma unroll
-  for (int i = 0; i < kSelGroups; ++i) {
-    const int64_t base = c0 + ((int64_t)i * kSelWaves + wave) * 64;
-    if (base >= n64) break;
-    const int64_t key = base + lane;
-    const bool valid = key < n;
-    uint32_t dg = bits[i] >> kHistShift;
-    if (dg > kHistBins - 1) dg = kHistBins - 1;
-    const bool sel = valid && dg > bd.d1;
-    const bool cnd = valid && dg == bd.d1;
-    const uint64_t smask = __ballot(sel);
-    const uint64_t cmask = __ballot(cnd);
-    if (lane == 0) *reinterpret_cast<uint2*>(bm + (base >> 5)) =
-        make_uint2((uint32_t)smask, (uint32_t)(smask >> 32));
-    if (cmask) {
-      uint32_t pos0 = 0;
-      if (lane == 0) pos0 = atomicAdd(&lcount, (uint32_t)__popcll(cmask));
-      pos0 = __shfl(pos0, 0, 64);
-      if (cnd) lc[pos0 + __popcll(cmask & lanemask_lt64())] = make_uint2(bits[i], (uint32_t)key);
-    }
-  }
-  __syncthreads();
-  const uint32_t cnt = lcount;
-  if (cnt == 0) return;
-  if (tid == 0) gbase = atomicAdd(&counters[bg * 4 + 0], cnt);
-  __syncthreads();
-  uint2* crow = cand + (int64_t)bg * n_cap + gbase;
-  for (uint32_t t = tid; t < cnt; t += kSelThreads) crow[t] = lc[t];
-}
-
-// ---------------------------------------------------------------- top-k: resolve
 
 struct Pick {
   uint32_t digit, before, inbin;
@@ -630,14 +555,14 @@ struct Pick {
 // the `need`-th entry: counted from the top for scores, from the bottom for
 // indices (the lower index wins a tie).
 template <bool BY_INDEX>
-__device__ Pick radix_pick(const uint2* cand, uint32_t C, uint32_t vmask, uint32_t vval,
-                           uint32_t imask, uint32_t ival, int shift, uint32_t need,
+__device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask,
+                           uint32_t vval, uint32_t imask, uint32_t ival, int shift, uint32_t need,
                            uint32_t* h128, Pick* shpick) {
   const int tid = threadIdx.x;
   if (tid < 128) h128[tid] = 0u;
   __syncthreads();
   for (uint32_t i = tid; i < C; i += kSelThreads) {
-    const uint2 e = cand[i];
+    const uint2 e = cands[i];
     const uint32_t v = e.x & 0x1FFFFFu;
     if ((v & vmask) != vval) continue;
     if (BY_INDEX && ((e.y & imask) != ival)) continue;
@@ -665,17 +590,29 @@ __device__ Pick radix_pick(const uint2* cand, uint32_t C, uint32_t vmask, uint32
   return r;
 }
 
-constexpr int kSegWords = kSelThreads * 8;  // bitmap words turned into indices per pass
+__device__ __forceinline__ void clamp_nk(int64_t n_cap, int32_t len, int32_t kk, int k_max,
+                                         int64_t* n, int64_t* k) {
+  int64_t nn = len;
+  if (nn < 0) nn = 0;
+  if (nn > n_cap) nn = n_cap;
+  int64_t k2 = kk;
+  if (k2 < 0) k2 = 0;
+  if (k2 > nn) k2 = nn;
+  if (k2 > k_max) k2 = k_max;
+  *n = nn;
+  *k = k2;
+}
 
-// grid: B*Hq blocks of kSelThreads.
-__global__ __launch_bounds__(kSelThreads) void topk_resolve_kernel(
-    int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
-    int Hq, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ counters,
-    const uint32_t* __restrict__ bitmap, int64_t words, const uint2* __restrict__ cand,
-    int32_t* __restrict__ idx) {
+// grid: B*Hq blocks of kSelThreads.  `words` = bitmap words per head (a
+// multiple of kSelChunk / 32), `sstride` = score row stride (a multiple of 64).
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq,
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ bitmap, int64_t words,
+    uint2* __restrict__ cand, int32_t* __restrict__ idx) {
   const int bg = blockIdx.x;
   const int b = bg / Hq;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   int64_t n, k;
   clamp_nk(n_cap, lens[b], ks[b], k_max, &n, &k);
   int32_t* out = idx + (int64_t)bg * k_max;
@@ -687,83 +624,203 @@ __global__ __launch_bounds__(kSelThreads) void topk_resolve_kernel(
   __shared__ Boundary shb;
   __shared__ uint32_t h128[128];
   __shared__ Pick shpick;
-  __shared__ uint2 lcand[kCandLds];
-  __shared__ uint32_t lbm[kSegWords];
-  __shared__ uint32_t seg_total;
+  __shared__ uint32_t lcount, seg_total;
+  __shared__ uint2 lcand[kCandCap];
+  __shared__ uint32_t lbm[kSegBlocks * 8];
 
-  const Boundary bd = find_boundary(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
-  const uint32_t C = counters[bg * 4 + 0];
-  uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C
-  const uint2* crow = cand + (int64_t)bg * n_cap;
-  const uint2* cp = crow;
-  if (C <= (uint32_t)kCandLds) {
-    for (uint32_t i = tid; i < C; i += kSelThreads) lcand[i] = crow[i];
-    __syncthreads();
-    cp = lcand;
-  }
-  // low 21 bits of the score (the boundary bin fixes the rest)
-  uint32_t vmask = 0u, vval = 0u, ties = 0u;
-  for (int shift = 14; shift >= 0; shift -= 7) {
-    const Pick pk = radix_pick<false>(cp, C, vmask, vval, 0u, 0u, shift, need, h128, &shpick);
-    need -= pk.before;
-    vval |= pk.digit << shift;
-    vmask |= 127u << shift;
-    ties = pk.inbin;
-  }
-  // among keys with exactly that score, the lower indices win
-  uint32_t imax = 0xFFFFFFFFu;
-  if (ties > need) {
-    uint32_t imask = 0u, ival = 0u;
-    int top = 0;
-    while (((uint64_t)1 << top) < (uint64_t)n) ++top;
-    int shift = top > 7 ? top - 7 : 0;
-    for (;;) {
-      const Pick pk = radix_pick<true>(cp, C, vmask, vval, imask, ival, shift, need, h128, &shpick);
-      need -= pk.before;
-      ival |= pk.digit << shift;
-      imask |= 127u << shift;
-      if (shift == 0) break;
-      shift = shift > 7 ? shift - 7 : 0;
-    }
-    imax = ival;
-  }
-  // bitmap (+ the chosen candidates) -> ascending indices, one segment at a time
-  const uint32_t* bm = bitmap + (int64_t)bg * words;
-  const int64_t nwords = (n + 31) >> 5;
-  uint32_t written = 0;
-  for (int64_t w0 = 0; w0 < nwords; w0 += kSegWords) {
-    const int64_t segn = (nwords - w0) < kSegWords ? (nwords - w0) : kSegWords;
-    for (int i = tid; i < kSegWords; i += kSelThreads) lbm[i] = i < segn ? bm[w0 + i] : 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < C; i += kSelThreads) {
-      const uint2 e = cp[i];
-      const uint32_t v = e.x & 0x1FFFFFu;
-      const int64_t wi = (int64_t)(e.y >> 5) - w0;
-      if (wi >= 0 && wi < segn && (v > vval || (v == vval && e.y <= imax)))
-        atomicOr(&lbm[wi], 1u << (e.y & 31));
-    }
-    __syncthreads();
-    uint32_t wv[8];
-    uint32_t cnt = 0;
+  // the first chunks' scores, issued before anything waits (lane `lane` of
+  // wave w loads keys c*kSelChunk + 256w + 4*lane .. +3 of chunk c)
+  const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
+  const int64_t nch = (n + kSelChunk - 1) / kSelChunk;
+  auto load_chunk = [&](int64_t c, uint4& v) {
+    int64_t key = c * kSelChunk + tid * 4;
+    if (key > sstride - 4) key = sstride - 4;  // past the row: re-read its end
+    v = *reinterpret_cast<const uint4*>(srow + key);
+  };
+  uint4 ring[kSelRing];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      wv[t] = lbm[tid * 8 + t];
-      cnt += __popc(wv[t]);
-    }
-    const uint32_t inc = block_incl_scan(cnt, wsum);
-    uint32_t pos = written + inc - cnt;
+  for (int r = 0; r < kSelRing; ++r) load_chunk(r, ring[r]);
+
+  // 1. boundary bin (bins scanned from the top, one per thread)
+  const uint32_t hc = hist[(int64_t)bg * kHistBins + (kHistBins - 1 - tid)];
+  if (tid == 0) {
+    shb = Boundary{0u, 0u, 0u};
+    lcount = 0u;
+  }
+  const uint32_t inc = block_incl_scan(hc, wsum);
+  const uint32_t prev = inc - hc;
+  if (prev < (uint32_t)k && (uint32_t)k <= inc)
+    shb = Boundary{(uint32_t)(kHistBins - 1 - tid), prev, hc};
+  __syncthreads();
+  const Boundary bd = shb;
+
+  // 2. bitmap of the keys above d1, candidates of bin d1.  A key is above
+  // d1 when its bits exceed thr_sel, in d1 when they are at least thr_lo and
+  // not above (the histogram clamps the top digit to kHistBins - 1, and so
+  // does this).  Every step of the ring runs unconditionally (chunks past n
+  // write zero words into the bitmap's padding), so each wait covers one
+  // chunk.
+  uint32_t* bm = bitmap + (int64_t)bg * words;
+  uint2* gc = cand + (int64_t)bg * n_cap;
+  const bool lds_cands = bd.count <= (uint32_t)kCandCap;
+  const uint32_t thr_lo = bd.d1 << kHistShift;
+  const uint32_t thr_sel = bd.d1 < (uint32_t)(kHistBins - 1) ? ((bd.d1 + 1) << kHistShift) - 1u
+                                                            : 0xFFFFFFFFu;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t lt = lanemask_lt64();
+  // masks of this wave's lanes whose e-th key (base + 4*lane + e) is below n
+  auto valid_masks = [&](int64_t base, uint64_t* vm) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint32_t x = wv[t];
-      const int64_t wi = w0 + tid * 8 + t;
-      while (x) {
-        const int bit = __ffs(x) - 1;
-        x &= x - 1;
-        if (pos < (uint32_t)k_max) out[pos] = (int32_t)(wi * 32 + bit);
-        ++pos;
+    for (int e = 0; e < 4; ++e) {
+      const int64_t r = (n - base - e + 3) >> 2;  // lanes with 4*lane + e < n - base
+      vm[e] = r >= 64 ? ~0ull : r <= 0 ? 0ull : ((1ull << r) - 1ull);
+    }
+  };
+  // wave-level compaction of the candidates (mask m[e]: lanes whose e-th key is one)
+  auto gather = [&](const uint64_t* m, const uint32_t* sb, int64_t base, bool to_lds) {
+    const uint32_t tot = (uint32_t)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) +
+                                    __popcll(m[3]));
+    if (tot) {
+      uint32_t pos = 0u;
+      if (lane == 0) pos = atomicAdd(&lcount, tot);
+      pos = __builtin_amdgcn_readfirstlane(pos);  // every lane is active here
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((m[e] >> lane) & 1ull) {
+          const uint32_t p2 = pos + (uint32_t)__popcll(m[e] & lt);
+          const uint2 entry = make_uint2(sb[e], (uint32_t)(base + 4 * lane + e));
+          if (to_lds) {
+            if (p2 < (uint32_t)kCandCap) lcand[p2] = entry;
+          } else if (p2 < (uint32_t)n) {
+            gc[p2] = entry;
+          }
+        }
+        pos += (uint32_t)__popcll(m[e]);
       }
     }
-    if (tid == kSelThreads - 1) seg_total = inc;
+  };
+  for (int64_t c0 = 0; c0 < nch; c0 += kSelRing) {
+#pragma unroll
+    for (int r = 0; r < kSelRing; ++r) {
+      const int64_t c = c0 + r;
+      const int64_t base = c * kSelChunk + wave * 256;
+      const uint32_t sb[4] = {ring[r].x, ring[r].y, ring[r].z, ring[r].w};
+      uint64_t vm[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+      if (base + 256 > n) valid_masks(base, vm);
+      uint64_t ms[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ms[e] = __ballot(sb[e] > thr_sel) & vm[e];
+      // even lanes store words 0..3 of the block, odd lanes words 4..7
+      const bool odd = lane & 1;
+      const uint64_t a = odd ? ms[2] : ms[0], b2 = odd ? ms[3] : ms[1];
+      *reinterpret_cast<uint4*>(bm + (base >> 5) + (odd ? 4 : 0)) =
+          make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b2, (uint32_t)(b2 >> 32));
+      if (lds_cands) {
+        uint64_t mc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & vm[e];
+        gather(mc, sb, base, true);
+      }
+      load_chunk(c + kSelRing, ring[r]);
+    }
+  }
+  if (!lds_cands) {  // more candidates than LDS holds: gather them into the workspace
+    __syncthreads();
+    if (tid == 0) lcount = 0u;
+    __syncthreads();
+    for (int64_t c = 0; c < nch; ++c) {
+      uint4 v;
+      load_chunk(c, v);
+      const int64_t base = c * kSelChunk + wave * 256;
+      const uint32_t sb[4] = {v.x, v.y, v.z, v.w};
+      uint64_t vm[4];
+      valid_masks(base, vm);
+      uint64_t mc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mc[e] = __ballot(sb[e] >= thr_lo && !(sb[e] > thr_sel)) & vm[e];
+      gather(mc, sb, base, false);
+    }
+  }
+  __syncthreads();
+
+  // 3. the candidates that complete the top-k
+  uint32_t C = lcount;
+  if (lds_cands && C > (uint32_t)kCandCap) C = kCandCap;  // only with an inconsistent histogram
+  const uint2* lc = lds_cands ? lcand : gc;                 // candidate i (all of them in one place)
+  uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C
+  uint32_t vmask = 0u, vval = 0u, imax = 0xFFFFFFFFu;
+  if (need < C) {
+    uint32_t ties = 0u;
+    for (int shift = 14; shift >= 0; shift -= 7) {
+      const Pick pk = radix_pick<false>(lc, C, vmask, vval, 0u, 0u, shift, need, h128, &shpick);
+      need -= pk.before;
+      vval |= pk.digit << shift;
+      vmask |= 127u << shift;
+      ties = pk.inbin;
+    }
+    if (ties > need) {  // among keys with exactly that score, the lower indices win
+      uint32_t imask = 0u, ival = 0u;
+      int top = 0;
+      while (((uint64_t)1 << top) < (uint64_t)n) ++top;
+      int shift = top > 7 ? top - 7 : 0;
+      for (;;) {
+        const Pick pk = radix_pick<true>(lc, C, vmask, vval, imask, ival, shift, need, h128, &shpick);
+        need -= pk.before;
+        ival |= pk.digit << shift;
+        imask |= 127u << shift;
+        if (shift == 0) break;
+        shift = shift > 7 ? shift - 7 : 0;
+      }
+      imax = ival;
+    }
+  }
+
+  // 4. bitmap + chosen candidates -> ascending indices, kSegBlocks 256-key
+  // blocks at a time (thread t owns block t of the segment)
+  const int64_t nblocks = (n + 255) >> 8;
+  uint32_t written = 0;
+  for (int64_t b0 = 0; b0 < nblocks; b0 += kSegBlocks) {
+    const int64_t segb = (nblocks - b0) < kSegBlocks ? (nblocks - b0) : kSegBlocks;
+    const int64_t bl = tid < segb ? b0 + tid : b0;
+    const uint4 w0v = reinterpret_cast<const uint4*>(bm)[bl * 2];
+    const uint4 w1v = reinterpret_cast<const uint4*>(bm)[bl * 2 + 1];
+    const bool mine = tid < segb;
+    uint4* lb = reinterpret_cast<uint4*>(lbm);
+    lb[tid * 2] = mine ? w0v : make_uint4(0u, 0u, 0u, 0u);
+    lb[tid * 2 + 1] = mine ? w1v : make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    for (uint32_t i = tid; i < C; i += kSelThreads) {
+      const uint2 e = lc[i];
+      const uint32_t v = e.x & 0x1FFFFFu;
+      const int64_t blk = (int64_t)(e.y >> 8) - b0;
+      if (blk >= 0 && blk < segb && (v > vval || (v == vval && e.y <= imax))) {
+        const uint32_t i4 = (e.y >> 2) & 63u, ee = e.y & 3u;
+        atomicOr(&lbm[blk * 8 + ee * 2 + (i4 >> 5)], 1u << (i4 & 31));
+      }
+    }
+    __syncthreads();
+    uint64_t m[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      m[e] = (uint64_t)lbm[tid * 8 + 2 * e] | ((uint64_t)lbm[tid * 8 + 2 * e + 1] << 32);
+    const uint32_t cnt = (uint32_t)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) +
+                                    __popcll(m[3]));
+    const uint32_t incw = block_incl_scan(cnt, wsum);
+    uint32_t pos = written + incw - cnt;
+    const int64_t kbase = (b0 + tid) * 256;
+    uint64_t any = m[0] | m[1] | m[2] | m[3];
+    while (any) {
+      const int i = __ffsll((unsigned long long)any) - 1;
+      any &= any - 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((m[e] >> i) & 1ull) {
+          if (pos < (uint32_t)k_max) out[pos] = (int32_t)(kbase + 4 * i + e);
+          ++pos;
+        }
+      }
+    }
+    if (tid == kSelThreads - 1) seg_total = incw;
     __syncthreads();
     written += seg_total;
     __syncthreads();
@@ -818,18 +875,26 @@ hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, 
                               int L, int P, float tau, const ScoreWs& ws, hipStream_t s) {
   const int G = Hq / Hkv;
   const ImageDims im = image_dims(G, L);
-  const int heads = B * Hq;
-  // tables of a padded lane word (l >= L) must be written too, so cover 16*TL
-  const int ntb = (16 * im.TL + kTabTables - 1) / kTabTables;
-  const unsigned grid = (unsigned)(heads * ntb);
-  if (dtype == 1)
-    soft_tables_kernel<uint16_t><<<grid, kTabThreads, 0, s>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(W), Hq, Hkv, L, P, tau,
-        G, im.TL, im.NF, im.NS, im.full, im.floats, ntb, ws.img, ws.hist, ws.counters);
-  else
-    soft_tables_kernel<float><<<grid, kTabThreads, 0, s>>>(
-        static_cast<const float*>(q), static_cast<const float*>(W), Hq, Hkv, L, P, tau, G,
-        im.TL, im.NF, im.NS, im.full, im.floats, ntb, ws.img, ws.hist, ws.counters);
+  const unsigned grid = (unsigned)(B * Hkv * 16);
+  auto go = [&](auto tag, auto gtag) {
+    using T = decltype(tag);
+    constexpr int GG = decltype(gtag)::value;
+    soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
+        static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
+        im.NS, im.full, im.floats, ws.img, ws.hist);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  if (dtype == 1) {
+    if (G == 1) go(uint16_t{}, I1{});
+    else if (G == 2) go(uint16_t{}, I2{});
+    else go(uint16_t{}, I4{});
+  } else {
+    if (G == 1) go(float{}, I1{});
+    else if (G == 2) go(float{}, I2{});
+    else go(float{}, I4{});
+  }
   return hipGetLastError();
 }
 
@@ -847,14 +912,9 @@ hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, int32_t* idx, const ScoreWs& ws,
                        hipStream_t s) {
-  const int CH = (int)((n_cap + kSelChunk - 1) / kSelChunk);
-  topk_scan_kernel<<<(unsigned)(B * Hq * CH), kSelThreads, 0, s>>>(
-      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, CH, ws.hist, ws.counters,
-      ws.bitmap, ws.words, ws.cand);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  topk_resolve_kernel<<<(unsigned)(B * Hq), kSelThreads, 0, s>>>(
-      n_cap, lens, ks, k_max, Hq, ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand, idx);
+  topk_select_kernel<<<(unsigned)(B * Hq), kSelThreads, 0, s>>>(
+      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, ws.hist, ws.bitmap, ws.words,
+      ws.cand, idx);
   return hipGetLastError();
 }
 
