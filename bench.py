@@ -1,13 +1,13 @@
 """Benchmark of the SOCKET decode hot path on one MI355X.
 
 One step = one decode step of the GQA 32/8 workload at n = 32768 cached keys
-(d = 128, L = 64 tables x P = 8 planes, tau = 0.5, k = 656 = ceil(2% of n)):
+(d = 128, L = 64 tables x P = 8 planes, tau = 0.5, k = 656 = ceil(2% of n)),
+issued as a caller would, through three C calls:
 
-  append  : hash the new key of every KV head and store its value norm
-  tables  : float64 query projections -> per-table soft-bucket half-tables
-  score   : soft-count score of all n + 1 keys for the 32 query heads
-  top-k   : top-656 keys per query head
-  attend  : exact attention of each query head over its selected keys
+  socket_hash_keys     append: hash the new key of every KV head, store its norm
+  socket_score_topk    soft tables, soft-count scores of all n + 1 keys for the
+                       32 query heads, top-656 per query head
+  socket_sparse_decode exact attention of each query head over its keys
 
 `value` is keys scored+selected per second: 32 query heads x (n + 1) keys per
 step, divided by the wall time of K steps bracketed by device syncs.  Inputs
@@ -15,10 +15,12 @@ are resident in HBM.  The cache is replicated `--replicas` times (one replica
 per step, round robin, like successive layers) so the 256 MiB Infinity Cache
 cannot serve a step from the previous one.
 
-Also reported: per-kernel GPU times from HIP events (taken in a second pass
-whose launches queue up behind a long matrix product, so launch gaps do not
-enter the event pairs), the 128K-key step latency, the prefill hashing rate
-against the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
+Also reported: per-stage GPU time (batches of steps cut after each stage,
+timed with one pair of HIP events per batch while the launches queue behind a
+long matrix product, so host launch gaps stay out; a stage's time includes
+its dispatch), the scorer's average launch time (a batch of scorer launches
+alone) for the roofline, the 128K-key step, the prefill hashing rate against
+the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
 """
 from __future__ import annotations
 
@@ -111,7 +113,8 @@ class Case:
         w, lib = self.w, self.lib
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         st = vp(self.stream)
-        self.c_append, self.c_prefill, self.c_score, self.c_decode = [], [], [], []
+        self.c_append, self.c_prefill, self.c_score, self.c_decode, self.c_score_topk = \
+            [], [], [], [], []
         for r in range(self.replicas):
             K, V, ids, vn = self.K[r].data_ptr(), self.V[r].data_ptr(), self.ids[r].data_ptr(), \
                 self.vn[r].data_ptr()
@@ -124,6 +127,12 @@ class Case:
                                  vp(self.lens.data_ptr()), i64(w.n_cap),
                                  vp(self.scores.data_ptr()), vp(self.sws_p),
                                  ctypes.c_size_t(self.sws_n), st))
+            self.c_score_topk.append((vp(self.q.data_ptr()), 1, w.B, w.Hq, w.Hkv, w.d,
+                                      vp(self.W.data_ptr()), w.L, w.P, ctypes.c_float(w.tau),
+                                      vp(ids), vp(vn), vp(self.lens.data_ptr()), i64(w.n_cap),
+                                      vp(self.ks.data_ptr()), self.k, vp(self.idx.data_ptr()),
+                                      vp(self.scores.data_ptr()), vp(self.sws_p),
+                                      ctypes.c_size_t(self.sws_n), st))
             self.c_decode.append((vp(self.q.data_ptr()), vp(K), vp(V), 1, w.B, w.Hq, w.Hkv, w.d,
                                   i64(w.n_cap), vp(self.idx.data_ptr()), self.k,
                                   ctypes.c_float(w.scale), vp(self.out.data_ptr()),
@@ -143,22 +152,28 @@ class Case:
     def prefill(self, r):
         self._ok(self.lib.socket_hash_keys(*self.c_prefill[r]), "socket_hash_keys")
 
-    def step(self, r, ev=None):
-        """One decode step on replica r; ev = list of 6 events to bracket the 5 stages."""
+    def step(self, r):
+        """One decode step on replica r through the three C calls."""
         lib = self.lib
-        if ev: ev[0].record()
         rc = lib.socket_hash_keys(*self.c_append[r])
-        if ev: ev[1].record()
-        rc |= lib.socket_soft_tables(*self.c_tables)
-        if ev: ev[2].record()
-        rc |= lib.socket_score(*self.c_score[r])
-        if ev: ev[3].record()
-        rc |= lib.socket_topk(*self.c_topk)
-        if ev: ev[4].record()
+        rc |= lib.socket_score_topk(*self.c_score_topk[r])
         rc |= lib.socket_sparse_decode(*self.c_decode[r])
-        if ev: ev[5].record()
         if rc:
             raise RuntimeError(f"a decode-step call failed (status bits {rc})")
+
+    STAGES = ["append", "tables", "score", "topk", "attend"]
+
+    def stages(self, r, upto):
+        """The first `upto` stages of one step on replica r, through the stage entry points."""
+        lib = self.lib
+        calls = [(lib.socket_hash_keys, self.c_append[r]), (lib.socket_soft_tables, self.c_tables),
+                 (lib.socket_score, self.c_score[r]), (lib.socket_topk, self.c_topk),
+                 (lib.socket_sparse_decode, self.c_decode[r])]
+        rc = 0
+        for fn, a in calls[:upto]:
+            rc |= fn(*a)
+        if rc:
+            raise RuntimeError(f"a decode-stage call failed (status bits {rc})")
 
     def free(self):
         for a in ("K", "V", "ids", "vn"):
@@ -188,30 +203,45 @@ def timed_steps(case, torch, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def per_kernel(case, torch, steps):
-    """Mean GPU time of each stage from HIP events (launches queued behind a busy prologue)."""
+def gpu_batch_us(torch, run, count):
+    """GPU microseconds per item of `count` items enqueued by run(i), all queued
+    behind a busy prologue so that the events see GPU time only."""
     run_busy, busy_ms = busy_prologue(torch)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-    e_all0, e_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     run_busy()
     t0 = time.perf_counter()
-    e_all0.record()
-    for i in range(steps):
-        case.step(i % case.replicas, evs[i])
-    e_all1.record()
+    e0.record()
+    for i in range(count):
+        run(i)
+    e1.record()
     host_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     if host_ms > busy_ms:
         log(f"[bench] warning: host enqueue {host_ms:.1f} ms exceeded the busy prologue "
-            f"{busy_ms:.1f} ms; per-kernel times may include launch gaps")
-    names = ["append", "tables", "score", "topk", "attend"]
-    t = {n: [] for n in names}
-    for ev in evs:
-        for j, n in enumerate(names):
-            t[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
-    gpu_step_us = e_all0.elapsed_time(e_all1) * 1e3 / steps
-    return {n: float(np.mean(v)) for n, v in t.items()}, gpu_step_us, host_ms * 1e3 / steps
+            f"{busy_ms:.1f} ms; GPU times may include launch gaps")
+    return e0.elapsed_time(e1) * 1e3 / count, host_ms * 1e3 / count
+
+
+def per_stage(case, torch, steps):
+    """GPU time of each stage: batches of `steps` steps cut after stage 1..5;
+    successive differences are the stages' costs (dispatch included)."""
+    cum = []
+    for upto in range(1, len(case.STAGES) + 1):
+        us, _ = gpu_batch_us(torch, lambda i: case.stages(i % case.replicas, upto), steps)
+        cum.append(us)
+    full_us, host_us = gpu_batch_us(torch, lambda i: case.step(i % case.replicas), steps)
+    st = {n: cum[i] - (cum[i - 1] if i else 0.0) for i, n in enumerate(case.STAGES)}
+    return st, full_us, host_us
+
+
+def scorer_launch_us(case, torch, launches):
+    """Average GPU time of one scorer launch (launches back to back on the replicas)."""
+    lib = case.lib
+    case.stages(0, 2)   # a table image for the scorer to read
+    us, _ = gpu_batch_us(torch, lambda i: lib.socket_score(*case.c_score[i % case.replicas]),
+                         launches)
+    return us
 
 
 def prefill_rate(case, torch, reps=5):
@@ -324,21 +354,20 @@ def main():
     log(f"[bench] prefill hash 32K: {pre32}")
     sec = timed_steps(case, torch, args.steps, args.warmup)
     log(f"[bench] 32K step wall {sec * 1e6:.1f} us")
-    stages, gpu_step_us, host_step_us = per_kernel(case, torch, min(args.steps, 200))
-    log(f"[bench] 32K per-kernel us {stages}; gpu step {gpu_step_us:.1f} us; "
+    stages, gpu_step_us, host_step_us = per_stage(case, torch, min(args.steps, 200))
+    log(f"[bench] 32K per-stage GPU us {stages}; full step GPU {gpu_step_us:.1f} us; "
         f"host enqueue {host_step_us:.1f} us/step")
+    score_us = scorer_launch_us(case, torch, 4 * case.replicas)
+    log(f"[bench] 32K scorer launch {score_us:.2f} us")
     launch_bytes, kv_keys = scorer_bytes(case)
-    scorer_s = stages["score"] * 1e-6
-    achieved = launch_bytes / scorer_s / 1e9
+    achieved = launch_bytes / (score_us * 1e-6) / 1e9
     traffic = counters_traffic(launch_bytes)
     w = case.w
     keys_per_step = w.B * w.Hq * (case.n + 1)
-    topk_bytes = keys_per_step * 4
     extra32 = dict(
         step_us_wall=sec * 1e6, step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
-        kernel_us=stages,
+        stage_us=stages, scorer_launch_us=score_us,
         score_topk_us=stages["tables"] + stages["score"] + stages["topk"],
-        topk_gbs=topk_bytes / (stages["topk"] * 1e-6) / 1e9,
         prefill=pre32)
     case.free()
     del case
@@ -353,11 +382,13 @@ def main():
         pre128 = prefill_rate(c3, torch)
         log(f"[bench] prefill hash 128K (the decode-loop prefill): {pre128}")
         sec3 = timed_steps(c3, torch, max(20, args.steps // 4), max(5, args.warmup // 4))
-        st3, gpu3, host3 = per_kernel(c3, torch, max(20, args.steps // 4))
+        st3, gpu3, host3 = per_stage(c3, torch, max(20, args.steps // 4))
+        sc3 = scorer_launch_us(c3, torch, 4 * c3.replicas)
         lb3, _ = scorer_bytes(c3)
-        extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, kernel_us=st3,
+        extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, stage_us=st3,
+                        scorer_launch_us=sc3,
                         keys_per_s=c3.w.B * c3.w.Hq * (c3.n + 1) / sec3,
-                        scorer_gbs=lb3 / (st3["score"] * 1e-6) / 1e9,
+                        scorer_gbs=lb3 / (sc3 * 1e-6) / 1e9,
                         prefill=pre128)
         log(f"[bench] 128K: {extra128}")
         c3.free()

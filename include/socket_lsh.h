@@ -144,8 +144,8 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
  *   q[b][g] and the bucket distribution of every table, stored in the
  *   workspace either as the full table p_l(c) or as its two factors
  *   lo_l(c & 15) (planes 0..3) and hi_l(c >> 4) (planes 4..P-1), each value
- *   rounded once to float32.  Also clears the selection histograms held in
- *   the workspace.
+ *   rounded once to float32.  Also clears the selection histograms and
+ *   counters held in the workspace.
  * socket_score -- Algorithm 2, second half: s_i for every i < lens[b] of every
  *   query head, written to `scores` (or into the workspace when scores is
  *   NULL), plus a histogram of the top bits of each score in the workspace.

@@ -64,6 +64,20 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP only: shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then row_bcast:15 adds row r's total to
+// rows 1 and 3 and row_bcast:31 adds rows 0-1's total to rows 2 and 3.
+// Lanes without a source read 0 (`old`).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // OR over each group of 8 lanes (quad swaps, then the mirror inside each
 // half row, which pairs lane i with lane 7 - i of the other quad).
 __device__ __forceinline__ uint32_t or8_lanes(uint32_t x) {

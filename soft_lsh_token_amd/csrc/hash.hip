@@ -11,9 +11,10 @@
 //    every lane's accumulators hold complete tables, which turns the sign
 //    test + bit packing into lane-local work and one 32-bit store.  The value
 //    rows of the same keys stream through the tile loop for their norms.
-//  * hash_generic_kernel: any dtype, P <= 8, any L; one workgroup per key,
-//    one thread per plane.  Used for float32 keys, for odd shapes and for
-//    the decode-time append of a few keys.
+//  * hash_generic_kernel: any dtype, P <= 8, any L; one-wave workgroups,
+//    each projecting one slice of a key's planes, one plane per lane.  Used
+//    for float32 keys, for odd shapes and for the decode-time append of a
+//    few keys.
 #include "common.h"
 #include "launch.h"
 
@@ -35,61 +36,80 @@ __device__ __forceinline__ void load8<float>(const float* p, float* f) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// grid: B*Hkv*count blocks (block = one key), kGenThreads threads; thread t
-// projects planes t, t + kGenThreads, ...  The 128-element plane row is read
-// with vector loads, all issued before the dot product.
-constexpr int kGenThreads = 512;
+// grid: B*Hkv*count*S one-wave blocks.  The 16 ID words of a key (word w =
+// tables w*TL .. w*TL+TL-1) are split into S slices of WPB words; block
+// (key, s) projects the planes of slice s, one plane per lane, so a block
+// reads only its slice of W.  The plane row is requested before the key
+// position and the K (and, in slice 0, V) row right after it: two dependent
+// global round trips per key.  The signs come out of one wave ballot, whose
+// bit t*P + j is plane j of the slice's table t.
+constexpr int kGenThreads = 64;
 
 template <typename T>
 __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int Hkv, int64_t n_cap,
-    const int32_t* __restrict__ pos0, int count, const T* __restrict__ W, int L, int P,
-    uint8_t* __restrict__ ids, float* __restrict__ vnorm) {
-  const int c = blockIdx.x % count;
-  const int bh = blockIdx.x / count;
+    const int32_t* __restrict__ pos0, int count, const T* __restrict__ W, int L, int P, int TL,
+    int WPB, int S, uint8_t* __restrict__ ids, float* __restrict__ vnorm) {
+  constexpr int NV = kHead * (int)sizeof(T) / 16;  // 16-byte vectors per row
+  const int s = blockIdx.x % S;
+  const int rc = blockIdx.x / S;
+  const int c = rc % count;
+  const int bh = rc / count;
   const int b = bh / Hkv;
+  const int lane = threadIdx.x;
+  const int wpl = TL * P;               // planes per ID word
+  const int pl = s * WPB * wpl + lane;  // this lane's plane
+  const bool live = lane < WPB * wpl && pl / P < L;
+  uint4 wv[NV];
+  if (live) {
+    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)pl * kHead);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) wv[v] = wr[v];
+  }
   const int64_t pos = (int64_t)pos0[b] + c;
   if (pos < 0 || pos >= n_cap) return;
   const int64_t row = (int64_t)bh * n_cap + pos;
   __shared__ float kf[kHead];
-  __shared__ uint32_t bits[256];
-  const int tid = threadIdx.x;
-  if (tid < kHead / 8) load8<T>(K + row * kHead + 8 * tid, kf + 8 * tid);
-  if (tid < 256) bits[tid] = 0u;
+  float vf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vf[i] = 0.f;
+  if (lane < 16) load8<T>(K + row * kHead + 8 * lane, kf + 8 * lane);
+  if (s == 0 && lane >= 16 && lane < 32) load8<T>(V + row * kHead + 8 * (lane - 16), vf);
   __syncthreads();
-  const int planes = L * P;
-  for (int pl = tid; pl < planes; pl += kGenThreads) {
-    const T* wr = W + (int64_t)pl * kHead;
-    float z = 0.f;
+  float z = 0.f;
+  if (live) {
 #pragma unroll
-    for (int h0 = 0; h0 < kHead; h0 += kHead / 2) {
-      float wf[kHead / 2];
+    for (int v = 0; v < NV; ++v) {
+      float f[8];
+      int cnt;
+      if constexpr (sizeof(T) == 2) {
+        unpack_bf16x8(wv[v], f);
+        cnt = 8;
+      } else {
+        f[0] = __uint_as_float(wv[v].x); f[1] = __uint_as_float(wv[v].y);
+        f[2] = __uint_as_float(wv[v].z); f[3] = __uint_as_float(wv[v].w);
+        cnt = 4;
+      }
 #pragma unroll
-      for (int t = 0; t < kHead / 2; t += 8) load8<T>(wr + h0 + t, wf + t);
-#pragma unroll
-      for (int t = 0; t < kHead / 2; ++t) z = fmaf(wf[t], kf[h0 + t], z);
+      for (int e = 0; e < cnt; ++e) z = fmaf(f[e], kf[v * cnt + e], z);
     }
-    if (z > 0.f) atomicOr(&bits[pl / P], 1u << (pl % P));
   }
-  if (tid < 16) {
-    float f[8];
-    load8<T>(V + row * kHead + 8 * tid, f);
+  const uint64_t m = __ballot(live && z > 0.f);
+  if (s == 0) {  // value norm: lanes 16..31 form one DPP row
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    for (int i = 0; i < 8; ++i) ss = fmaf(vf[i], vf[i], ss);
     ss = row16_sum(ss);
-    if (tid == 0) vnorm[row] = sqrtf(ss);
+    if (lane == 16) vnorm[row] = sqrtf(ss);
   }
-  __syncthreads();
-  // word j of this key: tables j*TL .. j*TL+TL-1 (0 past L), in the tiled layout
-  const int TL = ids_word_bytes(L);
-  if (tid < 16) {
+  if (lane < WPB) {
+    const int word = s * WPB + lane;
     uint64_t w = 0;
     for (int b8 = 0; b8 < TL; ++b8) {
-      const int l = tid * TL + b8;
-      if (l < L) w |= (uint64_t)(bits[l] & 255u) << (8 * b8);
+      const int t = word * TL + b8;  // table
+      if (t < L) w |= ((m >> ((lane * TL + b8) * P)) & ((1ull << P) - 1ull)) << (8 * b8);
     }
-    uint8_t* dst = ids + ids_word_offset(bh, n_cap, L, pos, tid);
+    uint8_t* dst = ids + ids_word_offset(bh, n_cap, L, pos, word);
     if (TL == 1) *dst = (uint8_t)w;
     else if (TL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
     else if (TL == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w;
@@ -234,15 +254,20 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     }
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)rows);
+  // words per slice: the largest power of two with WPB * TL * P <= 64 planes
+  const int TL = ids_word_bytes(L);
+  int WPB = 16;
+  while (WPB > 1 && WPB * TL * P > kGenThreads) WPB >>= 1;
+  const int S = 16 / WPB;
+  const dim3 grid((unsigned)(rows * S));
   if (bf16)
     hash_generic_kernel<uint16_t><<<grid, kGenThreads, 0, s>>>(
         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), Hkv, n_cap, pos0, count,
-        static_cast<const uint16_t*>(W), L, P, ids, vnorm);
+        static_cast<const uint16_t*>(W), L, P, TL, WPB, S, ids, vnorm);
   else
     hash_generic_kernel<float><<<grid, kGenThreads, 0, s>>>(
         static_cast<const float*>(K), static_cast<const float*>(V), Hkv, n_cap, pos0, count,
-        static_cast<const float*>(W), L, P, ids, vnorm);
+        static_cast<const float*>(W), L, P, TL, WPB, S, ids, vnorm);
   return hipGetLastError();
 }
 

@@ -14,8 +14,9 @@ struct ScoreWs {
   float* img;           // [B*Hkv][img_floats]  LDS images of the soft tables
   int img_floats;
   uint32_t* hist;       // [B*Hq][kHistBins]
-  uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/4096)*128
-  uint2* cand;          // [B*Hq][n_cap]  candidates past the LDS capacity (score bits, key)
+  uint32_t* counters;   // [B*Hq]  candidates gathered by the top-k scan
+  uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/8192)*256
+  uint2* cand;          // [B*Hq][n_cap]  top-k candidates (score bits, key)
   float* scores;        // [B*Hq][ns]  when the caller passes no score buffer
   int64_t words;
 };
@@ -23,7 +24,7 @@ struct ScoreWs {
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base);
 
 // Algorithm 2, part 1: the soft tables of every query head, written as the
-// scorer's LDS images; clears the selection histograms.
+// scorer's LDS images; clears the selection histograms and counters.
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
                               int L, int P, float tau, const ScoreWs& ws, hipStream_t s);
 

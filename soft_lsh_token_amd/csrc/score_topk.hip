@@ -26,11 +26,12 @@
 //
 // Top-k: the scorer also builds, per query head, a histogram of the top
 // digit of the float32 score bits (scores are non-negative, so their bit
-// patterns order like the values).  One select workgroup per query head then
-// finds the bin holding the k-th largest score, marks every key above it in
-// a bitmap, collects the keys of that bin as candidates, settles them exactly
-// (radix select on the remaining score bits, then on the index so that the
-// lower index wins a tie) and turns the bitmap into ascending indices.
+// patterns order like the values).  A scan kernel spread over many workgroups
+// per query head finds the bin holding the k-th largest score, marks every
+// key above it in a bitmap and collects the keys of that bin as candidates;
+// one resolve workgroup per head settles them exactly (radix select on the
+// remaining score bits, then on the index so that the lower index wins a tie)
+// and turns the bitmap into ascending indices.
 #include <type_traits>
 
 #include "common.h"
@@ -101,19 +102,17 @@ static ImageDims image_dims(int G, int L) {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kSelChunkKeys = 4096;  // keys per top-k chunk: its bitmap is a whole number of words
-constexpr int kSelRingChunks = 8;    // top-k chunks in flight; the bitmap covers whole rings
+constexpr int kScanKeys = 8192;  // keys per top-k scan workgroup (the bitmap covers whole ones)
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
   const size_t heads = (size_t)B * Hq;
   const int G = Hq / Hkv;
   const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L);
-  const int64_t chunks = (n_cap + kSelChunkKeys - 1) / kSelChunkKeys;
-  const int64_t words = (chunks + kSelRingChunks - 1) / kSelRingChunks * kSelRingChunks *
-                        (kSelChunkKeys / 32);
+  const int64_t words = (n_cap + kScanKeys - 1) / kScanKeys * (kScanKeys / 32);
   size_t off = 0;
   const size_t o_img = off; off = align256(off + (size_t)B * Hkv * im.floats * sizeof(float));
   const size_t o_hist = off; off = align256(off + heads * kHistBins * sizeof(uint32_t));
+  const size_t o_cnt = off; off = align256(off + heads * sizeof(uint32_t));
   const size_t o_bm = off; off = align256(off + heads * words * sizeof(uint32_t));
   const size_t o_cand = off; off = align256(off + heads * (size_t)n_cap * sizeof(uint2));
   const size_t o_sc = off; off = align256(off + heads * (size_t)score_stride(n_cap) * sizeof(float));
@@ -122,6 +121,7 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
     ws->img = reinterpret_cast<float*>(p + o_img);
     ws->img_floats = im.floats;
     ws->hist = reinterpret_cast<uint32_t*>(p + o_hist);
+    ws->counters = reinterpret_cast<uint32_t*>(p + o_cnt);
     ws->bitmap = reinterpret_cast<uint32_t*>(p + o_bm);
     ws->cand = reinterpret_cast<uint2*>(p + o_cand);
     ws->scores = reinterpret_cast<float*>(p + o_sc);
@@ -144,13 +144,14 @@ __device__ __forceinline__ void store_slot(float* dst, const float* v) {
 // grid: B*Hkv*16 blocks of kTabThreads.  Block (bh, j) computes the tables
 // j*TL .. j*TL+TL-1 (the tables of scorer lane j) for the G query heads of KV
 // row bh and writes their image slots whole (one slot = the G heads' values
-// of one entry).  It also clears a 1/16 share of those heads' histograms.
+// of one entry).  It also clears a 1/16 share of those heads' histograms
+// (block j = 0: their candidate counters).
 // Tables l >= L (padding of the last lane word) get all-zero entries.
 template <typename T, int G>
 __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
     int TL, int NF, int NS, int FULL, int img_floats, float* __restrict__ img,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters) {
   const int bh = blockIdx.x >> 4, j = blockIdx.x & 15;
   const int b = bh / Hkv, h = bh % Hkv;
   const int bg0 = b * Hq + h * G;
@@ -163,52 +164,67 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   constexpr int kHistShare = G * kHistBins / 16;
   for (int i = tid; i < kHistShare; i += kTabThreads)
     hist[(int64_t)bg0 * kHistBins + j * kHistShare + i] = 0u;
+  if (j == 0 && tid < G) counters[bg0 + tid] = 0u;
   for (int i = tid; i < G * kHead; i += kTabThreads) {
     const int64_t src = (int64_t)(bg0 + i / kHead) * kHead + i % kHead;
     if constexpr (sizeof(T) == 2) qf[i / kHead][i % kHead] = __uint_as_float((uint32_t)q[src] << 16);
     else qf[i / kHead][i % kHead] = q[src];
   }
-  // this thread's projection: table member m, plane pl, head g
-  const int m = tid / (P * G), pl = (tid / G) % P, g = tid % G;
-  const int l = j * TL + m;
-  const bool has = tid < TL * P * G;
-  const bool live = has && l < L;
-  constexpr int NV = kHead * (int)sizeof(T) / 16;  // 16-byte vectors per plane row
-  uint4 raw[NV];
-  if (live) {
-    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + pl) * kHead);
+  // projections: two threads (lanes 2p, 2p+1) per (table member m, plane
+  // pl, head g), each taking half of the 128-element dot product
+  constexpr int NV = kHead * (int)sizeof(T) / 32;  // 16-byte vectors per half row
+  const int nproj = TL * P * G;
+  const int hv = tid & 1;
+  uint4 raw[2][NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) raw[v] = wr[v];
+  for (int it = 0; it < 2; ++it) {
+    const int pr = (tid >> 1) + it * (kTabThreads / 2);
+    const int m = pr / (P * G), pl = (pr / G) % P;
+    const int l = j * TL + m;
+    if (pr < nproj && l < L) {
+      const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + pl) * kHead) + hv * NV;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) raw[it][v] = wr[v];
+    }
   }
   __syncthreads();
-  if (has) {
-    double u = 0.0;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int pr = (tid >> 1) + it * (kTabThreads / 2);
+    if (it * (kTabThreads / 2) >= nproj) break;  // uniform
+    const int m = pr / (P * G), pl = (pr / G) % P, g = pr % G;
+    const int l = j * TL + m;
+    const bool live = pr < nproj && l < L;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
     if (live) {
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         float f[8];
         int cnt;
         if constexpr (sizeof(T) == 2) {
-          unpack_bf16x8(raw[v], f);
+          unpack_bf16x8(raw[it][v], f);
           cnt = 8;
         } else {
-          f[0] = __uint_as_float(raw[v].x); f[1] = __uint_as_float(raw[v].y);
-          f[2] = __uint_as_float(raw[v].z); f[3] = __uint_as_float(raw[v].w);
+          f[0] = __uint_as_float(raw[it][v].x); f[1] = __uint_as_float(raw[it][v].y);
+          f[2] = __uint_as_float(raw[it][v].z); f[3] = __uint_as_float(raw[it][v].w);
           cnt = 4;
         }
+        const int base = hv * (kHead / 2) + v * cnt;
 #pragma unroll
         for (int e = 0; e < cnt; ++e)
-          acc[e & 3] = fma((double)f[e], (double)qf[g][v * cnt + e], acc[e & 3]);
+          acc[e & 3] = fma((double)f[e], (double)qf[g][base + e], acc[e & 3]);
       }
-      u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
-    // sigmoid(x) and sigmoid(-x) from one exponential of -|x|
-    const double x = 2.0 * u / (double)tau;
-    const double e = exp(-fabs(x));
-    const double big = 1.0 / (1.0 + e), small = e * big;
-    sig[tid][1] = x >= 0.0 ? big : small;  // bit set: corner sign +1
-    sig[tid][0] = x >= 0.0 ? small : big;  // bit clear: corner sign -1
+    double u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    u += __shfl_xor(u, 1, 64);  // the partner lane's half
+    if (pr < nproj && hv == 0) {
+      // sigmoid(x) and sigmoid(-x) from one exponential of -|x|
+      const double x = 2.0 * u / (double)tau;
+      const double e = exp(-fabs(x));
+      const double big = 1.0 / (1.0 + e), small = e * big;
+      sig[pr][1] = x >= 0.0 ? big : small;  // bit set: corner sign +1
+      sig[pr][0] = x >= 0.0 ? small : big;  // bit clear: corner sign -1
+    }
   }
   __syncthreads();
   const int plo = P < 4 ? P : 4;
@@ -501,94 +517,50 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
 
 // ---------------------------------------------------------------- top-k
 
-// One workgroup of kSelThreads per query head does the whole selection:
-//  1. the head's first-digit histogram (built by the scorer) gives the bin
-//     d1 holding the k-th largest score, the count `above` of keys in
-//     higher bins and the count C of keys in bin d1;
-//  2. one pass over the scores (4 consecutive keys per lane and chunk,
-//     kSelRing chunks in flight) writes a bitmap of the keys above d1 and
-//     gathers the keys of bin d1 as candidates in LDS (when the histogram
-//     shows more than kCandCap of them, a second pass gathers them into the
-//     workspace instead);
-//  3. a radix select on the remaining 21 score bits, then on the key index
-//     (the lower index wins a tie), picks the k - above candidates that
-//     complete the top-k;
-//  4. the bitmap plus those candidates become ascending indices.
+// Two kernels per call:
+//  scan    (kScanKeys keys per workgroup, many per query head): from the
+//          head's first-digit histogram (built by the scorer) find the bin d1
+//          holding the k-th largest score; write a bitmap of the keys in
+//          higher bins and append the keys of bin d1 to the head's candidate
+//          list (one counter per head).
+//  resolve (one workgroup per query head): radix select on the remaining 21
+//          score bits, then on the key index (the lower index wins a tie),
+//          picks the candidates that complete the top-k; the bitmap plus
+//          those candidates become ascending indices.
 // Bitmap layout: 256-key block j (keys 256j + 4i + e, i < 64, e < 4) is 8
 // words; words 8j + 2e and 8j + 2e + 1 hold bit i = key 256j + 4i + e (the
-// wave ballot of the e-th of the 4 keys each lane loaded).
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelChunk = kSelThreads * 4;   // keys per chunk (4 per thread)
-static_assert(kSelChunk == kSelChunkKeys, "bitmap sizing");
-constexpr int kSelRing = kSelRingChunks;     // chunks in flight per thread
-constexpr int kCandCap = 6144;               // candidates held in LDS
-constexpr int kSegBlocks = kSelThreads;      // 256-key bitmap blocks turned into indices per pass
+// ballot, over a wave that loaded 4 consecutive keys per lane, of the lanes'
+// e-th keys).
+constexpr int kScanThreads = 256;
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanLoads = kScanKeys / (kScanThreads * 4);  // 16-byte loads per thread (8)
+constexpr int kResThreads = 1024;
+constexpr int kResWaves = kResThreads / 64;
+constexpr int kCandCap = 6144;                     // candidates resolved in LDS
+constexpr int kCandPerThread = kCandCap / kResThreads;
+constexpr int kSegBlocks = kResThreads;            // 256-key bitmap blocks emitted per pass
 
-// Block-wide inclusive scan of one value per thread.
+// Block-wide inclusive scan of one value per thread (NT threads).
+template <int NT>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
   uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += wsum[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) off += w < wave ? wsum[w] : 0u;
   return v + off;
 }
 
 struct Boundary {
-  uint32_t d1, above, count;
+  uint32_t d1, above;
 };
 
 struct Pick {
   uint32_t digit, before, inbin;
 };
-
-// Among candidates whose low 21 score bits match (vmask, vval) -- and, when
-// BY_INDEX, whose index matches (imask, ival) -- histogram the 7-bit digit at
-// `shift` of the score bits (or of the index) and return the digit holding
-// the `need`-th entry: counted from the top for scores, from the bottom for
-// indices (the lower index wins a tie).
-template <bool BY_INDEX>
-__device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask,
-                           uint32_t vval, uint32_t imask, uint32_t ival, int shift, uint32_t need,
-                           uint32_t* h128, Pick* shpick) {
-  const int tid = threadIdx.x;
-  if (tid < 128) h128[tid] = 0u;
-  __syncthreads();
-  for (uint32_t i = tid; i < C; i += kSelThreads) {
-    const uint2 e = cands[i];
-    const uint32_t v = e.x & 0x1FFFFFu;
-    if ((v & vmask) != vval) continue;
-    if (BY_INDEX && ((e.y & imask) != ival)) continue;
-    const uint32_t x = BY_INDEX ? e.y : v;
-    atomicAdd(&h128[(x >> shift) & 127u], 1u);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int b0 = BY_INDEX ? 2 * tid : 127 - 2 * tid;
-    const int b1 = BY_INDEX ? 2 * tid + 1 : 126 - 2 * tid;
-    const uint32_t c0 = h128[b0], c1 = h128[b1];
-    uint32_t inc = c0 + c1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(inc, o, 64);
-      if (tid >= o) inc += t;
-    }
-    const uint32_t prev = inc - c0 - c1;
-    if (prev < need && need <= prev + c0) *shpick = Pick{(uint32_t)b0, prev, c0};
-    else if (prev + c0 < need && need <= inc) *shpick = Pick{(uint32_t)b1, prev + c0, c1};
-  }
-  __syncthreads();
-  const Pick r = *shpick;
-  __syncthreads();
-  return r;
-}
 
 __device__ __forceinline__ void clamp_nk(int64_t n_cap, int32_t len, int32_t kk, int k_max,
                                          int64_t* n, int64_t* k) {
@@ -603,150 +575,215 @@ __device__ __forceinline__ void clamp_nk(int64_t n_cap, int32_t len, int32_t kk,
   *k = k2;
 }
 
-// grid: B*Hq blocks of kSelThreads.  `words` = bitmap words per head (a
-// multiple of kSelChunk / 32), `sstride` = score row stride (a multiple of 64).
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+// Bin of the first digit that holds the k-th largest score, and how many keys
+// lie in higher bins, from the head's histogram.  Thread t of NT takes the
+// KPT = 1024/NT bins counted down from 1023 - KPT*t.  All threads must call it.
+template <int NT>
+__device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum, Boundary* sh) {
+  constexpr int KPT = kHistBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t c[KPT];
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    c[i] = hh[kHistBins - 1 - KPT * tid - i];
+    sum += c[i];
+  }
+  if (tid == 0) *sh = Boundary{0u, 0u};
+  const uint32_t inc = block_incl_scan<NT>(sum, wsum);
+  uint32_t prev = inc - sum;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (prev < k && k <= prev + c[i]) *sh = Boundary{(uint32_t)(kHistBins - 1 - KPT * tid - i), prev};
+    prev += c[i];
+  }
+  __syncthreads();
+  const Boundary r = *sh;
+  __syncthreads();
+  return r;
+}
+
+// grid: B*Hq*CH blocks of kScanThreads, CH = ceil(n_cap / kScanKeys).
+__global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
     const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
-    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq,
-    const uint32_t* __restrict__ hist, uint32_t* __restrict__ bitmap, int64_t words,
-    uint2* __restrict__ cand, int32_t* __restrict__ idx) {
-  const int bg = blockIdx.x;
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq, int CH,
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
+    uint32_t* __restrict__ bitmap, int64_t words, uint2* __restrict__ cand) {
+  const int bg = blockIdx.x / CH;
+  const int c = blockIdx.x % CH;
   const int b = bg / Hq;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t n, k;
   clamp_nk(n_cap, lens[b], ks[b], k_max, &n, &k);
-  int32_t* out = idx + (int64_t)bg * k_max;
-  if (k == 0) {
-    for (int t = tid; t < k_max; t += kSelThreads) out[t] = -1;
-    return;
-  }
-  __shared__ uint32_t wsum[kSelWaves];
-  __shared__ Boundary shb;
-  __shared__ uint32_t h128[128];
-  __shared__ Pick shpick;
-  __shared__ uint32_t lcount, seg_total;
-  __shared__ uint2 lcand[kCandCap];
-  __shared__ uint32_t lbm[kSegBlocks * 8];
+  if (k == 0) return;
+  const int64_t c0 = (int64_t)c * kScanKeys;
+  if (c0 >= n) return;
 
-  // the first chunks' scores, issued before anything waits (lane `lane` of
-  // wave w loads keys c*kSelChunk + 256w + 4*lane .. +3 of chunk c)
+  // every score of this workgroup first: load r covers keys
+  // c0 + r*1024 + 256*wave + 4*lane .. +3
   const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
-  const int64_t nch = (n + kSelChunk - 1) / kSelChunk;
-  auto load_chunk = [&](int64_t c, uint4& v) {
-    int64_t key = c * kSelChunk + tid * 4;
-    if (key > sstride - 4) key = sstride - 4;  // past the row: re-read its end
-    v = *reinterpret_cast<const uint4*>(srow + key);
-  };
-  uint4 ring[kSelRing];
+  uint4 v[kScanLoads];
 #pragma unroll
-  for (int r = 0; r < kSelRing; ++r) load_chunk(r, ring[r]);
-
-  // 1. boundary bin (bins scanned from the top, one per thread)
-  const uint32_t hc = hist[(int64_t)bg * kHistBins + (kHistBins - 1 - tid)];
-  if (tid == 0) {
-    shb = Boundary{0u, 0u, 0u};
-    lcount = 0u;
+  for (int r = 0; r < kScanLoads; ++r) {
+    int64_t key = c0 + r * (kScanThreads * 4) + tid * 4;
+    if (key > sstride - 4) key = sstride - 4;  // past the row: re-read its end
+    v[r] = *reinterpret_cast<const uint4*>(srow + key);
   }
-  const uint32_t inc = block_incl_scan(hc, wsum);
-  const uint32_t prev = inc - hc;
-  if (prev < (uint32_t)k && (uint32_t)k <= inc)
-    shb = Boundary{(uint32_t)(kHistBins - 1 - tid), prev, hc};
-  __syncthreads();
-  const Boundary bd = shb;
-
-  // 2. bitmap of the keys above d1, candidates of bin d1.  A key is above
-  // d1 when its bits exceed thr_sel, in d1 when they are at least thr_lo and
-  // not above (the histogram clamps the top digit to kHistBins - 1, and so
-  // does this).  Every step of the ring runs unconditionally (chunks past n
-  // write zero words into the bitmap's padding), so each wait covers one
-  // chunk.
-  uint32_t* bm = bitmap + (int64_t)bg * words;
-  uint2* gc = cand + (int64_t)bg * n_cap;
-  const bool lds_cands = bd.count <= (uint32_t)kCandCap;
+  __shared__ uint32_t wsum[kScanWaves];
+  __shared__ Boundary shb;
+  const Boundary bd = find_boundary<kScanThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
+  // above d1: bits > thr_sel; in d1: bits >= thr_lo and not above (the top
+  // digit is clamped to kHistBins - 1 here as in the histogram)
   const uint32_t thr_lo = bd.d1 << kHistShift;
   const uint32_t thr_sel = bd.d1 < (uint32_t)(kHistBins - 1) ? ((bd.d1 + 1) << kHistShift) - 1u
                                                             : 0xFFFFFFFFu;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint64_t lt = lanemask_lt64();
-  // masks of this wave's lanes whose e-th key (base + 4*lane + e) is below n
-  auto valid_masks = [&](int64_t base, uint64_t* vm) {
+  // candidates gather in LDS; one global reservation per workgroup at the end
+  __shared__ uint2 lc[kScanKeys];
+  __shared__ uint32_t lcount, gbase;
+  if (tid == 0) lcount = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kScanLoads; ++r) {
+    const int64_t base = c0 + r * (kScanThreads * 4) + wave * 256;
+    const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+    uint64_t vm[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t r = (n - base - e + 3) >> 2;  // lanes with 4*lane + e < n - base
-      vm[e] = r >= 64 ? ~0ull : r <= 0 ? 0ull : ((1ull << r) - 1ull);
+      const int64_t rr = (n - base - e + 3) >> 2;  // lanes with 4*lane + e < n - base
+      vm[e] = rr >= 64 ? ~0ull : rr <= 0 ? 0ull : ((1ull << rr) - 1ull);
     }
-  };
-  // wave-level compaction of the candidates (mask m[e]: lanes whose e-th key is one)
-  auto gather = [&](const uint64_t* m, const uint32_t* sb, int64_t base, bool to_lds) {
-    const uint32_t tot = (uint32_t)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) +
-                                    __popcll(m[3]));
+    uint64_t ms[4], mc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ms[e] = __ballot(sb[e] > thr_sel) & vm[e];
+      mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & vm[e];
+    }
+    // even lanes store words 0..3 of the block, odd lanes words 4..7
+    const bool odd = lane & 1;
+    const uint64_t a = odd ? ms[2] : ms[0], a2 = odd ? ms[3] : ms[1];
+    *reinterpret_cast<uint4*>(bm + (base >> 5) + (odd ? 4 : 0)) =
+        make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)a2, (uint32_t)(a2 >> 32));
+    const uint32_t tot = (uint32_t)(__popcll(mc[0]) + __popcll(mc[1]) + __popcll(mc[2]) +
+                                    __popcll(mc[3]));
     if (tot) {
       uint32_t pos = 0u;
       if (lane == 0) pos = atomicAdd(&lcount, tot);
       pos = __builtin_amdgcn_readfirstlane(pos);  // every lane is active here
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if ((m[e] >> lane) & 1ull) {
-          const uint32_t p2 = pos + (uint32_t)__popcll(m[e] & lt);
-          const uint2 entry = make_uint2(sb[e], (uint32_t)(base + 4 * lane + e));
-          if (to_lds) {
-            if (p2 < (uint32_t)kCandCap) lcand[p2] = entry;
-          } else if (p2 < (uint32_t)n) {
-            gc[p2] = entry;
-          }
+        if ((mc[e] >> lane) & 1ull) {
+          const uint32_t p2 = pos + (uint32_t)__popcll(mc[e] & lt);
+          lc[p2] = make_uint2(sb[e], (uint32_t)(base + 4 * lane + e));
         }
-        pos += (uint32_t)__popcll(m[e]);
+        pos += (uint32_t)__popcll(mc[e]);
       }
-    }
-  };
-  for (int64_t c0 = 0; c0 < nch; c0 += kSelRing) {
-#pragma unroll
-    for (int r = 0; r < kSelRing; ++r) {
-      const int64_t c = c0 + r;
-      const int64_t base = c * kSelChunk + wave * 256;
-      const uint32_t sb[4] = {ring[r].x, ring[r].y, ring[r].z, ring[r].w};
-      uint64_t vm[4] = {~0ull, ~0ull, ~0ull, ~0ull};
-      if (base + 256 > n) valid_masks(base, vm);
-      uint64_t ms[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ms[e] = __ballot(sb[e] > thr_sel) & vm[e];
-      // even lanes store words 0..3 of the block, odd lanes words 4..7
-      const bool odd = lane & 1;
-      const uint64_t a = odd ? ms[2] : ms[0], b2 = odd ? ms[3] : ms[1];
-      *reinterpret_cast<uint4*>(bm + (base >> 5) + (odd ? 4 : 0)) =
-          make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b2, (uint32_t)(b2 >> 32));
-      if (lds_cands) {
-        uint64_t mc[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & vm[e];
-        gather(mc, sb, base, true);
-      }
-      load_chunk(c + kSelRing, ring[r]);
-    }
-  }
-  if (!lds_cands) {  // more candidates than LDS holds: gather them into the workspace
-    __syncthreads();
-    if (tid == 0) lcount = 0u;
-    __syncthreads();
-    for (int64_t c = 0; c < nch; ++c) {
-      uint4 v;
-      load_chunk(c, v);
-      const int64_t base = c * kSelChunk + wave * 256;
-      const uint32_t sb[4] = {v.x, v.y, v.z, v.w};
-      uint64_t vm[4];
-      valid_masks(base, vm);
-      uint64_t mc[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mc[e] = __ballot(sb[e] >= thr_lo && !(sb[e] > thr_sel)) & vm[e];
-      gather(mc, sb, base, false);
     }
   }
   __syncthreads();
+  const uint32_t cnt = lcount;  // <= kScanKeys
+  if (cnt == 0) return;
+  if (tid == 0) gbase = atomicAdd(&counters[bg], cnt);
+  __syncthreads();
+  const uint32_t g0 = gbase;
+  uint2* gc = cand + (int64_t)bg * n_cap;
+  for (uint32_t t = tid; t < cnt; t += kScanThreads)
+    if (g0 + t < (uint32_t)n) gc[g0 + t] = lc[t];
+}
 
-  // 3. the candidates that complete the top-k
-  uint32_t C = lcount;
-  if (lds_cands && C > (uint32_t)kCandCap) C = kCandCap;  // only with an inconsistent histogram
-  const uint2* lc = lds_cands ? lcand : gc;                 // candidate i (all of them in one place)
+// Among candidates whose low 21 score bits match (vmask, vval) -- and, when
+// BY_INDEX, whose index matches (imask, ival) -- histogram the 7-bit digit at
+// `shift` of the score bits (or of the index) and return the digit holding
+// the `need`-th entry: counted from the top for scores, from the bottom for
+// indices (the lower index wins a tie).
+template <bool BY_INDEX>
+__device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask, uint32_t vval,
+                           uint32_t imask, uint32_t ival, int shift, uint32_t need,
+                           uint32_t* h128, Pick* shpick) {
+  const int tid = threadIdx.x;
+  if (tid < 128) h128[tid] = 0u;
+  __syncthreads();
+  for (uint32_t i = tid; i < C; i += kResThreads) {
+    const uint2 e = cands[i];
+    const uint32_t v = e.x & 0x1FFFFFu;
+    if ((v & vmask) != vval) continue;
+    if (BY_INDEX && ((e.y & imask) != ival)) continue;
+    const uint32_t x = BY_INDEX ? e.y : v;
+    atomicAdd(&h128[(x >> shift) & 127u], 1u);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int b0 = BY_INDEX ? 2 * tid : 127 - 2 * tid;
+    const int b1 = BY_INDEX ? 2 * tid + 1 : 126 - 2 * tid;
+    const uint32_t c0 = h128[b0], c1 = h128[b1];
+    const uint32_t inc = wave_incl_scan(c0 + c1);
+    const uint32_t prev = inc - c0 - c1;
+    if (prev < need && need <= prev + c0) *shpick = Pick{(uint32_t)b0, prev, c0};
+    else if (prev + c0 < need && need <= inc) *shpick = Pick{(uint32_t)b1, prev + c0, c1};
+  }
+  __syncthreads();
+  const Pick r = *shpick;
+  __syncthreads();
+  return r;
+}
+
+// grid: B*Hq blocks of kResThreads.
+__global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
+    int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
+    int Hq, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ counters,
+    const uint32_t* __restrict__ bitmap, int64_t words, const uint2* __restrict__ cand,
+    int32_t* __restrict__ idx) {
+  const int bg = blockIdx.x;
+  const int b = bg / Hq;
+  const int tid = threadIdx.x;
+  int64_t n, k;
+  clamp_nk(n_cap, lens[b], ks[b], k_max, &n, &k);
+  int32_t* out = idx + (int64_t)bg * k_max;
+  if (k == 0) {
+    for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
+    return;
+  }
+  __shared__ uint32_t wsum[kResWaves];
+  __shared__ Boundary shb;
+  __shared__ uint32_t h128[128];
+  __shared__ Pick shpick;
+  __shared__ uint32_t seg_total;
+  __shared__ uint2 lcand[kCandCap];
+  __shared__ uint32_t lbm[kSegBlocks * 8];
+
+  // every independent load at once: candidate count, the first kCandCap
+  // candidates (whatever their count), this thread's first bitmap block,
+  // its histogram bin (inside find_boundary)
+  const uint2* gc = cand + (int64_t)bg * n_cap;
+  const uint32_t* bm = bitmap + (int64_t)bg * words;
+  const uint32_t Cg = counters[bg];
+  uint2 cv[kCandPerThread];
+#pragma unroll
+  for (int i = 0; i < kCandPerThread; ++i) {
+    int64_t ci = (int64_t)i * kResThreads + tid;
+    if (ci >= n_cap) ci = n_cap - 1;
+    cv[i] = gc[ci];
+  }
+  const int64_t nblocks = (n + 255) >> 8;
+  const int64_t bl0 = tid < nblocks ? tid : 0;
+  uint4 bw0 = reinterpret_cast<const uint4*>(bm)[bl0 * 2];
+  uint4 bw1 = reinterpret_cast<const uint4*>(bm)[bl0 * 2 + 1];
+  const Boundary bd = find_boundary<kResThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
+  const uint32_t C = Cg < (uint32_t)n ? Cg : (uint32_t)n;
+  const bool in_lds = C <= (uint32_t)kCandCap;
+  if (in_lds) {
+#pragma unroll
+    for (int i = 0; i < kCandPerThread; ++i) {
+      const uint32_t ci = (uint32_t)(i * kResThreads + tid);
+      if (ci < C) lcand[ci] = cv[i];
+    }
+  }
+  __syncthreads();
+  const uint2* lc = in_lds ? lcand : gc;
+
+  // the candidates that complete the top-k
   uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C
   uint32_t vmask = 0u, vval = 0u, imax = 0xFFFFFFFFu;
   if (need < C) {
@@ -775,21 +812,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     }
   }
 
-  // 4. bitmap + chosen candidates -> ascending indices, kSegBlocks 256-key
+  // bitmap + chosen candidates -> ascending indices, kSegBlocks 256-key
   // blocks at a time (thread t owns block t of the segment)
-  const int64_t nblocks = (n + 255) >> 8;
   uint32_t written = 0;
   for (int64_t b0 = 0; b0 < nblocks; b0 += kSegBlocks) {
     const int64_t segb = (nblocks - b0) < kSegBlocks ? (nblocks - b0) : kSegBlocks;
-    const int64_t bl = tid < segb ? b0 + tid : b0;
-    const uint4 w0v = reinterpret_cast<const uint4*>(bm)[bl * 2];
-    const uint4 w1v = reinterpret_cast<const uint4*>(bm)[bl * 2 + 1];
+    if (b0 > 0) {
+      const int64_t bl = tid < segb ? b0 + tid : b0;
+      bw0 = reinterpret_cast<const uint4*>(bm)[bl * 2];
+      bw1 = reinterpret_cast<const uint4*>(bm)[bl * 2 + 1];
+    }
     const bool mine = tid < segb;
     uint4* lb = reinterpret_cast<uint4*>(lbm);
-    lb[tid * 2] = mine ? w0v : make_uint4(0u, 0u, 0u, 0u);
-    lb[tid * 2 + 1] = mine ? w1v : make_uint4(0u, 0u, 0u, 0u);
+    lb[tid * 2] = mine ? bw0 : make_uint4(0u, 0u, 0u, 0u);
+    lb[tid * 2 + 1] = mine ? bw1 : make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    for (uint32_t i = tid; i < C; i += kSelThreads) {
+    for (uint32_t i = tid; i < C; i += kResThreads) {
       const uint2 e = lc[i];
       const uint32_t v = e.x & 0x1FFFFFu;
       const int64_t blk = (int64_t)(e.y >> 8) - b0;
@@ -805,7 +843,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       m[e] = (uint64_t)lbm[tid * 8 + 2 * e] | ((uint64_t)lbm[tid * 8 + 2 * e + 1] << 32);
     const uint32_t cnt = (uint32_t)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) +
                                     __popcll(m[3]));
-    const uint32_t incw = block_incl_scan(cnt, wsum);
+    const uint32_t incw = block_incl_scan<kResThreads>(cnt, wsum);
     uint32_t pos = written + incw - cnt;
     const int64_t kbase = (b0 + tid) * 256;
     uint64_t any = m[0] | m[1] | m[2] | m[3];
@@ -820,12 +858,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         }
       }
     }
-    if (tid == kSelThreads - 1) seg_total = incw;
+    if (tid == kResThreads - 1) seg_total = incw;
     __syncthreads();
     written += seg_total;
     __syncthreads();
   }
-  for (int64_t t = (int64_t)k + tid; t < k_max; t += kSelThreads) out[t] = -1;
+  for (int64_t t = (int64_t)k + tid; t < k_max; t += kResThreads) out[t] = -1;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -881,7 +919,7 @@ hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, 
     constexpr int GG = decltype(gtag)::value;
     soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
         static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
-        im.NS, im.full, im.floats, ws.img, ws.hist);
+        im.NS, im.full, im.floats, ws.img, ws.hist, ws.counters);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -912,9 +950,14 @@ hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, int32_t* idx, const ScoreWs& ws,
                        hipStream_t s) {
-  topk_select_kernel<<<(unsigned)(B * Hq), kSelThreads, 0, s>>>(
-      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, ws.hist, ws.bitmap, ws.words,
-      ws.cand, idx);
+  const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
+  topk_scan_kernel<<<(unsigned)(B * Hq * CH), kScanThreads, 0, s>>>(
+      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, CH, ws.hist, ws.counters,
+      ws.bitmap, ws.words, ws.cand);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  topk_resolve_kernel<<<(unsigned)(B * Hq), kResThreads, 0, s>>>(
+      n_cap, lens, ks, k_max, Hq, ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand, idx);
   return hipGetLastError();
 }
 
