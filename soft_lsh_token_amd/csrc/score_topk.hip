@@ -540,6 +540,14 @@ constexpr int kCandCap = 6144;                     // candidates resolved in LDS
 constexpr int kCandPerThread = kCandCap / kResThreads;
 constexpr int kSegBlocks = kResThreads;            // 256-key bitmap blocks emitted per pass
 
+// The 8 bits of b moved to bits 0, 4, ..., 28.
+__device__ __forceinline__ uint32_t spread4(uint32_t b) {
+  b = (b | (b << 12)) & 0x000F000Fu;
+  b = (b | (b << 6)) & 0x03030303u;
+  b = (b | (b << 3)) & 0x11111111u;
+  return b;
+}
+
 // Block-wide inclusive scan of one value per thread (NT threads).
 template <int NT>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) {
@@ -603,14 +611,19 @@ __device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum
   return r;
 }
 
-// grid: B*Hq*CH blocks of kScanThreads, CH = ceil(n_cap / kScanKeys).
+// grid: B*Hq*CH blocks of kScanThreads (rounded up to a multiple of kXcds),
+// CH = ceil(n_cap / kScanKeys).  Logical block lid (remapped as in the
+// scorer, so a KV row's query heads are scanned on the XCD whose L2 received
+// their scores) covers keys [c*kScanKeys, (c+1)*kScanKeys) of head lid / CH.
 __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
     const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq, int CH,
-    const uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
+    int heads, const uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
     uint32_t* __restrict__ bitmap, int64_t words, uint2* __restrict__ cand) {
-  const int bg = blockIdx.x / CH;
-  const int c = blockIdx.x % CH;
+  const int lid = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  if (lid >= heads * CH) return;
+  const int bg = lid / CH;
+  const int c = lid % CH;
   const int b = bg / Hq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -837,25 +850,39 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
       }
     }
     __syncthreads();
-    uint64_t m[4];
+    // thread t takes WPT consecutive 32-key words of the segment, each
+    // rebuilt in key order from the 8-bit slices of the block's 4 masks
+    const int64_t segw = ((n - b0 * 256) + 31) >> 5 < (int64_t)kSegBlocks * 8
+                             ? ((n - b0 * 256) + 31) >> 5 : (int64_t)kSegBlocks * 8;
+    const int WPT = (int)((segw + kResThreads - 1) / kResThreads);  // <= 8
+    uint32_t kw[8];
+    uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      m[e] = (uint64_t)lbm[tid * 8 + 2 * e] | ((uint64_t)lbm[tid * 8 + 2 * e + 1] << 32);
-    const uint32_t cnt = (uint32_t)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) +
-                                    __popcll(m[3]));
+    for (int q = 0; q < 8; ++q) {
+      const int64_t wi = (int64_t)tid * WPT + q;
+      uint32_t x = 0u;
+      if (q < WPT && wi < segw) {
+        const int blk = (int)(wi >> 3), sub = (int)(wi & 7);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t b8 = (lbm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
+          x |= spread4(b8) << e;  // key 4i + e of the word at bit 4i + e
+        }
+      }
+      kw[q] = x;
+      cnt += __popc(x);
+    }
     const uint32_t incw = block_incl_scan<kResThreads>(cnt, wsum);
     uint32_t pos = written + incw - cnt;
-    const int64_t kbase = (b0 + tid) * 256;
-    uint64_t any = m[0] | m[1] | m[2] | m[3];
-    while (any) {
-      const int i = __ffsll((unsigned long long)any) - 1;
-      any &= any - 1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((m[e] >> i) & 1ull) {
-          if (pos < (uint32_t)k_max) out[pos] = (int32_t)(kbase + 4 * i + e);
-          ++pos;
-        }
+    for (int q = 0; q < 8; ++q) {
+      uint32_t x = kw[q];
+      const int64_t kbase = b0 * 256 + ((int64_t)tid * WPT + q) * 32;
+      while (x) {
+        const int bit = __ffs(x) - 1;
+        x &= x - 1;
+        if (pos < (uint32_t)k_max) out[pos] = (int32_t)(kbase + bit);
+        ++pos;
       }
     }
     if (tid == kResThreads - 1) seg_total = incw;
@@ -951,8 +978,9 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
                        const int32_t* ks, int k_max, int32_t* idx, const ScoreWs& ws,
                        hipStream_t s) {
   const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
-  topk_scan_kernel<<<(unsigned)(B * Hq * CH), kScanThreads, 0, s>>>(
-      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, CH, ws.hist, ws.counters,
+  const int64_t nscan = (int64_t)B * Hq * CH;
+  topk_scan_kernel<<<(unsigned)((nscan + kXcds - 1) / kXcds * kXcds), kScanThreads, 0, s>>>(
+      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, CH, B * Hq, ws.hist, ws.counters,
       ws.bitmap, ws.words, ws.cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
