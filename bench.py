@@ -303,7 +303,7 @@ def cpu_baseline(seconds):
     # successive steps as fit in the time budget
     heads_done, t_used, c_used = 0, 0.0, 0.0
     group = w.Hq // w.Hkv
-    while t_used < seconds and heads_done < 4 * w.Hq:
+    while t_used < seconds and heads_done < 64 * w.Hq:
         g = heads_done % w.Hq
         h = g // group
         c0, t0 = time.process_time(), time.perf_counter()
