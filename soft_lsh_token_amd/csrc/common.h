@@ -64,6 +64,14 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's own LDS
+// operations, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads and stores, so prefetches stay in flight across
+// it.  Use only where the barrier protects LDS data.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP only: shifts by
 // 1, 2, 4, 8 inside each 16-lane row, then row_bcast:15 adds row r's total to
 // rows 1 and 3 and row_bcast:31 adds rows 0-1's total to rows 2 and 3.

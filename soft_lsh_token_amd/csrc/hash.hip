@@ -5,12 +5,13 @@
 // Two projection paths:
 //  * hash_mfma_kernel: bf16 keys, P = 8, L in {16, 32, 64}.  The projection
 //    Z = W K^T is a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
-//    accumulation).  W stays in registers for the whole workgroup (each wave
-//    owns 8 tables = 64 planes = two 32-row MFMA tiles); 32-key tiles of K
-//    pass through LDS.  The planes of each 32-row tile are ordered so that
-//    every lane's accumulators hold complete tables, which turns the sign
-//    test + bit packing into lane-local work and one 32-bit store.  The value
-//    rows of the same keys stream through the tile loop for their norms.
+//    accumulation).  W stays in registers for the whole workgroup (each
+//    consumer wave owns 8 tables = 64 planes = two 32-row MFMA tiles);
+//    producer waves stream 128-key tiles of K through two LDS buffers (and
+//    the value rows of the same keys to their norms) while the consumers
+//    multiply the previous tile.  The planes of each 32-row tile are ordered
+//    so that every lane's accumulators hold complete tables, which turns the
+//    sign test + bit packing into lane-local work and one 32-bit store.
 //  * hash_generic_kernel: any dtype, P <= 8, any L; one-wave workgroups,
 //    each projecting one slice of a key's planes, one plane per lane.  Used
 //    for float32 keys, for odd shapes and for the decode-time append of a
@@ -119,22 +120,31 @@ __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
 
 // ---------------------------------------------------------------- MFMA path
 
-constexpr int kTileKeys = 32;
-constexpr int kRowU4 = 17;  // K rows in LDS padded to 272 B: 16 consecutive keys hit 16 bank groups
+constexpr int kBTile = 32;     // keys per MFMA B tile
+constexpr int kTK = 128;       // keys per LDS tile
+constexpr int kProd = 4;       // producer waves
+constexpr int kRowU4 = 17;     // K rows in LDS padded to 272 B: 16 consecutive keys hit 16 bank groups
+constexpr int kProdU4 = kTK * 16 / (kProd * 64);  // K (and V) vectors per producer thread per tile (8)
 
-// Block = NW waves, NW = L / 8; wave w owns tables [8w, 8w+8).
+// Block = NW = L/8 consumer waves + kProd producer waves.  Consumer wave w
+// owns tables [8w, 8w+8) = two 32-plane MFMA A tiles, held in registers; it
+// only runs MFMAs and packs sign bits.  The producers load the next 128-key
+// tile of K and V, write K into the other of two LDS buffers and store the
+// value norms, while the consumers work on the current tile: one block
+// barrier per tile, passed by every wave the same number of times.  MFMA
+// k-slot (8*half + i) of step kk is head element 64*half + 8*kk + i for both
+// operands.  Row R of A tile tt is plane r&7 of table
+// 8w + 4*((R>>2)&1) + 2*tt + (r>>3), r = ((R>>3)<<2)|(R&3), so with the
+// 32x32 accumulator layout (register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + r%4) lane l holds whole tables.
 // grid: B*Hkv*nblk blocks; block blk hashes keys [pos0 + blk*kpb, +kpb) of (b, h).
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void hash_mfma_kernel(const uint16_t* __restrict__ K,
-                                                            const uint16_t* __restrict__ V,
-                                                            int Hkv, int64_t n_cap,
-                                                            const int32_t* __restrict__ pos0,
-                                                            int count,
-                                                            const uint16_t* __restrict__ W,
-                                                            uint8_t* __restrict__ ids,
-                                                            float* __restrict__ vnorm, int kpb,
-                                                            int nblk) {
+__global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int Hkv, int64_t n_cap,
+    const int32_t* __restrict__ pos0, int count, const uint16_t* __restrict__ W,
+    uint8_t* __restrict__ ids, float* __restrict__ vnorm, int kpb, int nblk) {
   constexpr int L = NW * 8;
+  constexpr int NB = kTK / kBTile;
   const int blk = blockIdx.x % nblk;
   const int bh = blockIdx.x / nblk;
   const int b = bh / Hkv;
@@ -146,87 +156,131 @@ __global__ __launch_bounds__(NW * 64) void hash_mfma_kernel(const uint16_t* __re
   if (start >= end || start < 0) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int half = lane >> 5;  // A/B operand: which 8 k-slots; C: which row quartet
-  const int col = lane & 31;
+  const bool producer = wave >= NW;
+  const int64_t rowbase = (int64_t)bh * n_cap;
+  const int ntiles = (int)((end - start + kTK - 1) / kTK);
+  __shared__ uint4 ktile[2][kTK * kRowU4];
 
-  // W-stationary A operands.  MFMA k-slot (8*half + i) of step kk is element
-  // d = 64*half + 8*kk + i (the same map is used for K below).
+  if (producer) {
+    // The next tile's K and V wait in registers (8 named vectors each, one
+    // per load u).  Loads use a uniform base of this workgroup's key range
+    // plus a 32-bit byte offset (at most kpb rows of 256 bytes), clamped to
+    // the range so every load is issued; K goes to LDS before any norm is
+    // stored.
+    static_assert(kProdU4 == 8, "eight vectors per producer thread");
+    const char* kbase = reinterpret_cast<const char*>(K + (rowbase + start) * kHead);
+    const char* vbase = reinterpret_cast<const char*>(V + (rowbase + start) * kHead);
+    const uint32_t last = (uint32_t)(end - start - 1);
+    const int pt = tid - NW * 64;  // 0 .. kProd*64-1
+    auto off_of = [&](int t, int u) -> uint32_t {
+      const int e = pt + u * kProd * 64;
+      uint32_t r = (uint32_t)(t * kTK + (e >> 4));
+      if (r > last) r = last;  // past the range: re-read its last key
+      return r * (kHead * 2) + (uint32_t)(e & 15) * 16u;
+    };
+#define SOCKET_LD(u) \
+    k##u = *reinterpret_cast<const uint4*>(kbase + off_of(tl, u)); \
+    v##u = *reinterpret_cast<const uint4*>(vbase + off_of(tl, u));
+#define SOCKET_ST(u) kt[((pt + u * kProd * 64) >> 4) * kRowU4 + (pt & 15)] = k##u;
+#define SOCKET_NRM(u) \
+    { float f[8]; unpack_bf16x8(v##u, f); float ss = 0.f; \
+      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss); n##u = sqrtf(row16_sum(ss)); }
+#define SOCKET_VN(u) \
+    { const int64_t pos = start + (int64_t)ts * kTK + ((pt + u * kProd * 64) >> 4); \
+      if (pos < end) vnorm[rowbase + pos] = n##u; }
+    uint4 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+    {
+      const int tl = 0;
+      SOCKET_LD(0) SOCKET_LD(1) SOCKET_LD(2) SOCKET_LD(3)
+      SOCKET_LD(4) SOCKET_LD(5) SOCKET_LD(6) SOCKET_LD(7)
+    }
+    for (int ts = 0; ts <= ntiles; ++ts) {
+      // stage tile ts (its loads were issued one step earlier), then load ts + 1
+      if (ts < ntiles) {
+        uint4* kt = ktile[ts & 1];
+        SOCKET_ST(0) SOCKET_ST(1) SOCKET_ST(2) SOCKET_ST(3)
+        SOCKET_ST(4) SOCKET_ST(5) SOCKET_ST(6) SOCKET_ST(7)
+        float n0, n1, n2, n3, n4, n5, n6, n7;
+        SOCKET_NRM(0) SOCKET_NRM(1) SOCKET_NRM(2) SOCKET_NRM(3)
+        SOCKET_NRM(4) SOCKET_NRM(5) SOCKET_NRM(6) SOCKET_NRM(7)
+        if ((pt & 15) == 0) {
+          SOCKET_VN(0) SOCKET_VN(1) SOCKET_VN(2) SOCKET_VN(3)
+          SOCKET_VN(4) SOCKET_VN(5) SOCKET_VN(6) SOCKET_VN(7)
+        }
+        const int tl = ts + 1;
+        SOCKET_LD(0) SOCKET_LD(1) SOCKET_LD(2) SOCKET_LD(3)
+        SOCKET_LD(4) SOCKET_LD(5) SOCKET_LD(6) SOCKET_LD(7)
+      }
+      lds_barrier();  // the next tile's loads stay in flight
+    }
+#undef SOCKET_LD
+#undef SOCKET_ST
+#undef SOCKET_NRM
+#undef SOCKET_VN
+    return;
+  }
+
+  // consumers: W-stationary A operands
+  const int half = lane >> 5;
+  const int col = lane & 31;
   bf16x8_t a[2][8];
   {
-    const int R = col;  // A row held by this lane
+    const int R = col;
     const int hout = (R >> 2) & 1;
     const int r = ((R >> 3) << 2) | (R & 3);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int table = 8 * wave + 4 * hout + 2 * tt + (r >> 3);
-      const int plane = r & 7;
-      const uint16_t* wr = W + ((int64_t)(table * 8 + plane)) * kHead + 64 * half;
+      const uint16_t* wr = W + ((int64_t)(table * 8 + (r & 7))) * kHead + 64 * half;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) a[tt][kk] = *reinterpret_cast<const bf16x8_t*>(wr + 8 * kk);
     }
   }
-
-  __shared__ uint4 ktile[kTileKeys * kRowU4];
-  const uint4* K4 = reinterpret_cast<const uint4*>(K);
-  const uint4* V4 = reinterpret_cast<const uint4*>(V);
-  const int64_t rowbase = (int64_t)bh * n_cap;
-
-  for (int64_t t0 = start; t0 < end; t0 += kTileKeys) {
-    // K rows into LDS; V rows straight to their norms (16 lanes per row)
-    for (int e = tid; e < kTileKeys * 16; e += NW * 64) {
-      const int key = e >> 4, part = e & 15;
-      const int64_t pos = t0 + key;
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+  lds_barrier();
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t t0 = start + (int64_t)t * kTK;
+    const uint4* kt = ktile[t & 1];
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) {
+      f32x16_t acc0 = {0}, acc1 = {0};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const uint4 bv = kt[(bt * kBTile + col) * kRowU4 + 8 * half + kk];
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bv);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][kk], bop, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][kk], bop, acc1, 0, 0, 0);
+      }
+      // register r of tile tt = plane r & 7 of table 8w + 4*half + 2*tt + (r >> 3):
+      // bit 16*tt + r of the 4-table word; a plane is set when its float bits,
+      // read as an int, clamp to 1 in [0, 1]
+      uint32_t word = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        word |= (uint32_t)min(max(__float_as_int(acc0[r]), 0), 1) << r;
+        word |= (uint32_t)min(max(__float_as_int(acc1[r]), 0), 1) << (16 + r);
+      }
+      // the 4 tables 8w + 4*half .. +3 of key pos, as ID words of the tiled layout
+      const int64_t pos = t0 + bt * kBTile + col;
       if (pos < end) {
-        kv = K4[(rowbase + pos) * 16 + part];
-        vv = V4[(rowbase + pos) * 16 + part];
-      }
-      ktile[key * kRowU4 + part] = kv;
-      float f[8];
-      unpack_bf16x8(vv, f);
-      float ss = 0.f;
+        constexpr int TL = ids_word_bytes(L);
+        const int t0w = (8 * wave + 4 * half) / TL;  // first word index
+        if constexpr (TL == 4) {
+          *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) = word;
+        } else if constexpr (TL == 2) {
+          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) =
+              (uint16_t)word;
+          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w + 1)) =
+              (uint16_t)(word >> 16);
+        } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
-      ss = row16_sum(ss);
-      if (part == 0 && pos < end) vnorm[rowbase + pos] = sqrtf(ss);
-    }
-    __syncthreads();
-    f32x16_t acc0 = {0}, acc1 = {0};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint4 bv = ktile[col * kRowU4 + 8 * half + kk];
-      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bv);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][kk], bop, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][kk], bop, acc1, 0, 0, 0);
-    }
-    __syncthreads();
-    // accumulator r of tile tt holds plane (r & 7) of table 8w + 4*half + 2*tt + (r >> 3)
-    uint32_t word = 0u;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      word |= (acc0[r] > 0.f ? 1u : 0u) << ((r >> 3) * 8 + (r & 7));
-      word |= (acc1[r] > 0.f ? 1u : 0u) << (16 + (r >> 3) * 8 + (r & 7));
-    }
-    // the 4 tables 8w + 4*half .. +3 of key pos, as IDs words of the tiled layout
-    const int64_t pos = t0 + col;
-    if (pos < end) {
-      constexpr int TL = ids_word_bytes(L);
-      const int t0w = (8 * wave + 4 * half) / TL;  // first word index
-      if constexpr (TL == 4) {
-        *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) = word;
-      } else if constexpr (TL == 2) {
-        *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) =
-            (uint16_t)word;
-        *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w + 1)) =
-            (uint16_t)(word >> 16);
-      } else {
-#pragma unroll
-        for (int b8 = 0; b8 < 4; ++b8)
-          ids[ids_word_offset(bh, n_cap, L, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+          for (int b8 = 0; b8 < 4; ++b8)
+            ids[ids_word_offset(bh, n_cap, L, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+        }
       }
     }
+    lds_barrier();  // the ID stores stay in flight
   }
 }
 
@@ -241,16 +295,18 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
   // the MFMA path covers every ID word when L is 16, 32 or 64
   const bool mfma_ok = bf16 && P == 8 && (L == 16 || L == 32 || L == 64) && count >= 64;
   if (mfma_ok) {
-    const int kpb = 1024;
-    const int nblk = (count + kpb - 1) / kpb;
+    // about one workgroup per CU, each streaming a contiguous key range
+    int64_t nblk = (256 + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
+    int64_t kpb = ((count + nblk - 1) / nblk + 127) / 128 * 128;
+    nblk = (count + kpb - 1) / kpb;
     const dim3 grid((unsigned)(B * Hkv * nblk));
     const uint16_t* Kb = static_cast<const uint16_t*>(K);
     const uint16_t* Vb = static_cast<const uint16_t*>(V);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     switch (L) {
-      case 16: hash_mfma_kernel<2><<<grid, 128, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
-      case 32: hash_mfma_kernel<4><<<grid, 256, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
-      default: hash_mfma_kernel<8><<<grid, 512, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, kpb, nblk); break;
+      case 16: hash_mfma_kernel<2><<<grid, (2 + kProd) * 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, (int)kpb, (int)nblk); break;
+      case 32: hash_mfma_kernel<4><<<grid, (4 + kProd) * 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, (int)kpb, (int)nblk); break;
+      default: hash_mfma_kernel<8><<<grid, (8 + kProd) * 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, (int)kpb, (int)nblk); break;
     }
     return hipGetLastError();
   }
