@@ -90,7 +90,7 @@ class Case:
         self.pos_append = torch.full((w.B,), self.n, dtype=torch.int32, device=dev)
         self.lens = torch.full((w.B,), self.n + 1, dtype=torch.int32, device=dev)
         self.ks = torch.from_numpy(w.ks).to(dev)
-        self.ids = [S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, dev) for _ in range(replicas)]
+        self.ids = [S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, dev) for _ in range(replicas)]
         self.vn = [torch.empty(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
                    for _ in range(replicas)]
         self.idx = torch.empty(w.B, w.Hq, self.k, dtype=torch.int32, device=dev)

@@ -33,18 +33,20 @@
  * - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
  *   Hq must be a multiple of Hkv; socket_score_topk needs Hq / Hkv in
  *   {1, 2, 4}.
- * - d must be 128.  1 <= P <= 8, 1 <= L <= 128, 1 <= k_max <= 65536.
+ * - d must be 128.  Either 1 <= P <= 8 and 1 <= L <= 128, or P in {9, 10}
+ *   and 1 <= L <= 64.  1 <= k_max <= 65536.
  *
  * Bucket-ID cache layout
  * ----------------------
- * The bucket ID of table l is one byte (bit j = sign of plane j).  The IDs of
- * a key are cut into 16 words of TL bytes, TL = 1, 2, 4 or 8 the smallest
- * power of two with 16*TL >= L; word w holds tables w*TL .. w*TL+TL-1 (byte
- * b of the word = table w*TL + b; tables >= L read as 0).  Keys are tiled in
- * groups of 64: key i of KV row r = b*Hkv + h lies in group i/64 at t = i%64,
- * t = 16*kg + x; with u = (x - w) mod 16 and R = 16/TL its word w is stored at
- * byte offset
- *   ((r * ceil(n_cap/64) + i/64) * 1024 + (u/R)*64*R + (16*kg + w)*R + u%R) * TL.
+ * The bucket ID of table l (bit j = sign of plane j) is a cell of C bytes:
+ * C = 1 for P <= 8, C = 2 (little-endian) for P = 9 or 10.  The IDs of a key
+ * are cut into 16 words of TL tables, TL = 1, 2, 4 or 8 the smallest power of
+ * two with 16*TL >= L; word w holds tables w*TL .. w*TL+TL-1 (cell b of the
+ * word = table w*TL + b; tables >= L read as 0) and is WB = TL*C bytes long.
+ * Keys are tiled in groups of 64: key i of KV row r = b*Hkv + h lies in group
+ * i/64 at t = i%64, t = 16*kg + x; with u = (x - w) mod 16 and R = 16/WB its
+ * word w is stored at byte offset
+ *   ((r * ceil(n_cap/64) + i/64) * 1024 + (u/R)*64*R + (16*kg + w)*R + u%R) * WB.
  * This order lets the scorer read its words with 16-byte loads, 1 KiB per
  * wave and load.
  * - Errors are reported as negative return codes before anything is
@@ -64,7 +66,7 @@ extern "C" {
 enum {
   SOCKET_OK = 0,
   SOCKET_EINVAL = -1,       /* null pointer, bad size, bad shape            */
-  SOCKET_EUNSUPPORTED = -2, /* valid but not implemented (d != 128, P > 8)  */
+  SOCKET_EUNSUPPORTED = -2, /* valid but not implemented (d != 128, P > 10) */
   SOCKET_ENOSPC = -3,       /* workspace smaller than the *_workspace size  */
   SOCKET_EHIP = -4          /* a HIP launch failed                          */
 };
@@ -77,9 +79,9 @@ const char* socket_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int socket_version(void);
 
-/* Size in bytes of the bucket-ID cache for B x Hkv rows of n_cap keys
- * (0 for invalid sizes). */
-size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L);
+/* Size in bytes of the bucket-ID cache for B x Hkv rows of n_cap keys and L
+ * tables of P planes (0 for invalid or unsupported sizes). */
+size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L, int P);
 
 /*
  * socket_hash_keys -- Algorithm 1 (SOCKET Sec. 4.1; bucket ID = sign pattern
@@ -94,7 +96,7 @@ size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L);
  * append passes pos0 = current length and count = 1 after the caller has
  * written the new row of K and V.
  *
- * pos0 is a device int32 array [B].  ids (socket_ids_bytes(B, Hkv, n_cap, L)
+ * pos0 is a device int32 array [B].  ids (socket_ids_bytes(B, Hkv, n_cap, L, P)
  * bytes) receives all 16 words of every hashed key in the tiled layout;
  * other keys and other rows of vnorm are untouched.
  */
@@ -142,9 +144,10 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
  *
  * socket_soft_tables -- Algorithm 2, first half: the float64 projections of
  *   q[b][g] and the bucket distribution of every table, stored in the
- *   workspace either as the full table p_l(c) or as its two factors
- *   lo_l(c & 15) (planes 0..3) and hi_l(c >> 4) (planes 4..P-1), each value
- *   rounded once to float32.  Also clears the selection histograms and
+ *   workspace either as the full table p_l(c) or as its two factors, each
+ *   value rounded once to float32: lo_l(c & 15) (planes 0..3) and
+ *   hi_l(c >> 4) (planes 4..P-1) for P <= 8, lo_l(c & 31) (planes 0..4) and
+ *   hi_l(c >> 5) (planes 5..P-1) for P = 9 or 10.  Also clears the selection histograms and
  *   counters held in the workspace.
  * socket_score -- Algorithm 2, second half: s_i for every i < lens[b] of every
  *   query head, written to `scores` (or into the workspace when scores is

@@ -26,7 +26,7 @@ _vp, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c
 _SIGS = {
     "socket_status_string": (ctypes.c_char_p, [_i]),
     "socket_version": (_i, []),
-    "socket_ids_bytes": (_sz, [_i, _i, _i64, _i]),
+    "socket_ids_bytes": (_sz, [_i, _i, _i64, _i, _i]),
     "socket_hash_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp, _vp]),
     "socket_score_topk_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
     "socket_score_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _i64, _vp,
@@ -105,21 +105,21 @@ def _stream(t: torch.Tensor, stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def socket_ids_bytes(B: int, Hkv: int, n_cap: int, L: int) -> int:
-    return int(lib().socket_ids_bytes(B, Hkv, n_cap, L))
+def socket_ids_bytes(B: int, Hkv: int, n_cap: int, L: int, P: int) -> int:
+    return int(lib().socket_ids_bytes(B, Hkv, n_cap, L, P))
 
 
-def alloc_ids(B: int, Hkv: int, n_cap: int, L: int, device) -> torch.Tensor:
+def alloc_ids(B: int, Hkv: int, n_cap: int, L: int, P: int, device) -> torch.Tensor:
     """A zeroed bucket-ID cache (tiled layout, see soft_lsh_token_amd.layout)."""
     from .layout import ids_shape
-    t = torch.zeros(ids_shape(B, Hkv, n_cap, L), dtype=torch.uint8, device=device)
-    assert t.numel() == socket_ids_bytes(B, Hkv, n_cap, L)
+    t = torch.zeros(ids_shape(B, Hkv, n_cap, L, P), dtype=torch.uint8, device=device)
+    assert t.numel() == socket_ids_bytes(B, Hkv, n_cap, L, P)
     return t
 
 
-def _ids(ids: torch.Tensor, B: int, Hkv: int, n_cap: int, L: int) -> int:
+def _ids(ids: torch.Tensor, B: int, Hkv: int, n_cap: int, L: int, P: int) -> int:
     from .layout import ids_shape
-    return _dev(ids, "ids", torch.uint8, ids_shape(B, Hkv, n_cap, L))
+    return _dev(ids, "ids", torch.uint8, ids_shape(B, Hkv, n_cap, L, P))
 
 
 def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
@@ -131,7 +131,7 @@ def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: tor
     rc = lib().socket_hash_keys(
         _dev(K, "K"), _dev(V, "V", K.dtype, K.shape), dt, B, Hkv, d, n_cap,
         _dev(pos0, "pos0", torch.int32, (B,)), int(count), _dev(W, "W", K.dtype, (L * P, d)),
-        L, P, _ids(ids, B, Hkv, n_cap, L),
+        L, P, _ids(ids, B, Hkv, n_cap, L, P),
         _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _stream(K, stream))
     _check("socket_hash_keys", rc)
 
@@ -176,7 +176,7 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
                                             (B, Hq, score_stride(n_cap)))
     rc = lib().socket_score_topk(
         _dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P,
-        float(tau), _ids(ids, B, Hkv, n_cap, L),
+        float(tau), _ids(ids, B, Hkv, n_cap, L, P),
         _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
         _dev(lens, "lens", torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)),
         int(k_max), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr, wptr, wbytes,
@@ -200,7 +200,7 @@ def socket_score(ids: torch.Tensor, vnorm: torch.Tensor, lens: torch.Tensor, Hq:
     """Algorithm 2, second half: soft-count scores (needs socket_soft_tables on ws first)."""
     B, Hkv, n_cap = vnorm.shape
     wptr, wbytes = _ws_ptr(ws, 0)
-    rc = lib().socket_score(B, Hq, Hkv, L, P, _ids(ids, B, Hkv, n_cap, L),
+    rc = lib().socket_score(B, Hq, Hkv, L, P, _ids(ids, B, Hkv, n_cap, L, P),
                             _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
                             _dev(lens, "lens", torch.int32, (B,)), n_cap,
                             _dev(scores, "scores", torch.float32, (B, Hq, score_stride(n_cap))),

@@ -12,6 +12,12 @@ constexpr int kMaxL = 128;       // 16 ID words of at most 8 tables each
 constexpr int kMaxScoreL = 128;
 constexpr int kMaxKmax = 1 << 16;  // 1024 attention splits of 64 keys
 
+// Table shapes with an ID layout: one-byte IDs (P <= 8) for up to 128
+// tables, two-byte IDs (P = 9 or 10) for up to 64.
+static bool tables_ok(int L, int P) {
+  return P <= 8 ? L <= kMaxL : P <= 10 && L <= 64;
+}
+
 bool group_ok(int Hq, int Hkv) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
   const int G = Hq / Hkv;
@@ -44,23 +50,23 @@ int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, in
   if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
   if (B <= 0 || Hkv <= 0 || n_cap <= 0 || count < 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
   if (n_cap >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
-  if (d != kHead || P > 8 || L > kMaxL) return SOCKET_EUNSUPPORTED;
+  if (d != kHead || !tables_ok(L, P)) return SOCKET_EUNSUPPORTED;
   if ((int64_t)B * Hkv * count >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
   if (count == 0) return SOCKET_OK;
   return from_hip(launch_hash_keys(K, V, dtype, B, Hkv, n_cap, pos0, count, W, L, P, ids, vnorm,
                                    static_cast<hipStream_t>(stream)));
 }
 
-size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L) {
-  if (B <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || L > kMaxL) return 0;
-  return (size_t)B * Hkv * ids_groups(n_cap) * 64 * ids_key_bytes(L);
+size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L, int P) {
+  if (B <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || P <= 0 || !tables_ok(L, P)) return 0;
+  return (size_t)B * Hkv * ids_groups(n_cap) * 64 * ids_key_bytes(L, P);
 }
 
 size_t socket_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
                                    int k_max) {
   (void)k_max;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || L > kMaxScoreL || P <= 0 ||
-      P > 8 || !group_ok(Hq, Hkv))
+      !tables_ok(L, P) || !group_ok(Hq, Hkv))
     return 0;
   return score_ws_layout(B, Hq, Hkv, n_cap, L, nullptr, nullptr);
 }
@@ -77,7 +83,7 @@ static int check_sizes(int B, int Hq, int Hkv, int L, int P, int64_t n_cap) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
   if (Hq % Hkv) return SOCKET_EINVAL;
   if (!group_ok(Hq, Hkv)) return SOCKET_EUNSUPPORTED;
-  if (P > 8 || L > kMaxScoreL) return SOCKET_EUNSUPPORTED;
+  if (!tables_ok(L, P) || L > kMaxScoreL) return SOCKET_EUNSUPPORTED;
   if (n_cap >= ((int64_t)1 << 31) || (int64_t)B * Hq * n_cap >= ((int64_t)1 << 40))
     return SOCKET_EUNSUPPORTED;
   return SOCKET_OK;

@@ -12,30 +12,35 @@ constexpr int kHistShift = 21;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Bucket-ID cache layout.  The IDs of one key are cut into 16 words of TL
-// bytes (word j = tables j*TL .. j*TL+TL-1; tables >= L read as 0), TL the
-// smallest power of two with 16*TL >= L.  Keys are tiled in groups of 64.
-// Inside a group, word j of key t = 16*kg + x belongs to scorer lane
-// 16*kg + j in round r = (x - j) mod 16 and is stored at word slot
-//   (r / R) * 64 * R + (16*kg + j) * R + r % R,   R = 16 / TL,
+// Bucket-ID cache layout.  Each table's ID is a cell of C bytes (C = 1 for
+// P <= 8, 2 for P <= 10).  The IDs of one key are cut into 16 words of T
+// tables (word j = tables j*T .. j*T+T-1; tables >= L read as 0), T the
+// smallest power of two with 16*T >= L, so a word is WB = T*C bytes.  Keys
+// are tiled in groups of 64.  Inside a group, word j of key t = 16*kg + x
+// belongs to scorer lane 16*kg + j in round r = (x - j) mod 16 and is stored
+// at word slot
+//   (r / R) * 64 * R + (16*kg + j) * R + r % R,   R = 16 / WB,
 // so that a lane's words of R consecutive rounds form one 16-byte vector and
 // a wave's 16-byte loads read 1 KiB contiguously.
-__host__ __device__ constexpr int ids_word_bytes(int L) {
+__host__ __device__ constexpr int ids_tables_per_word(int L) {
   return L <= 16 ? 1 : L <= 32 ? 2 : L <= 64 ? 4 : 8;
 }
-__host__ __device__ constexpr int ids_key_bytes(int L) { return 16 * ids_word_bytes(L); }
+__host__ __device__ constexpr int ids_cell_bytes(int P) { return P > 8 ? 2 : 1; }
+__host__ __device__ constexpr int ids_word_bytes(int L, int P) {
+  return ids_tables_per_word(L) * ids_cell_bytes(P);
+}
+__host__ __device__ constexpr int ids_key_bytes(int L, int P) { return 16 * ids_word_bytes(L, P); }
 __host__ __device__ inline int64_t ids_groups(int64_t n_cap) { return (n_cap + 63) / 64; }
 
-// Byte offset of word j of key `key` of KV row bh.
-__host__ __device__ inline int64_t ids_word_offset(int64_t bh, int64_t n_cap, int L, int64_t key,
+// Byte offset of word j of key `key` of KV row bh, for WB-byte words.
+__host__ __device__ inline int64_t ids_word_offset(int64_t bh, int64_t n_cap, int WB, int64_t key,
                                                    int j) {
-  const int TL = ids_word_bytes(L);
-  const int R = 16 / TL;
+  const int R = 16 / WB;
   const int64_t gi = key >> 6;
   const int t = (int)(key & 63), kg = t >> 4, x = t & 15;
   const int r = (x - j) & 15;
   const int slot = (r / R) * 64 * R + ((kg << 4) | j) * R + (r % R);
-  return ((bh * ids_groups(n_cap) + gi) * 1024 + slot) * TL;
+  return ((bh * ids_groups(n_cap) + gi) * 1024 + slot) * WB;
 }
 
 // Row stride (floats) of the per-head score rows: n_cap rounded up to 64, so

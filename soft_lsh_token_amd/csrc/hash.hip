@@ -50,7 +50,7 @@ template <typename T>
 __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int Hkv, int64_t n_cap,
     const int32_t* __restrict__ pos0, int count, const T* __restrict__ W, int L, int P, int TL,
-    int WPB, int S, uint8_t* __restrict__ ids, float* __restrict__ vnorm) {
+    int C, int WPB, int S, uint8_t* __restrict__ ids, float* __restrict__ vnorm) {
   constexpr int NV = kHead * (int)sizeof(T) / 16;  // 16-byte vectors per row
   const int s = blockIdx.x % S;
   const int rc = blockIdx.x / S;
@@ -104,17 +104,25 @@ __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
     if (lane == 16) vnorm[row] = sqrtf(ss);
   }
   if (lane < WPB) {
+    // word = TL tables of C-byte cells (WB = TL*C <= 16 bytes)
     const int word = s * WPB + lane;
-    uint64_t w = 0;
+    const int WB = TL * C;
+    uint64_t w[2] = {0ull, 0ull};
     for (int b8 = 0; b8 < TL; ++b8) {
       const int t = word * TL + b8;  // table
-      if (t < L) w |= ((m >> ((lane * TL + b8) * P)) & ((1ull << P) - 1ull)) << (8 * b8);
+      if (t < L) {
+        const uint64_t id = (m >> ((lane * TL + b8) * P)) & ((1ull << P) - 1ull);
+        const int bit = 8 * C * b8;
+        w[bit >> 6] |= id << (bit & 63);
+      }
     }
-    uint8_t* dst = ids + ids_word_offset(bh, n_cap, L, pos, word);
-    if (TL == 1) *dst = (uint8_t)w;
-    else if (TL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
-    else if (TL == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w;
-    else *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w, (uint32_t)(w >> 32));
+    uint8_t* dst = ids + ids_word_offset(bh, n_cap, WB, pos, word);
+    if (WB == 1) *dst = (uint8_t)w[0];
+    else if (WB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+    else if (WB == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w[0];
+    else if (WB == 8) *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w[0], (uint32_t)(w[0] >> 32));
+    else *reinterpret_cast<uint4*>(dst) = make_uint4((uint32_t)w[0], (uint32_t)(w[0] >> 32),
+                                                     (uint32_t)w[1], (uint32_t)(w[1] >> 32));
   }
 }
 
@@ -264,19 +272,19 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
       // the 4 tables 8w + 4*half .. +3 of key pos, as ID words of the tiled layout
       const int64_t pos = t0 + bt * kBTile + col;
       if (pos < end) {
-        constexpr int TL = ids_word_bytes(L);
+        constexpr int TL = ids_word_bytes(L, 8);   // P = 8: one byte per table
         const int t0w = (8 * wave + 4 * half) / TL;  // first word index
         if constexpr (TL == 4) {
-          *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) = word;
+          *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) = word;
         } else if constexpr (TL == 2) {
-          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w)) =
+          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) =
               (uint16_t)word;
-          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, L, pos, t0w + 1)) =
+          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w + 1)) =
               (uint16_t)(word >> 16);
         } else {
 #pragma unroll
           for (int b8 = 0; b8 < 4; ++b8)
-            ids[ids_word_offset(bh, n_cap, L, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+            ids[ids_word_offset(bh, n_cap, TL, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
         }
       }
     }
@@ -311,7 +319,8 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     return hipGetLastError();
   }
   // words per slice: the largest power of two with WPB * TL * P <= 64 planes
-  const int TL = ids_word_bytes(L);
+  const int TL = ids_tables_per_word(L);
+  const int C = ids_cell_bytes(P);
   int WPB = 16;
   while (WPB > 1 && WPB * TL * P > kGenThreads) WPB >>= 1;
   const int S = 16 / WPB;
@@ -319,11 +328,11 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
   if (bf16)
     hash_generic_kernel<uint16_t><<<grid, kGenThreads, 0, s>>>(
         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), Hkv, n_cap, pos0, count,
-        static_cast<const uint16_t*>(W), L, P, TL, WPB, S, ids, vnorm);
+        static_cast<const uint16_t*>(W), L, P, TL, C, WPB, S, ids, vnorm);
   else
     hash_generic_kernel<float><<<grid, kGenThreads, 0, s>>>(
         static_cast<const float*>(K), static_cast<const float*>(V), Hkv, n_cap, pos0, count,
-        static_cast<const float*>(W), L, P, TL, WPB, S, ids, vnorm);
+        static_cast<const float*>(W), L, P, TL, C, WPB, S, ids, vnorm);
   return hipGetLastError();
 }
 

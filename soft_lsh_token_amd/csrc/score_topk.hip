@@ -44,18 +44,23 @@ namespace socketlsh {
 // LDS image of the tables of one KV row (its G query heads).  Lane j of a
 // 16-lane scorer row owns tables j*TL .. j*TL+TL-1; the first NF of them are
 // kept as full tables, the other NS = TL - NF as their two factors:
-//   full slot (e*NF + m)*16 + j            e < 2^P, m < NF
-//   half slot FULL + ((hf*16 + c)*NS + m)*16 + j   hf = 0 (planes 0..3) or 1
-//                                            (planes 4..P-1), c < 16, m < NS
+//   full slot (e*NF + m)*16 + j                       e < 2^P, m < NF
+//   half slot FULL + ((hf*HE + c)*NS + m)*16 + j      hf = 0 (low planes) or
+//                                                      1 (high planes), c < HE, m < NS
 // one slot = G floats (the G query heads).  Bank group of a slot = j, so the
-// 16 lookups of a row never collide.  NF is the largest count whose image
-// fits in the 160 KiB of LDS next to the G-head score histogram.
-template <int G, int TL>
+// 16 lookups of a row never collide.  For P <= 8 the halves have HE = 16
+// entries (planes 0..3 and 4..P-1) and NF is the largest count whose image
+// fits in the 160 KiB of LDS next to the G-head score histogram; for
+// 8 < P <= 10 (WIDE) a full table would not fit, NF = 0 and the halves have
+// HE = 32 entries (planes 0..4 and 5..P-1).
+template <int G, int TL, bool WIDE>
 struct ImageShape {
+  static constexpr int HE = WIDE ? 32 : 16;
   static constexpr bool fit(int nf) {
-    return 256 * nf * 16 * G + 2 * 16 * (TL - nf) * 16 * G <= 40960 - G * kHistBins;
+    return 256 * nf * 16 * G + 2 * HE * (TL - nf) * 16 * G <= 40960 - G * kHistBins;
   }
   static constexpr int pick() {
+    if (WIDE) return 0;
     int nf = 0;
     for (int c = 0; c <= TL; ++c)
       if (fit(c)) nf = c;
@@ -64,38 +69,62 @@ struct ImageShape {
   static constexpr int NF = pick();
   static constexpr int NS = TL - NF;
   static constexpr int FULL = 256 * NF * 16 * G;   // floats
-  static constexpr int HALF = 2 * 16 * NS * 16 * G;
+  static constexpr int HALF = 2 * HE * NS * 16 * G;
   static constexpr int FLOATS = FULL + HALF;
 };
 
 struct ImageDims {
-  int G, TL, NF, NS, full, floats;
+  int G, TL, NF, NS, HE, full, floats;
 };
 
-static ImageDims image_dims(int G, int L) {
-  const int TL = ids_word_bytes(L);
-  auto make = [](auto g, auto tl) {
-    using S = ImageShape<decltype(g)::value, decltype(tl)::value>;
-    return ImageDims{decltype(g)::value, decltype(tl)::value, S::NF, S::NS, S::FULL, S::FLOATS};
+// Shape of the image for G query heads per KV head, L tables of P planes.
+static ImageDims image_dims(int G, int L, int P) {
+  const int TL = ids_tables_per_word(L);
+  auto make = [](auto g, auto tl, auto wide) {
+    using S = ImageShape<decltype(g)::value, decltype(tl)::value, decltype(wide)::value>;
+    return ImageDims{decltype(g)::value, decltype(tl)::value, S::NF, S::NS, S::HE, S::FULL,
+                     S::FLOATS};
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I8 = std::integral_constant<int, 8>;
-  switch (G * 16 + TL) {
-    case 17: return make(I1{}, I1{});
-    case 18: return make(I1{}, I2{});
-    case 20: return make(I1{}, I4{});
-    case 24: return make(I1{}, I8{});
-    case 33: return make(I2{}, I1{});
-    case 34: return make(I2{}, I2{});
-    case 36: return make(I2{}, I4{});
-    case 40: return make(I2{}, I8{});
-    case 65: return make(I4{}, I1{});
-    case 66: return make(I4{}, I2{});
-    case 68: return make(I4{}, I4{});
-    default: return make(I4{}, I8{});
+  using N = std::false_type;
+  using Y = std::true_type;
+  if (P > 8) {  // L <= 64
+    switch (G * 16 + TL) {
+      case 17: return make(I1{}, I1{}, Y{});
+      case 18: return make(I1{}, I2{}, Y{});
+      case 20: return make(I1{}, I4{}, Y{});
+      case 33: return make(I2{}, I1{}, Y{});
+      case 34: return make(I2{}, I2{}, Y{});
+      case 36: return make(I2{}, I4{}, Y{});
+      case 65: return make(I4{}, I1{}, Y{});
+      case 66: return make(I4{}, I2{}, Y{});
+      default: return make(I4{}, I4{}, Y{});
+    }
   }
+  switch (G * 16 + TL) {
+    case 17: return make(I1{}, I1{}, N{});
+    case 18: return make(I1{}, I2{}, N{});
+    case 20: return make(I1{}, I4{}, N{});
+    case 24: return make(I1{}, I8{}, N{});
+    case 33: return make(I2{}, I1{}, N{});
+    case 34: return make(I2{}, I2{}, N{});
+    case 36: return make(I2{}, I4{}, N{});
+    case 40: return make(I2{}, I8{}, N{});
+    case 65: return make(I4{}, I1{}, N{});
+    case 66: return make(I4{}, I2{}, N{});
+    case 68: return make(I4{}, I4{}, N{});
+    default: return make(I4{}, I8{}, N{});
+  }
+}
+
+// Floats reserved per KV row for its image: enough for either ID width.
+static int image_stride(int G, int L) {
+  const int a = image_dims(G, L, 8).floats;
+  const int b = L <= 64 ? image_dims(G, L, 10).floats : 0;
+  return a > b ? a : b;
 }
 
 // ---------------------------------------------------------------- workspace
@@ -107,10 +136,10 @@ constexpr int kScanKeys = 8192;  // keys per top-k scan workgroup (the bitmap co
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
   const size_t heads = (size_t)B * Hq;
   const int G = Hq / Hkv;
-  const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L);
+  const int img_floats = image_stride(G == 1 || G == 2 ? G : 4, L);
   const int64_t words = (n_cap + kScanKeys - 1) / kScanKeys * (kScanKeys / 32);
   size_t off = 0;
-  const size_t o_img = off; off = align256(off + (size_t)B * Hkv * im.floats * sizeof(float));
+  const size_t o_img = off; off = align256(off + (size_t)B * Hkv * img_floats * sizeof(float));
   const size_t o_hist = off; off = align256(off + heads * kHistBins * sizeof(uint32_t));
   const size_t o_cnt = off; off = align256(off + heads * sizeof(uint32_t));
   const size_t o_bm = off; off = align256(off + heads * words * sizeof(uint32_t));
@@ -119,7 +148,7 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
   if (ws) {
     char* p = static_cast<char*>(base);
     ws->img = reinterpret_cast<float*>(p + o_img);
-    ws->img_floats = im.floats;
+    ws->img_floats = img_floats;
     ws->hist = reinterpret_cast<uint32_t*>(p + o_hist);
     ws->counters = reinterpret_cast<uint32_t*>(p + o_cnt);
     ws->bitmap = reinterpret_cast<uint32_t*>(p + o_bm);
@@ -150,7 +179,7 @@ __device__ __forceinline__ void store_slot(float* dst, const float* v) {
 template <typename T, int G>
 __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
-    int TL, int NF, int NS, int FULL, int img_floats, float* __restrict__ img,
+    int TL, int NF, int NS, int HE, int FULL, int img_floats, float* __restrict__ img,
     uint32_t* __restrict__ hist, uint32_t* __restrict__ counters) {
   const int bh = blockIdx.x >> 4, j = blockIdx.x & 15;
   const int b = bh / Hkv, h = bh % Hkv;
@@ -159,7 +188,7 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   float* im = img + (int64_t)bh * img_floats;
   __shared__ float qf[G][kHead];         // the queries (exact in float32)
   __shared__ double sig[kTabThreads][2];  // [(m*P + plane)*G + g][bit] = sigmoid(+-2u/tau)
-  __shared__ double half[8][G][32];       // [m][g][hf*16 + c]
+  __shared__ double half[8][G][64];       // [m][g][hf*HE + c]
 
   constexpr int kHistShare = G * kHistBins / 16;
   for (int i = tid; i < kHistShare; i += kTabThreads)
@@ -227,10 +256,12 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     }
   }
   __syncthreads();
-  const int plo = P < 4 ? P : 4;
+  // halves: planes 0 .. plo-1 and plo .. P-1, HE entries each
+  const int plo = HE == 32 ? 5 : (P < 4 ? P : 4);
   const int phi = P - plo;
-  for (int i = tid; i < TL * G * 32; i += kTabThreads) {
-    const int mm = i / (G * 32), gg = (i / 32) % G, r = i & 31, hf = r >> 4, c = r & 15;
+  for (int i = tid; i < TL * G * 2 * HE; i += kTabThreads) {
+    const int mm = i / (G * 2 * HE), gg = (i / (2 * HE)) % G, r = i % (2 * HE);
+    const int hf = r / HE, c = r % HE;
     const int nb = hf ? phi : plo;
     double prod = 0.0;
     if (c < (1 << nb) && j * TL + mm < L) {
@@ -249,11 +280,11 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     float v[G];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg)
-      v[gg] = (float)(half[mm][gg][e & lomask] * half[mm][gg][16 + (e >> plo)]);
+      v[gg] = (float)(half[mm][gg][e & lomask] * half[mm][gg][HE + (e >> plo)]);
     store_slot<G>(im + ((int64_t)i * 16 + j) * G, v);
   }
-  // factored tables: slot FULL/G + ((hc*NS + m - NF)*16 + j), hc = hf*16 + c
-  for (int i = tid; i < 32 * NS; i += kTabThreads) {
+  // factored tables: slot FULL/G + ((hc*NS + m - NF)*16 + j), hc = hf*HE + c
+  for (int i = tid; i < 2 * HE * NS; i += kTabThreads) {
     const int hc = i / NS, mm = NF + i % NS;
     float v[G];
 #pragma unroll
@@ -286,24 +317,26 @@ constexpr int kScoreWaves = kScoreThreads / 64;
 // the value lane j - d holds for the same key (its slot x + d); row_ror:d
 // gives lane j the register of lane (j - d) mod 16.
 
-// The TL-byte ID word of round x from the lane's TL 16-byte vectors.
-template <int TL>
-__device__ __forceinline__ uint2 round_word(const uint4 (&v)[TL], int x) {
-  constexpr int R = 16 / TL;
+// The WB-byte ID word of round x from the lane's WB 16-byte vectors.
+template <int WB>
+__device__ __forceinline__ uint2 round_word(const uint4 (&v)[WB], int x) {
+  constexpr int R = 16 / WB;
   const uint4 q = v[x / R];
   const int k = x % R;  // word index inside the vector
-  if constexpr (TL == 8) {
+  if constexpr (WB == 8) {
     return k == 0 ? make_uint2(q.x, q.y) : make_uint2(q.z, q.w);
   } else {
-    const int byte = k * TL;
+    const int byte = k * WB;
     const uint32_t d = byte < 4 ? q.x : byte < 8 ? q.y : byte < 12 ? q.z : q.w;
-    return make_uint2(TL == 4 ? d : (d >> (8 * (byte & 3))) & (TL == 2 ? 0xFFFFu : 0xFFu), 0u);
+    return make_uint2(WB == 4 ? d : (d >> (8 * (byte & 3))) & (WB == 2 ? 0xFFFFu : 0xFFu), 0u);
   }
 }
 
-template <int K>
-__device__ __forceinline__ uint32_t word_byte(uint2 w) {
-  return ((K < 4 ? w.x : w.y) >> (8 * (K & 3))) & 255u;
+// Cell M of a word of C-byte cells.
+template <int C, int M>
+__device__ __forceinline__ uint32_t word_cell(uint2 w) {
+  if constexpr (C == 1) return ((M < 4 ? w.x : w.y) >> (8 * (M & 3))) & 255u;
+  else return ((M < 2 ? w.x : w.y) >> (16 * (M & 1))) & 0xFFFFu;
 }
 
 constexpr int kXcds = 8;      // workgroup i of a dispatch runs on XCD i mod 8
@@ -317,34 +350,23 @@ struct RoundVals {
   float hi[NS > 0 ? NS : 1][G];
 };
 
-template <int M>
-__device__ __forceinline__ uint32_t id_byte(uint2 w) {
-  if constexpr (M == 0) return word_byte<0>(w);
-  else if constexpr (M == 1) return word_byte<1>(w);
-  else if constexpr (M == 2) return word_byte<2>(w);
-  else if constexpr (M == 3) return word_byte<3>(w);
-  else if constexpr (M == 4) return word_byte<4>(w);
-  else if constexpr (M == 5) return word_byte<5>(w);
-  else if constexpr (M == 6) return word_byte<6>(w);
-  else return word_byte<7>(w);
-}
-
 template <int NF, int NS, int G, int M = 0>
 __device__ __forceinline__ void issue_full(const float* lds, uint2 w, int j, RoundVals<NF, NS, G>& r) {
   if constexpr (M < NF) {
-    lds_get<G>(lds, ((int)id_byte<M>(w) * NF + M) * 16 + j, r.f[M]);
+    lds_get<G>(lds, ((int)word_cell<1, M>(w) * NF + M) * 16 + j, r.f[M]);
     issue_full<NF, NS, G, M + 1>(lds, w, j, r);
   }
 }
 
-template <int NF, int NS, int G, int M = 0>
+// Half-table lookups of tables NF .. NF+NS-1 (C-byte cells, HE-entry halves).
+template <int NF, int NS, int G, int C, int HE, int M = 0>
 __device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, uint32_t lomask, int plo,
                                            RoundVals<NF, NS, G>& r) {
   if constexpr (M < NS) {
-    const uint32_t e = id_byte<NF + M>(w);
+    const uint32_t e = word_cell<C, NF + M>(w);
     lds_get<G>(lds, ((int)(e & lomask) * NS + M) * 16 + j, r.lo[M]);
-    lds_get<G>(lds, ((16 + (int)(e >> plo)) * NS + M) * 16 + j, r.hi[M]);
-    issue_half<NF, NS, G, M + 1>(lds, w, j, lomask, plo, r);
+    lds_get<G>(lds, ((HE + (int)(e >> plo)) * NS + M) * 16 + j, r.hi[M]);
+    issue_half<NF, NS, G, C, HE, M + 1>(lds, w, j, lomask, plo, r);
   }
 }
 
@@ -366,22 +388,22 @@ __device__ __forceinline__ void round_sum(const RoundVals<NF, NS, G>& r, float (
 // x + 1 are issued before round x is summed.  The first reduce-scatter stage
 // (row_ror 8) is applied as soon as round x + 8 is summed, so only 8 rounds of
 // partial sums stay live.  On exit u[0] of lane j holds the sums of its key.
-template <int NF, int NS, int G, int TL>
-__device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[TL], int j,
+template <int NF, int NS, int G, int C, int HE, int WB>
+__device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[WB], int j,
                                             uint32_t lomask, int plo, float (&u)[8][G]) {
   constexpr int FULL = 256 * NF * 16 * G;
   RoundVals<NF, NS, G> cur, nxt;
   {
-    const uint2 w = round_word<TL>(ids, 0);
+    const uint2 w = round_word<WB>(ids, 0);
     issue_full<NF, NS, G>(lds, w, j, cur);
-    issue_half<NF, NS, G>(lds + FULL, w, j, lomask, plo, cur);
+    issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, lomask, plo, cur);
   }
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     if (x < 15) {
-      const uint2 w = round_word<TL>(ids, x + 1);
+      const uint2 w = round_word<WB>(ids, x + 1);
       issue_full<NF, NS, G>(lds, w, j, nxt);
-      issue_half<NF, NS, G>(lds + FULL, w, j, lomask, plo, nxt);
+      issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, lomask, plo, nxt);
     }
     float acc[G];
     round_sum<NF, NS, G>(cur, acc);
@@ -415,14 +437,16 @@ __device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)
 // by compile-time constants so no copy waits on a load).  Each score also
 // goes into an LDS histogram of its top digit, merged into the head's global
 // histogram at the end.
-template <int G, int TL>
+template <int G, int TL, bool WIDE>
 __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
-    const float* __restrict__ img, const uint8_t* __restrict__ ids,
+    const float* __restrict__ img, int img_floats, const uint8_t* __restrict__ ids,
     const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
     int64_t n_cap, int rows, int nblk, int gpb, float* __restrict__ scores,
     uint32_t* __restrict__ hist) {
-  using Sh = ImageShape<G, TL>;
-  constexpr int NF = Sh::NF, NS = Sh::NS;
+  using Sh = ImageShape<G, TL, WIDE>;
+  constexpr int NF = Sh::NF, NS = Sh::NS, HE = Sh::HE;
+  constexpr int C = WIDE ? 2 : 1;  // bytes per ID
+  constexpr int WB = TL * C;       // bytes per ID word
   constexpr int D = kPrefetch;
   __shared__ __attribute__((aligned(16))) float lds[Sh::FLOATS];
   __shared__ uint32_t lhist[G * kHistBins];
@@ -442,24 +466,24 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bg0 = b * Hq + h * G;
   const int64_t sst = score_stride(n_cap);
-  const int plo = P < 4 ? P : 4;
+  const int plo = WIDE ? 5 : (P < 4 ? P : 4);
   const uint32_t lomask = (1u << plo) - 1u;
 
   // The first D groups' IDs and norms, then the table image.  Group loads
   // are issued unconditionally (a group past the block's range re-reads its
   // last group, keys past n_cap re-read the last norm) so that no branch sits
   // between a load and its use and each wait covers only the group needed.
-  const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * TL;
+  const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * WB;
   const float* vrow = vnorm + (int64_t)bh * n_cap;
-  auto load_group = [&](int64_t gi, uint4 (&v)[TL], float& vn) {
+  auto load_group = [&](int64_t gi, uint4 (&v)[WB], float& vn) {
     const int64_t gl = gi < g_end ? gi : g_end - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * TL) + lane;
+    const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * WB) + lane;
 #pragma unroll
-    for (int qv = 0; qv < TL; ++qv) v[qv] = src[qv * 64];
+    for (int qv = 0; qv < WB; ++qv) v[qv] = src[qv * 64];
     const int64_t key = gl * 64 + lane;
     vn = vrow[key < n_cap ? key : n_cap - 1];
   };
-  uint4 buf[D + 1][TL];
+  uint4 buf[D + 1][WB];
   float vb[D + 1];
   int64_t gi = g_begin + wave;
 #pragma unroll
@@ -467,7 +491,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   {
     // The image goes straight from global memory into LDS (16 bytes per lane,
     // no registers), every load of the block in flight at once.
-    const uint4* src = reinterpret_cast<const uint4*>(img + (int64_t)bh * Sh::FLOATS);
+    const uint4* src = reinterpret_cast<const uint4*>(img + (int64_t)bh * img_floats);
     uint4* dst = reinterpret_cast<uint4*>(lds);
     constexpr int NV = Sh::FLOATS / 4;
     constexpr int PER = (NV + kScoreThreads - 1) / kScoreThreads;
@@ -489,7 +513,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
       if (more) {
         load_group(gi + (int64_t)D * kScoreWaves, buf[(s + D) % (D + 1)], vb[(s + D) % (D + 1)]);
         float u[8][G];
-        score_group<NF, NS, G, TL>(lds, buf[s], j, lomask, plo, u);
+        score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, lomask, plo, u);
         const int64_t key = gi * 64 + lane;
         const bool valid = key < n;
 #pragma unroll
@@ -907,7 +931,7 @@ static int device_cus() {
   return cus;
 }
 
-template <int G, int TL>
+template <int G, int TL, bool WIDE>
 static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, const ScoreWs& ws,
                           const uint8_t* ids, const float* vnorm, const int32_t* lens,
                           float* scores, hipStream_t s) {
@@ -919,8 +943,8 @@ static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, const Sc
   const int64_t gpb = (ng + nblk - 1) / nblk;
   nblk = (ng + gpb - 1) / gpb;
   const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
-  scorer_kernel<G, TL><<<(unsigned)grid, kScoreThreads, 0, s>>>(
-      ws.img, ids, vnorm, lens, Hq, Hkv, P, n_cap, (int)rows, (int)nblk, (int)gpb, scores,
+  scorer_kernel<G, TL, WIDE><<<(unsigned)grid, kScoreThreads, 0, s>>>(
+      ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, P, n_cap, (int)rows, (int)nblk, (int)gpb, scores,
       ws.hist);
 }
 
@@ -928,25 +952,33 @@ template <int G>
 static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap,
                             const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
                             const int32_t* lens, float* scores, hipStream_t s) {
-  switch (ids_word_bytes(L)) {
-    case 1: launch_scorer<G, 1>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer<G, 2>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    case 4: launch_scorer<G, 4>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer<G, 8>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+  if (P > 8) {  // two-byte IDs, L <= 64
+    switch (ids_tables_per_word(L)) {
+      case 1: launch_scorer<G, 1, true>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+      case 2: launch_scorer<G, 2, true>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+      default: launch_scorer<G, 4, true>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    }
+    return;
+  }
+  switch (ids_tables_per_word(L)) {
+    case 1: launch_scorer<G, 1, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer<G, 2, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    case 4: launch_scorer<G, 4, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer<G, 8, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
   }
 }
 
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
                               int L, int P, float tau, const ScoreWs& ws, hipStream_t s) {
   const int G = Hq / Hkv;
-  const ImageDims im = image_dims(G, L);
+  const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L, P);
   const unsigned grid = (unsigned)(B * Hkv * 16);
   auto go = [&](auto tag, auto gtag) {
     using T = decltype(tag);
     constexpr int GG = decltype(gtag)::value;
     soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
         static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
-        im.NS, im.full, im.floats, ws.img, ws.hist, ws.counters);
+        im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;

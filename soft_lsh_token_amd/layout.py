@@ -1,63 +1,78 @@
 """Host-side view of the bucket-ID cache layout (include/socket_lsh.h).
 
 The HIP library stores the bucket IDs tiled in groups of 64 keys, each key's
-IDs cut into 16 words of TL bytes, in a diagonal order (see the header).
-These helpers convert between that layout and a plain [B, Hkv, n, L] uint8
-array.  They are index permutations only (for inspection, tests, and
-loading IDs computed elsewhere); nothing of the method is computed here.
+IDs cut into 16 words of TL tables (cells of one byte for P <= 8, two
+little-endian bytes for P = 9 or 10), in a diagonal order (see the header).
+These helpers convert between that layout and a plain [B, Hkv, n, L] array
+(uint8 for one-byte cells, uint16 for two-byte cells).  They are index
+permutations only (for inspection, tests, and loading IDs computed
+elsewhere); nothing of the method is computed here.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def word_bytes(L: int) -> int:
+def tables_per_word(L: int) -> int:
     return 1 if L <= 16 else 2 if L <= 32 else 4 if L <= 64 else 8
 
 
-def key_bytes(L: int) -> int:
-    return 16 * word_bytes(L)
+def cell_bytes(P: int) -> int:
+    return 2 if P > 8 else 1
+
+
+def word_bytes(L: int, P: int = 8) -> int:
+    return tables_per_word(L) * cell_bytes(P)
+
+
+def key_bytes(L: int, P: int = 8) -> int:
+    return 16 * word_bytes(L, P)
 
 
 def groups(n_cap: int) -> int:
     return (n_cap + 63) // 64
 
 
-def ids_shape(B: int, Hkv: int, n_cap: int, L: int) -> tuple:
+def ids_shape(B: int, Hkv: int, n_cap: int, L: int, P: int = 8) -> tuple:
     """Shape of the cache as a uint8 tensor: [B, Hkv, groups, 64 * key_bytes]."""
-    return (B, Hkv, groups(n_cap), 64 * key_bytes(L))
+    return (B, Hkv, groups(n_cap), 64 * key_bytes(L, P))
 
 
-def _perm(L: int):
-    """Byte position inside a 64-key group of (key t, word w, byte b)."""
-    TL = word_bytes(L)
+def _perm(L: int, P: int):
+    """Byte position inside a 64-key group of (key t, word w, byte b of the word)."""
+    WB = word_bytes(L, P)
     t = np.arange(64)[:, None, None]
     w = np.arange(16)[None, :, None]
-    b = np.arange(TL)[None, None, :]
+    b = np.arange(WB)[None, None, :]
     kg, x = t // 16, t % 16
-    R = 16 // TL
+    R = 16 // WB
     r = (x - w) % 16
     slot = (r // R) * 64 * R + (16 * kg + w) * R + r % R
-    return slot * TL + b          # [64, 16, TL]
+    return slot * WB + b          # [64, 16, WB]
 
 
-def unpack(tiled: np.ndarray, L: int, n: int | None = None) -> np.ndarray:
+def _cell_dtype(P: int):
+    return np.dtype("<u2") if cell_bytes(P) == 2 else np.dtype(np.uint8)
+
+
+def unpack(tiled: np.ndarray, L: int, n: int | None = None, P: int = 8) -> np.ndarray:
     """[B, Hkv, G, 64*key_bytes] tiled cache -> [B, Hkv, n, L] bucket IDs."""
     B, Hkv, G, gb = tiled.shape
-    pos = _perm(L).reshape(64, -1)                           # [64, 16*TL]
-    keys = tiled[:, :, :, pos]                               # [B, Hkv, G, 64, 16*TL]
-    keys = keys.reshape(B, Hkv, G * 64, -1)[..., :L]
+    pos = _perm(L, P).reshape(64, -1)                        # [64, 16*WB]
+    keys = np.ascontiguousarray(tiled[:, :, :, pos])         # [B, Hkv, G, 64, 16*WB]
+    keys = keys.view(_cell_dtype(P)).reshape(B, Hkv, G * 64, -1)[..., :L]
+    keys = keys.astype(np.uint16 if cell_bytes(P) == 2 else np.uint8)
     return keys if n is None else keys[:, :, :n]
 
 
-def pack(ids: np.ndarray, n_cap: int | None = None) -> np.ndarray:
+def pack(ids: np.ndarray, n_cap: int | None = None, P: int = 8) -> np.ndarray:
     """[B, Hkv, n, L] bucket IDs -> tiled cache (keys past n and tables past L are 0)."""
     B, Hkv, n, L = ids.shape
     n_cap = n if n_cap is None else n_cap
-    G, TL = groups(n_cap), word_bytes(L)
-    full = np.zeros((B, Hkv, G * 64, 16 * TL), dtype=np.uint8)
-    full[:, :, :n, :L] = ids
-    out = np.zeros((B, Hkv, G, 64 * 16 * TL), dtype=np.uint8)
-    pos = _perm(L).reshape(64, -1)
-    out[:, :, :, pos] = full.reshape(B, Hkv, G, 64, 16 * TL)
+    G, TL, WB = groups(n_cap), tables_per_word(L), word_bytes(L, P)
+    cells = np.zeros((B, Hkv, G * 64, 16 * TL), dtype=_cell_dtype(P))
+    cells[:, :, :n, :L] = ids
+    full = cells.view(np.uint8).reshape(B, Hkv, G, 64, 16 * WB)
+    out = np.zeros((B, Hkv, G, 64 * 16 * WB), dtype=np.uint8)
+    out[:, :, :, _perm(L, P).reshape(64, -1)] = full
     return out

@@ -44,7 +44,7 @@ def upload(w):
 def gpu_hash(w, d, pos0=None, count=None, ids=None, vnorm=None):
     B, Hkv, n_cap = w.B, w.Hkv, w.n_cap
     if ids is None:
-        ids = S.alloc_ids(B, Hkv, n_cap, w.L, DEV)
+        ids = S.alloc_ids(B, Hkv, n_cap, w.L, w.P, DEV)
     if vnorm is None:
         vnorm = torch.zeros(B, Hkv, n_cap, dtype=torch.float32, device=DEV)
     if pos0 is None:
@@ -73,15 +73,16 @@ def gpu_decode(w, d, idx, q=None):
     return out
 
 
-def ids_np(ids_dev, L, n=None):
+def ids_np(ids_dev, L, n=None, P=8):
     """Tiled device cache -> [B, Hkv, n, L] numpy bucket IDs."""
-    return layout.unpack(ids_dev.cpu().numpy(), L, n)
+    return layout.unpack(ids_dev.cpu().numpy(), L, n, P)
 
 
-def ids_dev(ids_plain, n_cap):
+def ids_dev(ids_plain, n_cap, P=8):
     """[B, Hkv, n, L] numpy bucket IDs -> tiled device cache."""
-    return torch.from_numpy(layout.pack(np.ascontiguousarray(ids_plain, dtype=np.uint8),
-                                        n_cap)).to(DEV)
+    dt = np.uint16 if P > 8 else np.uint8
+    return torch.from_numpy(layout.pack(np.ascontiguousarray(ids_plain, dtype=dt),
+                                        n_cap, P)).to(DEV)
 
 
 def check_ids(ids_gpu, K, W, L, P, n, detail=False):

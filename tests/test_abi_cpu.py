@@ -42,6 +42,10 @@ def test_workspace_sizes():
     assert S.socket_score_topk_workspace(0, 32, 8, 32768, 64, 8, 656) == 0
     assert S.socket_score_topk_workspace(1, 32, 4, 32768, 64, 8, 656) == 0  # 8 heads per KV head
     assert S.socket_score_topk_workspace(1, 32, 8, 32768, 129, 8, 656) == 0
+    assert S.socket_score_topk_workspace(1, 32, 8, 32768, 65, 10, 656) == 0
+    # one workspace size for both ID widths (the stage entries take no P)
+    assert S.socket_score_topk_workspace(1, 32, 8, 32768, 60, 10, 656) == \
+        S.socket_score_topk_workspace(1, 32, 8, 32768, 60, 8, 656)
     assert S.socket_sparse_decode_workspace(1, 32, 128, 1024) > 0
     assert S.socket_sparse_decode_workspace(1, 32, 64, 1024) == 0
 
@@ -60,7 +64,8 @@ def test_hash_argument_checks():
     assert _hash(B=0) == EINVAL
     assert _hash(count=-1) == EINVAL
     assert _hash(d=64) == EUNSUP
-    assert _hash(P=9) == EUNSUP
+    assert _hash(P=11) == EUNSUP
+    assert _hash(P=10, L=65) == EUNSUP    # two-byte IDs: at most 64 tables
     assert _hash(L=300) == EUNSUP
     assert _hash(count=0) == 0  # nothing to do, nothing enqueued
 
@@ -83,7 +88,8 @@ def test_score_argument_checks():
     assert _score(tau=float("inf")) == EINVAL
     assert _score(Hkv=5) == EINVAL        # 32 % 5
     assert _score(Hkv=4) == EUNSUP        # 8 query heads per KV head
-    assert _score(P=9) == EUNSUP
+    assert _score(P=11) == EUNSUP
+    assert _score(P=9, L=65) == EUNSUP
     assert _score(d=96) == EUNSUP
     assert _score(k_max=0) == EINVAL
     assert _score(ws=FAKE + 8) == EINVAL  # misaligned workspace
@@ -136,27 +142,43 @@ def test_stage_argument_checks():
     assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 32, FAKE, FAKE, 16, None) == ENOSPC
 
 
-@pytest.mark.parametrize("L", [3, 16, 20, 32, 60, 64, 100, 128])
-def test_ids_layout_roundtrip_and_formula(L):
-    """pack/unpack invert each other and place bytes where the header's formula says."""
+@pytest.mark.parametrize("L,P", [(3, 8), (16, 8), (20, 8), (32, 8), (60, 8), (64, 8), (100, 8),
+                                 (128, 8), (5, 10), (16, 9), (20, 10), (60, 10), (64, 10)])
+def test_ids_layout_roundtrip_and_formula(L, P):
+    """pack/unpack invert each other and place each ID's bytes where the header's formula says."""
     import numpy as np
     from soft_lsh_token_amd import layout
-    rng = np.random.default_rng(L)
+    rng = np.random.default_rng(L * 16 + P)
     B, Hkv, n, n_cap = 2, 3, 150, 200
-    ids = rng.integers(0, 256, size=(B, Hkv, n, L), dtype=np.uint8)
-    tiled = layout.pack(ids, n_cap)
-    assert tiled.shape == layout.ids_shape(B, Hkv, n_cap, L)
-    assert tiled.size == S.socket_ids_bytes(B, Hkv, n_cap, L)
-    np.testing.assert_array_equal(layout.unpack(tiled, L, n), ids)
-    TL = layout.word_bytes(L)
+    C = 2 if P > 8 else 1
+    ids = rng.integers(0, 1 << P, size=(B, Hkv, n, L)).astype(np.uint16 if C == 2 else np.uint8)
+    tiled = layout.pack(ids, n_cap, P)
+    assert tiled.dtype == np.uint8
+    assert tiled.shape == layout.ids_shape(B, Hkv, n_cap, L, P)
+    assert tiled.size == S.socket_ids_bytes(B, Hkv, n_cap, L, P)
+    np.testing.assert_array_equal(layout.unpack(tiled, L, n, P), ids)
+    TL = layout.tables_per_word(L)
     assert 16 * TL >= L and (TL == 1 or 8 * TL < L)
+    WB = TL * C
+    assert layout.word_bytes(L, P) == WB
     flat = tiled.reshape(-1)
     G = (n_cap + 63) // 64
     for (b, h, i, l) in [(0, 0, 0, 0), (1, 2, 149, L - 1), (0, 1, 77, L // 2), (1, 0, 64, 0)]:
-        r, w, byte = b * Hkv + h, l // TL, l % TL
+        r, w, cell = b * Hkv + h, l // TL, l % TL
         t = i % 64
         kg, x = t // 16, t % 16
-        u, R = (x - w) % 16, 16 // TL
-        off = ((r * G + i // 64) * 1024 + (u // R) * 64 * R + (16 * kg + w) * R + u % R) * TL + byte
-        assert flat[off] == ids[b, h, i, l]
-    assert S.socket_ids_bytes(1, 1, 10, 129) == 0
+        u, R = (x - w) % 16, 16 // WB
+        off = ((r * G + i // 64) * 1024 + (u // R) * 64 * R + (16 * kg + w) * R + u % R) * WB
+        off += cell * C
+        value = int(flat[off]) | (int(flat[off + 1]) << 8 if C == 2 else 0)
+        assert value == ids[b, h, i, l]
+
+
+def test_ids_bytes_limits():
+    """Table shapes without an ID layout are refused (size 0)."""
+    assert S.socket_ids_bytes(1, 1, 10, 129, 8) == 0
+    assert S.socket_ids_bytes(1, 1, 10, 65, 10) == 0
+    assert S.socket_ids_bytes(1, 1, 10, 64, 11) == 0
+    assert S.socket_ids_bytes(1, 1, 10, 64, 10) == 64 * 16 * 8
+    assert S.socket_ids_bytes(1, 1, 10, 60, 9) == 64 * 16 * 8
+    assert S.socket_ids_bytes(1, 1, 10, 128, 8) == 64 * 16 * 8

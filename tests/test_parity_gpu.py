@@ -40,6 +40,9 @@ def sync():
     dict(name="c2", n=500, L=7, P=5, Hkv=2, Hq=4),     # odd shapes: generic path
     dict(name="c2", n=300, L=3, P=8, Hkv=2, Hq=2),
     dict(name="c4", n=(300, 900), B=3, Hkv=2, Hq=8),   # batch with different lengths
+    dict(name="c2", n=1000, L=60, P=10),               # two-byte IDs, 4 tables per word
+    dict(name="c2", n=500, L=20, P=10, Hkv=2, Hq=4),   # two tables per word
+    dict(name="c2", n=300, L=5, P=9, Hkv=2, Hq=2),     # one table per word
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_hash_parity(case):
     print("case", case, flush=True)
@@ -47,7 +50,7 @@ def test_hash_parity(case):
     d = GC.upload(w)
     ids, vn = GC.gpu_hash(w, d)
     sync()
-    ids, vn = GC.ids_np(ids, w.L), vn.cpu().numpy()
+    ids, vn = GC.ids_np(ids, w.L, P=w.P), vn.cpu().numpy()
     n_cap = w.n_cap
     for b in range(w.B):
         for h in range(w.Hkv):
@@ -61,7 +64,7 @@ def test_hash_full_c2_mfma():
     d = GC.upload(w)
     ids, vn = GC.gpu_hash(w, d)
     sync()
-    ids, vn = GC.ids_np(ids, w.L), vn.cpu().numpy()
+    ids, vn = GC.ids_np(ids, w.L, P=w.P), vn.cpu().numpy()
     band = 0
     for h in range(w.Hkv):
         band += GC.check_ids(ids[0, h], w.K[0, h], w.W, w.L, w.P, w.n_cap)
@@ -69,16 +72,18 @@ def test_hash_full_c2_mfma():
     print("id bits inside the 1e-5 band:", band)
 
 
-def test_hash_append_rows_only():
+@pytest.mark.parametrize("L,P", [(64, 8), (60, 10)])
+def test_hash_append_rows_only(L, P):
     """count=1 at pos0=lens hashes exactly one new row per (sequence, head)."""
-    w = make_workload("c4", n=(200, 600), B=2, Hkv=2, Hq=8)
+    w = make_workload("c4", n=(200, 600), B=2, Hkv=2, Hq=8, L=L, P=P)
     d = GC.upload(w)
-    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, DEV).fill_(0xAB)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV).fill_(0xAB)
+    fill = 0xABAB if P > 8 else 0xAB
     vn = torch.full((w.B, w.Hkv, w.n_cap), -1.0, dtype=torch.float32, device=DEV)
     pos0 = d["lens"].clone()
     GC.gpu_hash(w, d, pos0=pos0, count=1, ids=ids, vnorm=vn)
     sync()
-    ids, vn = GC.ids_np(ids, w.L, w.n_cap), vn.cpu().numpy()
+    ids, vn = GC.ids_np(ids, w.L, w.n_cap, w.P), vn.cpu().numpy()
     for b in range(w.B):
         p = int(w.lens[b])
         for h in range(w.Hkv):
@@ -87,7 +92,7 @@ def test_hash_append_rows_only():
                 np.testing.assert_allclose(vn[b, h, p], SO.value_norms(w.V[b, h, p]), rtol=2e-6)
             mask = np.ones(w.n_cap, bool)
             mask[p:p + 1] = False
-            assert (ids[b, h, mask] == 0xAB).all()
+            assert (ids[b, h, mask] == fill).all()
             assert (vn[b, h, mask] == -1.0).all()
 
 
@@ -103,15 +108,21 @@ SCORE_CASES = [
     dict(name="c2", n=2000, L=20, P=5, Hq=8, Hkv=2),
     dict(name="c2", n=2000, tau=0.3),
     dict(name="c4", n=(1000, 9000), B=4, k=0.02),  # ragged batch
+    # two-byte IDs (P = 9, 10): every table kept as two 32-entry halves
+    dict(name="c2", n=5000, L=60, P=10),
+    dict(name="c2", n=3000, L=60, P=10, Hq=8, Hkv=8),
+    dict(name="c2", n=3000, L=64, P=10, Hq=16, Hkv=8),
+    dict(name="c2", n=2000, L=9, P=9, Hq=8, Hkv=2),
+    dict(name="c2", n=2000, L=30, P=10, Hq=8, Hkv=2, tau=0.3),
 ]
 
 
 def _oracle_ids(w):
-    ids = np.empty((w.B, w.Hkv, w.n_cap, w.L), np.uint8)
+    ids = np.empty((w.B, w.Hkv, w.n_cap, w.L), np.uint16 if w.P > 8 else np.uint8)
     vn = np.empty((w.B, w.Hkv, w.n_cap), np.float32)
     for b in range(w.B):
         for h in range(w.Hkv):
-            ids[b, h] = SO.hash_keys(w.K[b, h], w.W, w.L, w.P)[0].astype(np.uint8)
+            ids[b, h] = SO.hash_keys(w.K[b, h], w.W, w.L, w.P)[0]
             vn[b, h] = SO.value_norms(w.V[b, h]).astype(np.float32)
     return ids, vn
 
@@ -123,7 +134,7 @@ def test_score_topk_parity(case):
     w = make_workload(**case)
     d = GC.upload(w)
     ids_np, vn_np = _oracle_ids(w)
-    ids = GC.ids_dev(ids_np, w.n_cap)
+    ids = GC.ids_dev(ids_np, w.n_cap, w.P)
     vn = torch.from_numpy(vn_np).to(DEV)
     idx, sc = GC.gpu_score_topk(w, d, ids, vn)
     sync()
@@ -142,7 +153,7 @@ def test_topk_ties_lower_index_wins():
     """All keys of a head share one bucket pattern and norm -> equal scores."""
     w = make_workload("c2", n=3000, Hq=8, Hkv=2, k=100)
     d = GC.upload(w)
-    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, DEV)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
     vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
     # KV head 1: second half of the keys gets a larger norm -> they win, ties among them
     vn[:, 1, 1500:] = 2.0
@@ -160,7 +171,7 @@ def test_topk_edge_lengths():
     w = make_workload("c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 777, 300], n_cap=1000, k=5)
     d = GC.upload(w)
     ids_np, vn_np = _oracle_ids(w)
-    ids = GC.ids_dev(ids_np, w.n_cap)
+    ids = GC.ids_dev(ids_np, w.n_cap, w.P)
     vn = torch.from_numpy(vn_np).to(DEV)
     ks = torch.tensor([5, 5, 777, 999], dtype=torch.int32, device=DEV)
     k_max = 1000
@@ -207,7 +218,7 @@ def _e2e(w, heads=None):
     idx, sc = GC.gpu_score_topk(w, d, ids, vn)
     out = GC.gpu_decode(w, d, idx)
     sync()
-    ids = GC.ids_np(ids, w.L, w.n_cap)
+    ids = GC.ids_np(ids, w.L, w.n_cap, w.P)
     vn, idx, sc, out = (t.cpu().numpy() for t in (vn, idx, sc, out))
     group = w.Hq // w.Hkv
     tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
@@ -243,6 +254,11 @@ def test_e2e_c2_full():
     _e2e(workload("c2"))
 
 
+def test_e2e_c2_p10_l60_full():
+    """The 32K GQA step at 10 planes x 60 tables (600 bits per key)."""
+    _e2e(workload("c2", L=60, P=10))
+
+
 def test_e2e_c3_full_sampled_heads():
     _e2e(workload("c3"), heads=[0, 5, 14, 22, 31])
 
@@ -273,7 +289,7 @@ def test_decode_loop_c5():
         if t in check_steps:
             keep[t] = [x.cpu().numpy() for x in (idx, sc, out)]
     sync()
-    ids_np, vn_np = GC.ids_np(ids, w.L, w.n_cap), vn.cpu().numpy()
+    ids_np, vn_np = GC.ids_np(ids, w.L, w.n_cap, w.P), vn.cpu().numpy()
     group = w.Hq // w.Hkv
     for h in sorted({g // group for g in heads}):
         n_all = n0 + w.steps
