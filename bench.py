@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=40)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-128k", action="store_true")
+    p.add_argument("--no-p10", action="store_true",
+                   help="skip the 10-plane, 60-table measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -68,10 +70,10 @@ def parse():
 class Case:
     """Device buffers and pre-marshalled C calls of one decode workload."""
 
-    def __init__(self, name, replicas, lib, torch, S):
+    def __init__(self, name, replicas, lib, torch, S, **over):
         from soft_lsh_token_amd.inputs import make_workload
         t0 = time.time()
-        self.w = w = make_workload(name, steps=1)   # one extra row: the appended key
+        self.w = w = make_workload(name, steps=1, **over)   # one extra row: the appended key
         log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s (n={int(w.lens[0])}, "
             f"n_cap={w.n_cap}, replicas={replicas})")
         dev = "cuda:0"
@@ -262,12 +264,22 @@ def prefill_rate(case, torch, reps=5):
 
 
 def scorer_bytes(case):
-    """Algorithmic bytes of one scorer launch: per KV key its L one-byte IDs and
-    its float32 norm are read and G float32 scores are written."""
+    """Algorithmic bytes of one scorer launch: per KV key its L P-bit IDs (bit
+    packed) and its float32 norm are read and G float32 scores are written."""
     w = case.w
     G = w.Hq // w.Hkv
     kv_keys = w.B * w.Hkv * (case.n + 1)
-    return kv_keys * (w.L * w.P // 8 + 4 + 4 * G), kv_keys
+    return kv_keys * ((w.L * w.P + 7) // 8 + 4 + 4 * G), kv_keys
+
+
+def scorer_stored_bytes(case):
+    """Bytes one scorer launch moves in the cache's own layout (cells of one or
+    two bytes, tables padded to 16 words per key)."""
+    from soft_lsh_token_amd import layout
+    w = case.w
+    G = w.Hq // w.Hkv
+    kv_keys = w.B * w.Hkv * (case.n + 1)
+    return kv_keys * (layout.key_bytes(w.L, w.P) + 4 + 4 * G)
 
 
 def counters_traffic(launch_bytes):
@@ -395,6 +407,28 @@ def main():
         del c3
         torch.cuda.empty_cache()
 
+    extra_p10 = None
+    if not args.no_p10:
+        c10 = Case("c2", max(8, args.replicas // 2), lib, torch, S, L=60, P=10)
+        for r in range(c10.replicas):
+            c10.prefill(r)
+        torch.cuda.synchronize()
+        pre10 = prefill_rate(c10, torch)
+        sec10 = timed_steps(c10, torch, max(50, args.steps // 2), max(5, args.warmup // 2))
+        st10, gpu10, _ = per_stage(c10, torch, max(50, args.steps // 2))
+        sc10 = scorer_launch_us(c10, torch, 4 * c10.replicas)
+        lb10, _ = scorer_bytes(c10)
+        extra_p10 = dict(step_us_wall=sec10 * 1e6, step_us_gpu=gpu10, stage_us=st10,
+                         scorer_launch_us=sc10,
+                         keys_per_s=c10.w.B * c10.w.Hq * (c10.n + 1) / sec10,
+                         scorer_gbs_algorithmic=lb10 / (sc10 * 1e-6) / 1e9,
+                         scorer_gbs_stored=scorer_stored_bytes(c10) / (sc10 * 1e-6) / 1e9,
+                         prefill=pre10)
+        log(f"[bench] 32K at P=10, L=60: {extra_p10}")
+        c10.free()
+        del c10
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -422,7 +456,7 @@ def main():
                      "kernel": "scorer_kernel (soft-count scores + first-digit histogram)",
                      "bytes_per_launch": launch_bytes, "kv_keys_per_launch": kv_keys},
         "cpu_baseline": cpu,
-        "extra": {"ctx32k": extra32, "ctx128k": extra128},
+        "extra": {"ctx32k": extra32, "ctx128k": extra128, "ctx32k_p10_l60": extra_p10},
     }
     print(json.dumps(line), flush=True)
 

@@ -3,16 +3,17 @@
 // Appendix B.2: the bucket ID is the sign pattern of W^(l) k).
 //
 // Two projection paths:
-//  * hash_mfma_kernel: bf16 keys, P = 8, L in {16, 32, 64}.  The projection
-//    Z = W K^T is a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
-//    accumulation).  W stays in registers for the whole workgroup (each
-//    consumer wave owns 8 tables = 64 planes = two 32-row MFMA tiles);
-//    producer waves stream 128-key tiles of K through two LDS buffers (and
-//    the value rows of the same keys to their norms) while the consumers
-//    multiply the previous tile.  The planes of each 32-row tile are ordered
-//    so that every lane's accumulators hold complete tables, which turns the
-//    sign test + bit packing into lane-local work and one 32-bit store.
-//  * hash_generic_kernel: any dtype, P <= 8, any L; one-wave workgroups,
+//  * hash_mfma_kernel: bf16 keys, P = 8 with L in {16, 32, 64}, or P = 10
+//    with any L <= 64.  The projection Z = W K^T is a bf16 MFMA GEMM
+//    (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  W stays in registers
+//    for the whole workgroup (each consumer wave owns two 32-row MFMA tiles
+//    of planes: 8 tables of 8 planes, or 6 tables of 10 planes plus 4 zero
+//    rows); producer waves stream 128-key tiles of K through two LDS buffers
+//    (and the value rows of the same keys to their norms) while the
+//    consumers multiply the previous tile.  The planes of each tile are
+//    ordered so that every lane's accumulators hold complete tables, which
+//    turns the sign test + bit packing into lane-local work.
+//  * hash_generic_kernel: any dtype, P <= 10, any L; one-wave workgroups,
 //    each projecting one slice of a key's planes, one plane per lane.  Used
 //    for float32 keys, for odd shapes and for the decode-time append of a
 //    few keys.
@@ -134,9 +135,42 @@ constexpr int kProd = 4;       // producer waves
 constexpr int kRowU4 = 17;     // K rows in LDS padded to 272 B: 16 consecutive keys hit 16 bank groups
 constexpr int kProdU4 = kTK * 16 / (kProd * 64);  // K (and V) vectors per producer thread per tile (8)
 
-// Block = NW = L/8 consumer waves + kProd producer waves.  Consumer wave w
-// owns tables [8w, 8w+8) = two 32-plane MFMA A tiles, held in registers; it
-// only runs MFMAs and packs sign bits.  The producers load the next 128-key
+// Two-byte IDs of tables t0, t0+1, t0+2 of key pos (those < L), in the tiled
+// layout of L tables (TL per word, 2*TL-byte words).  The lane holding table
+// L - 1 also clears the rest of its word, and `pad` lanes clear the words
+// past the last table, so that tables >= L read as 0.
+__device__ __forceinline__ void store_wide(uint8_t* ids, int64_t bh, int64_t n_cap, int64_t pos,
+                                           int L, int t0, uint32_t id0, uint32_t id1,
+                                           uint32_t id2, bool pad) {
+  const int TL = ids_tables_per_word(L), WB = 2 * TL;
+  const uint32_t v[3] = {id0, id1, id2};
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int t = t0 + k;
+    if (t < L) {
+      *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, WB, pos, t / TL) +
+                                   2 * (t % TL)) = (uint16_t)v[k];
+      if (t == L - 1)
+        for (int z = L; z % TL; ++z)
+          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, WB, pos, z / TL) +
+                                       2 * (z % TL)) = (uint16_t)0;
+    }
+  }
+  if (pad) {
+    for (int w = (L + TL - 1) / TL; w < 16; ++w) {
+      uint8_t* dst = ids + ids_word_offset(bh, n_cap, WB, pos, w);
+      if (WB == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+      else if (WB == 4) *reinterpret_cast<uint32_t*>(dst) = 0u;
+      else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)0;
+    }
+  }
+}
+
+// Block = NW consumer waves + kProd producer waves.  With one-byte IDs
+// (WIDE false, P = 8, L = 8*NW) consumer wave w owns tables [8w, 8w+8) = two
+// 32-plane MFMA A tiles, held in registers; with two-byte IDs (WIDE, P = 10,
+// L <= 6*NW) it owns tables [6w, 6w+6).  Consumers only run MFMAs, pack sign
+// bits and store IDs.  The producers load the next 128-key
 // tile of K and V, write K into the other of two LDS buffers and store the
 // value norms, while the consumers work on the current tile: one block
 // barrier per tile, passed by every wave the same number of times.  MFMA
@@ -144,14 +178,16 @@ constexpr int kProdU4 = kTK * 16 / (kProd * 64);  // K (and V) vectors per produ
 // operands.  Row R of A tile tt is plane r&7 of table
 // 8w + 4*((R>>2)&1) + 2*tt + (r>>3), r = ((R>>3)<<2)|(R&3), so with the
 // 32x32 accumulator layout (register r of lane l holds row
-// 8*(r/4) + 4*(l/32) + r%4) lane l holds whole tables.
+// 8*(r/4) + 4*(l/32) + r%4) lane l holds whole tables.  WIDE: register r of
+// tile tt in lane half h is accumulator c = 16*tt + r of that half; c < 30
+// is plane c % 10 of table 6w + 3h + c / 10, and c = 30, 31 are zero rows.
 // grid: B*Hkv*nblk blocks; block blk hashes keys [pos0 + blk*kpb, +kpb) of (b, h).
-template <int NW>
+template <int NW, bool WIDE>
 __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int Hkv, int64_t n_cap,
-    const int32_t* __restrict__ pos0, int count, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ pos0, int count, const uint16_t* __restrict__ W, int Lw,
     uint8_t* __restrict__ ids, float* __restrict__ vnorm, int kpb, int nblk) {
-  constexpr int L = NW * 8;
+  constexpr int L8 = NW * 8;  // tables of the one-byte layout
   constexpr int NB = kTK / kBTile;
   const int blk = blockIdx.x % nblk;
   const int bh = blockIdx.x / nblk;
@@ -240,10 +276,23 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     const int r = ((R >> 3) << 2) | (R & 3);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int table = 8 * wave + 4 * hout + 2 * tt + (r >> 3);
-      const uint16_t* wr = W + ((int64_t)(table * 8 + (r & 7))) * kHead + 64 * half;
+      if constexpr (WIDE) {
+        const int c = 16 * tt + r;
+        const int table = 6 * wave + 3 * hout + c / 10;
+        const bool live = c < 30 && table < Lw;
+        const uint16_t* wr = W + (int64_t)(live ? table * 10 + c % 10 : 0) * kHead + 64 * half;
+        const bf16x8_t zero = {};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) a[tt][kk] = *reinterpret_cast<const bf16x8_t*>(wr + 8 * kk);
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(wr + 8 * kk);
+          a[tt][kk] = live ? v : zero;
+        }
+      } else {
+        const int table = 8 * wave + 4 * hout + 2 * tt + (r >> 3);
+        const uint16_t* wr = W + ((int64_t)(table * 8 + (r & 7))) * kHead + 64 * half;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) a[tt][kk] = *reinterpret_cast<const bf16x8_t*>(wr + 8 * kk);
+      }
     }
   }
   lds_barrier();
@@ -260,31 +309,46 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][kk], bop, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][kk], bop, acc1, 0, 0, 0);
       }
-      // register r of tile tt = plane r & 7 of table 8w + 4*half + 2*tt + (r >> 3):
-      // bit 16*tt + r of the 4-table word; a plane is set when its float bits,
-      // read as an int, clamp to 1 in [0, 1]
-      uint32_t word = 0u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        word |= (uint32_t)min(max(__float_as_int(acc0[r]), 0), 1) << r;
-        word |= (uint32_t)min(max(__float_as_int(acc1[r]), 0), 1) << (16 + r);
-      }
-      // the 4 tables 8w + 4*half .. +3 of key pos, as ID words of the tiled layout
       const int64_t pos = t0 + bt * kBTile + col;
-      if (pos < end) {
-        constexpr int TL = ids_word_bytes(L, 8);   // P = 8: one byte per table
-        const int t0w = (8 * wave + 4 * half) / TL;  // first word index
-        if constexpr (TL == 4) {
-          *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) = word;
-        } else if constexpr (TL == 2) {
-          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) =
-              (uint16_t)word;
-          *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w + 1)) =
-              (uint16_t)(word >> 16);
-        } else {
+      if constexpr (WIDE) {
+        // a plane is set when its float bits, read as an int, clamp to 1 in [0, 1]
+        uint32_t id0 = 0u, id1 = 0u, id2 = 0u;
 #pragma unroll
-          for (int b8 = 0; b8 < 4; ++b8)
-            ids[ids_word_offset(bh, n_cap, TL, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+        for (int c = 0; c < 30; ++c) {
+          const float v = c < 16 ? acc0[c] : acc1[c - 16];
+          const uint32_t bit = (uint32_t)min(max(__float_as_int(v), 0), 1) << (c % 10);
+          if (c < 10) id0 |= bit;
+          else if (c < 20) id1 |= bit;
+          else id2 |= bit;
+        }
+        if (pos < end) store_wide(ids, bh, n_cap, pos, Lw, 6 * wave + 3 * half, id0, id1, id2,
+                                  wave == 0 && half == 0);
+      } else {
+        // register r of tile tt = plane r & 7 of table 8w + 4*half + 2*tt + (r >> 3):
+        // bit 16*tt + r of the 4-table word; a plane is set when its float bits,
+        // read as an int, clamp to 1 in [0, 1]
+        uint32_t word = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          word |= (uint32_t)min(max(__float_as_int(acc0[r]), 0), 1) << r;
+          word |= (uint32_t)min(max(__float_as_int(acc1[r]), 0), 1) << (16 + r);
+        }
+        // the 4 tables 8w + 4*half .. +3 of key pos, as ID words of the tiled layout
+        if (pos < end) {
+          constexpr int TL = ids_word_bytes(L8, 8);   // P = 8: one byte per table
+          const int t0w = (8 * wave + 4 * half) / TL;  // first word index
+          if constexpr (TL == 4) {
+            *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) = word;
+          } else if constexpr (TL == 2) {
+            *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) =
+                (uint16_t)word;
+            *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w + 1)) =
+                (uint16_t)(word >> 16);
+          } else {
+#pragma unroll
+            for (int b8 = 0; b8 < 4; ++b8)
+              ids[ids_word_offset(bh, n_cap, TL, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+          }
         }
       }
     }
@@ -302,7 +366,8 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
   const bool bf16 = dtype == 1;
   // the MFMA path covers every ID word when L is 16, 32 or 64
   const bool mfma_ok = bf16 && P == 8 && (L == 16 || L == 32 || L == 64) && count >= 64;
-  if (mfma_ok) {
+  const bool wide_ok = bf16 && P == 10 && L <= 64 && count >= 64;
+  if (mfma_ok || wide_ok) {
     // about one workgroup per CU, each streaming a contiguous key range
     int64_t nblk = (256 + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
     int64_t kpb = ((count + nblk - 1) / nblk + 127) / 128 * 128;
@@ -311,10 +376,27 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     const uint16_t* Kb = static_cast<const uint16_t*>(K);
     const uint16_t* Vb = static_cast<const uint16_t*>(V);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
-    switch (L) {
-      case 16: hash_mfma_kernel<2><<<grid, (2 + kProd) * 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, (int)kpb, (int)nblk); break;
-      case 32: hash_mfma_kernel<4><<<grid, (4 + kProd) * 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, (int)kpb, (int)nblk); break;
-      default: hash_mfma_kernel<8><<<grid, (8 + kProd) * 64, 0, s>>>(Kb, Vb, Hkv, n_cap, pos0, count, Wb, ids, vnorm, (int)kpb, (int)nblk); break;
+    auto go = [&](auto nw, auto wide) {
+      constexpr int NW = decltype(nw)::value;
+      hash_mfma_kernel<NW, decltype(wide)::value><<<grid, (NW + kProd) * 64, 0, s>>>(
+          Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk);
+    };
+    using N = std::false_type;
+    using Y = std::true_type;
+    if (mfma_ok) {
+      switch (L) {
+        case 16: go(std::integral_constant<int, 2>{}, N{}); break;
+        case 32: go(std::integral_constant<int, 4>{}, N{}); break;
+        default: go(std::integral_constant<int, 8>{}, N{}); break;
+      }
+    } else {  // six 10-plane tables per consumer wave
+      const int nw = (L + 5) / 6;
+      if (nw <= 2) go(std::integral_constant<int, 2>{}, Y{});
+      else if (nw <= 4) go(std::integral_constant<int, 4>{}, Y{});
+      else if (nw <= 6) go(std::integral_constant<int, 6>{}, Y{});
+      else if (nw <= 8) go(std::integral_constant<int, 8>{}, Y{});
+      else if (nw <= 10) go(std::integral_constant<int, 10>{}, Y{});
+      else go(std::integral_constant<int, 11>{}, Y{});
     }
     return hipGetLastError();
   }

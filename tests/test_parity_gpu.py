@@ -40,9 +40,13 @@ def sync():
     dict(name="c2", n=500, L=7, P=5, Hkv=2, Hq=4),     # odd shapes: generic path
     dict(name="c2", n=300, L=3, P=8, Hkv=2, Hq=2),
     dict(name="c4", n=(300, 900), B=3, Hkv=2, Hq=8),   # batch with different lengths
-    dict(name="c2", n=1000, L=60, P=10),               # two-byte IDs, 4 tables per word
-    dict(name="c2", n=500, L=20, P=10, Hkv=2, Hq=4),   # two tables per word
-    dict(name="c2", n=300, L=5, P=9, Hkv=2, Hq=2),     # one table per word
+    dict(name="c2", n=1000, L=60, P=10),               # two-byte IDs, MFMA, 10 consumer waves
+    dict(name="c2", n=700, L=64, P=10, Hkv=4, Hq=8),   # MFMA, 11 consumer waves
+    dict(name="c2", n=500, L=20, P=10, Hkv=2, Hq=4),   # MFMA, two tables per word
+    dict(name="c2", n=300, L=5, P=10, Hkv=2, Hq=2),    # MFMA, one table per word
+    dict(name="c2", n=40, L=60, P=10),                 # few keys: generic, two-byte IDs
+    dict(name="c2", n=300, L=5, P=9, Hkv=2, Hq=2),     # generic, one table per word
+    dict(name="c1", L=60, P=10),                       # fp32: generic
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_hash_parity(case):
     print("case", case, flush=True)
@@ -70,6 +74,23 @@ def test_hash_full_c2_mfma():
         band += GC.check_ids(ids[0, h], w.K[0, h], w.W, w.L, w.P, w.n_cap)
         np.testing.assert_allclose(vn[0, h], SO.value_norms(w.V[0, h]), rtol=2e-6)
     print("id bits inside the 1e-5 band:", band)
+
+
+@pytest.mark.parametrize("L,n", [(60, 1000), (20, 333), (5, 200), (37, 64)])
+def test_hash_wide_pads_and_range(L, n):
+    """Two-byte IDs: the hashed keys' cells of tables >= L (up to 16 words) are
+    cleared, and keys past the hashed range keep their bytes."""
+    w = make_workload("c2", n=n, L=L, P=10, Hkv=2, Hq=4, n_cap=n + 100)
+    d = GC.upload(w)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV).fill_(0xAB)
+    ids, _ = GC.gpu_hash(w, d, ids=ids)
+    sync()
+    slots = 16 * S.layout.tables_per_word(L)
+    full = GC.ids_np(ids, slots, P=10)            # every cell of every word
+    for h in range(w.Hkv):
+        GC.check_ids(full[0, h, :, :L], w.K[0, h], w.W, w.L, w.P, n)
+    assert (full[0, :, :n, L:] == 0).all()
+    assert (full[0, :, n:, :] == 0xABAB).all()
 
 
 @pytest.mark.parametrize("L,P", [(64, 8), (60, 10)])
