@@ -70,7 +70,7 @@ def parse():
 class Case:
     """Device buffers and pre-marshalled C calls of one decode workload."""
 
-    def __init__(self, name, replicas, lib, torch, S, **over):
+    def __init__(self, name, replicas, lib, torch, S, sink=0, window=0, **over):
         from soft_lsh_token_amd.inputs import make_workload
         t0 = time.time()
         self.w = w = make_workload(name, steps=1, **over)   # one extra row: the appended key
@@ -81,6 +81,8 @@ class Case:
         self.n = int(w.lens[0])
         self.B, self.Hq, self.Hkv, self.L, self.P = w.B, w.Hq, w.Hkv, w.L, w.P
         self.k = int(w.ks[0])
+        self.sink, self.window = int(sink), int(window)
+        self.k_max = self.k + self.sink + self.window   # index row: top-k + sink + window
         K0 = torch.from_numpy(w.K).to(dev).to(bf)
         V0 = torch.from_numpy(w.V).to(dev).to(bf)
         self.K = [K0] + [K0.clone() for _ in range(replicas - 1)]
@@ -95,12 +97,12 @@ class Case:
         self.ids = [S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, dev) for _ in range(replicas)]
         self.vn = [torch.empty(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
                    for _ in range(replicas)]
-        self.idx = torch.empty(w.B, w.Hq, self.k, dtype=torch.int32, device=dev)
+        self.idx = torch.empty(w.B, w.Hq, self.k_max, dtype=torch.int32, device=dev)
         self.scores = torch.empty(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32,
                                   device=dev)
         self.out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
-        sws = S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, self.k)
-        dws = S.socket_sparse_decode_workspace(w.B, w.Hq, w.d, self.k)
+        sws = S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, self.k_max)
+        dws = S.socket_sparse_decode_workspace(w.B, w.Hq, w.d, self.k_max)
         self.sws = S.alloc_workspace(sws, dev)
         self.dws = S.alloc_workspace(dws, dev)
         self.sws_p = self.sws.data_ptr() + (-self.sws.data_ptr()) % 256
@@ -126,24 +128,26 @@ class Case:
             self.c_append.append(common + (vp(self.pos_append.data_ptr()), 1,
                                             vp(self.W.data_ptr()), w.L, w.P, vp(ids), vp(vn), st))
             self.c_score.append((w.B, w.Hq, w.Hkv, w.L, w.P, vp(ids), vp(vn),
-                                 vp(self.lens.data_ptr()), i64(w.n_cap),
+                                 vp(self.lens.data_ptr()), i64(w.n_cap), self.sink, self.window,
                                  vp(self.scores.data_ptr()), vp(self.sws_p),
                                  ctypes.c_size_t(self.sws_n), st))
             self.c_score_topk.append((vp(self.q.data_ptr()), 1, w.B, w.Hq, w.Hkv, w.d,
                                       vp(self.W.data_ptr()), w.L, w.P, ctypes.c_float(w.tau),
                                       vp(ids), vp(vn), vp(self.lens.data_ptr()), i64(w.n_cap),
-                                      vp(self.ks.data_ptr()), self.k, vp(self.idx.data_ptr()),
+                                      vp(self.ks.data_ptr()), self.k_max, self.sink, self.window,
+                                      vp(self.idx.data_ptr()),
                                       vp(self.scores.data_ptr()), vp(self.sws_p),
                                       ctypes.c_size_t(self.sws_n), st))
             self.c_decode.append((vp(self.q.data_ptr()), vp(K), vp(V), 1, w.B, w.Hq, w.Hkv, w.d,
-                                  i64(w.n_cap), vp(self.idx.data_ptr()), self.k,
+                                  i64(w.n_cap), vp(self.idx.data_ptr()), self.k_max,
                                   ctypes.c_float(w.scale), vp(self.out.data_ptr()),
                                   vp(self.dws_p), ctypes.c_size_t(self.dws_n), st))
         self.c_tables = (vp(self.q.data_ptr()), 1, w.B, w.Hq, w.Hkv, w.d, vp(self.W.data_ptr()), w.L,
                          w.P, ctypes.c_float(w.tau), i64(w.n_cap), vp(self.sws_p),
                          ctypes.c_size_t(self.sws_n), st)
         self.c_topk = (w.B, w.Hq, w.Hkv, w.L, vp(self.scores.data_ptr()), vp(self.lens.data_ptr()),
-                       i64(w.n_cap), vp(self.ks.data_ptr()), self.k, vp(self.idx.data_ptr()),
+                       i64(w.n_cap), vp(self.ks.data_ptr()), self.k_max, self.sink, self.window,
+                       vp(self.idx.data_ptr()),
                        vp(self.sws_p), ctypes.c_size_t(self.sws_n), st)
 
     @staticmethod

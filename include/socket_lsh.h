@@ -117,9 +117,14 @@ size_t socket_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L,
  *               s_j(c) = +1 if bit j of c is set else -1
  *               (equivalently prod_j sigmoid(2 s_j(c) u[l][j] / tau))
  *   s_i       = vnorm[b][h][i] * sum_l p_l(ID of table l of key i)   for i < lens[b]
- *   idx[b][g] = the min(ks[b], lens[b]) keys with the largest s_i; among
- *               equal scores the lower index wins.  The indices are written
- *               in ascending order and the row is padded with -1 up to k_max.
+ *   F_b       = { i < n : i < sink or i >= n - window },  n = lens[b]
+ *               (sink and local-window keys, always attended; SOCKET Sec. 6
+ *               setup includes 64 or 128 of them)
+ *   idx[b][g] = F_b united with the min(ks[b], n - |F_b|) keys outside F_b
+ *               with the largest s_i; among equal scores the lower index
+ *               wins.  The indices are written in ascending order and the
+ *               row is padded with -1 up to k_max.  sink = window = 0 gives
+ *               plain top-k.
  * Scores are float32, score row stride ns = n_cap rounded up to a multiple of
  * 64 (rows start 256-byte aligned).  A table entry is either the float32 rounding of the
  * float64 p_l(c), or the float32 product lo * hi of the float32 roundings of
@@ -127,14 +132,17 @@ size_t socket_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L,
  * written there (entries i >= lens[b] are left untouched).
  *
  * lens and ks are device int32 arrays [B] with 0 <= lens[b] <= n_cap and
- * ks[b] <= k_max (a negative ks[b] is treated as 0).  tau > 0.
+ * ks[b] + sink + window <= k_max (a negative ks[b] is treated as 0; a larger
+ * one is cut to k_max - |F_b|).  sink, window >= 0 with sink + window <=
+ * k_max, else SOCKET_EINVAL.  tau > 0.
  * ws must hold socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max) bytes
  * and be 256-byte aligned; its contents need not be initialised.
  */
 int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
                       int L, int P, float tau, const uint8_t* ids, const float* vnorm,
-                      const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max,
-                      int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream);
+                      const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max, int sink,
+                      int window, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /*
  * The three stages of socket_score_topk, for callers that schedule or time
@@ -151,20 +159,22 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
  *   counters held in the workspace.
  * socket_score -- Algorithm 2, second half: s_i for every i < lens[b] of every
  *   query head, written to `scores` (or into the workspace when scores is
- *   NULL), plus a histogram of the top bits of each score in the workspace.
+ *   NULL), plus a histogram of the top bits of the scores of the keys
+ *   outside F_b in the workspace.
  * socket_topk -- Algorithm 3: the top-k indices per query head, from the same
  *   `scores` pointer (NULL = workspace) and the histogram left by
- *   socket_score.  Output as in socket_score_topk.
+ *   socket_score, which must have been given the same sink and window.
+ *   Output as in socket_score_topk.
  */
 int socket_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
                        int L, int P, float tau, int64_t n_cap, void* ws, size_t ws_bytes,
                        void* stream);
 int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const float* vnorm,
-                 const int32_t* lens, int64_t n_cap, float* scores, void* ws, size_t ws_bytes,
-                 void* stream);
+                 const int32_t* lens, int64_t n_cap, int sink, int window, float* scores,
+                 void* ws, size_t ws_bytes, void* stream);
 int socket_topk(int B, int Hq, int Hkv, int L, const float* scores, const int32_t* lens,
-                int64_t n_cap, const int32_t* ks, int k_max, int32_t* idx, void* ws,
-                size_t ws_bytes, void* stream);
+                int64_t n_cap, const int32_t* ks, int k_max, int sink, int window, int32_t* idx,
+                void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by socket_sparse_decode for these sizes. */
 size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max);

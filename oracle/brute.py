@@ -69,6 +69,25 @@ def top_k(s, k):
     return sorted(chosen)
 
 
+def select(s, k, sink, window):
+    """Attended keys of one head: the first `sink` and last `window` keys, plus
+    the k best of the others (k-fold arg max, lower index first on equal
+    scores)."""
+    n = len(s)
+    forced = [i for i in range(n) if i < sink or i >= n - window]
+    others = [i for i in range(n) if i not in forced]
+    chosen = []
+    for _ in range(min(k, len(others))):
+        best = None
+        for i in others:
+            if i in chosen:
+                continue
+            if best is None or s[i] > s[best]:
+                best = i
+        chosen.append(best)
+    return sorted(forced + chosen)
+
+
 def attention(q, Ks, Vs, scale):
     logits = [dot(kk, q) * scale for kk in Ks]
     m = max(logits)

@@ -35,6 +35,10 @@ Readings where the pages are silent (each listed in the design notes):
 * Bucket IDs belong to KV heads and are shared by the GQA query heads that
   read that KV head (query head g reads KV head g // (Hq / Hkv)).
 * Top-k ties go to the lower key index.  Attention uses scale 1/sqrt(d).
+* Sink and local-window tokens (Sec. 6 setup: a small number, 64 or 128,
+  always attended): the first `sink` and the last `window` keys of the
+  sequence are always selected, and the top-k budget goes to the other
+  keys, so a head attends min(n, k + sink + window) distinct keys.
 
 Every input is taken as given (already rounded to its storage dtype) and
 promoted to float64.
@@ -44,7 +48,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "hash_keys", "value_norms", "projections", "soft_tables", "scores", "topk",
+    "hash_keys", "value_norms", "projections", "soft_tables", "scores", "topk", "select",
     "sparse_attention", "decode_step", "hard_collision_scores",
 ]
 
@@ -159,6 +163,25 @@ def topk(s, k: int, n: int | None = None) -> np.ndarray:
     return np.sort(order[:k])
 
 
+def select(s, k: int, n: int | None = None, sink: int = 0, window: int = 0) -> np.ndarray:
+    """Algorithm 3's selection with always-attended sink and local-window tokens
+    (Sec. 6 setup).  Keys [0, sink) and [n - window, n) are always taken; the
+    k highest scores among the remaining keys are added (ties -> lower index).
+
+    Returns the attended key indices sorted ascending.
+    """
+    s = _f64(s)
+    if n is None:
+        n = s.shape[-1]
+    forced = np.zeros(n, dtype=bool)
+    forced[:min(sink, n)] = True
+    forced[max(n - window, 0):] = True
+    rest = np.nonzero(~forced)[0]
+    order = np.argsort(-s[rest], kind="stable")        # stable: lower index first on ties
+    picked = rest[order[:max(int(k), 0)]]
+    return np.sort(np.concatenate([np.nonzero(forced)[0], picked]))
+
+
 def sparse_attention(q, K, V, idx, scale: float):
     """Exact softmax attention of one query over the selected keys (SOCKET Sec. 2, 4.1).
 
@@ -174,7 +197,8 @@ def sparse_attention(q, K, V, idx, scale: float):
     return a @ Vs
 
 
-def decode_step(w, q=None, lens=None, ks=None, K=None, V=None, ids=None, vnorm=None):
+def decode_step(w, q=None, lens=None, ks=None, K=None, V=None, ids=None, vnorm=None,
+                sink: int = 0, window: int = 0):
     """Hash (if needed), score, select and attend for every (sequence, query head).
 
     ``w`` is a workload from the shared input module.  Returns a dict with
@@ -197,7 +221,7 @@ def decode_step(w, q=None, lens=None, ks=None, K=None, V=None, ids=None, vnorm=N
     sel = {}
     for b in range(w.B):
         for g in range(w.Hq):
-            idx = topk(s[b, g], int(ks[b]), int(lens[b]))
+            idx = select(s[b, g], int(ks[b]), int(lens[b]), sink, window)
             sel[(b, g)] = idx
             out[b, g] = sparse_attention(q[b, g], K[b, g // group], V[b, g // group], idx,
                                          w.scale)

@@ -30,10 +30,10 @@ _SIGS = {
     "socket_hash_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp, _vp]),
     "socket_score_topk_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
     "socket_score_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _i64, _vp,
-                               _i, _vp, _vp, _vp, _sz, _vp]),
+                               _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "socket_soft_tables": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _i64, _vp, _sz, _vp]),
-    "socket_score": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
-    "socket_topk": (_i, [_i, _i, _i, _i, _vp, _vp, _i64, _vp, _i, _vp, _vp, _sz, _vp]),
+    "socket_score": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i64, _i, _i, _vp, _vp, _sz, _vp]),
+    "socket_topk": (_i, [_i, _i, _i, _i, _vp, _vp, _i64, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "socket_sparse_decode_workspace": (_sz, [_i, _i, _i, _i]),
     "socket_sparse_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i64, _vp, _i, _f, _vp, _vp,
                                   _sz, _vp]),
@@ -164,8 +164,10 @@ def _ws_ptr(ws: torch.Tensor, need: int) -> tuple[int, int]:
 def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm: torch.Tensor,
                       lens: torch.Tensor, ks: torch.Tensor, k_max: int, tau: float, L: int, P: int,
                       idx: torch.Tensor, scores: torch.Tensor | None = None,
-                      ws: torch.Tensor | None = None, stream=None) -> None:
-    """Soft-LSH scores of every key and the top-k indices per query head."""
+                      ws: torch.Tensor | None = None, stream=None, sink: int = 0,
+                      window: int = 0) -> None:
+    """Soft-LSH scores of every key and the selected indices per query head: the
+    top-k keys plus the first `sink` and last `window` keys of each sequence."""
     B, Hq, d = q.shape
     Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
     need = socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
@@ -179,8 +181,8 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
         float(tau), _ids(ids, B, Hkv, n_cap, L, P),
         _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
         _dev(lens, "lens", torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)),
-        int(k_max), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr, wptr, wbytes,
-        _stream(q, stream))
+        int(k_max), int(sink), int(window), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr,
+        wptr, wbytes, _stream(q, stream))
     _check("socket_score_topk", rc)
 
 
@@ -196,13 +198,14 @@ def socket_soft_tables(q: torch.Tensor, W: torch.Tensor, Hkv: int, L: int, P: in
 
 
 def socket_score(ids: torch.Tensor, vnorm: torch.Tensor, lens: torch.Tensor, Hq: int, L: int,
-                 P: int, scores: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+                 P: int, scores: torch.Tensor, ws: torch.Tensor, stream=None, sink: int = 0,
+                 window: int = 0) -> None:
     """Algorithm 2, second half: soft-count scores (needs socket_soft_tables on ws first)."""
     B, Hkv, n_cap = vnorm.shape
     wptr, wbytes = _ws_ptr(ws, 0)
     rc = lib().socket_score(B, Hq, Hkv, L, P, _ids(ids, B, Hkv, n_cap, L, P),
                             _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
-                            _dev(lens, "lens", torch.int32, (B,)), n_cap,
+                            _dev(lens, "lens", torch.int32, (B,)), n_cap, int(sink), int(window),
                             _dev(scores, "scores", torch.float32, (B, Hq, score_stride(n_cap))),
                             wptr, wbytes,
                             _stream(ids, stream))
@@ -210,7 +213,8 @@ def socket_score(ids: torch.Tensor, vnorm: torch.Tensor, lens: torch.Tensor, Hq:
 
 
 def socket_topk(scores: torch.Tensor, lens: torch.Tensor, ks: torch.Tensor, Hkv: int, L: int,
-                n_cap: int, idx: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+                n_cap: int, idx: torch.Tensor, ws: torch.Tensor, stream=None, sink: int = 0,
+                window: int = 0) -> None:
     """Algorithm 3: top-k per query head from scores + the histogram socket_score left in ws."""
     B, Hq, _ = scores.shape
     k_max = idx.shape[-1]
@@ -218,7 +222,8 @@ def socket_topk(scores: torch.Tensor, lens: torch.Tensor, ks: torch.Tensor, Hkv:
     rc = lib().socket_topk(B, Hq, Hkv, L, _dev(scores, "scores", torch.float32,
                            (B, Hq, score_stride(n_cap))), _dev(lens, "lens",
                            torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)), k_max,
-                           _dev(idx, "idx", torch.int32, (B, Hq, k_max)), wptr, wbytes,
+                           int(sink), int(window), _dev(idx, "idx", torch.int32, (B, Hq, k_max)),
+                           wptr, wbytes,
                            _stream(scores, stream))
     _check("socket_topk", rc)
 

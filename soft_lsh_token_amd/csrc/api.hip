@@ -104,39 +104,49 @@ int socket_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, int d, 
                                      static_cast<hipStream_t>(stream)));
 }
 
+// Sink and window sizes: non-negative, and (with k_max > 0) their sum fits in
+// an index row.
+static bool sink_window_ok(int sink, int window, int k_max) {
+  if (sink < 0 || window < 0 || sink > (1 << 30) || window > (1 << 30)) return false;
+  return k_max <= 0 || sink + window <= k_max;
+}
+
 int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const float* vnorm,
-                 const int32_t* lens, int64_t n_cap, float* scores, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 const int32_t* lens, int64_t n_cap, int sink, int window, float* scores,
+                 void* ws, size_t ws_bytes, void* stream) {
   if (!ids || !vnorm || !lens) return SOCKET_EINVAL;
+  if (!sink_window_ok(sink, window, 0)) return SOCKET_EINVAL;
   int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
   if (rc) return rc;
   ScoreWs w;
   if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
-  return from_hip(launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap,
+  return from_hip(launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, SinkWindow{sink, window},
                                scores ? scores : w.scores, w, static_cast<hipStream_t>(stream)));
 }
 
 int socket_topk(int B, int Hq, int Hkv, int L, const float* scores, const int32_t* lens,
-                int64_t n_cap, const int32_t* ks, int k_max, int32_t* idx, void* ws,
-                size_t ws_bytes, void* stream) {
+                int64_t n_cap, const int32_t* ks, int k_max, int sink, int window, int32_t* idx,
+                void* ws, size_t ws_bytes, void* stream) {
   if (!lens || !ks || !idx) return SOCKET_EINVAL;
-  if (k_max <= 0) return SOCKET_EINVAL;
+  if (k_max <= 0 || !sink_window_ok(sink, window, k_max)) return SOCKET_EINVAL;
   if (k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
   int rc = check_sizes(B, Hq, Hkv, L, 1, n_cap);
   if (rc) return rc;
   ScoreWs w;
   if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
-  return from_hip(launch_topk(B, Hq, scores ? scores : w.scores, lens, n_cap, ks, k_max, idx, w,
+  return from_hip(launch_topk(B, Hq, scores ? scores : w.scores, lens, n_cap, ks, k_max,
+                              SinkWindow{sink, window}, idx, w,
                               static_cast<hipStream_t>(stream)));
 }
 
 int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
                       int L, int P, float tau, const uint8_t* ids, const float* vnorm,
-                      const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max,
-                      int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream) {
+                      const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max, int sink,
+                      int window, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                      void* stream) {
   if (!q || !W || !ids || !vnorm || !lens || !ks || !idx || !ws) return SOCKET_EINVAL;
   if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
-  if (k_max <= 0) return SOCKET_EINVAL;
+  if (k_max <= 0 || !sink_window_ok(sink, window, k_max)) return SOCKET_EINVAL;
   if (!(tau > 0.f) || !(tau < INFINITY)) return SOCKET_EINVAL;
   int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
   if (rc) return rc;
@@ -146,8 +156,9 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* sc = scores ? scores : w.scores;
   hipError_t e = launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w, s);
-  if (e == hipSuccess) e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sc, w, s);
-  if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, idx, w, s);
+  const SinkWindow sw{sink, window};
+  if (e == hipSuccess) e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sw, sc, w, s);
+  if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s);
   return from_hip(e);
 }
 

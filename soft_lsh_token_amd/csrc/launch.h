@@ -28,15 +28,23 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
                               int L, int P, float tau, const ScoreWs& ws, hipStream_t s);
 
-// Algorithm 2, part 2: scores of every key plus the first-digit histogram.
-hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,
-                        const float* vnorm, const int32_t* lens, int64_t n_cap, float* scores,
-                        const ScoreWs& ws, hipStream_t s);
+// Keys always selected besides the top-k: the first `sink` and the last
+// `window` keys of each sequence.
+struct SinkWindow {
+  int sink, window;
+};
 
-// Algorithm 3: top-k selection from the scores and their histogram.
+// Algorithm 2, part 2: scores of every key plus the first-digit histogram of
+// the keys that compete for the top-k.
+hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,
+                        const float* vnorm, const int32_t* lens, int64_t n_cap, SinkWindow sw,
+                        float* scores, const ScoreWs& ws, hipStream_t s);
+
+// Algorithm 3: top-k selection from the scores and their histogram, united
+// with the sink and window keys.
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
-                       const int32_t* ks, int k_max, int32_t* idx, const ScoreWs& ws,
-                       hipStream_t s);
+                       const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx,
+                       const ScoreWs& ws, hipStream_t s);
 
 struct DecodeWs {
   float* part;          // [B*Hq][splits][kHead + 2]

@@ -441,7 +441,7 @@ template <int G, int TL, bool WIDE>
 __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     const float* __restrict__ img, int img_floats, const uint8_t* __restrict__ ids,
     const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
-    int64_t n_cap, int rows, int nblk, int gpb, float* __restrict__ scores,
+    int64_t n_cap, int sink, int window, int rows, int nblk, int gpb, float* __restrict__ scores,
     uint32_t* __restrict__ hist) {
   using Sh = ImageShape<G, TL, WIDE>;
   constexpr int NF = Sh::NF, NS = Sh::NS, HE = Sh::HE;
@@ -458,6 +458,11 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   const int h = bh % Hkv;
   int64_t n = lens[b];
   if (n > n_cap) n = n_cap;
+  if (n < 0) n = 0;
+  // sink and window keys [0, f_lo) and [f_hi, n) are always selected: scored,
+  // but kept out of the selection histogram
+  const int64_t f_lo = sink < n ? sink : n;
+  const int64_t f_hi = n - window > 0 ? n - window : 0;
   const int64_t g_begin = (int64_t)blk * gpb;
   int64_t g_end = (n + 63) >> 6;
   if (g_end > g_begin + gpb) g_end = g_begin + gpb;
@@ -516,12 +521,13 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
         score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, lomask, plo, u);
         const int64_t key = gi * 64 + lane;
         const bool valid = key < n;
+        const uint32_t ranked = valid && key >= f_lo && key < f_hi ? 1u : 0u;
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) {
           const float sv = vb[s] * u[0][gg];
           uint32_t dg = __float_as_uint(sv) >> kHistShift;
           if (dg > kHistBins - 1) dg = kHistBins - 1;
-          atomicAdd(&lhist[gg * kHistBins + dg], valid ? 1u : 0u);
+          atomicAdd(&lhist[gg * kHistBins + dg], ranked);
         }
         if (valid) {
 #pragma unroll
@@ -594,17 +600,30 @@ struct Pick {
   uint32_t digit, before, inbin;
 };
 
-__device__ __forceinline__ void clamp_nk(int64_t n_cap, int32_t len, int32_t kk, int k_max,
-                                         int64_t* n, int64_t* k) {
+// Selection sizes of one sequence: n keys; the sink and window keys
+// [0, f_lo) and [f_hi, n) (nf of them) are always selected; k of the other
+// n - nf keys are chosen by score; total = k + nf <= k_max indices out.
+struct SelSizes {
+  int64_t n, k, total, f_lo, f_hi;
+};
+
+__device__ __forceinline__ SelSizes sel_sizes(int64_t n_cap, int32_t len, int32_t kk, int k_max,
+                                              int sink, int window) {
+  SelSizes z;
   int64_t nn = len;
   if (nn < 0) nn = 0;
   if (nn > n_cap) nn = n_cap;
+  z.n = nn;
+  z.f_lo = sink < nn ? sink : nn;
+  z.f_hi = nn - window > 0 ? nn - window : 0;
+  const int64_t nf = z.f_lo + (nn - (z.f_hi > z.f_lo ? z.f_hi : z.f_lo));
   int64_t k2 = kk;
   if (k2 < 0) k2 = 0;
-  if (k2 > nn) k2 = nn;
-  if (k2 > k_max) k2 = k_max;
-  *n = nn;
-  *k = k2;
+  if (k2 > nn - nf) k2 = nn - nf;
+  if (k2 > k_max - nf) k2 = k_max - nf > 0 ? k_max - nf : 0;
+  z.k = k2;
+  z.total = k2 + nf;
+  return z;
 }
 
 // Bin of the first digit that holds the k-th largest score, and how many keys
@@ -641,9 +660,10 @@ __device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum
 // their scores) covers keys [c*kScanKeys, (c+1)*kScanKeys) of head lid / CH.
 __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
     const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
-    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int Hq, int CH,
-    int heads, const uint32_t* __restrict__ hist, uint32_t* __restrict__ counters,
-    uint32_t* __restrict__ bitmap, int64_t words, uint2* __restrict__ cand) {
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int sink,
+    int window, int Hq, int CH, int heads, const uint32_t* __restrict__ hist,
+    uint32_t* __restrict__ counters, uint32_t* __restrict__ bitmap, int64_t words,
+    uint2* __restrict__ cand) {
   const int lid = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
   if (lid >= heads * CH) return;
   const int bg = lid / CH;
@@ -651,9 +671,9 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   const int b = bg / Hq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int64_t n, k;
-  clamp_nk(n_cap, lens[b], ks[b], k_max, &n, &k);
-  if (k == 0) return;
+  const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
+  const int64_t n = z.n, k = z.k;
+  if (z.total == 0) return;
   const int64_t c0 = (int64_t)c * kScanKeys;
   if (c0 >= n) return;
 
@@ -671,10 +691,12 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   __shared__ Boundary shb;
   const Boundary bd = find_boundary<kScanThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
   // above d1: bits > thr_sel; in d1: bits >= thr_lo and not above (the top
-  // digit is clamped to kHistBins - 1 here as in the histogram)
+  // digit is clamped to kHistBins - 1 here as in the histogram).  Sink and
+  // window keys are selected whatever their score and never candidates.
   const uint32_t thr_lo = bd.d1 << kHistShift;
   const uint32_t thr_sel = bd.d1 < (uint32_t)(kHistBins - 1) ? ((bd.d1 + 1) << kHistShift) - 1u
                                                             : 0xFFFFFFFFu;
+  const uint64_t by_score = k > 0 ? ~0ull : 0ull;
   uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint64_t lt = lanemask_lt64();
   // candidates gather in LDS; one global reservation per workgroup at the end
@@ -695,8 +717,12 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
     uint64_t ms[4], mc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ms[e] = __ballot(sb[e] > thr_sel) & vm[e];
-      mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & vm[e];
+      const int64_t key = base + 4 * lane + e;
+      const uint64_t fm = __ballot(key < z.f_lo || key >= z.f_hi) & vm[e];
+      const uint64_t rk = vm[e] & ~fm & by_score;
+      ms[e] = __ballot(sb[e] > thr_sel) & rk;
+      mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & rk;
+      ms[e] |= fm;
     }
     // even lanes store words 0..3 of the block, odd lanes words 4..7
     const bool odd = lane & 1;
@@ -769,16 +795,17 @@ __device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask, uint3
 // grid: B*Hq blocks of kResThreads.
 __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
     int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
-    int Hq, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ counters,
+    int sink, int window, int Hq, const uint32_t* __restrict__ hist,
+    const uint32_t* __restrict__ counters,
     const uint32_t* __restrict__ bitmap, int64_t words, const uint2* __restrict__ cand,
     int32_t* __restrict__ idx) {
   const int bg = blockIdx.x;
   const int b = bg / Hq;
   const int tid = threadIdx.x;
-  int64_t n, k;
-  clamp_nk(n_cap, lens[b], ks[b], k_max, &n, &k);
+  const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
+  const int64_t n = z.n, k = z.k;
   int32_t* out = idx + (int64_t)bg * k_max;
-  if (k == 0) {
+  if (z.total == 0) {
     for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
     return;
   }
@@ -821,9 +848,9 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
   const uint2* lc = in_lds ? lcand : gc;
 
   // the candidates that complete the top-k
-  uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C
+  uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C when k > 0
   uint32_t vmask = 0u, vval = 0u, imax = 0xFFFFFFFFu;
-  if (need < C) {
+  if (k > 0 && need < C) {
     uint32_t ties = 0u;
     for (int shift = 14; shift >= 0; shift -= 7) {
       const Pick pk = radix_pick<false>(lc, C, vmask, vval, 0u, 0u, shift, need, h128, &shpick);
@@ -914,7 +941,7 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
     written += seg_total;
     __syncthreads();
   }
-  for (int64_t t = (int64_t)k + tid; t < k_max; t += kResThreads) out[t] = -1;
+  for (int64_t t = z.total + tid; t < k_max; t += kResThreads) out[t] = -1;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -932,7 +959,8 @@ static int device_cus() {
 }
 
 template <int G, int TL, bool WIDE>
-static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, const ScoreWs& ws,
+static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, SinkWindow sw,
+                          const ScoreWs& ws,
                           const uint8_t* ids, const float* vnorm, const int32_t* lens,
                           float* scores, hipStream_t s) {
   // one block per CU: the 64-key groups of every KV row are split evenly
@@ -944,27 +972,27 @@ static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, const Sc
   nblk = (ng + gpb - 1) / gpb;
   const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
   scorer_kernel<G, TL, WIDE><<<(unsigned)grid, kScoreThreads, 0, s>>>(
-      ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, P, n_cap, (int)rows, (int)nblk, (int)gpb, scores,
-      ws.hist);
+      ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, P, n_cap, sw.sink, sw.window, (int)rows,
+      (int)nblk, (int)gpb, scores, ws.hist);
 }
 
 template <int G>
-static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap,
+static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap, SinkWindow sw,
                             const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
                             const int32_t* lens, float* scores, hipStream_t s) {
   if (P > 8) {  // two-byte IDs, L <= 64
     switch (ids_tables_per_word(L)) {
-      case 1: launch_scorer<G, 1, true>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-      case 2: launch_scorer<G, 2, true>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-      default: launch_scorer<G, 4, true>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+      case 1: launch_scorer<G, 1, true>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+      case 2: launch_scorer<G, 2, true>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+      default: launch_scorer<G, 4, true>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
     }
     return;
   }
   switch (ids_tables_per_word(L)) {
-    case 1: launch_scorer<G, 1, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer<G, 2, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    case 4: launch_scorer<G, 4, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer<G, 8, false>(B, Hkv, Hq, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    case 1: launch_scorer<G, 1, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer<G, 2, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    case 4: launch_scorer<G, 4, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer<G, 8, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
   }
 }
 
@@ -996,28 +1024,30 @@ hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, 
 }
 
 hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,
-                        const float* vnorm, const int32_t* lens, int64_t n_cap, float* scores,
+                        const float* vnorm, const int32_t* lens, int64_t n_cap, SinkWindow sw,
+                        float* scores,
                         const ScoreWs& ws, hipStream_t s) {
   switch (Hq / Hkv) {
-    case 1: launch_scorer_g<1>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer_g<2>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer_g<4>(B, Hkv, Hq, L, P, n_cap, ws, ids, vnorm, lens, scores, s); break;
+    case 1: launch_scorer_g<1>(B, Hkv, Hq, L, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer_g<2>(B, Hkv, Hq, L, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer_g<4>(B, Hkv, Hq, L, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
-                       const int32_t* ks, int k_max, int32_t* idx, const ScoreWs& ws,
+                       const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx, const ScoreWs& ws,
                        hipStream_t s) {
   const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
   const int64_t nscan = (int64_t)B * Hq * CH;
   topk_scan_kernel<<<(unsigned)((nscan + kXcds - 1) / kXcds * kXcds), kScanThreads, 0, s>>>(
-      scores, n_cap, score_stride(n_cap), lens, ks, k_max, Hq, CH, B * Hq, ws.hist, ws.counters,
-      ws.bitmap, ws.words, ws.cand);
+      scores, n_cap, score_stride(n_cap), lens, ks, k_max, sw.sink, sw.window, Hq, CH, B * Hq,
+      ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_resolve_kernel<<<(unsigned)(B * Hq), kResThreads, 0, s>>>(
-      n_cap, lens, ks, k_max, Hq, ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand, idx);
+      n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, ws.hist, ws.counters, ws.bitmap, ws.words,
+      ws.cand, idx);
   return hipGetLastError();
 }
 

@@ -55,14 +55,15 @@ def gpu_hash(w, d, pos0=None, count=None, ids=None, vnorm=None):
     return ids, vnorm
 
 
-def gpu_score_topk(w, d, ids, vnorm, lens=None, ks=None, k_max=None, q=None):
+def gpu_score_topk(w, d, ids, vnorm, lens=None, ks=None, k_max=None, q=None, sink=0, window=0):
     lens = d["lens"] if lens is None else lens
     ks = d["ks"] if ks is None else ks
-    k_max = w.k_max if k_max is None else k_max
+    k_max = w.k_max + sink + window if k_max is None else k_max
     q = d["q"] if q is None else q
     idx = torch.full((w.B, w.Hq, k_max), -7, dtype=torch.int32, device=DEV)
     scores = torch.zeros(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=DEV)
-    S.socket_score_topk(q, d["W"], ids, vnorm, lens, ks, k_max, w.tau, w.L, w.P, idx, scores)
+    S.socket_score_topk(q, d["W"], ids, vnorm, lens, ks, k_max, w.tau, w.L, w.P, idx, scores,
+                        sink=sink, window=window)
     return idx, scores
 
 
@@ -145,6 +146,39 @@ def check_exact_topk(idx_row, s_gpu_row, k, n):
     got = idx_row[:k]
     assert got.tolist() == ref.tolist()
     assert (idx_row[k:] == -1).all()
+
+
+def forced_keys(n, sink, window):
+    return sorted(set(range(min(sink, n))) | set(range(max(n - window, 0), n)))
+
+
+def check_exact_select(idx_row, s_gpu_row, k, n, sink, window):
+    """Sink + window + top-k of the rest, on the GPU's own float32 scores: exact."""
+    ref = SO.select(s_gpu_row[:n].astype(np.float64), k, n, sink, window)
+    got = idx_row[:len(ref)]
+    assert got.tolist() == ref.tolist()
+    assert (idx_row[len(ref):] == -1).all()
+    return len(ref)
+
+
+def check_select_set(sel_gpu, s_ref, k, n, sink, window):
+    """Against the oracle's scores: the forced keys exactly, the top-k part up to
+    keys whose score is within SET_BAND of the k-th one among the rest."""
+    sel = [int(i) for i in sel_gpu if i >= 0]
+    forced = forced_keys(n, sink, window)
+    ref = SO.select(s_ref, k, n, sink, window)
+    assert len(sel) == len(ref) == len(set(sel))
+    assert set(forced) <= set(sel)
+    rest = np.array([i for i in range(n) if i not in set(forced)], dtype=np.int64)
+    kk = min(k, len(rest))
+    if kk == 0:
+        assert sorted(sel) == forced
+        return 0
+    kth = float(np.sort(s_ref[rest])[::-1][kk - 1])
+    diff = set(sel) ^ set(ref.tolist())
+    for i in diff:
+        assert abs(s_ref[i] - kth) <= SET_BAND * abs(kth) + SCORE_ATOL, (i, s_ref[i], kth)
+    return len(diff)
 
 
 def check_out(out_gpu, q, K, V, idx, scale):

@@ -74,8 +74,8 @@ def _score(**kw):
     B, Hq, n_cap, L, P, k_max = 1, 32, 1024, 64, 8, 32
     need = S.socket_score_topk_workspace(B, Hq, 8, n_cap, L, P, k_max)
     args = dict(q=FAKE, dtype=1, B=B, Hq=Hq, Hkv=8, d=128, W=FAKE, L=L, P=P, tau=0.5, ids=FAKE,
-                vnorm=FAKE, lens=FAKE, n_cap=n_cap, ks=FAKE, k_max=k_max, idx=FAKE, scores=None,
-                ws=FAKE, ws_bytes=need, stream=None)
+                vnorm=FAKE, lens=FAKE, n_cap=n_cap, ks=FAKE, k_max=k_max, sink=0, window=0, idx=FAKE,
+                scores=None, ws=FAKE, ws_bytes=need, stream=None)
     args.update(kw)
     return S.lib().socket_score_topk(*args.values())
 
@@ -94,6 +94,9 @@ def test_score_argument_checks():
     assert _score(k_max=0) == EINVAL
     assert _score(ws=FAKE + 8) == EINVAL  # misaligned workspace
     assert _score(ws_bytes=1024) == ENOSPC
+    assert _score(sink=-1) == EINVAL
+    assert _score(window=-4) == EINVAL
+    assert _score(sink=20, window=13) == EINVAL   # the forced keys alone overflow k_max = 32
 
 
 def _decode(**kw):
@@ -132,14 +135,18 @@ def test_stage_argument_checks():
     assert lib.socket_soft_tables(FAKE, 1, 1, 32, 8, 128, FAKE, 64, 8, -1.0, 1024, FAKE, need, None) == EINVAL
     assert lib.socket_soft_tables(FAKE, 1, 1, 32, 8, 64, FAKE, 64, 8, 0.5, 1024, FAKE, need, None) == EUNSUP
     assert lib.socket_soft_tables(FAKE, 1, 1, 32, 8, 128, FAKE, 64, 8, 0.5, 1024, FAKE, 64, None) == ENOSPC
-    # socket_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, scores, ws, ws_bytes, stream)
-    assert lib.socket_score(1, 32, 8, 64, 8, None, FAKE, FAKE, 1024, FAKE, FAKE, need, None) == EINVAL
-    assert lib.socket_score(1, 32, 5, 64, 8, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, need, None) == EINVAL
-    assert lib.socket_score(1, 32, 8, 64, 8, FAKE, FAKE, FAKE, 1024, FAKE, None, need, None) == EINVAL
-    # socket_topk(B, Hq, Hkv, L, scores, lens, n_cap, ks, k_max, idx, ws, ws_bytes, stream)
-    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 0, FAKE, FAKE, need, None) == EINVAL
-    assert lib.socket_topk(1, 32, 8, 64, FAKE, None, 1024, FAKE, 32, FAKE, FAKE, need, None) == EINVAL
-    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 32, FAKE, FAKE, 16, None) == ENOSPC
+    # socket_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sink, window, scores, ws,
+    #              ws_bytes, stream)
+    assert lib.socket_score(1, 32, 8, 64, 8, None, FAKE, FAKE, 1024, 0, 0, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_score(1, 32, 5, 64, 8, FAKE, FAKE, FAKE, 1024, 0, 0, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_score(1, 32, 8, 64, 8, FAKE, FAKE, FAKE, 1024, 0, 0, FAKE, None, need, None) == EINVAL
+    assert lib.socket_score(1, 32, 8, 64, 8, FAKE, FAKE, FAKE, 1024, -1, 0, FAKE, FAKE, need, None) == EINVAL
+    # socket_topk(B, Hq, Hkv, L, scores, lens, n_cap, ks, k_max, sink, window, idx, ws,
+    #             ws_bytes, stream)
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 0, 0, 0, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, None, 1024, FAKE, 32, 0, 0, FAKE, FAKE, need, None) == EINVAL
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 32, 0, 0, FAKE, FAKE, 16, None) == ENOSPC
+    assert lib.socket_topk(1, 32, 8, 64, FAKE, FAKE, 1024, FAKE, 32, 16, 17, FAKE, FAKE, need, None) == EINVAL
 
 
 @pytest.mark.parametrize("L,P", [(3, 8), (16, 8), (20, 8), (32, 8), (60, 8), (64, 8), (100, 8),

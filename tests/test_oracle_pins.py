@@ -43,7 +43,7 @@ def impl(**over):
     """The oracle as a namespace, optionally with functions replaced."""
     ns = types.SimpleNamespace(
         hash_keys=SO.hash_keys, value_norms=SO.value_norms, soft_tables=SO.soft_tables,
-        scores=SO.scores, topk=SO.topk, sparse_attention=SO.sparse_attention)
+        scores=SO.scores, topk=SO.topk, select=SO.select, sparse_attention=SO.sparse_attention)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -208,6 +208,27 @@ def check_topk_ties_and_sort(so):
     assert x[sel].min() >= x[rest].max()
 
 
+def check_select_sink_window(so):
+    """Selection with always-attended sink and local-window keys (Sec. 6 setup)
+    against k-fold arg max loops, plus the cases it reduces to."""
+    rng = np.random.default_rng(9)
+    for trial in range(200):
+        n = int(rng.integers(0, 40))
+        k = int(rng.integers(0, 12))
+        sink, window = int(rng.integers(0, 8)), int(rng.integers(0, 8))
+        s = rng.integers(0, 6, size=n).astype(float)     # many equal scores
+        sel = so.select(s, k, n, sink, window)
+        assert sel.tolist() == brute.select(s.tolist(), k, sink, window), (n, k, sink, window)
+        assert len(sel) == min(n, k + sink + window)
+        assert len(set(sel.tolist())) == len(sel)
+    s = np.array([3.0, 5.0, 5.0, 1.0, 5.0, 2.0, 3.0, 4.0])
+    assert so.select(s, 3, None, 0, 0).tolist() == so.topk(s, 3).tolist()
+    assert so.select(s, 0, None, 2, 1).tolist() == [0, 1, 7]       # k = 0: forced keys only
+    assert so.select(s, 2, None, 2, 1).tolist() == [0, 1, 2, 4, 7]  # 5, 5 of the rest; tie -> 2, 4
+    assert so.select(s, 1, 6, 1, 2).tolist() == [0, 1, 4, 5]        # only the first n keys count
+    assert so.select(s, 3, None, 5, 5).tolist() == list(range(8))   # sink + window cover all
+
+
 def check_attention_library(so):
     """k = n equals dense softmax attention (torch SDPA, float64 CPU); k = 1 returns v[argmax]."""
     import torch
@@ -231,7 +252,7 @@ def check_attention_library(so):
 ALL_CHECKS = [check_golden_hash, check_golden_soft_table, check_golden_score_topk,
               check_golden_attention, check_tables_sum_to_one, check_product_of_sigmoids,
               check_tau_to_zero, check_tau_to_inf_and_p1, check_brute_force,
-              check_topk_ties_and_sort, check_attention_library]
+              check_topk_ties_and_sort, check_select_sink_window, check_attention_library]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -326,6 +347,24 @@ def _topk_high_index(s, k, n=None):   # ties -> higher index
     return np.sort((n - 1 - order)[:k])
 
 
+def _select_budget_shared(s, k, n=None, sink=0, window=0):   # top-k over all keys, then union
+    s = np.asarray(s, float)
+    n = len(s) if n is None else n
+    forced = set(range(min(sink, n))) | set(range(max(n - window, 0), n))
+    return np.array(sorted(forced | set(SO.topk(s, k, n).tolist())), dtype=np.int64)
+
+
+def _select_window_shift(s, k, n=None, sink=0, window=0):    # window one key too early
+    s = np.asarray(s, float)
+    n = len(s) if n is None else n
+    forced = np.zeros(n, bool)
+    forced[:min(sink, n)] = True
+    forced[max(n - window - 1, 0):max(n - 1, 0)] = True
+    rest = np.nonzero(~forced)[0]
+    picked = rest[np.argsort(-s[:n][rest], kind="stable")[:k]]
+    return np.sort(np.concatenate([np.nonzero(forced)[0], picked]))
+
+
 def _attn_no_scale(q, K, V, idx, scale):
     return SO.sparse_attention(q, K, V, idx, 1.0)
 
@@ -343,6 +382,8 @@ MUTANTS = {
     "scores_no_norm": dict(scores=_scores_no_norm),
     "scores_mean": dict(scores=_scores_mean),
     "topk_high_index": dict(topk=_topk_high_index),
+    "select_budget_shared": dict(select=_select_budget_shared),
+    "select_window_shift": dict(select=_select_window_shift),
     "attn_no_scale": dict(sparse_attention=_attn_no_scale),
     "attn_transposed": dict(sparse_attention=_attn_transposed),
 }

@@ -170,6 +170,49 @@ def test_score_topk_parity(case):
             GC.check_set(idx[b, g], s_ref[b, g, :n], k)
 
 
+SINK_WINDOW_CASES = [
+    dict(case=dict(name="c2", n=5000), sink=64, window=128),
+    dict(case=dict(name="c2", n=4500, Hq=8, Hkv=8, L=60, P=10), sink=128, window=64),
+    dict(case=dict(name="c2", n=20000, k=300), sink=64, window=64),    # several scan workgroups
+    dict(case=dict(name="c4", n=(1000, 9000), B=4, k=0.02), sink=64, window=128),
+    dict(case=dict(name="c4", n=(10, 20), B=5, Hq=8, Hkv=2, lens=[0, 50, 191, 192, 700],
+                   n_cap=1000, k=5), sink=64, window=128),        # n <= sink + window, n = 0
+    dict(case=dict(name="c2", n=3000, Hq=8, Hkv=2, k=0), sink=7, window=33),  # k = 0: forced only
+    dict(case=dict(name="c2", n=3000, Hq=8, Hkv=2), sink=0, window=100),
+    dict(case=dict(name="c2", n=3000, Hq=8, Hkv=2), sink=100, window=0),
+]
+
+
+@pytest.mark.parametrize("sw", SINK_WINDOW_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c["case"].items())
+                         + f"-s{c['sink']}-w{c['window']}")
+def test_select_sink_window_parity(sw):
+    """Sink and window keys always selected, top-k over the rest, then attention."""
+    print("case", sw, flush=True)
+    w = make_workload(**sw["case"])
+    sink, window = sw["sink"], sw["window"]
+    d = GC.upload(w)
+    ids_np, vn_np = _oracle_ids(w)
+    ids = GC.ids_dev(ids_np, w.n_cap, w.P)
+    vn = torch.from_numpy(vn_np).to(DEV)
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn, sink=sink, window=window)
+    out = GC.gpu_decode(w, d, idx)
+    sync()
+    idx, sc, out = idx.cpu().numpy(), sc.cpu().numpy(), out.cpu().numpy()
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    s_ref = SO.scores(tables, ids_np, vn_np.astype(np.float64), w.lens)
+    group = w.Hq // w.Hkv
+    for b in range(w.B):
+        n, k = int(w.lens[b]), int(w.ks[b])
+        for g in range(w.Hq):
+            GC.check_scores(sc[b, g, :n], s_ref[b, g, :n])
+            GC.check_exact_select(idx[b, g], sc[b, g], k, n, sink, window)
+            GC.check_select_set(idx[b, g], s_ref[b, g, :n], k, n, sink, window)
+            if g % 3 == 0:
+                GC.check_out(out[b, g], w.q[b, g], w.K[b, g // group], w.V[b, g // group],
+                             idx[b, g], w.scale)
+
+
 def test_topk_ties_lower_index_wins():
     """All keys of a head share one bucket pattern and norm -> equal scores."""
     w = make_workload("c2", n=3000, Hq=8, Hkv=2, k=100)
@@ -275,6 +318,27 @@ def test_e2e_c2_full():
     _e2e(workload("c2"))
 
 
+def test_e2e_c2_sink_window_full():
+    """The 32K GQA step with 64 sink and 128 window keys next to the top-656."""
+    w = workload("c2")
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn, sink=64, window=128)
+    out = GC.gpu_decode(w, d, idx)
+    sync()
+    ids = GC.ids_np(ids, w.L, w.n_cap, w.P)
+    vn, idx, sc, out = (t.cpu().numpy() for t in (vn, idx, sc, out))
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    n, k, group = int(w.lens[0]), int(w.ks[0]), w.Hq // w.Hkv
+    for g in range(w.Hq):
+        h = g // group
+        s_ref = GC.ref_scores(tables[0, g], ids[0, h, :n], SO.value_norms(w.V[0, h, :n]))
+        GC.check_scores(sc[0, g, :n], s_ref)
+        assert GC.check_exact_select(idx[0, g], sc[0, g], k, n, 64, 128) == k + 192
+        GC.check_select_set(idx[0, g], s_ref, k, n, 64, 128)
+        GC.check_out(out[0, g], w.q[0, g], w.K[0, h], w.V[0, h], idx[0, g], w.scale)
+
+
 def test_e2e_c2_p10_l60_full():
     """The 32K GQA step at 10 planes x 60 tables (600 bits per key)."""
     _e2e(workload("c2", L=60, P=10))
@@ -366,3 +430,15 @@ def test_stage_entry_points_match_fused_call():
     sync()
     assert torch.equal(sc1, sc2)
     assert torch.equal(idx1, idx2)
+    # and with sink and window keys
+    idx3, sc3 = GC.gpu_score_topk(w, d, ids, vn, sink=64, window=128)
+    ws = S.alloc_workspace(S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P,
+                                                         idx3.shape[-1]), DEV)
+    sc4 = torch.zeros_like(sc3)
+    idx4 = torch.full_like(idx3, -7)
+    S.socket_soft_tables(d["q"], d["W"], w.Hkv, w.L, w.P, w.tau, w.n_cap, ws)
+    S.socket_score(ids, vn, d["lens"], w.Hq, w.L, w.P, sc4, ws, sink=64, window=128)
+    S.socket_topk(sc4, d["lens"], d["ks"], w.Hkv, w.L, w.n_cap, idx4, ws, sink=64, window=128)
+    sync()
+    assert torch.equal(sc3, sc4)
+    assert torch.equal(idx3, idx4)
