@@ -108,6 +108,10 @@ class Case:
         self.sws_p = self.sws.data_ptr() + (-self.sws.data_ptr()) % 256
         self.dws_p = self.dws.data_ptr() + (-self.dws.data_ptr()) % 256
         self.sws_n, self.dws_n = sws, dws
+        xws = S.socket_dense_decode_workspace(w.B, w.Hq, w.Hkv, w.d, w.n_cap)
+        self.xws = S.alloc_workspace(xws, dev)
+        self.xws_p = self.xws.data_ptr() + (-self.xws.data_ptr()) % 256
+        self.xws_n = xws
         self.replicas = replicas
         self.lib = lib
         self.stream = torch.cuda.current_stream().cuda_stream
@@ -119,6 +123,7 @@ class Case:
         st = vp(self.stream)
         self.c_append, self.c_prefill, self.c_score, self.c_decode, self.c_score_topk = \
             [], [], [], [], []
+        self.c_dense = []
         for r in range(self.replicas):
             K, V, ids, vn = self.K[r].data_ptr(), self.V[r].data_ptr(), self.ids[r].data_ptr(), \
                 self.vn[r].data_ptr()
@@ -142,6 +147,10 @@ class Case:
                                   i64(w.n_cap), vp(self.idx.data_ptr()), self.k_max,
                                   ctypes.c_float(w.scale), vp(self.out.data_ptr()),
                                   vp(self.dws_p), ctypes.c_size_t(self.dws_n), st))
+            self.c_dense.append((vp(self.q.data_ptr()), vp(K), vp(V), 1, w.B, w.Hq, w.Hkv, w.d,
+                                 i64(w.n_cap), vp(self.lens.data_ptr()), ctypes.c_float(w.scale),
+                                 vp(self.out.data_ptr()), vp(self.xws_p),
+                                 ctypes.c_size_t(self.xws_n), st))
         self.c_tables = (vp(self.q.data_ptr()), 1, w.B, w.Hq, w.Hkv, w.d, vp(self.W.data_ptr()), w.L,
                          w.P, ctypes.c_float(w.tau), i64(w.n_cap), vp(self.sws_p),
                          ctypes.c_size_t(self.sws_n), st)
@@ -248,6 +257,18 @@ def scorer_launch_us(case, torch, launches):
     us, _ = gpu_batch_us(torch, lambda i: lib.socket_score(*case.c_score[i % case.replicas]),
                          launches)
     return us
+
+
+def dense_decode(case, torch, launches):
+    """The dense reference: full attention over all n + 1 keys of every query
+    head, back to back on the replicas (cold caches), as GPU us per call and
+    the HBM rate of its K and V reads."""
+    lib = case.lib
+    us, _ = gpu_batch_us(torch, lambda i: case._ok(lib.socket_dense_decode(
+        *case.c_dense[i % case.replicas]), "socket_dense_decode"), launches)
+    w = case.w
+    kv_bytes = w.B * w.Hkv * (case.n + 1) * 2 * w.d * 2
+    return dict(us=us, kv_gbs=kv_bytes / (us * 1e-6) / 1e9)
 
 
 def prefill_rate(case, torch, reps=5):
@@ -375,6 +396,9 @@ def main():
         f"host enqueue {host_step_us:.1f} us/step")
     score_us = scorer_launch_us(case, torch, 4 * case.replicas)
     log(f"[bench] 32K scorer launch {score_us:.2f} us")
+    dense32 = dense_decode(case, torch, 2 * case.replicas)
+    dense32["socket_speedup"] = dense32["us"] / gpu_step_us
+    log(f"[bench] 32K dense decode {dense32}")
     launch_bytes, kv_keys = scorer_bytes(case)
     achieved = launch_bytes / (score_us * 1e-6) / 1e9
     traffic = counters_traffic(launch_bytes)
@@ -384,7 +408,7 @@ def main():
         step_us_wall=sec * 1e6, step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
         stage_us=stages, scorer_launch_us=score_us,
         score_topk_us=stages["tables"] + stages["score"] + stages["topk"],
-        prefill=pre32)
+        prefill=pre32, dense_decode=dense32)
     case.free()
     del case
     torch.cuda.empty_cache()
@@ -401,11 +425,13 @@ def main():
         st3, gpu3, host3 = per_stage(c3, torch, max(20, args.steps // 4))
         sc3 = scorer_launch_us(c3, torch, 4 * c3.replicas)
         lb3, _ = scorer_bytes(c3)
+        dense128 = dense_decode(c3, torch, 4 * c3.replicas)
+        dense128["socket_speedup"] = dense128["us"] / gpu3
         extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, stage_us=st3,
                         scorer_launch_us=sc3,
                         keys_per_s=c3.w.B * c3.w.Hq * (c3.n + 1) / sec3,
                         scorer_gbs=lb3 / (sc3 * 1e-6) / 1e9,
-                        prefill=pre128)
+                        prefill=pre128, dense_decode=dense128)
         log(f"[bench] 128K: {extra128}")
         c3.free()
         del c3

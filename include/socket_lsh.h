@@ -194,6 +194,65 @@ int socket_sparse_decode(const void* q, const void* K, const void* V, int dtype,
                          int Hkv, int d, int64_t n_cap, const int32_t* idx, int k_max,
                          float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Hard-LSH comparison mode -- the estimator SOCKET is compared with (SOCKET
+ * Sec. 3.1, Sec. 5.3; Appendix A.2, Table 9: best at P = 2 with L = 300 or
+ * 500 tables): the score of key i is
+ *   s_i = vnorm[b][h][i] * #{ l : ID_l(K_i) == ID_l(q) },
+ * IDs as in socket_hash_keys, the query's IDs from the same float32
+ * projections.  P must divide 32 (1, 2, 4, 8 or 16) and L*P <= 4096.
+ *
+ * Codes: the L*P sign bits of a key, bit p = l*P + j = [<W[p], K_i> > 0],
+ * 32 bits per word (bit p in word p/32 at bit p%32), cw = ceil(L*P/32)
+ * words, stored word-major as uint32 codes[B][Hkv][cw][n_cap]; bits at or
+ * past L*P are 0.  socket_codes_bytes() gives the size (0 if unsupported).
+ */
+size_t socket_codes_bytes(int B, int Hkv, int64_t n_cap, int L, int P);
+
+/* Hashing for the hard mode: like socket_hash_keys (same projections,
+ * positions and value norms), writing codes instead of tiled IDs. */
+int socket_hash_codes(const void* K, const void* V, int dtype, int B, int Hkv, int d,
+                      int64_t n_cap, const int32_t* pos0, int count, const void* W, int L, int P,
+                      uint32_t* codes, float* vnorm, void* stream);
+
+/* Workspace bytes needed by socket_hard_score_topk (0 if unsupported). */
+size_t socket_hard_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
+                                        int k_max);
+
+/*
+ * socket_hard_score_topk -- hard collision-count scores of every key and the
+ * selection of socket_score_topk (sink and window keys, then the top-k of
+ * the rest, ties to the lower index, ascending, padded with -1) from them.
+ * Arguments as in socket_score_topk with codes in place of ids; ws must hold
+ * socket_hard_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max) bytes,
+ * 256-byte aligned.
+ */
+int socket_hard_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                           int L, int P, const uint32_t* codes, const float* vnorm,
+                           const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max,
+                           int sink, int window, int32_t* idx, float* scores, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by socket_dense_decode for these sizes (0 if unsupported). */
+size_t socket_dense_decode_workspace(int B, int Hq, int Hkv, int d, int64_t n_cap);
+
+/*
+ * socket_dense_decode -- full softmax attention of each decode query over
+ * every key of its sequence: the dense (FlashAttention-style) reference point
+ * against which the SOCKET paper quotes its decode speedups (Sec. 1,
+ * contributions; Sec. 6), computed at the same shapes as the sparse path.
+ *   out[b][g] = sum_{i < lens[b]} a_i V_i,
+ *   a_i = exp(scale * <q, K_i>) / sum_{i' < lens[b]} exp(scale * <q, K_i'>)
+ * with K, V of KV head g / (Hq/Hkv), Hq / Hkv in {1, 2, 4}.  Accumulation is
+ * float32.  lens is a device int32 array [B], 0 <= lens[b] <= n_cap; an
+ * empty sequence produces zeros.  ws must hold
+ * socket_dense_decode_workspace(B, Hq, Hkv, d, n_cap) bytes, 256-byte aligned;
+ * its contents need not be initialised.
+ */
+int socket_dense_decode(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
+                        int Hkv, int d, int64_t n_cap, const int32_t* lens, float scale,
+                        float* out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,15 @@ _SIGS = {
     "socket_sparse_decode_workspace": (_sz, [_i, _i, _i, _i]),
     "socket_sparse_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i64, _vp, _i, _f, _vp, _vp,
                                   _sz, _vp]),
+    "socket_dense_decode_workspace": (_sz, [_i, _i, _i, _i, _i64]),
+    "socket_codes_bytes": (_sz, [_i, _i, _i64, _i, _i]),
+    "socket_hash_codes": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp,
+                               _vp]),
+    "socket_hard_score_topk_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
+    "socket_hard_score_topk": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _i64,
+                                    _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "socket_dense_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i64, _vp, _f, _vp, _vp, _sz,
+                                 _vp]),
 }
 
 _lib = None
@@ -244,3 +253,83 @@ def socket_sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx:
         Hkv, d, n_cap, _dev(idx, "idx", torch.int32, (B, Hq, k_max)), k_max, float(scale),
         _dev(out, "out", torch.float32, (B, Hq, d)), wptr, wbytes, _stream(q, stream))
     _check("socket_sparse_decode", rc)
+
+
+def socket_dense_decode_workspace(B: int, Hq: int, Hkv: int, d: int, n_cap: int) -> int:
+    return int(lib().socket_dense_decode_workspace(B, Hq, Hkv, d, n_cap))
+
+
+def socket_dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lens: torch.Tensor,
+                        scale: float, out: torch.Tensor, ws: torch.Tensor | None = None,
+                        stream=None) -> None:
+    """Full attention of q over keys [0, lens[b]) of its KV head (the dense reference)."""
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = K.shape
+    need = socket_dense_decode_workspace(B, Hq, Hkv, d, n_cap)
+    if ws is None:
+        ws = alloc_workspace(need, q.device)
+    wptr, wbytes = _ws_ptr(ws, need)
+    rc = lib().socket_dense_decode(
+        _dev(q, "q"), _dev(K, "K", q.dtype), _dev(V, "V", q.dtype, K.shape), _dtype_code(q), B, Hq,
+        Hkv, d, n_cap, _dev(lens, "lens", torch.int32, (B,)), float(scale),
+        _dev(out, "out", torch.float32, (B, Hq, d)), wptr, wbytes, _stream(q, stream))
+    _check("socket_dense_decode", rc)
+
+
+# ----------------------------------------------------------------------------- hard-LSH mode
+
+def codes_words(L: int, P: int) -> int:
+    return (L * P + 31) // 32
+
+
+def socket_codes_bytes(B: int, Hkv: int, n_cap: int, L: int, P: int) -> int:
+    return int(lib().socket_codes_bytes(B, Hkv, n_cap, L, P))
+
+
+def alloc_codes(B: int, Hkv: int, n_cap: int, L: int, P: int, device) -> torch.Tensor:
+    """A zeroed code cache for the hard-LSH mode: int32 [B, Hkv, words, n_cap]."""
+    t = torch.zeros(B, Hkv, codes_words(L, P), n_cap, dtype=torch.int32, device=device)
+    assert t.numel() * 4 == socket_codes_bytes(B, Hkv, n_cap, L, P)
+    return t
+
+
+def socket_hash_codes(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, codes: torch.Tensor,
+                      vnorm: torch.Tensor, pos0: torch.Tensor, count: int, L: int, P: int,
+                      stream=None) -> None:
+    """Sign codes of rows [pos0[b], pos0[b]+count) of K, and ||V|| into vnorm."""
+    B, Hkv, n_cap, d = K.shape
+    rc = lib().socket_hash_codes(
+        _dev(K, "K"), _dev(V, "V", K.dtype, K.shape), _dtype_code(K), B, Hkv, d, n_cap,
+        _dev(pos0, "pos0", torch.int32, (B,)), int(count), _dev(W, "W", K.dtype, (L * P, d)),
+        L, P, _dev(codes, "codes", torch.int32, (B, Hkv, codes_words(L, P), n_cap)),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _stream(K, stream))
+    _check("socket_hash_codes", rc)
+
+
+def socket_hard_score_topk_workspace(B: int, Hq: int, Hkv: int, n_cap: int, L: int, P: int,
+                                     k_max: int) -> int:
+    return int(lib().socket_hard_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max))
+
+
+def socket_hard_score_topk(q: torch.Tensor, W: torch.Tensor, codes: torch.Tensor,
+                           vnorm: torch.Tensor, lens: torch.Tensor, ks: torch.Tensor, k_max: int,
+                           L: int, P: int, idx: torch.Tensor, scores: torch.Tensor | None = None,
+                           ws: torch.Tensor | None = None, stream=None, sink: int = 0,
+                           window: int = 0) -> None:
+    """Hard collision-count scores and the selected indices per query head."""
+    B, Hq, d = q.shape
+    Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
+    need = socket_hard_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
+    if ws is None:
+        ws = alloc_workspace(need, q.device)
+    wptr, wbytes = _ws_ptr(ws, need)
+    sptr = None if scores is None else _dev(scores, "scores", torch.float32,
+                                            (B, Hq, score_stride(n_cap)))
+    rc = lib().socket_hard_score_topk(
+        _dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P,
+        _dev(codes, "codes", torch.int32, (B, Hkv, codes_words(L, P), n_cap)),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
+        _dev(lens, "lens", torch.int32, (B,)), n_cap, _dev(ks, "ks", torch.int32, (B,)),
+        int(k_max), int(sink), int(window), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr,
+        wptr, wbytes, _stream(q, stream))
+    _check("socket_hard_score_topk", rc)

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsocket_lsh.so")
-SOURCES = ["api.hip", "hash.hip", "score_topk.hip", "sparse_decode.hip"]
+SOURCES = ["api.hip", "hash.hip", "score_topk.hip", "sparse_decode.hip", "dense_decode.hip",
+           "hard_lsh.hip"]
 ARCH = "gfx950"
 
 

@@ -11,6 +11,7 @@ namespace {
 constexpr int kMaxL = 128;       // 16 ID words of at most 8 tables each
 constexpr int kMaxScoreL = 128;
 constexpr int kMaxKmax = 1 << 16;  // 1024 attention splits of 64 keys
+constexpr int kMaxCodeBits = 4096;  // hard-LSH mode: L * P
 
 // Table shapes with an ID layout: one-byte IDs (P <= 8) for up to 128
 // tables, two-byte IDs (P = 9 or 10) for up to 64.
@@ -183,6 +184,94 @@ int socket_sparse_decode(const void* q, const void* K, const void* V, int dtype,
   if (ws_bytes < need) return SOCKET_ENOSPC;
   return from_hip(launch_sparse_decode(q, K, V, dtype, B, Hq, Hkv, n_cap, idx, k_max, scale, out,
                                        w, static_cast<hipStream_t>(stream)));
+}
+
+// Hard-LSH comparison mode: P divides 32 (no table straddles a code word).
+static bool hard_ok(int L, int P) {
+  return L >= 1 && (P == 1 || P == 2 || P == 4 || P == 8 || P == 16) && L * P <= kMaxCodeBits;
+}
+
+size_t socket_codes_bytes(int B, int Hkv, int64_t n_cap, int L, int P) {
+  if (B <= 0 || Hkv <= 0 || n_cap <= 0 || !hard_ok(L, P)) return 0;
+  return (size_t)B * Hkv * codes_words(L, P) * n_cap * sizeof(uint32_t);
+}
+
+int socket_hash_codes(const void* K, const void* V, int dtype, int B, int Hkv, int d,
+                      int64_t n_cap, const int32_t* pos0, int count, const void* W, int L, int P,
+                      uint32_t* codes, float* vnorm, void* stream) {
+  if (!K || !V || !pos0 || !W || !codes || !vnorm) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (B <= 0 || Hkv <= 0 || n_cap <= 0 || count < 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
+  if (d != kHead || !hard_ok(L, P)) return SOCKET_EUNSUPPORTED;
+  if (n_cap >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
+  const int64_t blocks = (int64_t)B * Hkv * count * ((L * P + 63) / 64);
+  if (blocks >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
+  if (count == 0) return SOCKET_OK;
+  return from_hip(launch_hash_codes(K, V, dtype, B, Hkv, n_cap, pos0, count, W, L, P, codes,
+                                    vnorm, static_cast<hipStream_t>(stream)));
+}
+
+size_t socket_hard_score_topk_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
+                                        int k_max) {
+  (void)k_max;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || !hard_ok(L, P) || !group_ok(Hq, Hkv) ||
+      n_cap >= ((int64_t)1 << 31))
+    return 0;
+  return select_ws_layout((size_t)B * Hq * codes_words(L, P) * sizeof(uint32_t), B, Hq, n_cap,
+                          nullptr, nullptr);
+}
+
+int socket_hard_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                           int L, int P, const uint32_t* codes, const float* vnorm,
+                           const int32_t* lens, int64_t n_cap, const int32_t* ks, int k_max,
+                           int sink, int window, int32_t* idx, float* scores, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!q || !W || !codes || !vnorm || !lens || !ks || !idx || !ws) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
+  if (Hq % Hkv) return SOCKET_EINVAL;
+  if (k_max <= 0 || !sink_window_ok(sink, window, k_max)) return SOCKET_EINVAL;
+  if (d != kHead || k_max > kMaxKmax || !group_ok(Hq, Hkv) || !hard_ok(L, P))
+    return SOCKET_EUNSUPPORTED;
+  if (n_cap >= ((int64_t)1 << 31) || (int64_t)B * Hq * n_cap >= ((int64_t)1 << 40))
+    return SOCKET_EUNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return SOCKET_EINVAL;
+  ScoreWs w;
+  const size_t need = select_ws_layout((size_t)B * Hq * codes_words(L, P) * sizeof(uint32_t), B,
+                                       Hq, n_cap, &w, ws);
+  if (ws_bytes < need) return SOCKET_ENOSPC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sc = scores ? scores : w.scores;
+  const SinkWindow sw{sink, window};
+  hipError_t e = launch_hard_score(q, dtype, B, Hq, Hkv, W, L, P, codes, vnorm, lens, n_cap, sw,
+                                   sc, w, s);
+  if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s);
+  return from_hip(e);
+}
+
+size_t socket_dense_decode_workspace(int B, int Hq, int Hkv, int d, int64_t n_cap) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d != kHead || n_cap <= 0 ||
+      n_cap >= ((int64_t)1 << 31))
+    return 0;
+  return dense_ws_layout(B, Hq, Hkv, n_cap, nullptr, nullptr);
+}
+
+int socket_dense_decode(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
+                        int Hkv, int d, int64_t n_cap, const int32_t* lens, float scale,
+                        float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !lens || !out || !ws) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_cap <= 0) return SOCKET_EINVAL;
+  if (Hq % Hkv) return SOCKET_EINVAL;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return SOCKET_EINVAL;
+  if (d != kHead || !group_ok(Hq, Hkv)) return SOCKET_EUNSUPPORTED;
+  if (n_cap >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return SOCKET_EINVAL;
+  DenseWs w;
+  const size_t need = dense_ws_layout(B, Hq, Hkv, n_cap, &w, ws);
+  if (ws_bytes < need) return SOCKET_ENOSPC;
+  return from_hip(launch_dense_decode(q, K, V, dtype, B, Hq, Hkv, n_cap, lens, scale, out, w,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

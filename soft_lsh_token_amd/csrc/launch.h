@@ -11,7 +11,8 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
                             int P, uint8_t* ids, float* vnorm, hipStream_t s);
 
 struct ScoreWs {
-  float* img;           // [B*Hkv][img_floats]  LDS images of the soft tables
+  float* img;           // [B*Hkv][img_floats]  LDS images of the soft tables (soft mode)
+  uint32_t* qcodes;     // [B*Hq][words per code]  query codes (hard mode; same region)
   int img_floats;
   uint32_t* hist;       // [B*Hq][kHistBins]
   uint32_t* counters;   // [B*Hq]  candidates gathered by the top-k scan
@@ -22,6 +23,11 @@ struct ScoreWs {
 };
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base);
+
+// The selection workspace behind a first region of first_bytes (table images
+// or query codes): histograms, counters, bitmaps, candidates, scores.
+size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreWs* ws,
+                        void* base);
 
 // Algorithm 2, part 1: the soft tables of every query head, written as the
 // scorer's LDS images; clears the selection histograms and counters.
@@ -46,6 +52,19 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
                        const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx,
                        const ScoreWs& ws, hipStream_t s);
 
+// Hard-LSH comparison mode: packed sign codes of the L*P planes per key,
+// stored word-major: codes[(b*Hkv + h) * words + w][n_cap].
+int codes_words(int L, int P);  // 32-bit words per code: ceil(L*P / 32)
+
+hipError_t launch_hash_codes(const void* K, const void* V, int dtype, int B, int Hkv,
+                             int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
+                             int P, uint32_t* codes, float* vnorm, hipStream_t s);
+
+hipError_t launch_hard_score(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
+                             int L, int P, const uint32_t* codes, const float* vnorm,
+                             const int32_t* lens, int64_t n_cap, SinkWindow sw, float* scores,
+                             const ScoreWs& ws, hipStream_t s);
+
 struct DecodeWs {
   float* part;          // [B*Hq][splits][kHead + 2]
   int splits;
@@ -56,5 +75,22 @@ size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base);
 hipError_t launch_sparse_decode(const void* q, const void* K, const void* V, int dtype, int B,
                                 int Hq, int Hkv, int64_t n_cap, const int32_t* idx, int k_max,
                                 float scale, float* out, const DecodeWs& ws, hipStream_t s);
+
+// Merge per-split partials [heads][splits][kHead + 2] (o, m, l) into out.
+hipError_t launch_decode_combine(const float* part, int heads, int splits, float* out,
+                                 hipStream_t s);
+
+struct DenseWs {
+  float* part;          // [B*Hq][splits][kHead + 2]
+  int splits, chunk;    // splits of `chunk` keys each
+};
+
+size_t dense_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, DenseWs* ws, void* base);
+
+// Full attention over keys [0, lens[b]) of every query head (GQA groups of
+// 1, 2 or 4 query heads per KV head).
+hipError_t launch_dense_decode(const void* q, const void* K, const void* V, int dtype, int B,
+                               int Hq, int Hkv, int64_t n_cap, const int32_t* lens, float scale,
+                               float* out, const DenseWs& ws, hipStream_t s);
 
 }  // namespace socketlsh

@@ -134,12 +134,20 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kScanKeys = 8192;  // keys per top-k scan workgroup (the bitmap covers whole ones)
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
-  const size_t heads = (size_t)B * Hq;
   const int G = Hq / Hkv;
   const int img_floats = image_stride(G == 1 || G == 2 ? G : 4, L);
+  const size_t n = select_ws_layout((size_t)B * Hkv * img_floats * sizeof(float), B, Hq, n_cap,
+                                    ws, base);
+  if (ws) ws->img_floats = img_floats;
+  return n;
+}
+
+size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreWs* ws,
+                        void* base) {
+  const size_t heads = (size_t)B * Hq;
   const int64_t words = (n_cap + kScanKeys - 1) / kScanKeys * (kScanKeys / 32);
   size_t off = 0;
-  const size_t o_img = off; off = align256(off + (size_t)B * Hkv * img_floats * sizeof(float));
+  const size_t o_img = off; off = align256(off + first_bytes);
   const size_t o_hist = off; off = align256(off + heads * kHistBins * sizeof(uint32_t));
   const size_t o_cnt = off; off = align256(off + heads * sizeof(uint32_t));
   const size_t o_bm = off; off = align256(off + heads * words * sizeof(uint32_t));
@@ -148,7 +156,8 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
   if (ws) {
     char* p = static_cast<char*>(base);
     ws->img = reinterpret_cast<float*>(p + o_img);
-    ws->img_floats = img_floats;
+    ws->qcodes = reinterpret_cast<uint32_t*>(p + o_img);
+    ws->img_floats = 0;
     ws->hist = reinterpret_cast<uint32_t*>(p + o_hist);
     ws->counters = reinterpret_cast<uint32_t*>(p + o_cnt);
     ws->bitmap = reinterpret_cast<uint32_t*>(p + o_bm);
@@ -339,7 +348,6 @@ __device__ __forceinline__ uint32_t word_cell(uint2 w) {
   else return ((M < 2 ? w.x : w.y) >> (16 * (M & 1))) & 0xFFFFu;
 }
 
-constexpr int kXcds = 8;      // workgroup i of a dispatch runs on XCD i mod 8
 constexpr int kPrefetch = 1;  // 64-key groups of IDs each wave keeps in flight
 
 // The lookups of one round: NF full-table slots and NS lo/hi half slots.
@@ -697,6 +705,7 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   const uint32_t thr_sel = bd.d1 < (uint32_t)(kHistBins - 1) ? ((bd.d1 + 1) << kHistShift) - 1u
                                                             : 0xFFFFFFFFu;
   const uint64_t by_score = k > 0 ? ~0ull : 0ull;
+  const bool any_forced = z.f_lo > 0 || z.f_hi < n;  // uniform
   uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint64_t lt = lanemask_lt64();
   // candidates gather in LDS; one global reservation per workgroup at the end
@@ -718,7 +727,7 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t key = base + 4 * lane + e;
-      const uint64_t fm = __ballot(key < z.f_lo || key >= z.f_hi) & vm[e];
+      const uint64_t fm = any_forced ? __ballot(key < z.f_lo || key >= z.f_hi) & vm[e] : 0ull;
       const uint64_t rk = vm[e] & ~fm & by_score;
       ms[e] = __ballot(sb[e] > thr_sel) & rk;
       mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & rk;

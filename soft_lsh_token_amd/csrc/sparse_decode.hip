@@ -215,7 +215,13 @@ hipError_t launch_sparse_decode(const void* q, const void* K, const void* V, int
         Hq, Hkv, n_cap, idx, k_max, scale, ws.splits, ws.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<<<heads, kHead, 0, s>>>(ws.part, ws.splits, out);
+  return launch_decode_combine(ws.part, heads, ws.splits, out, s);
+}
+
+hipError_t launch_decode_combine(const float* part, int heads, int splits, float* out,
+                                 hipStream_t s) {
+  if (splits > kMaxSplits) return hipErrorInvalidValue;
+  decode_combine_kernel<<<heads, kHead, 0, s>>>(part, splits, out);
   return hipGetLastError();
 }
 

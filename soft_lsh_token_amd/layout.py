@@ -76,3 +76,17 @@ def pack(ids: np.ndarray, n_cap: int | None = None, P: int = 8) -> np.ndarray:
     out = np.zeros((B, Hkv, G, 64 * 16 * WB), dtype=np.uint8)
     out[:, :, :, _perm(L, P).reshape(64, -1)] = full
     return out
+
+
+def codes_to_ids(codes: np.ndarray, L: int, P: int, n: int | None = None) -> np.ndarray:
+    """Hard-mode codes [B, Hkv, words, n_cap] (any 32-bit integer dtype) ->
+    [B, Hkv, n, L] bucket IDs: bit j of table l's ID is code bit l*P + j."""
+    c = np.asarray(codes).astype(np.uint32)
+    B, Hkv, nw, n_cap = c.shape
+    n = n_cap if n is None else n
+    c = c[..., :n]
+    p = np.arange(L * P)
+    bits = (c[:, :, p // 32, :] >> (p % 32)[None, None, :, None].astype(np.uint32)) & 1
+    bits = bits.reshape(B, Hkv, L, P, n).astype(np.int64)
+    ids = (bits << np.arange(P)[None, None, None, :, None]).sum(axis=3)
+    return np.ascontiguousarray(ids.transpose(0, 1, 3, 2))

@@ -99,6 +99,83 @@ def test_score_argument_checks():
     assert _score(sink=20, window=13) == EINVAL   # the forced keys alone overflow k_max = 32
 
 
+def test_dense_decode_argument_checks():
+    lib = S.lib()
+    need = S.socket_dense_decode_workspace(1, 32, 8, 128, 32768)
+    assert need >= 32 * 128 * 130 * 4            # 128 splits of 256 keys, (o, m, l) per head
+    assert S.socket_dense_decode_workspace(1, 32, 8, 64, 32768) == 0
+    assert S.socket_dense_decode_workspace(1, 32, 8, 128, 0) == 0
+    assert S.socket_dense_decode_workspace(1, 32, 5, 128, 100) == 0
+    args = dict(q=FAKE, K=FAKE, V=FAKE, dtype=1, B=1, Hq=32, Hkv=8, d=128, n_cap=32768, lens=FAKE,
+                scale=0.088, out=FAKE, ws=FAKE, ws_bytes=need, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.socket_dense_decode(*a.values())
+    assert call(lens=None) == EINVAL
+    assert call(Hkv=5) == EINVAL
+    assert call(Hkv=4) == EUNSUP               # 8 query heads per KV head
+    assert call(d=96) == EUNSUP
+    assert call(scale=float("nan")) == EINVAL
+    assert call(ws=FAKE + 8) == EINVAL
+    assert call(ws_bytes=need - 1) == ENOSPC
+
+
+def test_hard_mode_argument_checks():
+    lib = S.lib()
+    assert S.socket_codes_bytes(1, 8, 1000, 300, 2) == 8 * 19 * 1000 * 4   # 600 bits -> 19 words
+    assert S.socket_codes_bytes(1, 8, 1000, 500, 2) == 8 * 32 * 1000 * 4
+    assert S.socket_codes_bytes(1, 8, 1000, 100, 3) == 0                   # P must divide 32
+    assert S.socket_codes_bytes(1, 8, 1000, 4097, 1) == 0
+    need = S.socket_hard_score_topk_workspace(1, 32, 8, 1024, 300, 2, 64)
+    assert need > 0
+    assert S.socket_hard_score_topk_workspace(1, 32, 4, 1024, 300, 2, 64) == 0
+    h = dict(K=FAKE, V=FAKE, dtype=1, B=1, Hkv=8, d=128, n_cap=1024, pos0=FAKE, count=16, W=FAKE,
+             L=300, P=2, codes=FAKE, vnorm=FAKE, stream=None)
+
+    def hc(**kw):
+        a = dict(h)
+        a.update(kw)
+        return lib.socket_hash_codes(*a.values())
+    assert hc(codes=None) == EINVAL
+    assert hc(P=3) == EUNSUP
+    assert hc(d=64) == EUNSUP
+    assert hc(count=0) == 0
+    a = dict(q=FAKE, dtype=1, B=1, Hq=32, Hkv=8, d=128, W=FAKE, L=300, P=2, codes=FAKE,
+             vnorm=FAKE, lens=FAKE, n_cap=1024, ks=FAKE, k_max=64, sink=0, window=0, idx=FAKE,
+             scores=None, ws=FAKE, ws_bytes=need, stream=None)
+
+    def hs(**kw):
+        b = dict(a)
+        b.update(kw)
+        return lib.socket_hard_score_topk(*b.values())
+    assert hs(codes=None) == EINVAL
+    assert hs(Hkv=5) == EINVAL
+    assert hs(P=6) == EUNSUP
+    assert hs(sink=40, window=40) == EINVAL
+    assert hs(ws=FAKE + 4) == EINVAL
+    assert hs(ws_bytes=need - 1) == ENOSPC
+
+
+def test_codes_to_ids_bits():
+    """The host view of hard-mode codes: ID bit j of table l is code bit l*P + j."""
+    import numpy as np
+    from soft_lsh_token_amd import layout
+    rng = np.random.default_rng(4)
+    for L, P in ((300, 2), (9, 4), (33, 1), (4, 16)):
+        nw = (L * P + 31) // 32
+        codes = rng.integers(0, 2 ** 32, size=(2, 3, nw, 5), dtype=np.uint64).astype(np.uint32)
+        ids = layout.codes_to_ids(codes.view(np.int32), L, P)
+        assert ids.shape == (2, 3, 5, L)
+        for (b, h, i, l) in [(0, 0, 0, 0), (1, 2, 4, L - 1), (0, 1, 3, L // 2)]:
+            want = 0
+            for j in range(P):
+                p = l * P + j
+                want |= int((int(codes[b, h, p // 32, i]) >> (p % 32)) & 1) << j
+            assert ids[b, h, i, l] == want
+
+
 def _decode(**kw):
     B, Hq, k_max = 1, 32, 64
     need = S.socket_sparse_decode_workspace(B, Hq, 128, k_max)

@@ -43,7 +43,8 @@ def impl(**over):
     """The oracle as a namespace, optionally with functions replaced."""
     ns = types.SimpleNamespace(
         hash_keys=SO.hash_keys, value_norms=SO.value_norms, soft_tables=SO.soft_tables,
-        scores=SO.scores, topk=SO.topk, select=SO.select, sparse_attention=SO.sparse_attention)
+        scores=SO.scores, topk=SO.topk, select=SO.select, sparse_attention=SO.sparse_attention,
+        hard_collision_scores=SO.hard_collision_scores)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -229,6 +230,30 @@ def check_select_sink_window(so):
     assert so.select(s, 3, None, 5, 5).tolist() == list(range(8))   # sink + window cover all
 
 
+def check_hard_scores_brute(so):
+    """Hard-LSH scores (value norm x number of tables where the key shares the
+    query's bucket) against loops over tables, on GQA inputs with ragged lengths."""
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, n, d = 2, 4, 2, 30, 6
+    for L, P in ((7, 2), (3, 4), (12, 1)):
+        W = rng.standard_normal((L * P, d))
+        K = rng.standard_normal((B, Hkv, n, d))
+        V = rng.standard_normal((B, Hkv, n, d))
+        q = rng.standard_normal((B, Hq, d))
+        lens = [30, 19]
+        ids, _ = so.hash_keys(K, W, L, P)
+        s = so.hard_collision_scores(q, W, ids, so.value_norms(V), L, P, lens)
+        for b in range(B):
+            for g in range(Hq):
+                h = g // (Hq // Hkv)
+                qb = [brute.bucket_id(W, q[b, g], l, P) for l in range(L)]
+                for i in range(lens[b]):
+                    hits = sum(brute.bucket_id(W, K[b, h, i], l, P) == qb[l] for l in range(L))
+                    vn = math.sqrt(sum(float(x) * float(x) for x in V[b, h, i]))
+                    assert s[b, g, i] == pytest.approx(vn * hits, rel=1e-12, abs=1e-300)
+                assert np.isnan(s[b, g, lens[b]:]).all()
+
+
 def check_attention_library(so):
     """k = n equals dense softmax attention (torch SDPA, float64 CPU); k = 1 returns v[argmax]."""
     import torch
@@ -252,7 +277,8 @@ def check_attention_library(so):
 ALL_CHECKS = [check_golden_hash, check_golden_soft_table, check_golden_score_topk,
               check_golden_attention, check_tables_sum_to_one, check_product_of_sigmoids,
               check_tau_to_zero, check_tau_to_inf_and_p1, check_brute_force,
-              check_topk_ties_and_sort, check_select_sink_window, check_attention_library]
+              check_topk_ties_and_sort, check_select_sink_window, check_hard_scores_brute,
+              check_attention_library]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -365,6 +391,22 @@ def _select_window_shift(s, k, n=None, sink=0, window=0):    # window one key to
     return np.sort(np.concatenate([np.nonzero(forced)[0], picked]))
 
 
+def _hard_any_plane(q, W, ids, vnorm, L, P, lens=None):   # counts plane agreements, not tables
+    qids, _ = SO.hash_keys(np.asarray(q, float)[..., None, :], W, L, P)
+    qids = qids[..., 0, :]
+    B, Hq = qids.shape[:2]
+    Hkv = ids.shape[1]
+    out = np.empty((B, Hq, ids.shape[2]))
+    for b in range(B):
+        for g in range(Hq):
+            h = g // (Hq // Hkv)
+            same = ~((ids[b, h] ^ qids[b, g][None, :])[..., None] >> np.arange(P) & 1).astype(bool)
+            out[b, g] = np.asarray(vnorm, float)[b, h] * same.sum(axis=(-1, -2))
+            if lens is not None:
+                out[b, g, int(lens[b]):] = np.nan
+    return out
+
+
 def _attn_no_scale(q, K, V, idx, scale):
     return SO.sparse_attention(q, K, V, idx, 1.0)
 
@@ -384,6 +426,7 @@ MUTANTS = {
     "topk_high_index": dict(topk=_topk_high_index),
     "select_budget_shared": dict(select=_select_budget_shared),
     "select_window_shift": dict(select=_select_window_shift),
+    "hard_any_plane": dict(hard_collision_scores=_hard_any_plane),
     "attn_no_scale": dict(sparse_attention=_attn_no_scale),
     "attn_transposed": dict(sparse_attention=_attn_transposed),
 }

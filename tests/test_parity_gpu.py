@@ -273,6 +273,127 @@ def test_sparse_decode_parity(dtype, k_max):
         GC.check_out(out[0, g], w.q[0, g], w.K[0, g // 4], w.V[0, g // 4], idx[0, g], w.scale)
 
 
+# ----------------------------------------------------------------------------- hard-LSH mode
+
+HARD_CASES = [
+    dict(case=dict(name="c2", n=5000, L=300, P=2), sink=0, window=0),
+    dict(case=dict(name="c2", n=3000, L=500, P=2, Hq=16, Hkv=8), sink=0, window=0),
+    dict(case=dict(name="c2", n=3000, L=64, P=1, Hq=8, Hkv=8), sink=0, window=0),
+    dict(case=dict(name="c1", L=100, P=4), sink=0, window=0),              # float32
+    dict(case=dict(name="c2", n=2000, L=64, P=8, Hq=8, Hkv=2), sink=0, window=0),
+    dict(case=dict(name="c2", n=2000, L=8, P=16, Hq=8, Hkv=2), sink=0, window=0),
+    dict(case=dict(name="c4", n=(1000, 9000), B=3, L=300, P=2), sink=64, window=128),
+    dict(case=dict(name="c4", n=(10, 20), B=4, Hq=8, Hkv=2, L=300, P=2, lens=[0, 1, 150, 900],
+                   n_cap=1000, k=5), sink=16, window=16),
+]
+
+
+def _hard_run(w, d, sink, window, heads=None):
+    """Hard mode on the GPU (codes, query codes, scores, selection, attention)
+    against the oracle; IDs are float-decided integers, so the scores are
+    compared on the GPU's key IDs after those are checked against the oracle's."""
+    L, P = w.L, w.P
+    zeros = torch.zeros(w.B, dtype=torch.int32, device=DEV)
+    codes = S.alloc_codes(w.B, w.Hkv, w.n_cap, L, P, DEV)
+    vn = torch.zeros(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+    S.socket_hash_codes(d["K"], d["V"], d["W"], codes, vn, zeros, int(w.lens.max()), L, P)
+    # the query codes through the same projections: each query head as a one-key row
+    q4 = d["q"].reshape(w.B, w.Hq, 1, w.d).contiguous()
+    qc = S.alloc_codes(w.B, w.Hq, 1, L, P, DEV)
+    qv = torch.zeros(w.B, w.Hq, 1, dtype=torch.float32, device=DEV)
+    S.socket_hash_codes(q4, q4, d["W"], qc, qv, zeros, 1, L, P)
+    k_max = w.k_max + sink + window
+    idx = torch.full((w.B, w.Hq, k_max), -7, dtype=torch.int32, device=DEV)
+    sc = torch.zeros(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=DEV)
+    S.socket_hard_score_topk(d["q"], d["W"], codes, vn, d["lens"], d["ks"], k_max, L, P, idx, sc,
+                             sink=sink, window=window)
+    out = GC.gpu_decode(w, d, idx)
+    sync()
+    ids = S.layout.codes_to_ids(codes.cpu().numpy(), L, P)
+    qids = S.layout.codes_to_ids(qc.cpu().numpy(), L, P)[:, :, 0]
+    vn, idx, sc, out = (t.cpu().numpy() for t in (vn, idx, sc, out))
+    group = w.Hq // w.Hkv
+    for b in range(w.B):
+        n = int(w.lens[b])
+        for h in range(w.Hkv):
+            GC.check_ids(ids[b, h], w.K[b, h], w.W, L, P, n)
+            np.testing.assert_allclose(vn[b, h, :n], SO.value_norms(w.V[b, h, :n]), rtol=2e-6)
+    qref, _ = SO.hash_keys(w.q[:, :, None, :], w.W, L, P)
+    assert (qids == qref[:, :, 0]).all(), "a query plane fell inside the float32 band"
+    s_ref = SO.hard_collision_scores(w.q, w.W, ids, vn.astype(np.float64), L, P, w.lens)
+    for b in range(w.B):
+        n, k = int(w.lens[b]), int(w.ks[b])
+        for g in (heads if heads is not None else range(w.Hq)):
+            GC.check_scores(sc[b, g, :n], s_ref[b, g, :n])
+            GC.check_exact_select(idx[b, g], sc[b, g], k, n, sink, window)
+            GC.check_select_set(idx[b, g], s_ref[b, g, :n], k, n, sink, window)
+            if g % 5 == 0:
+                GC.check_out(out[b, g], w.q[b, g], w.K[b, g // group], w.V[b, g // group],
+                             idx[b, g], w.scale)
+
+
+@pytest.mark.parametrize("hc", HARD_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c["case"].items())
+                         + f"-s{c['sink']}-w{c['window']}")
+def test_hard_mode_parity(hc):
+    print("case", hc, flush=True)
+    w = make_workload(**hc["case"])
+    _hard_run(w, GC.upload(w), hc["sink"], hc["window"])
+
+
+def test_hard_mode_c2_full_600_bits():
+    """The 32K GQA step in hard mode at the pages' 600-bit budget (P = 2, L = 300)."""
+    w = workload("c2", L=300, P=2)
+    _hard_run(w, GC.upload(w), 0, 0)
+
+
+# ----------------------------------------------------------------------------- dense reference
+
+DENSE_CASES = [
+    dict(name="c2", n=5000),                                    # ragged last split
+    dict(name="c2", n=4500, Hq=8, Hkv=8),                       # one query head per KV head
+    dict(name="c2", n=4500, Hq=16, Hkv=8),                      # two
+    dict(name="c1"),                                            # float32
+    dict(name="c4", n=(10, 20), B=5, Hq=8, Hkv=2, lens=[0, 1, 17, 256, 3000], n_cap=3001),
+    dict(name="c4", n=(1000, 9000), B=3),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_dense_decode_parity(case):
+    """Full attention over every key of the sequence against the oracle."""
+    print("case", case, flush=True)
+    w = make_workload(**case)
+    d = GC.upload(w)
+    out = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device=DEV)
+    S.socket_dense_decode(d["q"], d["K"], d["V"], d["lens"], w.scale, out)
+    sync()
+    out = out.cpu().numpy()
+    group = w.Hq // w.Hkv
+    for b in range(w.B):
+        n = int(w.lens[b])
+        for g in range(w.Hq):
+            h = g // group
+            GC.check_out(out[b, g], w.q[b, g], w.K[b, h], w.V[b, h], np.arange(n, dtype=np.int64),
+                         w.scale)
+
+
+@pytest.mark.parametrize("name,heads", [("c2", range(32)), ("c3", [0, 7, 13, 31])])
+def test_dense_decode_full_size(name, heads):
+    """The dense reference at the 32K and 128K GQA shapes (sampled heads at 128K)."""
+    w = workload(name)
+    d = GC.upload(w)
+    out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=DEV)
+    S.socket_dense_decode(d["q"], d["K"], d["V"], d["lens"], w.scale, out)
+    sync()
+    out = out.cpu().numpy()
+    n, group = int(w.lens[0]), w.Hq // w.Hkv
+    for g in heads:
+        h = g // group
+        GC.check_out(out[0, g], w.q[0, g], w.K[0, h], w.V[0, h], np.arange(n, dtype=np.int64),
+                     w.scale)
+
+
 # ----------------------------------------------------------------------------- end to end
 
 def _e2e(w, heads=None):
