@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=40)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-128k", action="store_true")
+    p.add_argument("--no-hard", action="store_true",
+                   help="skip the hard-LSH comparison mode")
     p.add_argument("--no-p10", action="store_true",
                    help="skip the 10-plane, 60-table measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -271,6 +273,41 @@ def dense_decode(case, torch, launches):
     return dict(us=us, kv_gbs=kv_bytes / (us * 1e-6) / 1e9)
 
 
+def hard_mode(lib, torch, S, L, P, replicas):
+    """Hard-LSH comparison mode at the 32K GQA shape: GPU us per
+    socket_hard_score_topk call (query codes, collision-count scores, top-k),
+    back to back on `replicas` copies of the code cache."""
+    from soft_lsh_token_amd.inputs import make_workload
+    w = make_workload("c2", steps=1, L=L, P=P)
+    dev, bf = "cuda:0", torch.bfloat16
+    n = int(w.lens[0])
+    K = torch.from_numpy(w.K).to(dev).to(bf)
+    V = torch.from_numpy(w.V).to(dev).to(bf)
+    Wt = torch.from_numpy(w.W).to(dev).to(bf)
+    q = torch.from_numpy(w.q).to(dev).to(bf)
+    codes = S.alloc_codes(w.B, w.Hkv, w.n_cap, L, P, dev)
+    vn = torch.zeros(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
+    S.socket_hash_codes(K, V, Wt, codes, vn, torch.zeros(w.B, dtype=torch.int32, device=dev),
+                        n + 1, L, P)
+    del K, V
+    reps = [codes] + [codes.clone() for _ in range(replicas - 1)]
+    lens = torch.full((w.B,), n + 1, dtype=torch.int32, device=dev)
+    ks = torch.from_numpy(w.ks).to(dev)
+    k = int(w.ks[0])
+    idx = torch.empty(w.B, w.Hq, k, dtype=torch.int32, device=dev)
+    sc = torch.empty(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=dev)
+    ws = S.alloc_workspace(S.socket_hard_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, L, P, k),
+                           dev)
+    for r in range(replicas):
+        S.socket_hard_score_topk(q, Wt, reps[r], vn, lens, ks, k, L, P, idx, sc, ws)
+    torch.cuda.synchronize()
+    us, _ = gpu_batch_us(torch, lambda i: S.socket_hard_score_topk(
+        q, Wt, reps[i % replicas], vn, lens, ks, k, L, P, idx, sc, ws), 4 * replicas)
+    code_bytes = w.B * w.Hkv * (n + 1) * (4 * S.codes_words(L, P) + 4)
+    return dict(L=L, P=P, bits_per_key=L * P, score_topk_us=us,
+                code_gbs=code_bytes / (us * 1e-6) / 1e9)
+
+
 def prefill_rate(case, torch, reps=5):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     case.prefill(0)
@@ -436,6 +473,15 @@ def main():
         c3.free()
         del c3
         torch.cuda.empty_cache()
+
+    hard = None
+    if not args.no_hard:
+        hard = [hard_mode(lib, torch, S, L, 2, 16) for L in (300, 500)]
+        for h in hard:
+            h["soft_score_topk_us"] = extra32["score_topk_us"]
+        log(f"[bench] 32K hard-LSH mode: {hard}")
+        torch.cuda.empty_cache()
+    extra32["hard_lsh"] = hard
 
     extra_p10 = None
     if not args.no_p10:
