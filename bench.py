@@ -273,6 +273,29 @@ def dense_decode(case, torch, launches):
     return dict(us=us, kv_gbs=kv_bytes / (us * 1e-6) / 1e9)
 
 
+def sample_estimate(case, torch, S, M=1024):
+    """The value-aware sampling estimator at the case's shape: GPU us per
+    socket_sample_estimate call (tables, scores + soft-count sums, M draws per
+    head and the mean of the drawn unit value rows)."""
+    from soft_lsh_token_amd.inputs import uniforms
+    w = case.w
+    dev = "cuda:0"
+    u = torch.from_numpy(uniforms(w.B, w.Hq, M, 0)).to(dev)
+    out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+    sc = torch.empty(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=dev)
+    ws = S.alloc_workspace(S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, 1),
+                           dev)
+
+    def run(i):
+        r = i % case.replicas
+        S.socket_sample_estimate(case.q, case.W, case.ids[r], case.vn[r], case.V[r], case.lens, u,
+                                 w.tau, w.L, w.P, out, None, sc, ws)
+    run(0)
+    torch.cuda.synchronize()
+    us, _ = gpu_batch_us(torch, run, 2 * case.replicas)
+    return dict(draws_per_head=M, us=us)
+
+
 def hard_mode(lib, torch, S, L, P, replicas):
     """Hard-LSH comparison mode at the 32K GQA shape: GPU us per
     socket_hard_score_topk call (query codes, collision-count scores, top-k),
@@ -436,6 +459,8 @@ def main():
     dense32 = dense_decode(case, torch, 2 * case.replicas)
     dense32["socket_speedup"] = dense32["us"] / gpu_step_us
     log(f"[bench] 32K dense decode {dense32}")
+    est32 = sample_estimate(case, torch, S)
+    log(f"[bench] 32K sampling estimator {est32}")
     launch_bytes, kv_keys = scorer_bytes(case)
     achieved = launch_bytes / (score_us * 1e-6) / 1e9
     traffic = counters_traffic(launch_bytes)
@@ -445,7 +470,7 @@ def main():
         step_us_wall=sec * 1e6, step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
         stage_us=stages, scorer_launch_us=score_us,
         score_topk_us=stages["tables"] + stages["score"] + stages["topk"],
-        prefill=pre32, dense_decode=dense32)
+        prefill=pre32, dense_decode=dense32, sampling_estimator=est32)
     case.free()
     del case
     torch.cuda.empty_cache()

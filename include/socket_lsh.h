@@ -195,6 +195,27 @@ int socket_sparse_decode(const void* q, const void* K, const void* V, int dtype,
                          float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * socket_sample_estimate -- the value-aware sampling estimator T(q) of the
+ * SOCKET analysis (Sec. 5.1, Theorem 3; Appendix B.2), an unbiased Monte
+ * Carlo estimate of the soft-attention output y(q) = sum_j a~_j v_j:
+ *   s~_j = sum_l p_l(ID_l(K_j)), a~_j = s~_j / sum_i s~_i   (i, j < lens[b])
+ *   p_j  = a~_j ||v_j|| / S_1,  S_1 = sum_j a~_j ||v_j||
+ *   J_m  = the first j whose running sum of s_j exceeds u[b][g][m] * sum_i s_i
+ *          (s_j = vnorm_j * s~_j, the score of socket_score_topk; so J_m ~ p)
+ *   out[b][g] = (S_1 / M) * sum_{m < M} V_{J_m} / vnorm_{J_m}
+ * The M uniforms u (device float32 [B][Hq][M], values in [0, 1)) are
+ * inputs; draws (device int32 [B][Hq][M], may be NULL) receives J_m.  A head
+ * with no key of positive score gives zeros (and draws of -1).  Arguments
+ * otherwise as in socket_score_topk (same workspace size, tables and IDs);
+ * V is the value cache [B][Hkv][n_cap][d]; 1 <= M <= 8192.
+ */
+int socket_sample_estimate(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                           int L, int P, float tau, const uint8_t* ids, const float* vnorm,
+                           const void* V, const int32_t* lens, int64_t n_cap, const float* u,
+                           int M, float* out, int32_t* draws, float* scores, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * Hard-LSH comparison mode -- the estimator SOCKET is compared with (SOCKET
  * Sec. 3.1, Sec. 5.3; Appendix A.2, Table 9: best at P = 2 with L = 300 or
  * 500 tables): the score of key i is

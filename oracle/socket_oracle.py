@@ -49,7 +49,8 @@ import numpy as np
 
 __all__ = [
     "hash_keys", "value_norms", "projections", "soft_tables", "scores", "topk", "select",
-    "sparse_attention", "decode_step", "hard_collision_scores",
+    "sparse_attention", "decode_step", "hard_collision_scores", "soft_counts",
+    "sampling_distribution", "soft_attention", "inverse_cdf", "sample_estimate",
 ]
 
 
@@ -195,6 +196,58 @@ def sparse_attention(q, K, V, idx, scale: float):
     a = np.exp(logits)
     a = a / a.sum()
     return a @ Vs
+
+
+def soft_counts(tables_row, ids_rows):
+    """L-table soft count of each key, s~_j = sum_l p_l(b_l(j) | q) (App. B.2).
+
+    tables_row: [L, 2^P] of one query head; ids_rows: [n, L].  Returns [n].
+    """
+    t = _f64(tables_row)
+    L = t.shape[0]
+    return t[np.arange(L)[None, :], np.asarray(ids_rows, dtype=np.int64)].sum(axis=-1)
+
+
+def sampling_distribution(tables_row, ids_rows, vnorm_row):
+    """Value-aware sampling law of the estimator T(q) (Sec. 5.1; App. B.2):
+    a~_j = s~_j / sum_i s~_i (soft attention weights) and
+    p_j = a~_j ||v_j|| / S_1 with S_1 = sum_j a~_j ||v_j||.
+    Returns (p [n], S_1, a~ [n])."""
+    sc = soft_counts(tables_row, ids_rows)
+    a = sc / sc.sum()
+    wv = a * _f64(vnorm_row)
+    S1 = wv.sum()
+    return (wv / S1 if S1 > 0 else wv), S1, a
+
+
+def soft_attention(tables_row, ids_rows, V_rows):
+    """The soft-attention output y_{tau,L}(q) = sum_j a~_j v_j (App. B.2)."""
+    _, _, a = sampling_distribution(tables_row, ids_rows, value_norms(V_rows))
+    return a @ _f64(V_rows)
+
+
+def inverse_cdf(p, u) -> np.ndarray:
+    """Index drawn from the law p by the uniform u in [0, 1): the first j whose
+    cumulative mass exceeds u (keys without mass are never drawn)."""
+    cdf = np.cumsum(_f64(p))
+    J = np.searchsorted(cdf, np.asarray(u, dtype=np.float64) * cdf[-1], side="right")
+    last = int(np.nonzero(_f64(p) > 0)[0][-1])
+    return np.minimum(J, last)
+
+
+def sample_estimate(tables_row, ids_rows, V_rows, u):
+    """The value-aware sampling estimator of Theorem 3 (Sec. 5.1, App. B.2):
+    M draws J_m ~ p (value-aware law above), X_m = a~_J v_J / p_J =
+    S_1 v_J / ||v_J||, T(q) = (1/M) sum_m X_m.  The draws come from the given
+    uniforms u [M].  Returns (T [d], J [M])."""
+    V = _f64(V_rows)
+    vn = value_norms(V)
+    p, S1, _ = sampling_distribution(tables_row, ids_rows, vn)
+    if S1 <= 0:
+        return np.zeros(V.shape[-1]), np.zeros(len(u), dtype=np.int64)
+    J = inverse_cdf(p, u)
+    X = S1 * V[J] / vn[J][:, None]
+    return X.mean(axis=0), J
 
 
 def decode_step(w, q=None, lens=None, ks=None, K=None, V=None, ids=None, vnorm=None,

@@ -39,6 +39,8 @@ _SIGS = {
                                   _sz, _vp]),
     "socket_dense_decode_workspace": (_sz, [_i, _i, _i, _i, _i64]),
     "socket_codes_bytes": (_sz, [_i, _i, _i64, _i, _i]),
+    "socket_sample_estimate": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _vp,
+                                    _i64, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "socket_hash_codes": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp,
                                _vp]),
     "socket_hard_score_topk_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
@@ -333,3 +335,32 @@ def socket_hard_score_topk(q: torch.Tensor, W: torch.Tensor, codes: torch.Tensor
         int(k_max), int(sink), int(window), _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr,
         wptr, wbytes, _stream(q, stream))
     _check("socket_hard_score_topk", rc)
+
+
+# ----------------------------------------------------------------------------- sampling estimator
+
+def socket_sample_estimate(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
+                           vnorm: torch.Tensor, V: torch.Tensor, lens: torch.Tensor,
+                           u: torch.Tensor, tau: float, L: int, P: int, out: torch.Tensor,
+                           draws: torch.Tensor | None = None, scores: torch.Tensor | None = None,
+                           ws: torch.Tensor | None = None, stream=None) -> None:
+    """Value-aware sampling estimate T(q) of the soft-attention output, from the
+    uniforms u [B, Hq, M]; the drawn key indices go to draws when given."""
+    B, Hq, d = q.shape
+    Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
+    M = u.shape[-1]
+    need = socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, 1)
+    if ws is None:
+        ws = alloc_workspace(need, q.device)
+    wptr, wbytes = _ws_ptr(ws, need)
+    dptr = None if draws is None else _dev(draws, "draws", torch.int32, (B, Hq, M))
+    sptr = None if scores is None else _dev(scores, "scores", torch.float32,
+                                            (B, Hq, score_stride(n_cap)))
+    rc = lib().socket_sample_estimate(
+        _dev(q, "q"), _dtype_code(q), B, Hq, Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P,
+        float(tau), _ids(ids, B, Hkv, n_cap, L, P),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
+        _dev(V, "V", q.dtype, (B, Hkv, n_cap, d)), _dev(lens, "lens", torch.int32, (B,)), n_cap,
+        _dev(u, "u", torch.float32, (B, Hq, M)), M, _dev(out, "out", torch.float32, (B, Hq, d)),
+        dptr, sptr, wptr, wbytes, _stream(q, stream))
+    _check("socket_sample_estimate", rc)

@@ -12,6 +12,7 @@ constexpr int kMaxL = 128;       // 16 ID words of at most 8 tables each
 constexpr int kMaxScoreL = 128;
 constexpr int kMaxKmax = 1 << 16;  // 1024 attention splits of 64 keys
 constexpr int kMaxCodeBits = 4096;  // hard-LSH mode: L * P
+constexpr int kMaxDraws = 8192;     // sampling estimator: draws per query head
 
 // Table shapes with an ID layout: one-byte IDs (P <= 8) for up to 128
 // tables, two-byte IDs (P = 9 or 10) for up to 64.
@@ -122,7 +123,8 @@ int socket_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids, const
   ScoreWs w;
   if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
   return from_hip(launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, SinkWindow{sink, window},
-                               scores ? scores : w.scores, w, static_cast<hipStream_t>(stream)));
+                               scores ? scores : w.scores, false, w,
+                               static_cast<hipStream_t>(stream)));
 }
 
 int socket_topk(int B, int Hq, int Hkv, int L, const float* scores, const int32_t* lens,
@@ -158,7 +160,8 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
   float* sc = scores ? scores : w.scores;
   hipError_t e = launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w, s);
   const SinkWindow sw{sink, window};
-  if (e == hipSuccess) e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sw, sc, w, s);
+  if (e == hipSuccess)
+    e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sw, sc, false, w, s);
   if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s);
   return from_hip(e);
 }
@@ -246,6 +249,30 @@ int socket_hard_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int
   hipError_t e = launch_hard_score(q, dtype, B, Hq, Hkv, W, L, P, codes, vnorm, lens, n_cap, sw,
                                    sc, w, s);
   if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s);
+  return from_hip(e);
+}
+
+int socket_sample_estimate(const void* q, int dtype, int B, int Hq, int Hkv, int d, const void* W,
+                           int L, int P, float tau, const uint8_t* ids, const float* vnorm,
+                           const void* V, const int32_t* lens, int64_t n_cap, const float* u,
+                           int M, float* out, int32_t* draws, float* scores, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!q || !W || !ids || !vnorm || !V || !lens || !u || !out || !ws) return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (M <= 0) return SOCKET_EINVAL;
+  if (!(tau > 0.f) || !(tau < INFINITY)) return SOCKET_EINVAL;
+  int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
+  if (rc) return rc;
+  if (d != kHead || M > kMaxDraws) return SOCKET_EUNSUPPORTED;
+  ScoreWs w;
+  if ((rc = score_ws(B, Hq, Hkv, n_cap, L, ws, ws_bytes, &w))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sc = scores ? scores : w.scores;
+  hipError_t e = launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w, s);
+  if (e == hipSuccess)
+    e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, SinkWindow{0, 0}, sc, true, w, s);
+  if (e == hipSuccess)
+    e = launch_estimate(sc, vnorm, V, dtype, B, Hq, Hkv, lens, n_cap, u, M, out, draws, w, s);
   return from_hip(e);
 }
 

@@ -19,6 +19,7 @@ struct ScoreWs {
   uint32_t* bitmap;     // [B*Hq][words]  selection bitmap, words = ceil(n_cap/8192)*256
   uint2* cand;          // [B*Hq][n_cap]  top-k candidates (score bits, key)
   float* scores;        // [B*Hq][ns]  when the caller passes no score buffer
+  float* usum;          // [B*Hq]  sums of the soft counts (sampling estimator)
   int64_t words;
 };
 
@@ -44,7 +45,14 @@ struct SinkWindow {
 // the keys that compete for the top-k.
 hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,
                         const float* vnorm, const int32_t* lens, int64_t n_cap, SinkWindow sw,
-                        float* scores, const ScoreWs& ws, hipStream_t s);
+                        float* scores, bool soft_sums, const ScoreWs& ws, hipStream_t s);
+
+// The value-aware sampling estimator T(q) from the scores and soft-count sums
+// left in the workspace by launch_score(..., soft_sums = true).
+hipError_t launch_estimate(const float* scores, const float* vnorm, const void* V, int dtype,
+                           int B, int Hq, int Hkv, const int32_t* lens, int64_t n_cap,
+                           const float* u, int M, float* out, int32_t* draws, const ScoreWs& ws,
+                           hipStream_t s);
 
 // Algorithm 3: top-k selection from the scores and their histogram, united
 // with the sink and window keys.

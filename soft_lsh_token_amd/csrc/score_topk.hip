@@ -153,6 +153,7 @@ size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreW
   const size_t o_bm = off; off = align256(off + heads * words * sizeof(uint32_t));
   const size_t o_cand = off; off = align256(off + heads * (size_t)n_cap * sizeof(uint2));
   const size_t o_sc = off; off = align256(off + heads * (size_t)score_stride(n_cap) * sizeof(float));
+  const size_t o_us = off; off = align256(off + heads * sizeof(float));
   if (ws) {
     char* p = static_cast<char*>(base);
     ws->img = reinterpret_cast<float*>(p + o_img);
@@ -163,6 +164,7 @@ size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreW
     ws->bitmap = reinterpret_cast<uint32_t*>(p + o_bm);
     ws->cand = reinterpret_cast<uint2*>(p + o_cand);
     ws->scores = reinterpret_cast<float*>(p + o_sc);
+    ws->usum = reinterpret_cast<float*>(p + o_us);
     ws->words = words;
   }
   return off;
@@ -183,13 +185,13 @@ __device__ __forceinline__ void store_slot(float* dst, const float* v) {
 // j*TL .. j*TL+TL-1 (the tables of scorer lane j) for the G query heads of KV
 // row bh and writes their image slots whole (one slot = the G heads' values
 // of one entry).  It also clears a 1/16 share of those heads' histograms
-// (block j = 0: their candidate counters).
+// (block j = 0: their candidate counters and soft-count sums).
 // Tables l >= L (padding of the last lane word) get all-zero entries.
 template <typename T, int G>
 __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
     int TL, int NF, int NS, int HE, int FULL, int img_floats, float* __restrict__ img,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters) {
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters, float* __restrict__ usum) {
   const int bh = blockIdx.x >> 4, j = blockIdx.x & 15;
   const int b = bh / Hkv, h = bh % Hkv;
   const int bg0 = b * Hq + h * G;
@@ -202,7 +204,10 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   constexpr int kHistShare = G * kHistBins / 16;
   for (int i = tid; i < kHistShare; i += kTabThreads)
     hist[(int64_t)bg0 * kHistBins + j * kHistShare + i] = 0u;
-  if (j == 0 && tid < G) counters[bg0 + tid] = 0u;
+  if (j == 0 && tid < G) {
+    counters[bg0 + tid] = 0u;
+    usum[bg0 + tid] = 0.f;
+  }
   for (int i = tid; i < G * kHead; i += kTabThreads) {
     const int64_t src = (int64_t)(bg0 + i / kHead) * kHead + i % kHead;
     if constexpr (sizeof(T) == 2) qf[i / kHead][i % kHead] = __uint_as_float((uint32_t)q[src] << 16);
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     const float* __restrict__ img, int img_floats, const uint8_t* __restrict__ ids,
     const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
     int64_t n_cap, int sink, int window, int rows, int nblk, int gpb, float* __restrict__ scores,
-    uint32_t* __restrict__ hist) {
+    uint32_t* __restrict__ hist, float* __restrict__ usum) {
   using Sh = ImageShape<G, TL, WIDE>;
   constexpr int NF = Sh::NF, NS = Sh::NS, HE = Sh::HE;
   constexpr int C = WIDE ? 2 : 1;  // bytes per ID
@@ -519,6 +524,9 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   }
   __syncthreads();
 
+  float us[G];  // this lane's soft counts (before the value norm), summed when usum is set
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) us[gg] = 0.f;
   bool more = gi < g_end;
   while (more) {
 #pragma unroll
@@ -539,7 +547,10 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
         }
         if (valid) {
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) scores[(int64_t)(bg0 + gg) * sst + key] = vb[s] * u[0][gg];
+          for (int gg = 0; gg < G; ++gg) {
+            scores[(int64_t)(bg0 + gg) * sst + key] = vb[s] * u[0][gg];
+            us[gg] += u[0][gg];
+          }
         }
         gi += kScoreWaves;
         more = gi < g_end;
@@ -550,6 +561,22 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   for (int i = tid; i < G * kHistBins; i += kScoreThreads) {
     const uint32_t v = lhist[i];
     if (v) atomicAdd(&hist[(int64_t)(bg0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
+  }
+  if (usum) {  // per-head sums of the soft counts, for the sampling estimator
+    __syncthreads();  // the merge above has read the histogram: reuse its LDS
+    float* red = reinterpret_cast<float*>(lhist);  // [kScoreWaves][G]
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float t = wave_sum(us[gg]);
+      if (lane == 0) red[wave * G + gg] = t;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < kScoreWaves; ++w) t += red[w * G + tid];
+      atomicAdd(&usum[bg0 + tid], t);
+    }
   }
 }
 
@@ -969,7 +996,7 @@ static int device_cus() {
 
 template <int G, int TL, bool WIDE>
 static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, SinkWindow sw,
-                          const ScoreWs& ws,
+                          float* usum, const ScoreWs& ws,
                           const uint8_t* ids, const float* vnorm, const int32_t* lens,
                           float* scores, hipStream_t s) {
   // one block per CU: the 64-key groups of every KV row are split evenly
@@ -982,26 +1009,27 @@ static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, SinkWind
   const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
   scorer_kernel<G, TL, WIDE><<<(unsigned)grid, kScoreThreads, 0, s>>>(
       ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, P, n_cap, sw.sink, sw.window, (int)rows,
-      (int)nblk, (int)gpb, scores, ws.hist);
+      (int)nblk, (int)gpb, scores, ws.hist, usum);
 }
 
 template <int G>
 static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap, SinkWindow sw,
+                            float* usum,
                             const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
                             const int32_t* lens, float* scores, hipStream_t s) {
   if (P > 8) {  // two-byte IDs, L <= 64
     switch (ids_tables_per_word(L)) {
-      case 1: launch_scorer<G, 1, true>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-      case 2: launch_scorer<G, 2, true>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-      default: launch_scorer<G, 4, true>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+      case 1: launch_scorer<G, 1, true>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+      case 2: launch_scorer<G, 2, true>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+      default: launch_scorer<G, 4, true>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
     }
     return;
   }
   switch (ids_tables_per_word(L)) {
-    case 1: launch_scorer<G, 1, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer<G, 2, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-    case 4: launch_scorer<G, 4, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer<G, 8, false>(B, Hkv, Hq, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    case 1: launch_scorer<G, 1, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer<G, 2, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 4: launch_scorer<G, 4, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer<G, 8, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
   }
 }
 
@@ -1015,7 +1043,7 @@ hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, 
     constexpr int GG = decltype(gtag)::value;
     soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
         static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
-        im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters);
+        im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -1034,12 +1062,13 @@ hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, 
 
 hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids,
                         const float* vnorm, const int32_t* lens, int64_t n_cap, SinkWindow sw,
-                        float* scores,
+                        float* scores, bool soft_sums,
                         const ScoreWs& ws, hipStream_t s) {
+  float* usum = soft_sums ? ws.usum : nullptr;
   switch (Hq / Hkv) {
-    case 1: launch_scorer_g<1>(B, Hkv, Hq, L, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer_g<2>(B, Hkv, Hq, L, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer_g<4>(B, Hkv, Hq, L, P, n_cap, sw, ws, ids, vnorm, lens, scores, s); break;
+    case 1: launch_scorer_g<1>(B, Hkv, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer_g<2>(B, Hkv, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer_g<4>(B, Hkv, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
   }
   return hipGetLastError();
 }

@@ -34,7 +34,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "make_workload", "to_bf16_exact"]
+__all__ = ["Workload", "CONFIGS", "make_workload", "to_bf16_exact", "uniforms"]
 
 
 @dataclass
@@ -184,3 +184,11 @@ def make_workload(name: str = "c2", *, seed: int | None = None, n: int | None = 
                     L=Ln, P=Pn, tau=float(base["tau"]), dtype=dt, W=W, K=K, V=V, q=q,
                     steps=steps_, K_new=K_new, V_new=V_new, q_steps=q_steps,
                     meta={"mu": mu})
+
+
+def uniforms(B: int, Hq: int, M: int, seed: int = 0) -> np.ndarray:
+    """Seeded float32 uniforms in [0, 1), [B, Hq, M]: the random draws of the
+    sampling estimator, passed to both the oracle and the HIP path."""
+    rng = np.random.default_rng(np.random.SeedSequence(4242 + seed))
+    u = rng.random((B, Hq, M)).astype(np.float32)
+    return np.minimum(u, np.nextafter(np.float32(1.0), np.float32(0.0)))

@@ -44,7 +44,9 @@ def impl(**over):
     ns = types.SimpleNamespace(
         hash_keys=SO.hash_keys, value_norms=SO.value_norms, soft_tables=SO.soft_tables,
         scores=SO.scores, topk=SO.topk, select=SO.select, sparse_attention=SO.sparse_attention,
-        hard_collision_scores=SO.hard_collision_scores)
+        hard_collision_scores=SO.hard_collision_scores, soft_counts=SO.soft_counts,
+        sampling_distribution=SO.sampling_distribution, soft_attention=SO.soft_attention,
+        inverse_cdf=SO.inverse_cdf, sample_estimate=SO.sample_estimate)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -254,6 +256,88 @@ def check_hard_scores_brute(so):
                 assert np.isnan(s[b, g, lens[b]:]).all()
 
 
+def _sampling_case(seed=11, n=40, L=5, P=3, d=6):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((L * P, d))
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d)) * rng.lognormal(0, 0.5, size=(n, 1))
+    q = rng.standard_normal(d)
+    return W, K, V, q, L, P
+
+
+def check_sampling_law_brute(so):
+    """Soft counts, the value-aware law and the inverse-CDF draw against loops."""
+    W, K, V, q, L, P = _sampling_case()
+    tau = 0.5
+    tab = so.soft_tables(q, W, L, P, tau)
+    ids, _ = so.hash_keys(K, W, L, P)
+    vn = so.value_norms(V)
+    sc = so.soft_counts(tab, ids)
+    for i in range(len(K)):
+        ref = brute.score(W, q, K[i], V[i], L, P, tau) / math.sqrt(sum(x * x for x in V[i]))
+        assert sc[i] == pytest.approx(ref, rel=1e-12)
+    p, S1, a = so.sampling_distribution(tab, ids, vn)
+    total = sum(sc)
+    S1_ref = sum(sc[i] / total * vn[i] for i in range(len(K)))
+    assert S1 == pytest.approx(S1_ref, rel=1e-12)
+    for i in range(len(K)):
+        assert a[i] == pytest.approx(sc[i] / total, rel=1e-12)
+        assert p[i] == pytest.approx(sc[i] / total * vn[i] / S1_ref, rel=1e-12)
+    pz = np.array([0.0, 0.25, 0.0, 0.5, 0.25, 0.0])
+    for u, want in [(0.0, 1), (0.2499, 1), (0.25, 3), (0.7499, 3), (0.75, 4), (0.99999, 4)]:
+        acc, got = 0.0, None
+        for j, pj in enumerate(pz):
+            acc += pj
+            if acc > u:
+                got = j
+                break
+        assert got == want
+        assert int(so.inverse_cdf(pz, np.array([u]))[0]) == want
+
+
+def check_sampling_unbiased_identity(so):
+    """E[X | W] over the law equals the soft-attention output y (Theorem 3, part 1),
+    summed exactly over every key instead of sampled."""
+    W, K, V, q, L, P = _sampling_case(seed=12)
+    tab = so.soft_tables(q, W, L, P, 0.4)
+    ids, _ = so.hash_keys(K, W, L, P)
+    vn = so.value_norms(V)
+    p, S1, a = so.sampling_distribution(tab, ids, vn)
+    assert p.sum() == pytest.approx(1.0, rel=1e-12)
+    # X(j) as the estimator forms it: run it with all the mass of one draw on key j
+    ex = np.zeros(V.shape[1])
+    for j in range(len(K)):
+        lo = float(np.cumsum(p)[j] - p[j])
+        u = (lo + 0.5 * p[j]) if p[j] > 0 else None
+        if u is None:
+            continue
+        T, J = so.sample_estimate(tab, ids, V, np.array([u]))
+        assert int(J[0]) == j
+        ex += p[j] * T
+    y = so.soft_attention(tab, ids, V)
+    np.testing.assert_allclose(ex, y, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(y, (a[:, None] * V).sum(0), rtol=1e-12)
+
+
+def check_sampling_concentration(so):
+    """Theorem 3, part 2: with probability >= 1 - delta,
+    ||T(q) - y|| <= ||V||_2 sqrt(8 log(2/delta) / M); 20 seeded draws of M = 2000."""
+    W, K, V, q, L, P = _sampling_case(seed=13, n=300, L=8, P=4, d=16)
+    tab = so.soft_tables(q, W, L, P, 0.5)
+    ids, _ = so.hash_keys(K, W, L, P)
+    y = so.soft_attention(tab, ids, V)
+    M, delta = 2000, 1e-3
+    bound = np.linalg.norm(V, 2) * math.sqrt(8 * math.log(2 / delta) / M)
+    rng = np.random.default_rng(14)
+    errs = []
+    for _ in range(20):
+        T, _ = so.sample_estimate(tab, ids, V, rng.random(M))
+        errs.append(float(np.linalg.norm(T - y)))
+    assert max(errs) <= bound, (max(errs), bound)
+    # and the error shrinks like M^-1/2: mean error at M is within a factor of the bound
+    assert np.mean(errs) < 0.25 * bound
+
+
 def check_attention_library(so):
     """k = n equals dense softmax attention (torch SDPA, float64 CPU); k = 1 returns v[argmax]."""
     import torch
@@ -278,7 +362,8 @@ ALL_CHECKS = [check_golden_hash, check_golden_soft_table, check_golden_score_top
               check_golden_attention, check_tables_sum_to_one, check_product_of_sigmoids,
               check_tau_to_zero, check_tau_to_inf_and_p1, check_brute_force,
               check_topk_ties_and_sort, check_select_sink_window, check_hard_scores_brute,
-              check_attention_library]
+              check_sampling_law_brute, check_sampling_unbiased_identity,
+              check_sampling_concentration, check_attention_library]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -407,6 +492,22 @@ def _hard_any_plane(q, W, ids, vnorm, L, P, lens=None):   # counts plane agreeme
     return out
 
 
+def _law_no_norm(tables_row, ids_rows, vnorm_row):     # draws by a~ only, X unchanged
+    p, S1, a = SO.sampling_distribution(tables_row, ids_rows, vnorm_row)
+    return a, S1, a
+
+
+def _estimate_raw_v(tables_row, ids_rows, V_rows, u):    # X = v_J (no S_1 / ||v_J||)
+    p, S1, _ = SO.sampling_distribution(tables_row, ids_rows, SO.value_norms(V_rows))
+    J = SO.inverse_cdf(p, u)
+    return np.asarray(V_rows, float)[J].mean(axis=0), J
+
+
+def _icdf_left(p, u):                                    # boundary goes to the lower key
+    cdf = np.cumsum(np.asarray(p, float))
+    return np.minimum(np.searchsorted(cdf, np.asarray(u) * cdf[-1], side="left"), len(cdf) - 1)
+
+
 def _attn_no_scale(q, K, V, idx, scale):
     return SO.sparse_attention(q, K, V, idx, 1.0)
 
@@ -427,6 +528,9 @@ MUTANTS = {
     "select_budget_shared": dict(select=_select_budget_shared),
     "select_window_shift": dict(select=_select_window_shift),
     "hard_any_plane": dict(hard_collision_scores=_hard_any_plane),
+    "law_no_norm": dict(sampling_distribution=_law_no_norm),
+    "estimate_raw_v": dict(sample_estimate=_estimate_raw_v),
+    "icdf_left": dict(inverse_cdf=_icdf_left),
     "attn_no_scale": dict(sparse_attention=_attn_no_scale),
     "attn_transposed": dict(sparse_attention=_attn_transposed),
 }

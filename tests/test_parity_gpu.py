@@ -6,6 +6,7 @@ heads where the oracle would take too long."""
 from __future__ import annotations
 
 import functools
+import math
 
 import numpy as np
 import pytest
@@ -271,6 +272,89 @@ def test_sparse_decode_parity(dtype, k_max):
     out = out.cpu().numpy()
     for g in range(w.Hq):
         GC.check_out(out[0, g], w.q[0, g], w.K[0, g // 4], w.V[0, g // 4], idx[0, g], w.scale)
+
+
+# ----------------------------------------------------------------------------- sampling estimator
+
+def _estimate_run(w, M, seed=0):
+    from soft_lsh_token_amd.inputs import uniforms
+    d = GC.upload(w)
+    ids_np, vn_np = _oracle_ids(w)
+    ids = GC.ids_dev(ids_np, w.n_cap, w.P)
+    vn = torch.from_numpy(vn_np).to(DEV)
+    u = uniforms(w.B, w.Hq, M, seed)
+    out = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device=DEV)
+    draws = torch.full((w.B, w.Hq, M), -7, dtype=torch.int32, device=DEV)
+    sc = torch.zeros(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=DEV)
+    S.socket_sample_estimate(d["q"], d["W"], ids, vn, d["V"], d["lens"], torch.from_numpy(u).to(DEV),
+                             w.tau, w.L, w.P, out, draws, sc)
+    sync()
+    return ids_np, vn_np, u, out.cpu().numpy(), draws.cpu().numpy(), sc.cpu().numpy()
+
+
+def _check_estimate(w, ids_np, vn_np, u, out, draws, sc, heads=None):
+    """Draws against the oracle's inverse-CDF draws (a different key only where
+    the uniform lies within 1e-5 of the boundary between the two), and T
+    against the oracle run on uniforms that reproduce the GPU's draws."""
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    group = w.Hq // w.Hkv
+    moved = 0
+    for b in range(w.B):
+        n = int(w.lens[b])
+        for g in (heads if heads is not None else range(w.Hq)):
+            h = g // group
+            if n == 0:
+                assert (out[b, g] == 0).all() and (draws[b, g] == -1).all()
+                continue
+            vref = vn_np[b, h, :n].astype(np.float64)
+            s_ref = GC.ref_scores(tables[b, g], ids_np[b, h, :n], vref)
+            GC.check_scores(sc[b, g, :n], s_ref)
+            p, S1, _ = SO.sampling_distribution(tables[b, g], ids_np[b, h, :n], vref)
+            cdf = np.cumsum(p)
+            J = draws[b, g].astype(np.int64)
+            assert (J >= 0).all() and (J < n).all()
+            assert (p[J] > 0).all()
+            Jr = SO.inverse_cdf(p, u[b, g])
+            for m in np.nonzero(J != Jr)[0]:
+                lo, hi = cdf[J[m]] - p[J[m]], cdf[J[m]]
+                assert lo - 1e-5 <= u[b, g, m] <= hi + 1e-5, (b, g, m, J[m], Jr[m], u[b, g, m])
+            moved += int((J != Jr).sum())
+            umid = (cdf[J] - 0.5 * p[J]).astype(np.float64)   # uniforms that draw exactly J
+            T, Jm = SO.sample_estimate(tables[b, g], ids_np[b, h, :n], w.V[b, h, :n], umid)
+            assert (Jm == J).all()
+            err = float(np.linalg.norm(out[b, g] - T))
+            assert err <= 1e-4 * S1, (b, g, err, S1)
+    return moved
+
+
+@pytest.mark.parametrize("case,M", [
+    (dict(name="c2", n=5000), 1024),
+    (dict(name="c2", n=3000, Hq=8, Hkv=8, L=60, P=10), 512),
+    (dict(name="c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 100, 3000], n_cap=3000), 2048),
+    (dict(name="c1"), 8192),
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else f"M{c}")
+def test_sample_estimate_parity(case, M):
+    print("case", case, M, flush=True)
+    w = make_workload(**case)
+    moved = _check_estimate(w, *_estimate_run(w, M))
+    print("draws decided by rounding at a CDF boundary:", moved)
+
+
+def test_sample_estimate_c2_concentration():
+    """At the 32K GQA shape the estimate lies within the pages' concentration
+    bound (Theorem 3, part 2) of the oracle's soft-attention output, delta = 1e-3."""
+    w = workload("c2")
+    M = 4096
+    ids_np, vn_np, u, out, draws, sc = _estimate_run(w, M, seed=1)
+    _check_estimate(w, ids_np, vn_np, u, out, draws, sc, heads=[0, 11, 30])
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    n, group = int(w.lens[0]), w.Hq // w.Hkv
+    for g in range(w.Hq):
+        h = g // group
+        y = SO.soft_attention(tables[0, g], ids_np[0, h, :n], w.V[0, h, :n])
+        bound = np.linalg.norm(w.V[0, h, :n].astype(np.float64), 2) * math.sqrt(
+            8 * math.log(2 / 1e-3) / M)
+        assert np.linalg.norm(out[0, g] - y) <= bound
 
 
 # ----------------------------------------------------------------------------- hard-LSH mode
