@@ -110,6 +110,10 @@ class Case:
         self.sws_p = self.sws.data_ptr() + (-self.sws.data_ptr()) % 256
         self.dws_p = self.dws.data_ptr() + (-self.dws.data_ptr()) % 256
         self.sws_n, self.dws_n = sws, dws
+        xsw = S.socket_decode_step_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, self.k_max)
+        self.fws = S.alloc_workspace(xsw, dev)
+        self.fws_p = self.fws.data_ptr() + (-self.fws.data_ptr()) % 256
+        self.fws_n = xsw
         xws = S.socket_dense_decode_workspace(w.B, w.Hq, w.Hkv, w.d, w.n_cap)
         self.xws = S.alloc_workspace(xws, dev)
         self.xws_p = self.xws.data_ptr() + (-self.xws.data_ptr()) % 256
@@ -126,6 +130,7 @@ class Case:
         self.c_append, self.c_prefill, self.c_score, self.c_decode, self.c_score_topk = \
             [], [], [], [], []
         self.c_dense = []
+        self.c_fused = []
         for r in range(self.replicas):
             K, V, ids, vn = self.K[r].data_ptr(), self.V[r].data_ptr(), self.ids[r].data_ptr(), \
                 self.vn[r].data_ptr()
@@ -149,6 +154,13 @@ class Case:
                                   i64(w.n_cap), vp(self.idx.data_ptr()), self.k_max,
                                   ctypes.c_float(w.scale), vp(self.out.data_ptr()),
                                   vp(self.dws_p), ctypes.c_size_t(self.dws_n), st))
+            self.c_fused.append((vp(self.q.data_ptr()), vp(K), vp(V), 1, w.B, w.Hq, w.Hkv, w.d,
+                                 vp(self.W.data_ptr()), w.L, w.P, ctypes.c_float(w.tau), vp(ids),
+                                 vp(vn), vp(self.lens.data_ptr()), i64(w.n_cap),
+                                 vp(self.ks.data_ptr()), self.k_max, self.sink, self.window,
+                                 ctypes.c_float(w.scale), vp(self.idx.data_ptr()),
+                                 vp(self.scores.data_ptr()), vp(self.out.data_ptr()),
+                                 vp(self.fws_p), ctypes.c_size_t(self.fws_n), st))
             self.c_dense.append((vp(self.q.data_ptr()), vp(K), vp(V), 1, w.B, w.Hq, w.Hkv, w.d,
                                  i64(w.n_cap), vp(self.lens.data_ptr()), ctypes.c_float(w.scale),
                                  vp(self.out.data_ptr()), vp(self.xws_p),
@@ -170,7 +182,12 @@ class Case:
         self._ok(self.lib.socket_hash_keys(*self.c_prefill[r]), "socket_hash_keys")
 
     def step(self, r):
-        """One decode step on replica r through the three C calls."""
+        """One decode step on replica r through socket_decode_step (the new key
+        hashed inside the table kernel, then selection and attention)."""
+        self._ok(self.lib.socket_decode_step(*self.c_fused[r]), "socket_decode_step")
+
+    def step3(self, r):
+        """The same step through the three separate C calls."""
         lib = self.lib
         rc = lib.socket_hash_keys(*self.c_append[r])
         rc |= lib.socket_score_topk(*self.c_score_topk[r])
@@ -209,13 +226,14 @@ def busy_prologue(torch, ms_target=40.0):
     return lambda: [a @ b for _ in range(reps)], reps * one
 
 
-def timed_steps(case, torch, steps, warmup):
+def timed_steps(case, torch, steps, warmup, step=None):
+    step = step or case.step
     for i in range(warmup):
-        case.step(i % case.replicas)
+        step(i % case.replicas)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        case.step(i % case.replicas)
+        step(i % case.replicas)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
 
@@ -451,6 +469,8 @@ def main():
     log(f"[bench] prefill hash 32K: {pre32}")
     sec = timed_steps(case, torch, args.steps, args.warmup)
     log(f"[bench] 32K step wall {sec * 1e6:.1f} us")
+    sec3 = timed_steps(case, torch, args.steps, args.warmup, case.step3)
+    log(f"[bench] 32K step wall through the three calls {sec3 * 1e6:.1f} us")
     stages, gpu_step_us, host_step_us = per_stage(case, torch, min(args.steps, 200))
     log(f"[bench] 32K per-stage GPU us {stages}; full step GPU {gpu_step_us:.1f} us; "
         f"host enqueue {host_step_us:.1f} us/step")
@@ -467,7 +487,8 @@ def main():
     w = case.w
     keys_per_step = w.B * w.Hq * (case.n + 1)
     extra32 = dict(
-        step_us_wall=sec * 1e6, step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
+        step_us_wall=sec * 1e6, step_us_wall_three_calls=sec3 * 1e6,
+        step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
         stage_us=stages, scorer_launch_us=score_us,
         score_topk_us=stages["tables"] + stages["score"] + stages["topk"],
         prefill=pre32, dense_decode=dense32, sampling_estimator=est32)

@@ -176,6 +176,27 @@ int socket_topk(int B, int Hq, int Hkv, int L, const float* scores, const int32_
                 int64_t n_cap, const int32_t* ks, int k_max, int sink, int window, int32_t* idx,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes needed by socket_decode_step (0 if unsupported). */
+size_t socket_decode_step_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
+                                    int k_max);
+
+/*
+ * socket_decode_step -- one whole decode step for callers that have written
+ * the new token's key and value at position lens[b] - 1 of K and V (lens
+ * counts the new token): hashes that key and stores its value norm (as
+ * socket_hash_keys with pos0 = lens - 1 and count = 1), then selects as
+ * socket_score_topk (with sink and window) and attends as
+ * socket_sparse_decode, writing idx, scores (may be NULL) and out.  The key is
+ * hashed inside the table kernel, so the step takes one launch fewer than the
+ * three calls.  ws must hold socket_decode_step_workspace(...) bytes,
+ * 256-byte aligned.
+ */
+int socket_decode_step(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
+                       int Hkv, int d, const void* W, int L, int P, float tau, uint8_t* ids,
+                       float* vnorm, const int32_t* lens, int64_t n_cap, const int32_t* ks,
+                       int k_max, int sink, int window, float scale, int32_t* idx, float* scores,
+                       float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes needed by socket_sparse_decode for these sizes. */
 size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max);
 

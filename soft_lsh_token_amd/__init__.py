@@ -12,7 +12,8 @@ from ._lib import (  # noqa: F401
     socket_score_topk, socket_score_topk_workspace, socket_soft_tables, socket_sparse_decode,
     socket_sparse_decode_workspace, socket_topk, score_stride,
     alloc_codes, codes_words, socket_codes_bytes, socket_hash_codes, socket_hard_score_topk,
-    socket_hard_score_topk_workspace, socket_sample_estimate,
+    socket_hard_score_topk_workspace, socket_sample_estimate, socket_decode_step,
+    socket_decode_step_workspace,
 )
 
 __version__ = "0.1.0"

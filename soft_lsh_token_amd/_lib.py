@@ -39,6 +39,9 @@ _SIGS = {
                                   _sz, _vp]),
     "socket_dense_decode_workspace": (_sz, [_i, _i, _i, _i, _i64]),
     "socket_codes_bytes": (_sz, [_i, _i, _i64, _i, _i]),
+    "socket_decode_step_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
+    "socket_decode_step": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp,
+                                _i64, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "socket_sample_estimate": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _vp,
                                     _i64, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "socket_hash_codes": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp,
@@ -364,3 +367,35 @@ def socket_sample_estimate(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
         _dev(u, "u", torch.float32, (B, Hq, M)), M, _dev(out, "out", torch.float32, (B, Hq, d)),
         dptr, sptr, wptr, wbytes, _stream(q, stream))
     _check("socket_sample_estimate", rc)
+
+
+# ----------------------------------------------------------------------------- fused step
+
+def socket_decode_step_workspace(B: int, Hq: int, Hkv: int, n_cap: int, L: int, P: int,
+                                 k_max: int) -> int:
+    return int(lib().socket_decode_step_workspace(B, Hq, Hkv, n_cap, L, P, k_max))
+
+
+def socket_decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: torch.Tensor,
+                       ids: torch.Tensor, vnorm: torch.Tensor, lens: torch.Tensor,
+                       ks: torch.Tensor, k_max: int, tau: float, L: int, P: int, scale: float,
+                       idx: torch.Tensor, out: torch.Tensor, scores: torch.Tensor | None = None,
+                       ws: torch.Tensor | None = None, stream=None, sink: int = 0,
+                       window: int = 0) -> None:
+    """One decode step: hash key lens[b] - 1, select, attend (see the header)."""
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = K.shape
+    need = socket_decode_step_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
+    if ws is None:
+        ws = alloc_workspace(need, q.device)
+    wptr, wbytes = _ws_ptr(ws, need)
+    sptr = None if scores is None else _dev(scores, "scores", torch.float32,
+                                            (B, Hq, score_stride(n_cap)))
+    rc = lib().socket_decode_step(
+        _dev(q, "q"), _dev(K, "K", q.dtype), _dev(V, "V", q.dtype, K.shape), _dtype_code(q), B, Hq,
+        Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P, float(tau), _ids(ids, B, Hkv, n_cap, L, P),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _dev(lens, "lens", torch.int32, (B,)),
+        n_cap, _dev(ks, "ks", torch.int32, (B,)), int(k_max), int(sink), int(window), float(scale),
+        _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr,
+        _dev(out, "out", torch.float32, (B, Hq, d)), wptr, wbytes, _stream(q, stream))
+    _check("socket_decode_step", rc)

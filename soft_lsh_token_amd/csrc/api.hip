@@ -166,6 +166,62 @@ int socket_score_topk(const void* q, int dtype, int B, int Hq, int Hkv, int d, c
   return from_hip(e);
 }
 
+// The fused step's workspace: the selection workspace, then the attention's.
+static size_t step_ws(int B, int Hq, int Hkv, int64_t n_cap, int L, int k_max, ScoreWs* sw,
+                      DecodeWs* dw, void* base) {
+  const size_t a = (score_ws_layout(B, Hq, Hkv, n_cap, L, nullptr, nullptr) + 255) & ~(size_t)255;
+  if (base) score_ws_layout(B, Hq, Hkv, n_cap, L, sw, base);
+  const size_t d = decode_ws_layout(B, Hq, k_max, dw, base ? static_cast<char*>(base) + a : nullptr);
+  return a + d;
+}
+
+size_t socket_decode_step_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L, int P,
+                                    int k_max) {
+  if (socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max) == 0 || k_max <= 0 ||
+      k_max > kMaxKmax)
+    return 0;
+  return step_ws(B, Hq, Hkv, n_cap, L, k_max, nullptr, nullptr, nullptr);
+}
+
+int socket_decode_step(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
+                       int Hkv, int d, const void* W, int L, int P, float tau, uint8_t* ids,
+                       float* vnorm, const int32_t* lens, int64_t n_cap, const int32_t* ks,
+                       int k_max, int sink, int window, float scale, int32_t* idx, float* scores,
+                       float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !W || !ids || !vnorm || !lens || !ks || !idx || !out || !ws)
+    return SOCKET_EINVAL;
+  if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
+  if (k_max <= 0 || !sink_window_ok(sink, window, k_max)) return SOCKET_EINVAL;
+  if (!(tau > 0.f) || !(tau < INFINITY)) return SOCKET_EINVAL;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return SOCKET_EINVAL;
+  int rc = check_sizes(B, Hq, Hkv, L, P, n_cap);
+  if (rc) return rc;
+  if (d != kHead || k_max > kMaxKmax) return SOCKET_EUNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return SOCKET_EINVAL;
+  ScoreWs w;
+  DecodeWs dw;
+  if (ws_bytes < step_ws(B, Hq, Hkv, n_cap, L, k_max, nullptr, nullptr, nullptr))
+    return SOCKET_ENOSPC;
+  step_ws(B, Hq, Hkv, n_cap, L, k_max, &w, &dw, ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sc = scores ? scores : w.scores;
+  AppendKey ak;
+  ak.K = K;
+  ak.V = V;
+  ak.lens = lens;
+  ak.ids = ids;
+  ak.vnorm = vnorm;
+  ak.n_cap = n_cap;
+  const SinkWindow sw{sink, window};
+  hipError_t e = launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w, s, ak);
+  if (e == hipSuccess)
+    e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sw, sc, false, w, s);
+  if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s);
+  if (e == hipSuccess)
+    e = launch_sparse_decode(q, K, V, dtype, B, Hq, Hkv, n_cap, idx, k_max, scale, out, dw, s);
+  return from_hip(e);
+}
+
 size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max) {
   if (B <= 0 || Hq <= 0 || d != kHead || k_max <= 0) return 0;
   return decode_ws_layout(B, Hq, k_max, nullptr, nullptr);

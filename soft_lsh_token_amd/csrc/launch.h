@@ -30,10 +30,23 @@ size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws
 size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreWs* ws,
                         void* base);
 
+// A key to hash while the tables are built: position lens[b] - 1 of every KV
+// row (K == nullptr: none).
+struct AppendKey {
+  const void* K = nullptr;
+  const void* V = nullptr;
+  const int32_t* lens = nullptr;
+  uint8_t* ids = nullptr;
+  float* vnorm = nullptr;
+  int64_t n_cap = 0;
+};
+
 // Algorithm 2, part 1: the soft tables of every query head, written as the
 // scorer's LDS images; clears the selection histograms and counters.
+// Optionally hashes the key appended at lens[b] - 1 (Algorithm 1 for one key).
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
-                              int L, int P, float tau, const ScoreWs& ws, hipStream_t s);
+                              int L, int P, float tau, const ScoreWs& ws, hipStream_t s,
+                              AppendKey ak = AppendKey{});
 
 // Keys always selected besides the top-k: the first `sink` and the last
 // `window` keys of each sequence.

@@ -187,11 +187,22 @@ __device__ __forceinline__ void store_slot(float* dst, const float* v) {
 // of one entry).  It also clears a 1/16 share of those heads' histograms
 // (block j = 0: their candidate counters and soft-count sums).
 // Tables l >= L (padding of the last lane word) get all-zero entries.
+// With ak.K set, blocks past the first B*Hkv*16 hash the key appended at
+// position lens[b] - 1 of each KV row (append_block below) alongside.
+template <typename T>
+__device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int TL, int nab,
+                             int rows, const AppendKey& ak);
+
 template <typename T, int G>
 __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
     int TL, int NF, int NS, int HE, int FULL, int img_floats, float* __restrict__ img,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters, float* __restrict__ usum) {
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ counters, float* __restrict__ usum,
+    AppendKey ak, int rows, int nab) {
+  if ((int)blockIdx.x >= rows * 16) {  // uniform
+    append_block<T>(W, Hkv, L, P, TL, nab, rows, ak);
+    return;
+  }
   const int bh = blockIdx.x >> 4, j = blockIdx.x & 15;
   const int b = bh / Hkv, h = bh % Hkv;
   const int bg0 = b * Hq + h * G;
@@ -307,6 +318,105 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   }
 }
 
+// Append blocks: block a of KV row bh (a < nab) projects the new key at
+// lens[b] - 1 on the planes of ID words a*WPB .. a*WPB+WPB-1, one plane per
+// thread, in float32 with the accumulation order of the hashing kernels, and
+// stores those words; block 0 also stores the value norm.  WPB = the whole
+// words of TL*P planes that fit in kTabThreads threads.
+template <typename T>
+__device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int TL, int nab,
+                             int rows, const AppendKey& ak) {
+  const int ag = (int)blockIdx.x - rows * 16;
+  const int bh = ag / nab, a = ag % nab;
+  const int b = bh / Hkv;
+  const int tid = threadIdx.x;
+  const int WP = TL * P;              // planes per ID word (<= 64)
+  const int WPB = kTabThreads / WP;   // whole words per block
+  const int w0 = a * WPB;
+  const int word = w0 + tid / WP, qq = tid % WP;
+  const int m = qq / P, pl = qq % P, l = word * TL + m;
+  const bool live = tid < WPB * WP && word < 16 && l < L;
+  // the plane's W row first: it does not depend on the key position
+  constexpr int NV = kHead * (int)sizeof(T) / 16;
+  uint4 wv[NV];
+  if (live) {
+    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + pl) * kHead);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) wv[v] = wr[v];
+  }
+  const int64_t pos = (int64_t)ak.lens[b] - 1;
+  if (pos < 0 || pos >= ak.n_cap) return;  // uniform: no key to append
+  const int64_t row = (int64_t)bh * ak.n_cap + pos;
+  const T* K = static_cast<const T*>(ak.K);
+  const T* V = static_cast<const T*>(ak.V);
+  __shared__ float kf[kHead];
+  __shared__ uint32_t kbit[kTabThreads];
+  if (tid < kHead) {
+    if constexpr (sizeof(T) == 2) kf[tid] = __uint_as_float((uint32_t)K[row * kHead + tid] << 16);
+    else kf[tid] = K[row * kHead + tid];
+  }
+  const bool norm = a == 0 && tid < 16;  // lanes 0..15 of wave 0: the value norm
+  float vf[8];
+  if (norm) {
+    if constexpr (sizeof(T) == 2) {
+      unpack_bf16x8(reinterpret_cast<const uint4*>(V + row * kHead)[tid], vf);
+    } else {
+      const float4 x = reinterpret_cast<const float4*>(V + row * kHead)[2 * tid];
+      const float4 y = reinterpret_cast<const float4*>(V + row * kHead)[2 * tid + 1];
+      vf[0] = x.x; vf[1] = x.y; vf[2] = x.z; vf[3] = x.w;
+      vf[4] = y.x; vf[5] = y.y; vf[6] = y.z; vf[7] = y.w;
+    }
+  }
+  __syncthreads();
+  float z = 0.f;
+  if (live) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      float f[8];
+      int cnt;
+      if constexpr (sizeof(T) == 2) {
+        unpack_bf16x8(wv[v], f);
+        cnt = 8;
+      } else {
+        f[0] = __uint_as_float(wv[v].x); f[1] = __uint_as_float(wv[v].y);
+        f[2] = __uint_as_float(wv[v].z); f[3] = __uint_as_float(wv[v].w);
+        cnt = 4;
+      }
+#pragma unroll
+      for (int e = 0; e < cnt; ++e) z = fmaf(f[e], kf[v * cnt + e], z);
+    }
+  }
+  kbit[tid] = live && z > 0.f ? 1u : 0u;  // z == 0 gives bit 0
+  if (a == 0 && tid < 64) {  // the whole row of 16 lanes joins the DPP sum
+    float ss = 0.f;
+    if (norm) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(vf[i], vf[i], ss);
+    }
+    ss = row16_sum(ss);
+    if (tid == 0) ak.vnorm[row] = sqrtf(ss);
+  }
+  __syncthreads();
+  if (tid < WPB && w0 + tid < 16) {
+    const int wd = w0 + tid;
+    const int C = P > 8 ? 2 : 1, WB = TL * C;
+    uint64_t w[2] = {0ull, 0ull};
+    for (int mm = 0; mm < TL; ++mm) {
+      uint64_t id = 0ull;
+      if (wd * TL + mm < L)
+        for (int p2 = 0; p2 < P; ++p2) id |= (uint64_t)kbit[tid * WP + mm * P + p2] << p2;
+      const int bit = 8 * C * mm;
+      w[bit >> 6] |= id << (bit & 63);
+    }
+    uint8_t* dst = ak.ids + ids_word_offset(bh, ak.n_cap, WB, pos, wd);
+    if (WB == 1) *dst = (uint8_t)w[0];
+    else if (WB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+    else if (WB == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w[0];
+    else if (WB == 8) *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w[0], (uint32_t)(w[0] >> 32));
+    else *reinterpret_cast<uint4*>(dst) = make_uint4((uint32_t)w[0], (uint32_t)(w[0] >> 32),
+                                                     (uint32_t)w[1], (uint32_t)(w[1] >> 32));
+  }
+}
 // ---------------------------------------------------------------- scorer
 
 template <int G>
@@ -980,6 +1090,266 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
   for (int64_t t = z.total + tid; t < k_max; t += kResThreads) out[t] = -1;
 }
 
+// ---------------------------------------------------------------- one-pass top-k
+
+// For n_cap <= kResThreads * 4 * kOneMaxRounds: one workgroup per query head
+// does the scan and the resolve above on its own, with the head's scores in
+// registers and the selection bitmap and candidates in LDS.  This saves the
+// second launch for short rows; for longer ones the per-key passes of a single
+// CU per head cost more than the launch, and the scan spreads them over
+// several workgroups per head.  Round r of
+// thread t holds keys r*4096 + 4t .. +3 (coalesced 16-byte loads); the
+// bitmap has the global bitmap's layout (wave ballots per 256-key block).
+// Candidates beyond the LDS capacity are settled from the registers instead.
+// Workgroups are remapped as in the scorer (logical head lid = (blockIdx mod
+// 8) * (grid / 8) + blockIdx / 8), so a head is selected on the XCD whose L2
+// received its scores.
+constexpr int kOneMaxRounds = 2;
+constexpr int kOneKeys = kResThreads * 4;  // keys per round
+
+// The boundary-bin candidates of this thread's keys in round r (4 bits).
+template <int NR>
+__device__ __forceinline__ uint32_t cand_bits(const uint4 (&v)[NR], int r, uint32_t key,
+                                              uint32_t n, uint32_t flo, uint32_t fhi,
+                                              uint32_t lo, uint32_t hi) {
+  const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+  uint32_t m = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t kk = key + (uint32_t)e;
+    m |= (uint32_t)(kk < n && kk >= flo && kk < fhi && sb[e] <= hi && sb[e] >= lo) << e;
+  }
+  return m;
+}
+
+// radix_pick over the candidates held in registers (overflow path).
+template <int NR, bool BY_INDEX>
+__device__ Pick radix_regs(const uint4 (&v)[NR], uint32_t n, uint32_t flo, uint32_t fhi,
+                           uint32_t lo, uint32_t hi, uint32_t vmask, uint32_t vval,
+                           uint32_t imask, uint32_t ival, int shift, uint32_t need,
+                           uint32_t* h128, Pick* shpick) {
+  const int tid = threadIdx.x;
+  if (tid < 128) h128[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t key = (uint32_t)(r * kOneKeys + 4 * tid);
+    const uint32_t m = cand_bits<NR>(v, r, key, n, flo, fhi, lo, hi);
+    const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t low = sb[e] & 0x1FFFFFu, kk = key + (uint32_t)e;
+      if (((m >> e) & 1u) && (low & vmask) == vval && (!BY_INDEX || (kk & imask) == ival))
+        atomicAdd(&h128[((BY_INDEX ? kk : low) >> shift) & 127u], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int b0 = BY_INDEX ? 2 * tid : 127 - 2 * tid;
+    const int b1 = BY_INDEX ? 2 * tid + 1 : 126 - 2 * tid;
+    const uint32_t c0 = h128[b0], c1 = h128[b1];
+    const uint32_t inc = wave_incl_scan(c0 + c1);
+    const uint32_t prev = inc - c0 - c1;
+    if (prev < need && need <= prev + c0) *shpick = Pick{(uint32_t)b0, prev, c0};
+    else if (prev + c0 < need && need <= inc) *shpick = Pick{(uint32_t)b1, prev + c0, c1};
+  }
+  __syncthreads();
+  const Pick r = *shpick;
+  __syncthreads();
+  return r;
+}
+
+// grid: B*Hq blocks of kResThreads.
+template <int NR>
+__global__ __launch_bounds__(kResThreads) void topk_onepass_kernel(
+    const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int sink,
+    int window, int Hq, int heads, const uint32_t* __restrict__ hist,
+    int32_t* __restrict__ idx) {
+  const int bg = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  if (bg >= heads) return;
+  const int b = bg / Hq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
+  const int64_t k = z.k;
+  int32_t* out = idx + (int64_t)bg * k_max;
+  if (z.total == 0) {
+    for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
+    return;
+  }
+  // every score load first (past the row: re-read its end, masked below)
+  const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
+  uint4 v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    int64_t kk = (int64_t)r * kOneKeys + 4 * tid;
+    if (kk > sstride - 4) kk = sstride - 4;
+    v[r] = *reinterpret_cast<const uint4*>(srow + kk);
+  }
+  __shared__ uint32_t wsum[kResWaves];
+  __shared__ Boundary shb;
+  __shared__ uint32_t h128[128];
+  __shared__ Pick shpick;
+  __shared__ uint32_t wcount[kResWaves];
+  __shared__ uint2 lcand[kCandCap];
+  __shared__ uint32_t lbm[NR * kOneKeys / 32];
+  Boundary bd{0u, 0u};
+  if (k > 0)  // uniform
+    bd = find_boundary<kResThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
+  const uint32_t n = (uint32_t)z.n, flo = (uint32_t)z.f_lo, fhi = (uint32_t)z.f_hi;
+  // candidates: lo <= bits <= hi; selected outright: bits > hi (nothing when k == 0)
+  const uint32_t lo = k > 0 ? bd.d1 << kHistShift : 1u;
+  const uint32_t hi = k > 0 ? (bd.d1 < (uint32_t)(kHistBins - 1)
+                                   ? ((bd.d1 + 1) << kHistShift) - 1u : 0xFFFFFFFFu)
+                            : 0u;
+  const bool above_ok = k > 0 && hi != 0xFFFFFFFFu;
+  // pass 1: selection ballots into the bitmap, candidates counted per wave
+  const uint64_t lt = lanemask_lt64();
+  uint32_t wc = 0u;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t base = (uint32_t)(r * kOneKeys + wave * 256);  // this wave's 256-key block
+    const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+    uint64_t ms[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = base + 4 * lane + e;
+      const bool valid = key < n;
+      const bool forced = key < flo || key >= fhi;
+      ms[e] = __ballot(valid && (forced || (above_ok && sb[e] > hi)));
+      wc += (uint32_t)__popcll(__ballot(valid && !forced && sb[e] <= hi && sb[e] >= lo));
+    }
+    // block j = base / 256: words 8j + 2e (+1) = the ballot of the lanes' e-th keys
+    if (lane < 8) {
+      const uint64_t a = ms[lane >> 1];
+      lbm[(base >> 5) + lane] = (lane & 1) ? (uint32_t)(a >> 32) : (uint32_t)a;
+    }
+  }
+  if (lane == 0) wcount[wave] = wc;
+  __syncthreads();
+  uint32_t cpos = 0u, C = 0u;
+#pragma unroll
+  for (int w = 0; w < kResWaves; ++w) {
+    const uint32_t c = wcount[w];
+    cpos += w < wave ? c : 0u;
+    C += c;
+  }
+  const bool in_lds = C <= (uint32_t)kCandCap;
+  // pass 2: this wave's candidates in key order from its base position
+  if (in_lds && wc) {  // uniform per wave
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t base = (uint32_t)(r * kOneKeys + wave * 256);
+      const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = base + 4 * lane + e;
+        const bool c = key < n && key >= flo && key < fhi && sb[e] <= hi && sb[e] >= lo;
+        const uint64_t mc = __ballot(c);
+        if (c) lcand[cpos + (uint32_t)__popcll(mc & lt)] = make_uint2(sb[e], key);
+        cpos += (uint32_t)__popcll(mc);
+      }
+    }
+  }
+  __syncthreads();
+
+  // the candidates that complete the top-k
+  uint32_t need = k > 0 ? (uint32_t)k - bd.above : 0u;  // 1 <= need <= C when k > 0
+  uint32_t vmask = 0u, vval = 0u, imax = 0xFFFFFFFFu;
+  if (k > 0 && need < C) {  // uniform
+    uint32_t ties = 0u;
+    for (int shift = 14; shift >= 0; shift -= 7) {
+      const Pick pk = in_lds
+          ? radix_pick<false>(lcand, C, vmask, vval, 0u, 0u, shift, need, h128, &shpick)
+          : radix_regs<NR, false>(v, n, flo, fhi, lo, hi, vmask, vval, 0u, 0u, shift, need,
+                                  h128, &shpick);
+      need -= pk.before;
+      vval |= pk.digit << shift;
+      vmask |= 127u << shift;
+      ties = pk.inbin;
+    }
+    if (ties > need) {  // among keys with exactly that score, the lower indices win
+      uint32_t imask = 0u, ival = 0u;
+      int top = 0;
+      while (((uint64_t)1 << top) < (uint64_t)n) ++top;
+      int shift = top > 7 ? top - 7 : 0;
+      for (;;) {
+        const Pick pk = in_lds
+            ? radix_pick<true>(lcand, C, vmask, vval, imask, ival, shift, need, h128, &shpick)
+            : radix_regs<NR, true>(v, n, flo, fhi, lo, hi, vmask, vval, imask, ival, shift,
+                                   need, h128, &shpick);
+        need -= pk.before;
+        ival |= pk.digit << shift;
+        imask |= 127u << shift;
+        if (shift == 0) break;
+        shift = shift > 7 ? shift - 7 : 0;
+      }
+      imax = ival;
+    }
+  }
+  // the chosen candidates join the bitmap
+  if (in_lds) {
+    for (uint32_t i = tid; i < C; i += kResThreads) {
+      const uint2 e = lcand[i];
+      const uint32_t low = e.x & 0x1FFFFFu;
+      if (low > vval || (low == vval && e.y <= imax)) {
+        const uint32_t i4 = (e.y >> 2) & 63u, ee = e.y & 3u;
+        atomicOr(&lbm[(e.y >> 8) * 8 + ee * 2 + (i4 >> 5)], 1u << (i4 & 31));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t key = (uint32_t)(r * kOneKeys + 4 * tid);
+      const uint32_t m = cand_bits<NR>(v, r, key, n, flo, fhi, lo, hi);
+      const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t low = sb[e] & 0x1FFFFFu, kk = key + (uint32_t)e;
+        if (((m >> e) & 1u) && (low > vval || (low == vval && kk <= imax))) {
+          const uint32_t i4 = (kk >> 2) & 63u;
+          atomicOr(&lbm[(kk >> 8) * 8 + (uint32_t)e * 2 + (i4 >> 5)], 1u << (i4 & 31));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // key-order 32-bit words from the block masks (W consecutive words a thread)
+  constexpr int W = (NR * kOneKeys / 32 + kResThreads - 1) / kResThreads;
+  const int64_t segw = ((int64_t)n + 31) >> 5;
+  uint32_t kw[W];
+  uint32_t cnt = 0u;
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    const int64_t wi = (int64_t)tid * W + q;
+    uint32_t x = 0u;
+    if (wi < segw) {
+      const int blk = (int)(wi >> 3), sub = (int)(wi & 7);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b8 = (lbm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
+        x |= spread4(b8) << e;  // key 4i + e of the word at bit 4i + e
+      }
+    }
+    kw[q] = x;
+    cnt += __popc(x);
+  }
+  const uint32_t incw = block_incl_scan<kResThreads>(cnt, wsum);
+  uint32_t pos = incw - cnt;
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    uint32_t x = kw[q];
+    const uint32_t kbase = (uint32_t)(((int64_t)tid * W + q) * 32);
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1;
+      if (pos < (uint32_t)k_max) out[pos] = (int32_t)(kbase + bit);
+      ++pos;
+    }
+  }
+  for (int64_t t = z.total + tid; t < k_max; t += kResThreads) out[t] = -1;
+}
+
 // ---------------------------------------------------------------- launchers
 
 static int device_cus() {
@@ -1034,16 +1404,21 @@ static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap,
 }
 
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
-                              int L, int P, float tau, const ScoreWs& ws, hipStream_t s) {
+                              int L, int P, float tau, const ScoreWs& ws, hipStream_t s,
+                              AppendKey ak) {
   const int G = Hq / Hkv;
   const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L, P);
-  const unsigned grid = (unsigned)(B * Hkv * 16);
+  const int rows = B * Hkv;
+  const int TLw = ids_tables_per_word(L);
+  const int nab = ak.K ? (16 + kTabThreads / (TLw * P) - 1) / (kTabThreads / (TLw * P)) : 0;
+  const unsigned grid = (unsigned)(rows * (16 + nab));
   auto go = [&](auto tag, auto gtag) {
     using T = decltype(tag);
     constexpr int GG = decltype(gtag)::value;
     soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
         static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
-        im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum);
+        im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum, ak, rows,
+        nab);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -1076,6 +1451,18 @@ hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx, const ScoreWs& ws,
                        hipStream_t s) {
+  if (n_cap <= (int64_t)kOneKeys * kOneMaxRounds) {  // every score of a head in one workgroup
+    const int rounds = (int)((n_cap + kOneKeys - 1) / kOneKeys);
+    auto go = [&](auto rt) {
+      constexpr int NR = decltype(rt)::value;
+      topk_onepass_kernel<NR><<<(unsigned)((B * Hq + kXcds - 1) / kXcds * kXcds), kResThreads, 0,
+                                s>>>(scores, n_cap, score_stride(n_cap), lens, ks, k_max,
+                                     sw.sink, sw.window, Hq, B * Hq, ws.hist, idx);
+    };
+    if (rounds <= 1) go(std::integral_constant<int, 1>{});
+    else go(std::integral_constant<int, 2>{});
+    return hipGetLastError();
+  }
   const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
   const int64_t nscan = (int64_t)B * Hq * CH;
   topk_scan_kernel<<<(unsigned)((nscan + kXcds - 1) / kXcds * kXcds), kScanThreads, 0, s>>>(

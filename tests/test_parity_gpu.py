@@ -214,21 +214,27 @@ def test_select_sink_window_parity(sw):
                              idx[b, g], w.scale)
 
 
-def test_topk_ties_lower_index_wins():
-    """All keys of a head share one bucket pattern and norm -> equal scores."""
-    w = make_workload("c2", n=3000, Hq=8, Hkv=2, k=100)
+@pytest.mark.parametrize("n", [3000, 8000, 20000, 70000])
+def test_topk_ties_lower_index_wins(n):
+    """All keys of a head share one bucket pattern and norm -> equal scores.
+    3000 and 8000 keys take the one-pass kernel (8000 equal keys overflow its
+    LDS candidate list), 20000 and 70000 the scan + resolve kernels (70000
+    with the candidates left in global memory)."""
+    w = make_workload("c2", n=n, Hq=8, Hkv=2, k=100)
     d = GC.upload(w)
     ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
     vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
     # KV head 1: second half of the keys gets a larger norm -> they win, ties among them
-    vn[:, 1, 1500:] = 2.0
+    half = n // 2
+    vn[:, 1, half:] = 2.0
     idx, sc = GC.gpu_score_topk(w, d, ids, vn)
     sync()
     idx = idx.cpu().numpy()
     for g in range(w.Hq):
         h = g // (w.Hq // w.Hkv)
-        expect = np.arange(100) if h == 0 else np.arange(1500, 1600)
+        expect = np.arange(100) if h == 0 else np.arange(half, half + 100)
         assert idx[0, g, :100].tolist() == expect.tolist()
+        assert (idx[0, g, 100:] == -1).all()
 
 
 def test_topk_edge_lengths():
@@ -557,9 +563,11 @@ def test_e2e_c4_full_sampled_heads():
     _e2e(workload("c4"), heads=[0, 13, 30])
 
 
-def test_decode_loop_c5():
-    """Prefill 131072 keys, then 256 steps each appending one key/value per KV head;
-    steps 0, 1, 2, 127 and 255 are checked against the oracle on sampled heads."""
+@pytest.mark.parametrize("fused", [False, True], ids=["three-calls", "decode-step"])
+def test_decode_loop_c5(fused):
+    """Prefill 131072 keys, then 256 steps each appending one key/value per KV head
+    (through the three calls, or through socket_decode_step); steps 0, 1, 2, 127
+    and 255 are checked against the oracle on sampled heads."""
     w = workload("c5")
     d = GC.upload(w)
     n0 = int(w.lens[0])
@@ -571,11 +579,19 @@ def test_decode_loop_c5():
     keep = {}
     for t in range(w.steps):
         # the caller has written row n0+t of K/V (the inputs already hold it); hash it
-        GC.gpu_hash(w, d, pos0=lens, count=1, ids=ids, vnorm=vn)
-        lens += 1
         q = torch.from_numpy(w.q_steps[t]).to(DEV).to(torch.bfloat16)
-        idx, sc = GC.gpu_score_topk(w, d, ids, vn, lens=lens, q=q)
-        out = GC.gpu_decode(w, d, idx, q=q)
+        if fused:
+            lens += 1
+            idx = torch.empty(w.B, w.Hq, w.k_max, dtype=torch.int32, device=DEV)
+            sc = torch.zeros(w.B, w.Hq, S.score_stride(w.n_cap), dtype=torch.float32, device=DEV)
+            out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=DEV)
+            S.socket_decode_step(q, d["K"], d["V"], d["W"], ids, vn, lens, ks, w.k_max, w.tau,
+                                 w.L, w.P, w.scale, idx, out, scores=sc)
+        else:
+            GC.gpu_hash(w, d, pos0=lens, count=1, ids=ids, vnorm=vn)
+            lens += 1
+            idx, sc = GC.gpu_score_topk(w, d, ids, vn, lens=lens, q=q)
+            out = GC.gpu_decode(w, d, idx, q=q)
         if t in check_steps:
             keep[t] = [x.cpu().numpy() for x in (idx, sc, out)]
     sync()
@@ -617,6 +633,60 @@ def test_run_twice_bitwise():
     assert torch.equal(ids, ids2) and torch.equal(vn, vn2)
     assert torch.equal(r1[0][0], r2[0][0]) and torch.equal(r1[0][1], r2[0][1])
     assert torch.equal(r1[1], r2[1])
+
+
+@pytest.mark.parametrize("case,sw", [
+    (dict(name="c2", n=5000), (0, 0)),
+    (dict(name="c4", n=(1000, 9000), B=3, k=0.02), (64, 128)),
+    (dict(name="c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 300, 999], n_cap=1000, k=5), (8, 8)),
+    (dict(name="c2", n=3000, L=60, P=10, Hq=16, Hkv=8), (0, 0)),
+    (dict(name="c1"), (0, 16)),
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else f"sw{c}")
+def test_decode_step_matches_three_calls(case, sw):
+    """socket_decode_step (append hashed inside the table kernel) equals
+    socket_hash_keys + socket_score_topk + socket_sparse_decode, bit for bit."""
+    print("case", case, sw, flush=True)
+    sink, window = sw
+    w = make_workload(**case)
+    d = GC.upload(w)
+    # every sequence's first lens-1 keys are cached; its key lens-1 is the new one
+    n0 = np.maximum(w.lens - 1, 0).astype(np.int32)
+    ids1 = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
+    vn1 = torch.zeros(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+    zero = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for b in range(w.B):
+        if n0[b]:
+            ib = S.alloc_ids(1, w.Hkv, w.n_cap, w.L, w.P, DEV)
+            vb = torch.zeros(1, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+            S.socket_hash_keys(d["K"][b:b + 1].contiguous(), d["V"][b:b + 1].contiguous(), d["W"],
+                               ib, vb, zero, int(n0[b]), w.L, w.P)
+            ids1[b:b + 1] = ib
+            vn1[b:b + 1] = vb
+    ids2, vn2 = ids1.clone(), vn1.clone()
+    k_max = w.k_max + sink + window
+    # three calls; a sequence with lens = 0 has no new key
+    for b in range(w.B):
+        if w.lens[b] > 0:
+            ib, vb = ids1[b:b + 1].clone(), vn1[b:b + 1].clone()
+            S.socket_hash_keys(d["K"][b:b + 1].contiguous(), d["V"][b:b + 1].contiguous(), d["W"],
+                               ib, vb, torch.full((1,), int(n0[b]), dtype=torch.int32, device=DEV),
+                               1, w.L, w.P)
+            ids1[b:b + 1] = ib
+            vn1[b:b + 1] = vb
+    idx1, sc1 = GC.gpu_score_topk(w, d, ids1, vn1, sink=sink, window=window)
+    out1 = GC.gpu_decode(w, d, idx1)
+    # one call
+    idx2 = torch.full_like(idx1, -7)
+    sc2 = torch.zeros_like(sc1)
+    out2 = torch.full_like(out1, float("nan"))
+    S.socket_decode_step(d["q"], d["K"], d["V"], d["W"], ids2, vn2, d["lens"], d["ks"], k_max, w.tau,
+                         w.L, w.P, w.scale, idx2, out2, scores=sc2, sink=sink, window=window)
+    sync()
+    assert torch.equal(ids1, ids2)
+    assert torch.equal(vn1, vn2)
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(sc1, sc2)
+    assert torch.equal(out1, out2)
 
 
 def test_stage_entry_points_match_fused_call():
