@@ -218,10 +218,48 @@ hipError_t launch_sparse_decode(const void* q, const void* K, const void* V, int
   return launch_decode_combine(ws.part, heads, ws.splits, out, s);
 }
 
+// The same merge for at most kFewSplits splits in one round trip: thread d
+// loads every split's (m, l) and its own o values at once and merges them in
+// registers, in split order, with no LDS and no barrier.
+constexpr int kFewSplits = 32;
+
+template <int NS>
+__global__ __launch_bounds__(kHead) void decode_combine_few_kernel(const float* __restrict__ part,
+                                                                   int splits,
+                                                                   float* __restrict__ out) {
+  const int bg = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* p = part + (int64_t)bg * splits * kPartStride;
+  float o[NS], m[NS], l[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int sc = s < splits ? s : splits - 1;  // past the last split: re-read it, weight 0
+    o[s] = p[(int64_t)sc * kPartStride + d];
+    m[s] = p[(int64_t)sc * kPartStride + kHead];
+    l[s] = p[(int64_t)sc * kPartStride + kHead + 1];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < splits && l[s] > 0.f) M = fmaxf(M, m[s]);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float w = (s < splits && l[s] > 0.f) ? __expf(m[s] - M) : 0.f;
+    L = fmaf(l[s], w, L);
+    acc = fmaf(o[s], w, acc);
+  }
+  out[(int64_t)bg * kHead + d] = L > 0.f ? acc / L : 0.f;
+}
+
 hipError_t launch_decode_combine(const float* part, int heads, int splits, float* out,
                                  hipStream_t s) {
   if (splits > kMaxSplits) return hipErrorInvalidValue;
-  decode_combine_kernel<<<heads, kHead, 0, s>>>(part, splits, out);
+  if (splits <= 8) decode_combine_few_kernel<8><<<heads, kHead, 0, s>>>(part, splits, out);
+  else if (splits <= 16) decode_combine_few_kernel<16><<<heads, kHead, 0, s>>>(part, splits, out);
+  else if (splits <= kFewSplits)
+    decode_combine_few_kernel<kFewSplits><<<heads, kHead, 0, s>>>(part, splits, out);
+  else decode_combine_kernel<<<heads, kHead, 0, s>>>(part, splits, out);
   return hipGetLastError();
 }
 
