@@ -841,65 +841,69 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   const uint32_t thr_lo = bd.d1 << kHistShift;
   const uint32_t thr_sel = bd.d1 < (uint32_t)(kHistBins - 1) ? ((bd.d1 + 1) << kHistShift) - 1u
                                                             : 0xFFFFFFFFu;
-  const uint64_t by_score = k > 0 ? ~0ull : 0ull;
-  const bool any_forced = z.f_lo > 0 || z.f_hi < n;  // uniform
+  const bool by_score = k > 0;
   uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint64_t lt = lanemask_lt64();
-  // candidates gather in LDS; one global reservation per workgroup at the end
+  // candidates gather in LDS, wave w in its own region [w*kWaveKeys, ...)
+  // (a wave meets at most kWaveKeys keys); one global reservation per
+  // workgroup at the end
+  constexpr int kWaveKeys = kScanKeys / kScanWaves;
   __shared__ uint2 lc[kScanKeys];
-  __shared__ uint32_t lcount, gbase;
-  if (tid == 0) lcount = 0u;
-  __syncthreads();
+  __shared__ uint32_t wcnt[kScanWaves], gbase;
+  uint32_t wpos = 0u;  // uniform per wave
+  // 32-bit key arithmetic (n_cap < 2^31); per-lane pointers computed once so
+  // the unrolled rounds keep few scalar registers live
+  const uint32_t n32 = (uint32_t)n, flo = (uint32_t)z.f_lo, fhi = (uint32_t)z.f_hi;
+  const uint32_t lo = by_score ? thr_lo : 0xFFFFFFFFu;  // k == 0: no candidates
+  const uint32_t hi = by_score ? thr_sel : 0xFFFFFFFFu;  // k == 0: nothing above
+  const uint32_t key0 = (uint32_t)c0 + (uint32_t)(wave * 256 + 4 * lane);
+  uint32_t* bml = bm + (((uint32_t)c0 + (uint32_t)wave * 256u) >> 5) + (lane & 7);
+  const uint32_t bsel = (uint32_t)((lane >> 1) & 3);
 #pragma unroll
   for (int r = 0; r < kScanLoads; ++r) {
-    const int64_t base = c0 + r * (kScanThreads * 4) + wave * 256;
+    const uint32_t kr = key0 + (uint32_t)(r * kScanThreads * 4);
     const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-    uint64_t vm[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t rr = (n - base - e + 3) >> 2;  // lanes with 4*lane + e < n - base
-      vm[e] = rr >= 64 ? ~0ull : rr <= 0 ? 0ull : ((1ull << rr) - 1ull);
-    }
     uint64_t ms[4], mc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t key = base + 4 * lane + e;
-      const uint64_t fm = any_forced ? __ballot(key < z.f_lo || key >= z.f_hi) & vm[e] : 0ull;
-      const uint64_t rk = vm[e] & ~fm & by_score;
-      ms[e] = __ballot(sb[e] > thr_sel) & rk;
-      mc[e] = __ballot(sb[e] >= thr_lo) & ~ms[e] & rk;
-      ms[e] |= fm;
+      const uint32_t key = kr + (uint32_t)e;
+      const bool valid = key < n32;
+      const bool forced = key < flo || key >= fhi;
+      const bool above = by_score && sb[e] > hi;
+      ms[e] = __ballot(valid && (forced || above));
+      mc[e] = __ballot(valid && !forced && !above && by_score && sb[e] >= lo);
     }
-    // even lanes store words 0..3 of the block, odd lanes words 4..7
-    const bool odd = lane & 1;
-    const uint64_t a = odd ? ms[2] : ms[0], a2 = odd ? ms[3] : ms[1];
-    *reinterpret_cast<uint4*>(bm + (base >> 5) + (odd ? 4 : 0)) =
-        make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)a2, (uint32_t)(a2 >> 32));
-    const uint32_t tot = (uint32_t)(__popcll(mc[0]) + __popcll(mc[1]) + __popcll(mc[2]) +
-                                    __popcll(mc[3]));
-    if (tot) {
-      uint32_t pos = 0u;
-      if (lane == 0) pos = atomicAdd(&lcount, tot);
-      pos = __builtin_amdgcn_readfirstlane(pos);  // every lane is active here
+    // lane l < 8 stores word l of the block (words 2e, 2e+1 = ballot e)
+    {
+      const uint64_t a = bsel == 0 ? ms[0] : bsel == 1 ? ms[1] : bsel == 2 ? ms[2] : ms[3];
+      if (lane < 8) bml[r * (kScanThreads * 4 / 32)] = (lane & 1) ? (uint32_t)(a >> 32) : (uint32_t)a;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((mc[e] >> lane) & 1ull) {
-          const uint32_t p2 = pos + (uint32_t)__popcll(mc[e] & lt);
-          lc[p2] = make_uint2(sb[e], (uint32_t)(base + 4 * lane + e));
-        }
-        pos += (uint32_t)__popcll(mc[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      if ((mc[e] >> lane) & 1ull)
+        lc[wave * kWaveKeys + wpos + (uint32_t)__popcll(mc[e] & lt)] = make_uint2(sb[e], kr + e);
+      wpos += (uint32_t)__popcll(mc[e]);
     }
   }
+  if (lane == 0) wcnt[wave] = wpos;
   __syncthreads();
-  const uint32_t cnt = lcount;  // <= kScanKeys
-  if (cnt == 0) return;
+  uint32_t pre[kScanWaves], cnt = 0u;
+#pragma unroll
+  for (int w = 0; w < kScanWaves; ++w) {
+    pre[w] = cnt;
+    cnt += wcnt[w];
+  }
+  if (cnt == 0) return;  // uniform
   if (tid == 0) gbase = atomicAdd(&counters[bg], cnt);
   __syncthreads();
   const uint32_t g0 = gbase;
   uint2* gc = cand + (int64_t)bg * n_cap;
-  for (uint32_t t = tid; t < cnt; t += kScanThreads)
-    if (g0 + t < (uint32_t)n) gc[g0 + t] = lc[t];
+  for (uint32_t t = tid; t < cnt; t += kScanThreads) {
+    int w = 0;
+#pragma unroll
+    for (int x = 1; x < kScanWaves; ++x) w += t >= pre[x] ? 1 : 0;
+    if (g0 + t < (uint32_t)n) gc[g0 + t] = lc[w * kWaveKeys + (t - pre[w])];
+  }
 }
 
 // Among candidates whose low 21 score bits match (vmask, vval) -- and, when
