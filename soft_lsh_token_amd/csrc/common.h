@@ -9,6 +9,8 @@ constexpr int kHead = 128;       // supported head dimension
 constexpr int kHistBins = 1024;  // first top-k digit: float bits >> 21 (non-negative floats)
 constexpr int kHistShift = 21;
 constexpr int kXcds = 8;         // workgroup i of a dispatch runs on XCD i mod 8
+constexpr int kSplitKeys = 64;   // idx entries per split of the split-k attention
+constexpr int kPartStride = kHead + 2;  // a split's partial: o[kHead], m, l
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

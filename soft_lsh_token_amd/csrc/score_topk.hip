@@ -942,30 +942,29 @@ __device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask, uint3
   return r;
 }
 
-// grid: B*Hq blocks of kResThreads.
-__global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
-    int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
-    int sink, int window, int Hq, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ counters,
-    const uint32_t* __restrict__ bitmap, int64_t words, const uint2* __restrict__ cand,
-    int32_t* __restrict__ idx) {
-  const int bg = blockIdx.x;
-  const int b = bg / Hq;
+// LDS of one resolve.
+struct ResolveSmem {
+  uint32_t wsum[kResWaves];
+  Boundary shb;
+  uint32_t h128[128];
+  Pick shpick;
+  uint32_t seg_total;
+  uint2 lcand[kCandCap];
+  uint32_t lbm[kSegBlocks * 8];
+};
+
+// The resolve of head bg (all threads of a kResThreads workgroup): radix
+// select of the candidates that complete the top-k, then every selected key
+// handed to emit(position, key), positions ascending with the key.
+template <typename Emit>
+__device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSizes& z,
+                                             const uint32_t* __restrict__ hist,
+                                             const uint32_t* __restrict__ counters,
+                                             const uint32_t* __restrict__ bitmap, int64_t words,
+                                             const uint2* __restrict__ cand, ResolveSmem& sm,
+                                             Emit emit) {
   const int tid = threadIdx.x;
-  const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
   const int64_t n = z.n, k = z.k;
-  int32_t* out = idx + (int64_t)bg * k_max;
-  if (z.total == 0) {
-    for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
-    return;
-  }
-  __shared__ uint32_t wsum[kResWaves];
-  __shared__ Boundary shb;
-  __shared__ uint32_t h128[128];
-  __shared__ Pick shpick;
-  __shared__ uint32_t seg_total;
-  __shared__ uint2 lcand[kCandCap];
-  __shared__ uint32_t lbm[kSegBlocks * 8];
 
   // every independent load at once: candidate count, the first kCandCap
   // candidates (whatever their count), this thread's first bitmap block,
@@ -984,18 +983,18 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
   const int64_t bl0 = tid < nblocks ? tid : 0;
   uint4 bw0 = reinterpret_cast<const uint4*>(bm)[bl0 * 2];
   uint4 bw1 = reinterpret_cast<const uint4*>(bm)[bl0 * 2 + 1];
-  const Boundary bd = find_boundary<kResThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
+  const Boundary bd = find_boundary<kResThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, sm.wsum, &sm.shb);
   const uint32_t C = Cg < (uint32_t)n ? Cg : (uint32_t)n;
   const bool in_lds = C <= (uint32_t)kCandCap;
   if (in_lds) {
 #pragma unroll
     for (int i = 0; i < kCandPerThread; ++i) {
       const uint32_t ci = (uint32_t)(i * kResThreads + tid);
-      if (ci < C) lcand[ci] = cv[i];
+      if (ci < C) sm.lcand[ci] = cv[i];
     }
   }
   __syncthreads();
-  const uint2* lc = in_lds ? lcand : gc;
+  const uint2* lc = in_lds ? sm.lcand : gc;
 
   // the candidates that complete the top-k
   uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C when k > 0
@@ -1003,7 +1002,7 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
   if (k > 0 && need < C) {
     uint32_t ties = 0u;
     for (int shift = 14; shift >= 0; shift -= 7) {
-      const Pick pk = radix_pick<false>(lc, C, vmask, vval, 0u, 0u, shift, need, h128, &shpick);
+      const Pick pk = radix_pick<false>(lc, C, vmask, vval, 0u, 0u, shift, need, sm.h128, &sm.shpick);
       need -= pk.before;
       vval |= pk.digit << shift;
       vmask |= 127u << shift;
@@ -1015,7 +1014,7 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
       while (((uint64_t)1 << top) < (uint64_t)n) ++top;
       int shift = top > 7 ? top - 7 : 0;
       for (;;) {
-        const Pick pk = radix_pick<true>(lc, C, vmask, vval, imask, ival, shift, need, h128, &shpick);
+        const Pick pk = radix_pick<true>(lc, C, vmask, vval, imask, ival, shift, need, sm.h128, &sm.shpick);
         need -= pk.before;
         ival |= pk.digit << shift;
         imask |= 127u << shift;
@@ -1037,7 +1036,7 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
       bw1 = reinterpret_cast<const uint4*>(bm)[bl * 2 + 1];
     }
     const bool mine = tid < segb;
-    uint4* lb = reinterpret_cast<uint4*>(lbm);
+    uint4* lb = reinterpret_cast<uint4*>(sm.lbm);
     lb[tid * 2] = mine ? bw0 : make_uint4(0u, 0u, 0u, 0u);
     lb[tid * 2 + 1] = mine ? bw1 : make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
@@ -1047,7 +1046,7 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
       const int64_t blk = (int64_t)(e.y >> 8) - b0;
       if (blk >= 0 && blk < segb && (v > vval || (v == vval && e.y <= imax))) {
         const uint32_t i4 = (e.y >> 2) & 63u, ee = e.y & 3u;
-        atomicOr(&lbm[blk * 8 + ee * 2 + (i4 >> 5)], 1u << (i4 & 31));
+        atomicOr(&sm.lbm[blk * 8 + ee * 2 + (i4 >> 5)], 1u << (i4 & 31));
       }
     }
     __syncthreads();
@@ -1066,14 +1065,14 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
         const int blk = (int)(wi >> 3), sub = (int)(wi & 7);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t b8 = (lbm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
+          const uint32_t b8 = (sm.lbm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
           x |= spread4(b8) << e;  // key 4i + e of the word at bit 4i + e
         }
       }
       kw[q] = x;
       cnt += __popc(x);
     }
-    const uint32_t incw = block_incl_scan<kResThreads>(cnt, wsum);
+    const uint32_t incw = block_incl_scan<kResThreads>(cnt, sm.wsum);
     uint32_t pos = written + incw - cnt;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -1082,15 +1081,38 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
       while (x) {
         const int bit = __ffs(x) - 1;
         x &= x - 1;
-        if (pos < (uint32_t)k_max) out[pos] = (int32_t)(kbase + bit);
+        emit(pos, (int32_t)(kbase + bit));
         ++pos;
       }
     }
-    if (tid == kResThreads - 1) seg_total = incw;
+    if (tid == kResThreads - 1) sm.seg_total = incw;
     __syncthreads();
-    written += seg_total;
+    written += sm.seg_total;
     __syncthreads();
   }
+}
+
+// grid: B*Hq blocks of kResThreads.
+__global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
+    int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
+    int sink, int window, int Hq, const uint32_t* __restrict__ hist,
+    const uint32_t* __restrict__ counters,
+    const uint32_t* __restrict__ bitmap, int64_t words, const uint2* __restrict__ cand,
+    int32_t* __restrict__ idx) {
+  const int bg = blockIdx.x;
+  const int b = bg / Hq;
+  const int tid = threadIdx.x;
+  const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
+  int32_t* out = idx + (int64_t)bg * k_max;
+  if (z.total == 0) {
+    for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
+    return;
+  }
+  __shared__ ResolveSmem sm;
+  resolve_head(bg, n_cap, z, hist, counters, bitmap, words, cand, sm,
+               [&](uint32_t pos, int32_t key) {
+                 if (pos < (uint32_t)k_max) out[pos] = key;
+               });
   for (int64_t t = z.total + tid; t < k_max; t += kResThreads) out[t] = -1;
 }
 

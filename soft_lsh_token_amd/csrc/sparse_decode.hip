@@ -16,8 +16,6 @@ namespace socketlsh {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kSplitKeys = 64;  // entries of idx per workgroup
-constexpr int kPartStride = kHead + 2;
 
 static inline size_t align256d(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -641,6 +641,11 @@ def test_run_twice_bitwise():
     (dict(name="c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 300, 999], n_cap=1000, k=5), (8, 8)),
     (dict(name="c2", n=3000, L=60, P=10, Hq=16, Hkv=8), (0, 0)),
     (dict(name="c1"), (0, 16)),
+    # longer rows: the scan + resolve top-k
+    (dict(name="c2", n=20000), (0, 0)),
+    (dict(name="c2", n=20000, k=300), (64, 128)),          # k_max 492: 8 splits
+    (dict(name="c4", n=(9000, 30000), B=3, Hq=8, Hkv=2, lens=[30000, 9000, 12345]), (16, 16)),
+    (dict(name="c1", n=10000, k=200), (0, 0)),              # float32
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else f"sw{c}")
 def test_decode_step_matches_three_calls(case, sw):
     """socket_decode_step (append hashed inside the table kernel) equals
