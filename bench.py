@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=40)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-128k", action="store_true")
+    p.add_argument("--no-batched", action="store_true",
+                   help="skip the 16-sequence ragged batch (lengths 8K-32K)")
     p.add_argument("--no-hard", action="store_true",
                    help="skip the hard-LSH comparison mode")
     p.add_argument("--no-p10", action="store_true",
@@ -80,9 +82,10 @@ class Case:
             f"n_cap={w.n_cap}, replicas={replicas})")
         dev = "cuda:0"
         bf = torch.bfloat16
-        self.n = int(w.lens[0])
+        self.n = int(w.lens.max())             # prefill count (every sequence's rows)
+        self.kv_keys = w.Hkv * int((w.lens.astype(np.int64) + 1).sum())  # keys scored per step
         self.B, self.Hq, self.Hkv, self.L, self.P = w.B, w.Hq, w.Hkv, w.L, w.P
-        self.k = int(w.ks[0])
+        self.k = int(w.ks.max())
         self.sink, self.window = int(sink), int(window)
         self.k_max = self.k + self.sink + self.window   # index row: top-k + sink + window
         K0 = torch.from_numpy(w.K).to(dev).to(bf)
@@ -93,8 +96,8 @@ class Case:
         self.W = torch.from_numpy(w.W).to(dev).to(bf)
         self.q = torch.from_numpy(w.q).to(dev).to(bf)
         self.pos_prefill = torch.zeros(w.B, dtype=torch.int32, device=dev)
-        self.pos_append = torch.full((w.B,), self.n, dtype=torch.int32, device=dev)
-        self.lens = torch.full((w.B,), self.n + 1, dtype=torch.int32, device=dev)
+        self.pos_append = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
+        self.lens = torch.from_numpy(w.lens.astype(np.int32) + 1).to(dev)
         self.ks = torch.from_numpy(w.ks).to(dev)
         self.ids = [S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, dev) for _ in range(replicas)]
         self.vn = [torch.empty(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
@@ -287,7 +290,7 @@ def dense_decode(case, torch, launches):
     us, _ = gpu_batch_us(torch, lambda i: case._ok(lib.socket_dense_decode(
         *case.c_dense[i % case.replicas]), "socket_dense_decode"), launches)
     w = case.w
-    kv_bytes = w.B * w.Hkv * (case.n + 1) * 2 * w.d * 2
+    kv_bytes = case.kv_keys * 2 * w.d * 2
     return dict(us=us, kv_gbs=kv_bytes / (us * 1e-6) / 1e9)
 
 
@@ -371,7 +374,7 @@ def scorer_bytes(case):
     packed) and its float32 norm are read and G float32 scores are written."""
     w = case.w
     G = w.Hq // w.Hkv
-    kv_keys = w.B * w.Hkv * (case.n + 1)
+    kv_keys = case.kv_keys
     return kv_keys * ((w.L * w.P + 7) // 8 + 4 + 4 * G), kv_keys
 
 
@@ -381,8 +384,7 @@ def scorer_stored_bytes(case):
     from soft_lsh_token_amd import layout
     w = case.w
     G = w.Hq // w.Hkv
-    kv_keys = w.B * w.Hkv * (case.n + 1)
-    return kv_keys * (layout.key_bytes(w.L, w.P) + 4 + 4 * G)
+    return case.kv_keys * (layout.key_bytes(w.L, w.P) + 4 + 4 * G)
 
 
 def counters_traffic(launch_bytes):
@@ -485,7 +487,7 @@ def main():
     achieved = launch_bytes / (score_us * 1e-6) / 1e9
     traffic = counters_traffic(launch_bytes)
     w = case.w
-    keys_per_step = w.B * w.Hq * (case.n + 1)
+    keys_per_step = case.kv_keys * (w.Hq // w.Hkv)
     extra32 = dict(
         step_us_wall=sec * 1e6, step_us_wall_three_calls=sec3 * 1e6,
         step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
@@ -512,7 +514,7 @@ def main():
         dense128["socket_speedup"] = dense128["us"] / gpu3
         extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, stage_us=st3,
                         scorer_launch_us=sc3,
-                        keys_per_s=c3.w.B * c3.w.Hq * (c3.n + 1) / sec3,
+                        keys_per_s=c3.kv_keys * (c3.w.Hq // c3.w.Hkv) / sec3,
                         scorer_gbs=lb3 / (sc3 * 1e-6) / 1e9,
                         prefill=pre128, dense_decode=dense128)
         log(f"[bench] 128K: {extra128}")
@@ -542,13 +544,38 @@ def main():
         lb10, _ = scorer_bytes(c10)
         extra_p10 = dict(step_us_wall=sec10 * 1e6, step_us_gpu=gpu10, stage_us=st10,
                          scorer_launch_us=sc10,
-                         keys_per_s=c10.w.B * c10.w.Hq * (c10.n + 1) / sec10,
+                         keys_per_s=c10.kv_keys * (c10.w.Hq // c10.w.Hkv) / sec10,
                          scorer_gbs_algorithmic=lb10 / (sc10 * 1e-6) / 1e9,
                          scorer_gbs_stored=scorer_stored_bytes(c10) / (sc10 * 1e-6) / 1e9,
                          prefill=pre10)
         log(f"[bench] 32K at P=10, L=60: {extra_p10}")
         c10.free()
         del c10
+        torch.cuda.empty_cache()
+
+    extra_b16 = None
+    if not args.no_batched:
+        c4 = Case("c4", 2, lib, torch, S)
+        for r in range(c4.replicas):
+            c4.prefill(r)
+        torch.cuda.synchronize()
+        sec4 = timed_steps(c4, torch, max(20, args.steps // 4), max(5, args.warmup // 4))
+        st4, gpu4, _ = per_stage(c4, torch, max(20, args.steps // 4))
+        sc4 = scorer_launch_us(c4, torch, 8 * c4.replicas)
+        lb4, kk4 = scorer_bytes(c4)
+        dense4 = dense_decode(c4, torch, 4 * c4.replicas)
+        dense4["socket_speedup"] = dense4["us"] / gpu4
+        lens4 = c4.w.lens
+        extra_b16 = dict(sequences=int(c4.w.B), lens_min=int(lens4.min()),
+                         lens_max=int(lens4.max()), kv_keys=kk4,
+                         step_us_wall=sec4 * 1e6, step_us_gpu=gpu4, stage_us=st4,
+                         keys_per_s=c4.kv_keys * (c4.w.Hq // c4.w.Hkv) / sec4,
+                         scorer_launch_us=sc4, scorer_gbs=lb4 / (sc4 * 1e-6) / 1e9,
+                         scorer_hbm_frac=lb4 / (sc4 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         dense_decode=dense4)
+        log(f"[bench] 16 ragged sequences: {extra_b16}")
+        c4.free()
+        del c4
         torch.cuda.empty_cache()
 
     cpu = None
@@ -578,7 +605,8 @@ def main():
                      "kernel": "scorer_kernel (soft-count scores + first-digit histogram)",
                      "bytes_per_launch": launch_bytes, "kv_keys_per_launch": kv_keys},
         "cpu_baseline": cpu,
-        "extra": {"ctx32k": extra32, "ctx128k": extra128, "ctx32k_p10_l60": extra_p10},
+        "extra": {"ctx32k": extra32, "ctx128k": extra128, "ctx32k_p10_l60": extra_p10,
+                  "batch16_ragged": extra_b16},
     }
     print(json.dumps(line), flush=True)
 
