@@ -203,7 +203,11 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     append_block<T>(W, Hkv, L, P, TL, nab, rows, ak);
     return;
   }
-  const int bh = blockIdx.x >> 4, j = blockIdx.x & 15;
+  // Logical table block lid = (blockIdx mod 8) * (2 rows) + blockIdx / 8: the
+  // 16 blocks of a KV row share an XCD (blocks go to the XCDs round robin),
+  // so the 16-byte slots they write into each image line meet in one L2.
+  const int lid = (int)(blockIdx.x % kXcds) * (rows * 16 / kXcds) + (int)(blockIdx.x / kXcds);
+  const int bh = lid >> 4, j = lid & 15;
   const int b = bh / Hkv, h = bh % Hkv;
   const int bg0 = b * Hq + h * G;
   const int tid = threadIdx.x;
