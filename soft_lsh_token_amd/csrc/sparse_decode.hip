@@ -250,6 +250,61 @@ __global__ __launch_bounds__(kHead) void decode_combine_few_kernel(const float* 
   out[(int64_t)bg * kHead + d] = L > 0.f ? acc / L : 0.f;
 }
 
+// The merge for up to NG*kFewSplits splits: group x (kHead threads) merges
+// splits [x*per, (x+1)*per) as decode_combine_few_kernel does, in one round
+// trip, and group 0 then merges the NG group results in group order.
+template <int NG>
+__global__ __launch_bounds__(NG * kHead) void decode_combine_wide_kernel(
+    const float* __restrict__ part, int splits, float* __restrict__ out) {
+  const int bg = blockIdx.x;
+  const int x = threadIdx.x / kHead, d = threadIdx.x % kHead;
+  const int per = (splits + NG - 1) / NG;
+  const int s0 = x * per;
+  const int s1 = s0 + per < splits ? s0 + per : splits;
+  const float* p = part + (int64_t)bg * splits * kPartStride;
+  __shared__ float gm[NG], gl[NG], go[NG][kHead];
+  float o[kFewSplits], m[kFewSplits], l[kFewSplits];
+#pragma unroll
+  for (int t = 0; t < kFewSplits; ++t) {
+    int sc = s0 + t < s1 ? s0 + t : s1 - 1;  // past the group's last split: re-read it, weight 0
+    if (sc < 0) sc = 0;
+    o[t] = p[(int64_t)sc * kPartStride + d];
+    m[t] = p[(int64_t)sc * kPartStride + kHead];
+    l[t] = p[(int64_t)sc * kPartStride + kHead + 1];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < kFewSplits; ++t)
+    if (s0 + t < s1 && l[t] > 0.f) M = fmaxf(M, m[t]);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < kFewSplits; ++t) {
+    const float w = (s0 + t < s1 && l[t] > 0.f) ? __expf(m[t] - M) : 0.f;
+    L = fmaf(l[t], w, L);
+    acc = fmaf(o[t], w, acc);
+  }
+  go[x][d] = acc;
+  if (d == 0) {
+    gm[x] = M;
+    gl[x] = L;
+  }
+  __syncthreads();
+  if (x == 0) {
+    float MM = -INFINITY;
+#pragma unroll
+    for (int y = 0; y < NG; ++y)
+      if (gl[y] > 0.f) MM = fmaxf(MM, gm[y]);
+    float LL = 0.f, oo = 0.f;
+#pragma unroll
+    for (int y = 0; y < NG; ++y) {
+      const float w = gl[y] > 0.f ? __expf(gm[y] - MM) : 0.f;
+      LL = fmaf(gl[y], w, LL);
+      oo = fmaf(go[y][d], w, oo);
+    }
+    out[(int64_t)bg * kHead + d] = LL > 0.f ? oo / LL : 0.f;
+  }
+}
+
 hipError_t launch_decode_combine(const float* part, int heads, int splits, float* out,
                                  hipStream_t s) {
   if (splits > kMaxSplits) return hipErrorInvalidValue;
@@ -257,6 +312,10 @@ hipError_t launch_decode_combine(const float* part, int heads, int splits, float
   else if (splits <= 16) decode_combine_few_kernel<16><<<heads, kHead, 0, s>>>(part, splits, out);
   else if (splits <= kFewSplits)
     decode_combine_few_kernel<kFewSplits><<<heads, kHead, 0, s>>>(part, splits, out);
+  else if (splits <= 4 * kFewSplits)
+    decode_combine_wide_kernel<4><<<heads, 4 * kHead, 0, s>>>(part, splits, out);
+  else if (splits <= 8 * kFewSplits)
+    decode_combine_wide_kernel<8><<<heads, 8 * kHead, 0, s>>>(part, splits, out);
   else decode_combine_kernel<<<heads, kHead, 0, s>>>(part, splits, out);
   return hipGetLastError();
 }
