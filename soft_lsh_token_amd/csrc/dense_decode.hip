@@ -24,7 +24,7 @@ namespace socketlsh {
 constexpr int kDenseThreads = 256;
 constexpr int kDenseRows = kDenseThreads / 16;  // keys per workgroup step
 constexpr int kDenseU = 4;                      // keys per row per batch
-constexpr int kDenseBlocks = 1024;              // workgroups aimed for (4 per CU)
+constexpr int kDenseBlocks = 512;               // workgroups aimed for (2 per CU)
 constexpr int kDenseMaxSplits = 1024;           // the combine kernel's limit
 constexpr int kDensePart = kHead + 2;
 
