@@ -131,7 +131,12 @@ static int image_stride(int G, int L) {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kScanKeys = 8192;  // keys per top-k scan workgroup (the bitmap covers whole ones)
+// Keys per top-k scan workgroup (the bitmap covers whole ones).  Its LDS
+// (one candidate slot per key, 72 KiB) lets two workgroups share a CU, 512
+// over the chip; 9216 rather than 8192 keeps a 32K or 128K row plus its
+// appended keys in 4 or 15 workgroups instead of adding a one-key fifth or
+// seventeenth, which at 32 heads would not fit in one wave of residency.
+constexpr int kScanKeys = 9216;
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
   const int G = Hq / Hkv;
@@ -712,7 +717,8 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
 // e-th keys).
 constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kScanLoads = kScanKeys / (kScanThreads * 4);  // 16-byte loads per thread (8)
+constexpr int kScanLoads = kScanKeys / (kScanThreads * 4);  // 16-byte loads per thread (9)
+static_assert(kScanKeys % (kScanThreads * 4) == 0, "whole 1024-key load rounds (and 256-key bitmap blocks)");
 constexpr int kResThreads = 1024;
 constexpr int kResWaves = kResThreads / 64;
 constexpr int kCandCap = 6144;                     // candidates resolved in LDS
