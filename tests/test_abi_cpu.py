@@ -102,7 +102,7 @@ def test_score_argument_checks():
 def test_dense_decode_argument_checks():
     lib = S.lib()
     need = S.socket_dense_decode_workspace(1, 32, 8, 128, 32768)
-    assert need >= 32 * 128 * 130 * 4            # 128 splits of 256 keys, (o, m, l) per head
+    assert need >= 32 * 64 * 130 * 4             # 64 splits of 512 keys, (o, m, l) per head
     assert S.socket_dense_decode_workspace(1, 32, 8, 64, 32768) == 0
     assert S.socket_dense_decode_workspace(1, 32, 8, 128, 0) == 0
     assert S.socket_dense_decode_workspace(1, 32, 5, 128, 100) == 0
