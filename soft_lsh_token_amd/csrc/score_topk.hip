@@ -715,10 +715,13 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
 // words; words 8j + 2e and 8j + 2e + 1 hold bit i = key 256j + 4i + e (the
 // ballot, over a wave that loaded 4 consecutive keys per lane, of the lanes'
 // e-th keys).
-constexpr int kScanThreads = 256;
+// 12 waves, each taking three rounds of 256 keys: every wave runs a short
+// serial chain of ballots and LDS appends, and with two workgroups a CU each
+// SIMD has six waves to issue from.
+constexpr int kScanThreads = 768;
 constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kScanLoads = kScanKeys / (kScanThreads * 4);  // 16-byte loads per thread (9)
-static_assert(kScanKeys % (kScanThreads * 4) == 0, "whole 1024-key load rounds (and 256-key bitmap blocks)");
+constexpr int kScanLoads = kScanKeys / (kScanThreads * 4);  // 16-byte loads per thread (3)
+static_assert(kScanKeys % (kScanThreads * 4) == 0, "whole load rounds of four keys a thread");
 constexpr int kResThreads = 1024;
 constexpr int kResWaves = kResThreads / 64;
 constexpr int kCandCap = 6144;                     // candidates resolved in LDS
@@ -783,16 +786,18 @@ __device__ __forceinline__ SelSizes sel_sizes(int64_t n_cap, int32_t len, int32_
 
 // Bin of the first digit that holds the k-th largest score, and how many keys
 // lie in higher bins, from the head's histogram.  Thread t of NT takes the
-// KPT = 1024/NT bins counted down from 1023 - KPT*t.  All threads must call it.
+// KPT = ceil(1024/NT) bins counted down from 1023 - KPT*t (none past bin 0).
+// All threads must call it.
 template <int NT>
 __device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum, Boundary* sh) {
-  constexpr int KPT = kHistBins / NT;
+  constexpr int KPT = (kHistBins + NT - 1) / NT;
   const int tid = threadIdx.x;
   uint32_t c[KPT];
   uint32_t sum = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    c[i] = hh[kHistBins - 1 - KPT * tid - i];
+    const int bin = kHistBins - 1 - KPT * tid - i;
+    c[i] = bin >= 0 ? hh[bin] : 0u;
     sum += c[i];
   }
   if (tid == 0) *sh = Boundary{0u, 0u};
@@ -800,7 +805,8 @@ __device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum
   uint32_t prev = inc - sum;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    if (prev < k && k <= prev + c[i]) *sh = Boundary{(uint32_t)(kHistBins - 1 - KPT * tid - i), prev};
+    const int bin = kHistBins - 1 - KPT * tid - i;
+    if (bin >= 0 && prev < k && k <= prev + c[i]) *sh = Boundary{(uint32_t)bin, prev};
     prev += c[i];
   }
   __syncthreads();
