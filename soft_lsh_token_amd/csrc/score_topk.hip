@@ -786,33 +786,54 @@ __device__ __forceinline__ SelSizes sel_sizes(int64_t n_cap, int32_t len, int32_
 
 // Bin of the first digit that holds the k-th largest score, and how many keys
 // lie in higher bins, from the head's histogram.  Thread t of NT takes the
-// KPT = ceil(1024/NT) bins counted down from 1023 - KPT*t (none past bin 0).
-// All threads must call it.
+// KPT = ceil(1024/NT) bins counted down from 1023 - KPT*t (none past bin 0):
+// load_hist_slice reads them (issued before a kernel's bulk loads, so the
+// boundary does not wait behind those), boundary_of finds the bin.  All
+// threads must call boundary_of.
 template <int NT>
-__device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum, Boundary* sh) {
-  constexpr int KPT = (kHistBins + NT - 1) / NT;
-  const int tid = threadIdx.x;
+struct HistSlice {
+  static constexpr int KPT = (kHistBins + NT - 1) / NT;
   uint32_t c[KPT];
+};
+
+template <int NT>
+__device__ __forceinline__ HistSlice<NT> load_hist_slice(const uint32_t* hh) {
+  HistSlice<NT> h;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < HistSlice<NT>::KPT; ++i) {
+    const int bin = kHistBins - 1 - HistSlice<NT>::KPT * tid - i;
+    h.c[i] = bin >= 0 ? hh[bin] : 0u;
+  }
+  return h;
+}
+
+template <int NT>
+__device__ Boundary boundary_of(const HistSlice<NT>& h, uint32_t k, uint32_t* wsum, Boundary* sh) {
+  constexpr int KPT = HistSlice<NT>::KPT;
+  const int tid = threadIdx.x;
   uint32_t sum = 0u;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int bin = kHistBins - 1 - KPT * tid - i;
-    c[i] = bin >= 0 ? hh[bin] : 0u;
-    sum += c[i];
-  }
+  for (int i = 0; i < KPT; ++i) sum += h.c[i];
   if (tid == 0) *sh = Boundary{0u, 0u};
   const uint32_t inc = block_incl_scan<NT>(sum, wsum);
   uint32_t prev = inc - sum;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int bin = kHistBins - 1 - KPT * tid - i;
-    if (bin >= 0 && prev < k && k <= prev + c[i]) *sh = Boundary{(uint32_t)bin, prev};
-    prev += c[i];
+    if (bin >= 0 && prev < k && k <= prev + h.c[i]) *sh = Boundary{(uint32_t)bin, prev};
+    prev += h.c[i];
   }
   __syncthreads();
   const Boundary r = *sh;
   __syncthreads();
   return r;
+}
+
+template <int NT>
+__device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum, Boundary* sh) {
+  const HistSlice<NT> h = load_hist_slice<NT>(hh);
+  return boundary_of<NT>(h, k, wsum, sh);
 }
 
 // grid: B*Hq*CH blocks of kScanThreads (rounded up to a multiple of kXcds),
@@ -838,8 +859,9 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   const int64_t c0 = (int64_t)c * kScanKeys;
   if (c0 >= n) return;
 
-  // every score of this workgroup first: load r covers keys
-  // c0 + r*1024 + 256*wave + 4*lane .. +3
+  // the head's histogram slice, then every score of this workgroup: load r
+  // covers keys c0 + r*4*kScanThreads + 256*wave + 4*lane .. +3
+  const HistSlice<kScanThreads> hs = load_hist_slice<kScanThreads>(hist + (int64_t)bg * kHistBins);
   const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
   uint4 v[kScanLoads];
 #pragma unroll
@@ -850,7 +872,7 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   }
   __shared__ uint32_t wsum[kScanWaves];
   __shared__ Boundary shb;
-  const Boundary bd = find_boundary<kScanThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
+  const Boundary bd = boundary_of<kScanThreads>(hs, (uint32_t)k, wsum, &shb);
   // above d1: bits > thr_sel; in d1: bits >= thr_lo and not above (the top
   // digit is clamped to kHistBins - 1 here as in the histogram).  Sink and
   // window keys are selected whatever their score and never candidates.
@@ -985,6 +1007,7 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   // every independent load at once: candidate count, the first kCandCap
   // candidates (whatever their count), this thread's first bitmap block,
   // its histogram bin (inside find_boundary)
+  const HistSlice<kResThreads> hs = load_hist_slice<kResThreads>(hist + (int64_t)bg * kHistBins);
   const uint2* gc = cand + (int64_t)bg * n_cap;
   const uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint32_t Cg = counters[bg];
@@ -997,9 +1020,9 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   }
   const int64_t nblocks = (n + 255) >> 8;
   const int64_t bl0 = tid < nblocks ? tid : 0;
-  uint4 bw0 = reinterpret_cast<const uint4*>(bm)[bl0 * 2];
-  uint4 bw1 = reinterpret_cast<const uint4*>(bm)[bl0 * 2 + 1];
-  const Boundary bd = find_boundary<kResThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, sm.wsum, &sm.shb);
+  const uint4 bw0 = reinterpret_cast<const uint4*>(bm)[bl0 * 2];
+  const uint4 bw1 = reinterpret_cast<const uint4*>(bm)[bl0 * 2 + 1];
+  const Boundary bd = boundary_of<kResThreads>(hs, (uint32_t)k, sm.wsum, &sm.shb);
   const uint32_t C = Cg < (uint32_t)n ? Cg : (uint32_t)n;
   const bool in_lds = C <= (uint32_t)kCandCap;
   if (in_lds) {
@@ -1008,6 +1031,14 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
       const uint32_t ci = (uint32_t)(i * kResThreads + tid);
       if (ci < C) sm.lcand[ci] = cv[i];
     }
+  }
+  // the first segment's bitmap blocks go to LDS now, while their loads are
+  // certainly in (the radix passes below do not touch lbm)
+  {
+    const bool mine = tid < nblocks;
+    uint4* lb = reinterpret_cast<uint4*>(sm.lbm);
+    lb[tid * 2] = mine ? bw0 : make_uint4(0u, 0u, 0u, 0u);
+    lb[tid * 2 + 1] = mine ? bw1 : make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
   const uint2* lc = in_lds ? sm.lcand : gc;
@@ -1046,16 +1077,16 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   uint32_t written = 0;
   for (int64_t b0 = 0; b0 < nblocks; b0 += kSegBlocks) {
     const int64_t segb = (nblocks - b0) < kSegBlocks ? (nblocks - b0) : kSegBlocks;
-    if (b0 > 0) {
+    if (b0 > 0) {  // later segments: their bitmap blocks now (segment 0 is in LDS already)
       const int64_t bl = tid < segb ? b0 + tid : b0;
-      bw0 = reinterpret_cast<const uint4*>(bm)[bl * 2];
-      bw1 = reinterpret_cast<const uint4*>(bm)[bl * 2 + 1];
+      const uint4 w0 = reinterpret_cast<const uint4*>(bm)[bl * 2];
+      const uint4 w1 = reinterpret_cast<const uint4*>(bm)[bl * 2 + 1];
+      const bool mine = tid < segb;
+      uint4* lb = reinterpret_cast<uint4*>(sm.lbm);
+      lb[tid * 2] = mine ? w0 : make_uint4(0u, 0u, 0u, 0u);
+      lb[tid * 2 + 1] = mine ? w1 : make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
     }
-    const bool mine = tid < segb;
-    uint4* lb = reinterpret_cast<uint4*>(sm.lbm);
-    lb[tid * 2] = mine ? bw0 : make_uint4(0u, 0u, 0u, 0u);
-    lb[tid * 2 + 1] = mine ? bw1 : make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
     for (uint32_t i = tid; i < C; i += kResThreads) {
       const uint2 e = lc[i];
       const uint32_t v = e.x & 0x1FFFFFu;
