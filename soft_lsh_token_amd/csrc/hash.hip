@@ -288,14 +288,97 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
           a[tt][kk] = live ? v : zero;
         }
       } else {
+        // stored negated: the accumulator of a plane is then -(W k), rounded as
+        // W k with the sign flipped, so the plane's bit (W k > 0) is its sign
+        // bit (an exact zero sums to +0 from the +0 start and gives 0)
         const int table = 8 * wave + 4 * hout + 2 * tt + (r >> 3);
         const uint16_t* wr = W + ((int64_t)(table * 8 + (r & 7))) * kHead + 64 * half;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) a[tt][kk] = *reinterpret_cast<const bf16x8_t*>(wr + 8 * kk);
+        for (int kk = 0; kk < 8; ++kk) {
+          const uint4 v = *reinterpret_cast<const uint4*>(wr + 8 * kk);
+          a[tt][kk] = __builtin_bit_cast(
+              bf16x8_t, make_uint4(v.x ^ 0x80008000u, v.y ^ 0x80008000u, v.z ^ 0x80008000u,
+                                   v.w ^ 0x80008000u));
+        }
       }
     }
   }
   lds_barrier();
+  if constexpr (!WIDE) {
+    // One-byte IDs: a software pipeline over the tile's four 32-key blocks.
+    // Block bt runs the tile-0 chain, then the tile-1 chain; the tile-0
+    // accumulators are packed while the tile-1 chain runs, and the tile-1
+    // accumulators while the next block's tile-0 chain runs, so the sign
+    // packing and the ID stores overlap MFMAs.  The B operands of the next
+    // block are read from LDS once the current tile-1 chain has taken them.
+    // Bit c of a block's word = accumulator c (register c of tile 0, then of
+    // tile 1); one funnel shift takes in each sign bit.
+    constexpr int TL = ids_word_bytes(L8, 8);     // P = 8: one byte per table
+    const int t0w = (8 * wave + 4 * half) / TL;   // first ID word of the lane's 4 tables
+    auto pack16 = [](const f32x16_t& x) {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int r = 15; r >= 0; --r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(x[r]), 31u);
+      return w;
+    };
+    // register r of tile tt = plane r & 7 of table 8w + 4*half + 2*tt + (r >> 3):
+    // the word holds the 4 tables 8w + 4*half .. +3 as ID bytes of the tiled layout
+    auto store = [&](int64_t pos, uint32_t word) {
+      if constexpr (TL == 4) {
+        *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) = word;
+      } else if constexpr (TL == 2) {
+        *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) =
+            (uint16_t)word;
+        *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w + 1)) =
+            (uint16_t)(word >> 16);
+      } else {
+#pragma unroll
+        for (int b8 = 0; b8 < 4; ++b8)
+          ids[ids_word_offset(bh, n_cap, TL, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
+      }
+    };
+    for (int t = 0; t < ntiles; ++t) {
+      const int64_t t0 = start + (int64_t)t * kTK;
+      const uint4* kt = ktile[t & 1] + col * kRowU4 + 8 * half;
+      const bool full = t0 + kTK <= end;
+      bf16x8_t b[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8_t, kt[kk]);
+      f32x16_t x0, x1;
+      uint32_t lo = 0u;
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        x0 = f32x16_t{0};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          x0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][kk], b[kk], x0, 0, 0, 0);
+        if (bt > 0) {  // the previous block's tile-1 half, then its word
+          uint32_t w = (pack16(x1) << 16) | lo;
+          asm volatile("" : "+v"(w));  // pack here, not inside the predicated store
+          const int64_t pos = t0 + (bt - 1) * kBTile + col;
+          if (full || pos < end) store(pos, w);
+        }
+        x1 = f32x16_t{0};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          x1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][kk], b[kk], x1, 0, 0, 0);
+        lo = pack16(x0);
+        if (bt + 1 < NB) {
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk)
+            b[kk] = __builtin_bit_cast(bf16x8_t, kt[(bt + 1) * kBTile * kRowU4 + kk]);
+        }
+      }
+      {
+        uint32_t w = (pack16(x1) << 16) | lo;
+        asm volatile("" : "+v"(w));
+        const int64_t pos = t0 + (NB - 1) * kBTile + col;
+        if (full || pos < end) store(pos, w);
+      }
+      lds_barrier();  // the ID stores stay in flight
+    }
+    return;
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int64_t t0 = start + (int64_t)t * kTK;
     const uint4* kt = ktile[t & 1];
@@ -310,47 +393,18 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][kk], bop, acc1, 0, 0, 0);
       }
       const int64_t pos = t0 + bt * kBTile + col;
-      if constexpr (WIDE) {
-        // a plane is set when its float bits, read as an int, clamp to 1 in [0, 1]
-        uint32_t id0 = 0u, id1 = 0u, id2 = 0u;
+      // a plane is set when its float bits, read as an int, clamp to 1 in [0, 1]
+      uint32_t id0 = 0u, id1 = 0u, id2 = 0u;
 #pragma unroll
-        for (int c = 0; c < 30; ++c) {
-          const float v = c < 16 ? acc0[c] : acc1[c - 16];
-          const uint32_t bit = (uint32_t)min(max(__float_as_int(v), 0), 1) << (c % 10);
-          if (c < 10) id0 |= bit;
-          else if (c < 20) id1 |= bit;
-          else id2 |= bit;
-        }
-        if (pos < end) store_wide(ids, bh, n_cap, pos, Lw, 6 * wave + 3 * half, id0, id1, id2,
-                                  wave == 0 && half == 0);
-      } else {
-        // register r of tile tt = plane r & 7 of table 8w + 4*half + 2*tt + (r >> 3):
-        // bit 16*tt + r of the 4-table word; a plane is set when its float bits,
-        // read as an int, clamp to 1 in [0, 1]
-        uint32_t word = 0u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          word |= (uint32_t)min(max(__float_as_int(acc0[r]), 0), 1) << r;
-          word |= (uint32_t)min(max(__float_as_int(acc1[r]), 0), 1) << (16 + r);
-        }
-        // the 4 tables 8w + 4*half .. +3 of key pos, as ID words of the tiled layout
-        if (pos < end) {
-          constexpr int TL = ids_word_bytes(L8, 8);   // P = 8: one byte per table
-          const int t0w = (8 * wave + 4 * half) / TL;  // first word index
-          if constexpr (TL == 4) {
-            *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) = word;
-          } else if constexpr (TL == 2) {
-            *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) =
-                (uint16_t)word;
-            *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w + 1)) =
-                (uint16_t)(word >> 16);
-          } else {
-#pragma unroll
-            for (int b8 = 0; b8 < 4; ++b8)
-              ids[ids_word_offset(bh, n_cap, TL, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
-          }
-        }
+      for (int c = 0; c < 30; ++c) {
+        const float v = c < 16 ? acc0[c] : acc1[c - 16];
+        const uint32_t bit = (uint32_t)min(max(__float_as_int(v), 0), 1) << (c % 10);
+        if (c < 10) id0 |= bit;
+        else if (c < 20) id1 |= bit;
+        else id2 |= bit;
       }
+      if (pos < end) store_wide(ids, bh, n_cap, pos, Lw, 6 * wave + 3 * half, id0, id1, id2,
+                                wave == 0 && half == 0);
     }
     lds_barrier();  // the ID stores stay in flight
   }
