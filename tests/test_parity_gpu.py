@@ -263,15 +263,18 @@ def test_topk_edge_lengths():
 # ----------------------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("k_max", [1, 63, 200, 1024])
-def test_sparse_decode_parity(dtype, k_max):
-    w = make_workload("c2", n=4096, Hq=8, Hkv=2, dtype=dtype)
+@pytest.mark.parametrize("k_max,n", [(1, 4096), (63, 4096), (200, 4096), (1024, 4096),
+                                     # 47, 188 and 266 splits of 64 entries: the merges for
+                                     # up to 128, up to 256 and any number of splits
+                                     (3000, 4096), (12000, 16384), (17000, 20480)])
+def test_sparse_decode_parity(dtype, k_max, n):
+    w = make_workload("c2", n=n, Hq=8, Hkv=2, dtype=dtype)
     d = GC.upload(w)
     rng = np.random.default_rng(k_max)
     idx = np.full((w.B, w.Hq, k_max), -1, np.int32)
     for g in range(w.Hq):
         kk = rng.integers(0, k_max + 1) if g else k_max
-        idx[0, g, :kk] = rng.choice(4096, size=kk, replace=False)
+        idx[0, g, :kk] = rng.choice(n, size=kk, replace=False)
         rng.shuffle(idx[0, g])
     out = GC.gpu_decode(w, d, torch.from_numpy(idx).to(DEV))
     sync()
@@ -446,6 +449,8 @@ DENSE_CASES = [
     dict(name="c1"),                                            # float32
     dict(name="c4", n=(10, 20), B=5, Hq=8, Hkv=2, lens=[0, 1, 17, 256, 3000], n_cap=3001),
     dict(name="c4", n=(1000, 9000), B=3),
+    dict(name="c2", n=20000, Hq=8, Hkv=2),                      # 157 splits: eight-group merge
+    dict(name="c2", n=20000, Hq=4, Hkv=1),                      # 313 splits: general merge
 ]
 
 
