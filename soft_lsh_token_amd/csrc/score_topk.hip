@@ -563,12 +563,18 @@ __device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)
 // grid: a multiple of kXcds blocks of kScoreThreads, at least B*Hkv*nblk.
 // Logical block lid = (blockIdx mod 8) * (grid / 8) + blockIdx / 8 keeps
 // consecutive logical blocks -- the blocks of one KV row -- on one XCD.
-// Logical block blk of KV row bh owns the 64-key groups
-// [blk*gpb, (blk+1)*gpb); its waves take them round robin, each keeping the
-// IDs of its next kPrefetch groups in flight (a ring of registers, indexed
-// by compile-time constants so no copy waits on a load).  Each score also
-// goes into an LDS histogram of its top digit, merged into the head's global
-// histogram at the end.
+// When every sequence has the same length, logical block blk of KV row bh
+// owns the 64-key groups [blk*gpb, (blk+1)*gpb) of that row.  With ragged
+// lengths a row-aligned split would leave the blocks of short rows idle while
+// those of the longest rows set the time, so the valid groups of all rows
+// (in row order) are cut into rows*nblk equal shares instead; a share may
+// span rows, and the block scores it row by row, loading each row's table
+// image and merging each row's histogram in turn.  Within a row segment the
+// waves take the groups round robin, each keeping the IDs of its next
+// kPrefetch groups in flight (a ring of registers, indexed by compile-time
+// constants so no copy waits on a load).  Each score also goes into an LDS
+// histogram of its top digit, merged into the head's global histogram at the
+// end of the segment.  Scores do not depend on the split.
 template <int G, int TL, bool WIDE>
 __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     const float* __restrict__ img, int img_floats, const uint8_t* __restrict__ ids,
@@ -584,118 +590,185 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   __shared__ uint32_t lhist[G * kHistBins];
   const int lid = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
   if (lid >= rows * nblk) return;
-  const int blk = lid % nblk;
-  const int bh = lid / nblk;
-  const int b = bh / Hkv;
-  const int h = bh % Hkv;
-  int64_t n = lens[b];
-  if (n > n_cap) n = n_cap;
-  if (n < 0) n = 0;
-  // sink and window keys [0, f_lo) and [f_hi, n) are always selected: scored,
-  // but kept out of the selection histogram
-  const int64_t f_lo = sink < n ? sink : n;
-  const int64_t f_hi = n - window > 0 ? n - window : 0;
-  const int64_t g_begin = (int64_t)blk * gpb;
-  int64_t g_end = (n + 63) >> 6;
-  if (g_end > g_begin + gpb) g_end = g_begin + gpb;
-  if (g_begin >= g_end) return;
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bg0 = b * Hq + h * G;
   const int64_t sst = score_stride(n_cap);
   const int plo = WIDE ? 5 : (P < 4 ? P : 4);
   const uint32_t lomask = (1u << plo) - 1u;
-
-  // The first D groups' IDs and norms, then the table image.  Group loads
-  // are issued unconditionally (a group past the block's range re-reads its
-  // last group, keys past n_cap re-read the last norm) so that no branch sits
-  // between a load and its use and each wait covers only the group needed.
-  const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * WB;
-  const float* vrow = vnorm + (int64_t)bh * n_cap;
-  auto load_group = [&](int64_t gi, uint4 (&v)[WB], float& vn) {
-    const int64_t gl = gi < g_end ? gi : g_end - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * WB) + lane;
-#pragma unroll
-    for (int qv = 0; qv < WB; ++qv) v[qv] = src[qv * 64];
-    const int64_t key = gl * 64 + lane;
-    vn = vrow[key < n_cap ? key : n_cap - 1];
+  auto seq_len = [&](int b) {
+    int64_t n = lens[b];
+    if (n > n_cap) n = n_cap;
+    if (n < 0) n = 0;
+    return n;
   };
-  uint4 buf[D + 1][WB];
-  float vb[D + 1];
-  int64_t gi = g_begin + wave;
-#pragma unroll
-  for (int d = 0; d < D; ++d) load_group(gi + (int64_t)d * kScoreWaves, buf[d], vb[d]);
-  {
-    // The image goes straight from global memory into LDS (16 bytes per lane,
-    // no registers), every load of the block in flight at once.
-    const uint4* src = reinterpret_cast<const uint4*>(img + (int64_t)bh * img_floats);
-    uint4* dst = reinterpret_cast<uint4*>(lds);
-    constexpr int NV = Sh::FLOATS / 4;
-    constexpr int PER = (NV + kScoreThreads - 1) / kScoreThreads;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int base = k * kScoreThreads + wave * 64;  // this wave's 64 vectors
-      if (NV % kScoreThreads == 0 || base + lane < NV)
-        __builtin_amdgcn_global_load_lds(src + base + lane, dst + base, 16, 0, 0);
-    }
-    for (int i = tid; i < G * kHistBins; i += kScoreThreads) lhist[i] = 0u;
-    __builtin_amdgcn_s_waitcnt(0);  // the LDS writes of those loads have landed
-  }
-  __syncthreads();
 
-  float us[G];  // this lane's soft counts (before the value norm), summed when usum is set
+  // Score groups [g_begin, g_end) (g_begin < g_end) of KV row bh; every wave
+  // of the block calls it.
+  auto segment = [&](int bh, int64_t g_begin, int64_t g_end) {
+    const int b = bh / Hkv;
+    const int h = bh % Hkv;
+    const int64_t n = seq_len(b);
+    // sink and window keys [0, f_lo) and [f_hi, n) are always selected:
+    // scored, but kept out of the selection histogram
+    const int64_t f_lo = sink < n ? sink : n;
+    const int64_t f_hi = n - window > 0 ? n - window : 0;
+    const int bg0 = b * Hq + h * G;
+
+    // The first D groups' IDs and norms, then the table image.  Group loads
+    // are issued unconditionally (a group past the segment re-reads its last
+    // group, keys past n_cap re-read the last norm) so that no branch sits
+    // between a load and its use and each wait covers only the group needed.
+    const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * WB;
+    const float* vrow = vnorm + (int64_t)bh * n_cap;
+    auto load_group = [&](int64_t gi, uint4 (&v)[WB], float& vn) {
+      const int64_t gl = gi < g_end ? gi : g_end - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * WB) + lane;
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg) us[gg] = 0.f;
-  bool more = gi < g_end;
-  while (more) {
+      for (int qv = 0; qv < WB; ++qv) v[qv] = src[qv * 64];
+      const int64_t key = gl * 64 + lane;
+      vn = vrow[key < n_cap ? key : n_cap - 1];
+    };
+    uint4 buf[D + 1][WB];
+    float vb[D + 1];
+    int64_t gi = g_begin + wave;
 #pragma unroll
-    for (int s = 0; s <= D; ++s) {
-      if (more) {
-        load_group(gi + (int64_t)D * kScoreWaves, buf[(s + D) % (D + 1)], vb[(s + D) % (D + 1)]);
-        float u[8][G];
-        score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, lomask, plo, u);
-        const int64_t key = gi * 64 + lane;
-        const bool valid = key < n;
-        const uint32_t ranked = valid && key >= f_lo && key < f_hi ? 1u : 0u;
+    for (int d = 0; d < D; ++d) load_group(gi + (int64_t)d * kScoreWaves, buf[d], vb[d]);
+    {
+      // The image goes straight from global memory into LDS (16 bytes per
+      // lane, no registers), every load of the block in flight at once.
+      const uint4* src = reinterpret_cast<const uint4*>(img + (int64_t)bh * img_floats);
+      uint4* dst = reinterpret_cast<uint4*>(lds);
+      constexpr int NV = Sh::FLOATS / 4;
+      constexpr int PER = (NV + kScoreThreads - 1) / kScoreThreads;
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-          const float sv = vb[s] * u[0][gg];
-          uint32_t dg = __float_as_uint(sv) >> kHistShift;
-          if (dg > kHistBins - 1) dg = kHistBins - 1;
-          atomicAdd(&lhist[gg * kHistBins + dg], ranked);
-        }
-        if (valid) {
-#pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            scores[(int64_t)(bg0 + gg) * sst + key] = vb[s] * u[0][gg];
-            us[gg] += u[0][gg];
-          }
-        }
-        gi += kScoreWaves;
-        more = gi < g_end;
+      for (int k = 0; k < PER; ++k) {
+        const int base = k * kScoreThreads + wave * 64;  // this wave's 64 vectors
+        if (NV % kScoreThreads == 0 || base + lane < NV)
+          __builtin_amdgcn_global_load_lds(src + base + lane, dst + base, 16, 0, 0);
       }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < G * kHistBins; i += kScoreThreads) {
-    const uint32_t v = lhist[i];
-    if (v) atomicAdd(&hist[(int64_t)(bg0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
-  }
-  if (usum) {  // per-head sums of the soft counts, for the sampling estimator
-    __syncthreads();  // the merge above has read the histogram: reuse its LDS
-    float* red = reinterpret_cast<float*>(lhist);  // [kScoreWaves][G]
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float t = wave_sum(us[gg]);
-      if (lane == 0) red[wave * G + gg] = t;
+      for (int i = tid; i < G * kHistBins; i += kScoreThreads) lhist[i] = 0u;
+      __builtin_amdgcn_s_waitcnt(0);  // the LDS writes of those loads have landed
     }
     __syncthreads();
-    if (tid < G) {
-      float t = 0.f;
+
+    float us[G];  // this lane's soft counts (before the value norm), summed when usum is set
 #pragma unroll
-      for (int w = 0; w < kScoreWaves; ++w) t += red[w * G + tid];
-      atomicAdd(&usum[bg0 + tid], t);
+    for (int gg = 0; gg < G; ++gg) us[gg] = 0.f;
+    bool more = gi < g_end;
+    while (more) {
+#pragma unroll
+      for (int s = 0; s <= D; ++s) {
+        if (more) {
+          load_group(gi + (int64_t)D * kScoreWaves, buf[(s + D) % (D + 1)], vb[(s + D) % (D + 1)]);
+          float u[8][G];
+          score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, lomask, plo, u);
+          const int64_t key = gi * 64 + lane;
+          const bool valid = key < n;
+          const uint32_t ranked = valid && key >= f_lo && key < f_hi ? 1u : 0u;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            const float sv = vb[s] * u[0][gg];
+            uint32_t dg = __float_as_uint(sv) >> kHistShift;
+            if (dg > kHistBins - 1) dg = kHistBins - 1;
+            atomicAdd(&lhist[gg * kHistBins + dg], ranked);
+          }
+          if (valid) {
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) {
+              scores[(int64_t)(bg0 + gg) * sst + key] = vb[s] * u[0][gg];
+              us[gg] += u[0][gg];
+            }
+          }
+          gi += kScoreWaves;
+          more = gi < g_end;
+        }
+      }
     }
+    __syncthreads();
+    for (int i = tid; i < G * kHistBins; i += kScoreThreads) {
+      const uint32_t v = lhist[i];
+      if (v) atomicAdd(&hist[(int64_t)(bg0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
+    }
+    if (usum) {  // per-head sums of the soft counts, for the sampling estimator
+      __syncthreads();  // the merge above has read the histogram: reuse its LDS
+      float* red = reinterpret_cast<float*>(lhist);  // [kScoreWaves][G]
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        const float t = wave_sum(us[gg]);
+        if (lane == 0) red[wave * G + gg] = t;
+      }
+      __syncthreads();
+      if (tid < G) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < kScoreWaves; ++w) t += red[w * G + tid];
+        atomicAdd(&usum[bg0 + tid], t);
+      }
+    }
+    __syncthreads();  // a following segment reuses the image and histogram LDS
+  };
+
+  // Whether the sequence lengths differ (in groups), the same in every wave:
+  // scalar loads for up to 64 sequences, else 64 a step across the lanes.
+  // Uniform lengths take the row-aligned split.
+  const int B = rows / Hkv;
+  const uint32_t ng0 = (uint32_t)((seq_len(0) + 63) >> 6);
+  bool ragged = false;
+  if (B <= 64) {
+    for (int b = 1; b < B; ++b) ragged |= (uint32_t)((seq_len(b) + 63) >> 6) != ng0;
+  } else {
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + lane;
+      const uint32_t ng = b < B ? (uint32_t)((seq_len(b) + 63) >> 6) : ng0;
+      ragged |= __ballot(ng != ng0) != 0ull;
+    }
+  }
+  if (!ragged) {
+    const int blk = lid % nblk;
+    const int64_t gb = (int64_t)blk * gpb;
+    int64_t ge = (int64_t)ng0;
+    if (ge > gb + gpb) ge = gb + gpb;
+    if (gb < ge) segment(lid / nblk, gb, ge);
+    return;
+  }
+  // Ragged lengths: share lid of the row-ordered valid groups, row by row.
+  // The totals and offsets are wave-uniform and kept in scalar registers.
+  uint32_t total = 0u;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const uint32_t ng = b < B ? (uint32_t)((seq_len(b) + 63) >> 6) : 0u;
+    total += (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(wave_incl_scan(ng), 63, 64)) *
+             (uint32_t)Hkv;
+  }
+  const uint32_t shares = (uint32_t)(rows * nblk);
+  const uint32_t per = (total + shares - 1) / shares;
+  uint32_t G0 = (uint32_t)lid * per;
+  const uint32_t G1 = G0 + per < total ? G0 + per : total;
+  int bcur = 0;
+  uint32_t base = 0u;  // groups of the sequences before bcur (all KV heads)
+  while (G0 < G1) {
+    // the sequence whose groups hold G0, by a wave scan over 64 sequences at a time
+    for (;;) {
+      const int b = bcur + lane;
+      const uint32_t ng = b < B ? (uint32_t)((seq_len(b) + 63) >> 6) * (uint32_t)Hkv : 0u;
+      const uint32_t inc = wave_incl_scan(ng);
+      const uint64_t past = __ballot(b < B && base + inc <= G0);  // sequences ending by G0
+      const int skip = __popcll(past);  // a prefix of the lanes
+      if (skip < 64) {
+        base += skip ? (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(inc, skip - 1, 64)) : 0u;
+        bcur += skip;
+        break;
+      }
+      base += (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(inc, 63, 64));
+      bcur += 64;
+    }
+    const uint32_t ngb = (uint32_t)((seq_len(bcur) + 63) >> 6);
+    const uint32_t h = (G0 - base) / ngb;
+    const uint32_t row0 = base + h * ngb;  // first group of KV row (bcur, h)
+    const uint32_t row1 = row0 + ngb;
+    const uint32_t s1 = G1 < row1 ? G1 : row1;
+    segment(bcur * Hkv + (int)h, (int64_t)(G0 - row0), (int64_t)(s1 - row0));
+    G0 = s1;
   }
 }
 
