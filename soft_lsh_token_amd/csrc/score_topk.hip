@@ -44,7 +44,7 @@ namespace socketlsh {
 // LDS image of the tables of one KV row (its G query heads).  Lane j of a
 // 16-lane scorer row owns tables j*TL .. j*TL+TL-1; the first NF of them are
 // kept as full tables, the other NS = TL - NF as their two factors:
-//   full slot (e*NF + m)*16 + j                       e < 2^P, m < NF
+//   full slot (m*256 + e)*16 + j                      e < 2^P, m < NF
 //   half slot FULL + ((hf*HE + c)*NS + m)*16 + j      hf = 0 (low planes) or
 //                                                      1 (high planes), c < HE, m < NS
 // one slot = G floats (the G query heads).  Bank group of a slot = j, so the
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     half[mm][gg][r] = prod;
   }
   __syncthreads();
-  // full tables: slot (e*NF + m)*16 + j for entries e < 2^P
+  // full tables, table-major: slot (m*256 + e)*16 + j for entries e < 2^P
   const int nent = 1 << P;
   const int lomask = (1 << plo) - 1;
   for (int i = tid; i < NF * nent; i += kTabThreads) {
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
 #pragma unroll
     for (int gg = 0; gg < G; ++gg)
       v[gg] = (float)(half[mm][gg][e & lomask] * half[mm][gg][HE + (e >> plo)]);
-    store_slot<G>(im + ((int64_t)i * 16 + j) * G, v);
+    store_slot<G>(im + ((int64_t)(mm * 256 + e) * 16 + j) * G, v);
   }
   // factored tables: slot FULL/G + ((hc*NS + m - NF)*16 + j), hc = hf*HE + c
   for (int i = tid; i < 2 * HE * NS; i += kTabThreads) {
@@ -482,11 +482,24 @@ struct RoundVals {
   float hi[NS > 0 ? NS : 1][G];
 };
 
+// Full tables are stored table-major: slot (M*256 + cell)*16 + j.  For G = 4
+// a slot is 16 bytes, so the byte address M*65536 + cell*256 + 16*j is one
+// byte permute of the ID word (cell -> byte 1) and jw = 16*j | 1 << 8 (16*j
+// -> byte 0, and table M = 1 -> byte 2); NF <= 2 at G = 4.
 template <int NF, int NS, int G, int M = 0>
-__device__ __forceinline__ void issue_full(const float* lds, uint2 w, int j, RoundVals<NF, NS, G>& r) {
+__device__ __forceinline__ void issue_full(const float* lds, uint2 w, int j, uint32_t jw,
+                                           RoundVals<NF, NS, G>& r) {
   if constexpr (M < NF) {
-    lds_get<G>(lds, ((int)word_cell<1, M>(w) * NF + M) * 16 + j, r.f[M]);
-    issue_full<NF, NS, G, M + 1>(lds, w, j, r);
+    if constexpr (G == 4) {
+      static_assert(NF <= 2, "a byte permute addresses two full tables");
+      constexpr uint32_t sel = 0x0c000000u | ((M ? 0x01u : 0x0cu) << 16) | ((4u + M) << 8);
+      const uint32_t a = __builtin_amdgcn_perm(w.x, jw, sel);
+      const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(lds) + a);
+      r.f[M][0] = t.x; r.f[M][1] = t.y; r.f[M][2] = t.z; r.f[M][3] = t.w;
+    } else {
+      lds_get<G>(lds, (M * 256 + (int)word_cell<1, M>(w)) * 16 + j, r.f[M]);
+    }
+    issue_full<NF, NS, G, M + 1>(lds, w, j, jw, r);
   }
 }
 
@@ -495,9 +508,15 @@ template <int NF, int NS, int G, int C, int HE, int M = 0>
 __device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, uint32_t lomask, int plo,
                                            RoundVals<NF, NS, G>& r) {
   if constexpr (M < NS) {
-    const uint32_t e = word_cell<C, NF + M>(w);
-    lds_get<G>(lds, ((int)(e & lomask) * NS + M) * 16 + j, r.lo[M]);
-    lds_get<G>(lds, ((HE + (int)(e >> plo)) * NS + M) * 16 + j, r.hi[M]);
+    // the two factors' entries as bit fields of the word (one extract each)
+    constexpr int T = NF + M, PER = 4 / C;  // cells per 32-bit half of the word
+    const uint32_t src = T < PER ? w.x : w.y;
+    constexpr uint32_t off = 8 * C * (T % PER);
+    const uint32_t lo = __builtin_amdgcn_ubfe(src, off, (uint32_t)plo);
+    const uint32_t hi = __builtin_amdgcn_ubfe(src, off + (uint32_t)plo, 8 * C - (uint32_t)plo);
+    (void)lomask;
+    lds_get<G>(lds, ((int)lo * NS + M) * 16 + j, r.lo[M]);
+    lds_get<G>(lds, ((HE + (int)hi) * NS + M) * 16 + j, r.hi[M]);
     issue_half<NF, NS, G, C, HE, M + 1>(lds, w, j, lomask, plo, r);
   }
 }
@@ -524,17 +543,18 @@ template <int NF, int NS, int G, int C, int HE, int WB>
 __device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[WB], int j,
                                             uint32_t lomask, int plo, float (&u)[8][G]) {
   constexpr int FULL = 256 * NF * 16 * G;
+  const uint32_t jw = ((uint32_t)j << 4) | 0x100u;
   RoundVals<NF, NS, G> cur, nxt;
   {
     const uint2 w = round_word<WB>(ids, 0);
-    issue_full<NF, NS, G>(lds, w, j, cur);
+    issue_full<NF, NS, G>(lds, w, j, jw, cur);
     issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, lomask, plo, cur);
   }
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     if (x < 15) {
       const uint2 w = round_word<WB>(ids, x + 1);
-      issue_full<NF, NS, G>(lds, w, j, nxt);
+      issue_full<NF, NS, G>(lds, w, j, jw, nxt);
       issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, lomask, plo, nxt);
     }
     float acc[G];
