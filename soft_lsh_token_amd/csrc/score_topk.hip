@@ -505,7 +505,7 @@ __device__ __forceinline__ void issue_full(const float* lds, uint2 w, int j, uin
 
 // Half-table lookups of tables NF .. NF+NS-1 (C-byte cells, HE-entry halves).
 template <int NF, int NS, int G, int C, int HE, int M = 0>
-__device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, uint32_t lomask, int plo,
+__device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, int plo,
                                            RoundVals<NF, NS, G>& r) {
   if constexpr (M < NS) {
     // the two factors' entries as bit fields of the word (one extract each)
@@ -514,10 +514,9 @@ __device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, uin
     constexpr uint32_t off = 8 * C * (T % PER);
     const uint32_t lo = __builtin_amdgcn_ubfe(src, off, (uint32_t)plo);
     const uint32_t hi = __builtin_amdgcn_ubfe(src, off + (uint32_t)plo, 8 * C - (uint32_t)plo);
-    (void)lomask;
     lds_get<G>(lds, ((int)lo * NS + M) * 16 + j, r.lo[M]);
     lds_get<G>(lds, ((HE + (int)hi) * NS + M) * 16 + j, r.hi[M]);
-    issue_half<NF, NS, G, C, HE, M + 1>(lds, w, j, lomask, plo, r);
+    issue_half<NF, NS, G, C, HE, M + 1>(lds, w, j, plo, r);
   }
 }
 
@@ -541,21 +540,21 @@ __device__ __forceinline__ void round_sum(const RoundVals<NF, NS, G>& r, float (
 // partial sums stay live.  On exit u[0] of lane j holds the sums of its key.
 template <int NF, int NS, int G, int C, int HE, int WB>
 __device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[WB], int j,
-                                            uint32_t lomask, int plo, float (&u)[8][G]) {
+                                            int plo, float (&u)[8][G]) {
   constexpr int FULL = 256 * NF * 16 * G;
   const uint32_t jw = ((uint32_t)j << 4) | 0x100u;
   RoundVals<NF, NS, G> cur, nxt;
   {
     const uint2 w = round_word<WB>(ids, 0);
     issue_full<NF, NS, G>(lds, w, j, jw, cur);
-    issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, lomask, plo, cur);
+    issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, plo, cur);
   }
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     if (x < 15) {
       const uint2 w = round_word<WB>(ids, x + 1);
       issue_full<NF, NS, G>(lds, w, j, jw, nxt);
-      issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, lomask, plo, nxt);
+      issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, plo, nxt);
     }
     float acc[G];
     round_sum<NF, NS, G>(cur, acc);
@@ -614,7 +613,6 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t sst = score_stride(n_cap);
   const int plo = WIDE ? 5 : (P < 4 ? P : 4);
-  const uint32_t lomask = (1u << plo) - 1u;
   auto seq_len = [&](int b) {
     int64_t n = lens[b];
     if (n > n_cap) n = n_cap;
@@ -681,7 +679,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
         if (more) {
           load_group(gi + (int64_t)D * kScoreWaves, buf[(s + D) % (D + 1)], vb[(s + D) % (D + 1)]);
           float u[8][G];
-          score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, lomask, plo, u);
+          score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, plo, u);
           const int64_t key = gi * 64 + lane;
           const bool valid = key < n;
           const uint32_t ranked = valid && key >= f_lo && key < f_hi ? 1u : 0u;
