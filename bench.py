@@ -506,7 +506,7 @@ def main():
         torch.cuda.synchronize()
         pre128 = prefill_rate(c3, torch)
         log(f"[bench] prefill hash 128K (the decode-loop prefill): {pre128}")
-        sec3 = timed_steps(c3, torch, max(20, args.steps // 4), max(5, args.warmup // 4))
+        sec3 = timed_steps(c3, torch, args.steps, args.warmup)
         st3, gpu3, host3 = per_stage(c3, torch, max(20, args.steps // 4))
         sc3 = scorer_launch_us(c3, torch, 4 * c3.replicas)
         lb3, _ = scorer_bytes(c3)
@@ -538,7 +538,7 @@ def main():
             c10.prefill(r)
         torch.cuda.synchronize()
         pre10 = prefill_rate(c10, torch)
-        sec10 = timed_steps(c10, torch, max(50, args.steps // 2), max(5, args.warmup // 2))
+        sec10 = timed_steps(c10, torch, args.steps, args.warmup)
         st10, gpu10, _ = per_stage(c10, torch, max(50, args.steps // 2))
         sc10 = scorer_launch_us(c10, torch, 4 * c10.replicas)
         lb10, _ = scorer_bytes(c10)
@@ -559,7 +559,7 @@ def main():
         for r in range(c4.replicas):
             c4.prefill(r)
         torch.cuda.synchronize()
-        sec4 = timed_steps(c4, torch, max(20, args.steps // 4), max(5, args.warmup // 4))
+        sec4 = timed_steps(c4, torch, args.steps, args.warmup)
         st4, gpu4, _ = per_stage(c4, torch, max(20, args.steps // 4))
         sc4 = scorer_launch_us(c4, torch, 8 * c4.replicas)
         lb4, kk4 = scorer_bytes(c4)
