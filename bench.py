@@ -352,15 +352,14 @@ def hard_mode(lib, torch, S, L, P, replicas):
                 code_gbs=code_bytes / (us * 1e-6) / 1e9)
 
 
-def prefill_rate(case, torch, reps=5):
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+def prefill_rate(case, torch):
+    """GPU time of one prefill hash launch (all n keys of every KV head): a batch
+    of launches on the replicas in turn, queued behind the busy prologue."""
     case.prefill(0)
     torch.cuda.synchronize()
-    times = []
-    for r in range(reps):
-        e0.record(); case.prefill(r % case.replicas); e1.record(); torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e-3)
-    t = float(np.median(times))
+    us, _ = gpu_batch_us(torch, lambda i: case.prefill(i % case.replicas),
+                         max(8, 2 * case.replicas))
+    t = us * 1e-6
     w = case.w
     keys = w.B * w.Hkv * case.n
     flops = 2.0 * keys * w.d * w.L * w.P
