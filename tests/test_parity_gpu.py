@@ -129,6 +129,8 @@ SCORE_CASES = [
     dict(name="c2", n=2000, L=3, Hq=8, Hkv=2),     # L not a multiple of 4
     dict(name="c2", n=2000, L=20, P=5, Hq=8, Hkv=2),
     dict(name="c2", n=2000, tau=0.3),
+    dict(name="c2", n=2500, L=100, Hq=8, Hkv=2),   # 8 tables a word: 1 full + 7 factored
+    dict(name="c2", n=2000, L=128, Hq=8, Hkv=4),   # the same at two query heads per KV head
     dict(name="c4", n=(1000, 9000), B=4, k=0.02),  # ragged batch
     # two-byte IDs (P = 9, 10): every table kept as two 32-entry halves
     dict(name="c2", n=5000, L=60, P=10),
