@@ -810,9 +810,6 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
 // serial chain of ballots and LDS appends, and with two workgroups a CU each
 // SIMD has six waves to issue from.
 constexpr int kScanThreads = 768;
-constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kScanLoads = kScanKeys / (kScanThreads * 4);  // 16-byte loads per thread (3)
-static_assert(kScanKeys % (kScanThreads * 4) == 0, "whole load rounds of four keys a thread");
 constexpr int kResThreads = 1024;
 constexpr int kResWaves = kResThreads / 64;
 constexpr int kCandCap = 6144;                     // candidates resolved in LDS
@@ -927,11 +924,18 @@ __device__ Boundary find_boundary(const uint32_t* hh, uint32_t k, uint32_t* wsum
   return boundary_of<NT>(h, k, wsum, sh);
 }
 
-// grid: B*Hq*CH blocks of kScanThreads (rounded up to a multiple of kXcds),
+// grid: B*Hq*CH blocks of NT threads (rounded up to a multiple of kXcds),
 // CH = ceil(n_cap / kScanKeys).  Logical block lid (remapped as in the
 // scorer, so a KV row's query heads are scanned on the XCD whose L2 received
 // their scores) covers keys [c*kScanKeys, (c+1)*kScanKeys) of head lid / CH.
-__global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
+// Each wave gathers its candidates in an LDS region of R slots; when a ballot
+// would overflow it, that ballot's candidates go straight to the global list
+// under a reservation of their own.  NT = kScanThreads with R = the keys a
+// wave meets (no overflow) suits a few workgroups a CU; NT = 256 with
+// R = 256 uses a ninth of the LDS and a third of the waves, so that large
+// batches keep eight workgroups a CU instead of two.
+template <int NT, int R>
+__global__ __launch_bounds__(NT) void topk_scan_kernel(
     const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int sink,
     int window, int Hq, int CH, int heads, const uint32_t* __restrict__ hist,
@@ -952,18 +956,22 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
 
   // the head's histogram slice, then every score of this workgroup: load r
   // covers keys c0 + r*4*kScanThreads + 256*wave + 4*lane .. +3
-  const HistSlice<kScanThreads> hs = load_hist_slice<kScanThreads>(hist + (int64_t)bg * kHistBins);
+  constexpr int NW = NT / 64;                  // waves
+  constexpr int NL = kScanKeys / (NT * 4);     // 16-byte loads per thread
+  static_assert(kScanKeys % (NT * 4) == 0, "whole load rounds of four keys a thread");
+  constexpr bool kNoOverflow = R >= NL * 256;  // a wave meets NL*256 keys
+  const HistSlice<NT> hs = load_hist_slice<NT>(hist + (int64_t)bg * kHistBins);
   const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
-  uint4 v[kScanLoads];
+  uint4 v[NL];
 #pragma unroll
-  for (int r = 0; r < kScanLoads; ++r) {
-    int64_t key = c0 + r * (kScanThreads * 4) + tid * 4;
+  for (int r = 0; r < NL; ++r) {
+    int64_t key = c0 + r * (NT * 4) + tid * 4;
     if (key > sstride - 4) key = sstride - 4;  // past the row: re-read its end
     v[r] = *reinterpret_cast<const uint4*>(srow + key);
   }
-  __shared__ uint32_t wsum[kScanWaves];
+  __shared__ uint32_t wsum[NW];
   __shared__ Boundary shb;
-  const Boundary bd = boundary_of<kScanThreads>(hs, (uint32_t)k, wsum, &shb);
+  const Boundary bd = boundary_of<NT>(hs, (uint32_t)k, wsum, &shb);
   // above d1: bits > thr_sel; in d1: bits >= thr_lo and not above (the top
   // digit is clamped to kHistBins - 1 here as in the histogram).  Sink and
   // window keys are selected whatever their score and never candidates.
@@ -973,12 +981,11 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   const bool by_score = k > 0;
   uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint64_t lt = lanemask_lt64();
-  // candidates gather in LDS, wave w in its own region [w*kWaveKeys, ...)
-  // (a wave meets at most kWaveKeys keys); one global reservation per
-  // workgroup at the end
-  constexpr int kWaveKeys = kScanKeys / kScanWaves;
-  __shared__ uint2 lc[kScanKeys];
-  __shared__ uint32_t wcnt[kScanWaves], gbase;
+  // candidates gather in LDS, wave w in its own region [w*R, (w+1)*R); one
+  // global reservation per workgroup at the end
+  __shared__ uint2 lc[NW * R];
+  __shared__ uint32_t wcnt[NW], gbase;
+  uint2* gc = cand + (int64_t)bg * n_cap;
   uint32_t wpos = 0u;  // uniform per wave
   // 32-bit key arithmetic (n_cap < 2^31); per-lane pointers computed once so
   // the unrolled rounds keep few scalar registers live
@@ -989,8 +996,8 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   uint32_t* bml = bm + (((uint32_t)c0 + (uint32_t)wave * 256u) >> 5) + (lane & 7);
   const uint32_t bsel = (uint32_t)((lane >> 1) & 3);
 #pragma unroll
-  for (int r = 0; r < kScanLoads; ++r) {
-    const uint32_t kr = key0 + (uint32_t)(r * kScanThreads * 4);
+  for (int r = 0; r < NL; ++r) {
+    const uint32_t kr = key0 + (uint32_t)(r * NT * 4);
     const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
     uint64_t ms[4], mc[4];
 #pragma unroll
@@ -1005,20 +1012,28 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
     // lane l < 8 stores word l of the block (words 2e, 2e+1 = ballot e)
     {
       const uint64_t a = bsel == 0 ? ms[0] : bsel == 1 ? ms[1] : bsel == 2 ? ms[2] : ms[3];
-      if (lane < 8) bml[r * (kScanThreads * 4 / 32)] = (lane & 1) ? (uint32_t)(a >> 32) : (uint32_t)a;
+      if (lane < 8) bml[r * (NT * 4 / 32)] = (lane & 1) ? (uint32_t)(a >> 32) : (uint32_t)a;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if ((mc[e] >> lane) & 1ull)
-        lc[wave * kWaveKeys + wpos + (uint32_t)__popcll(mc[e] & lt)] = make_uint2(sb[e], kr + e);
-      wpos += (uint32_t)__popcll(mc[e]);
+      const uint32_t pc = (uint32_t)__popcll(mc[e]);
+      const uint32_t rank = (uint32_t)__popcll(mc[e] & lt);
+      if (kNoOverflow || wpos + pc <= (uint32_t)R) {  // uniform per wave
+        if ((mc[e] >> lane) & 1ull) lc[wave * R + wpos + rank] = make_uint2(sb[e], kr + e);
+        wpos += pc;
+      } else {  // this ballot's candidates straight to the global list
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&counters[bg], pc);
+        base = __shfl(base, 0, 64);
+        if (((mc[e] >> lane) & 1ull) && base + rank < n32) gc[base + rank] = make_uint2(sb[e], kr + e);
+      }
     }
   }
   if (lane == 0) wcnt[wave] = wpos;
   __syncthreads();
-  uint32_t pre[kScanWaves], cnt = 0u;
+  uint32_t pre[NW], cnt = 0u;
 #pragma unroll
-  for (int w = 0; w < kScanWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     pre[w] = cnt;
     cnt += wcnt[w];
   }
@@ -1026,12 +1041,11 @@ __global__ __launch_bounds__(kScanThreads) void topk_scan_kernel(
   if (tid == 0) gbase = atomicAdd(&counters[bg], cnt);
   __syncthreads();
   const uint32_t g0 = gbase;
-  uint2* gc = cand + (int64_t)bg * n_cap;
-  for (uint32_t t = tid; t < cnt; t += kScanThreads) {
+  for (uint32_t t = tid; t < cnt; t += NT) {
     int w = 0;
 #pragma unroll
-    for (int x = 1; x < kScanWaves; ++x) w += t >= pre[x] ? 1 : 0;
-    if (g0 + t < (uint32_t)n) gc[g0 + t] = lc[w * kWaveKeys + (t - pre[w])];
+    for (int x = 1; x < NW; ++x) w += t >= pre[x] ? 1 : 0;
+    if (g0 + t < (uint32_t)n) gc[g0 + t] = lc[w * R + (t - pre[w])];
   }
 }
 
@@ -1629,9 +1643,16 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
   }
   const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
   const int64_t nscan = (int64_t)B * Hq * CH;
-  topk_scan_kernel<<<(unsigned)((nscan + kXcds - 1) / kXcds * kXcds), kScanThreads, 0, s>>>(
-      scores, n_cap, score_stride(n_cap), lens, ks, k_max, sw.sink, sw.window, Hq, CH, B * Hq,
-      ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
+  const unsigned sgrid = (unsigned)((nscan + kXcds - 1) / kXcds * kXcds);
+  // two kScanThreads workgroups fit a CU; beyond that, the small ones
+  if (nscan <= 2 * (int64_t)device_cus())
+    topk_scan_kernel<kScanThreads, kScanKeys / (kScanThreads / 64)><<<sgrid, kScanThreads, 0, s>>>(
+        scores, n_cap, score_stride(n_cap), lens, ks, k_max, sw.sink, sw.window, Hq, CH, B * Hq,
+        ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
+  else
+    topk_scan_kernel<256, 256><<<sgrid, 256, 0, s>>>(
+        scores, n_cap, score_stride(n_cap), lens, ks, k_max, sw.sink, sw.window, Hq, CH, B * Hq,
+        ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_resolve_kernel<<<(unsigned)(B * Hq), kResThreads, 0, s>>>(

@@ -239,6 +239,31 @@ def test_topk_ties_lower_index_wins(n):
         assert (idx[0, g, 100:] == -1).all()
 
 
+def test_topk_ties_small_scan_workgroups():
+    """Equal scores in a batch large enough (4 sequences x 32 heads x 5 chunks
+    of 40000 keys) for the scan's small workgroups: every key is a boundary
+    candidate, so each wave's LDS candidate region overflows into the global
+    list, and the lower indices must still win."""
+    n = 40000
+    w = make_workload("c4", n=(64, 64), B=4, Hq=32, Hkv=8, k=100)  # q and W; the keys are set below
+    w.n_cap = n + 1
+    w.lens = np.full(w.B, n, np.int32)
+    w.ks = np.full(w.B, 100, np.int32)
+    d = GC.upload(w)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
+    vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+    half = n // 2
+    vn[:, 1, half:] = 2.0  # KV head 1: the second half wins, ties among them
+    idx, _ = GC.gpu_score_topk(w, d, ids, vn)
+    sync()
+    idx = idx.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hq):
+            h = g // (w.Hq // w.Hkv)
+            expect = np.arange(half, half + 100) if h == 1 else np.arange(100)
+            assert idx[b, g].tolist() == expect.tolist(), (b, g)
+
+
 def test_topk_edge_lengths():
     """Empty sequence, one key, k = n, k > n (clamped) in one batch."""
     w = make_workload("c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 777, 300], n_cap=1000, k=5)
