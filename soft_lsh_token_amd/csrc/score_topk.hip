@@ -813,8 +813,6 @@ constexpr int kScanThreads = 768;
 constexpr int kResThreads = 1024;
 constexpr int kResWaves = kResThreads / 64;
 constexpr int kCandCap = 6144;                     // candidates resolved in LDS
-constexpr int kCandPerThread = kCandCap / kResThreads;
-constexpr int kSegBlocks = kResThreads;            // 256-key bitmap blocks emitted per pass
 
 // The 8 bits of b moved to bits 0, 4, ..., 28.
 __device__ __forceinline__ uint32_t spread4(uint32_t b) {
@@ -1054,14 +1052,14 @@ __global__ __launch_bounds__(NT) void topk_scan_kernel(
 // `shift` of the score bits (or of the index) and return the digit holding
 // the `need`-th entry: counted from the top for scores, from the bottom for
 // indices (the lower index wins a tie).
-template <bool BY_INDEX>
+template <bool BY_INDEX, int NT = kResThreads>
 __device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask, uint32_t vval,
                            uint32_t imask, uint32_t ival, int shift, uint32_t need,
                            uint32_t* h128, Pick* shpick) {
   const int tid = threadIdx.x;
   if (tid < 128) h128[tid] = 0u;
   __syncthreads();
-  for (uint32_t i = tid; i < C; i += kResThreads) {
+  for (uint32_t i = tid; i < C; i += NT) {
     const uint2 e = cands[i];
     const uint32_t v = e.x & 0x1FFFFFu;
     if ((v & vmask) != vval) continue;
@@ -1085,26 +1083,27 @@ __device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask, uint3
   return r;
 }
 
-// LDS of one resolve.
+// LDS of one resolve by NT threads.
+template <int NT>
 struct ResolveSmem {
-  uint32_t wsum[kResWaves];
+  uint32_t wsum[NT / 64];
   Boundary shb;
   uint32_t h128[128];
   Pick shpick;
   uint32_t seg_total;
   uint2 lcand[kCandCap];
-  uint32_t lbm[kSegBlocks * 8];
+  uint32_t lbm[NT * 8];  // NT 256-key bitmap blocks: one segment
 };
 
-// The resolve of head bg (all threads of a kResThreads workgroup): radix
+// The resolve of head bg (all threads of an NT-thread workgroup): radix
 // select of the candidates that complete the top-k, then every selected key
 // handed to emit(position, key), positions ascending with the key.
-template <typename Emit>
+template <int NT, typename Emit>
 __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSizes& z,
                                              const uint32_t* __restrict__ hist,
                                              const uint32_t* __restrict__ counters,
                                              const uint32_t* __restrict__ bitmap, int64_t words,
-                                             const uint2* __restrict__ cand, ResolveSmem& sm,
+                                             const uint2* __restrict__ cand, ResolveSmem<NT>& sm,
                                              Emit emit) {
   const int tid = threadIdx.x;
   const int64_t n = z.n, k = z.k;
@@ -1112,14 +1111,14 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   // every independent load at once: candidate count, the first kCandCap
   // candidates (whatever their count), this thread's first bitmap block,
   // its histogram bin (inside find_boundary)
-  const HistSlice<kResThreads> hs = load_hist_slice<kResThreads>(hist + (int64_t)bg * kHistBins);
+  const HistSlice<NT> hs = load_hist_slice<NT>(hist + (int64_t)bg * kHistBins);
   const uint2* gc = cand + (int64_t)bg * n_cap;
   const uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint32_t Cg = counters[bg];
-  uint2 cv[kCandPerThread];
+  uint2 cv[(kCandCap / NT)];
 #pragma unroll
-  for (int i = 0; i < kCandPerThread; ++i) {
-    int64_t ci = (int64_t)i * kResThreads + tid;
+  for (int i = 0; i < (kCandCap / NT); ++i) {
+    int64_t ci = (int64_t)i * NT + tid;
     if (ci >= n_cap) ci = n_cap - 1;
     cv[i] = gc[ci];
   }
@@ -1127,13 +1126,13 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   const int64_t bl0 = tid < nblocks ? tid : 0;
   const uint4 bw0 = reinterpret_cast<const uint4*>(bm)[bl0 * 2];
   const uint4 bw1 = reinterpret_cast<const uint4*>(bm)[bl0 * 2 + 1];
-  const Boundary bd = boundary_of<kResThreads>(hs, (uint32_t)k, sm.wsum, &sm.shb);
+  const Boundary bd = boundary_of<NT>(hs, (uint32_t)k, sm.wsum, &sm.shb);
   const uint32_t C = Cg < (uint32_t)n ? Cg : (uint32_t)n;
   const bool in_lds = C <= (uint32_t)kCandCap;
   if (in_lds) {
 #pragma unroll
-    for (int i = 0; i < kCandPerThread; ++i) {
-      const uint32_t ci = (uint32_t)(i * kResThreads + tid);
+    for (int i = 0; i < (kCandCap / NT); ++i) {
+      const uint32_t ci = (uint32_t)(i * NT + tid);
       if (ci < C) sm.lcand[ci] = cv[i];
     }
   }
@@ -1154,7 +1153,7 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   if (k > 0 && need < C) {
     uint32_t ties = 0u;
     for (int shift = 14; shift >= 0; shift -= 7) {
-      const Pick pk = radix_pick<false>(lc, C, vmask, vval, 0u, 0u, shift, need, sm.h128, &sm.shpick);
+      const Pick pk = radix_pick<false, NT>(lc, C, vmask, vval, 0u, 0u, shift, need, sm.h128, &sm.shpick);
       need -= pk.before;
       vval |= pk.digit << shift;
       vmask |= 127u << shift;
@@ -1166,7 +1165,7 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
       while (((uint64_t)1 << top) < (uint64_t)n) ++top;
       int shift = top > 7 ? top - 7 : 0;
       for (;;) {
-        const Pick pk = radix_pick<true>(lc, C, vmask, vval, imask, ival, shift, need, sm.h128, &sm.shpick);
+        const Pick pk = radix_pick<true, NT>(lc, C, vmask, vval, imask, ival, shift, need, sm.h128, &sm.shpick);
         need -= pk.before;
         ival |= pk.digit << shift;
         imask |= 127u << shift;
@@ -1177,11 +1176,11 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
     }
   }
 
-  // bitmap + chosen candidates -> ascending indices, kSegBlocks 256-key
+  // bitmap + chosen candidates -> ascending indices, NT 256-key
   // blocks at a time (thread t owns block t of the segment)
   uint32_t written = 0;
-  for (int64_t b0 = 0; b0 < nblocks; b0 += kSegBlocks) {
-    const int64_t segb = (nblocks - b0) < kSegBlocks ? (nblocks - b0) : kSegBlocks;
+  for (int64_t b0 = 0; b0 < nblocks; b0 += NT) {
+    const int64_t segb = (nblocks - b0) < NT ? (nblocks - b0) : NT;
     if (b0 > 0) {  // later segments: their bitmap blocks now (segment 0 is in LDS already)
       const int64_t bl = tid < segb ? b0 + tid : b0;
       const uint4 w0 = reinterpret_cast<const uint4*>(bm)[bl * 2];
@@ -1192,7 +1191,7 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
       lb[tid * 2 + 1] = mine ? w1 : make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
     }
-    for (uint32_t i = tid; i < C; i += kResThreads) {
+    for (uint32_t i = tid; i < C; i += NT) {
       const uint2 e = lc[i];
       const uint32_t v = e.x & 0x1FFFFFu;
       const int64_t blk = (int64_t)(e.y >> 8) - b0;
@@ -1204,9 +1203,9 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
     __syncthreads();
     // thread t takes WPT consecutive 32-key words of the segment, each
     // rebuilt in key order from the 8-bit slices of the block's 4 masks
-    const int64_t segw = ((n - b0 * 256) + 31) >> 5 < (int64_t)kSegBlocks * 8
-                             ? ((n - b0 * 256) + 31) >> 5 : (int64_t)kSegBlocks * 8;
-    const int WPT = (int)((segw + kResThreads - 1) / kResThreads);  // <= 8
+    const int64_t segw = ((n - b0 * 256) + 31) >> 5 < (int64_t)NT * 8
+                             ? ((n - b0 * 256) + 31) >> 5 : (int64_t)NT * 8;
+    const int WPT = (int)((segw + NT - 1) / NT);  // <= 8
     uint32_t kw[8];
     uint32_t cnt = 0;
 #pragma unroll
@@ -1224,7 +1223,7 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
       kw[q] = x;
       cnt += __popc(x);
     }
-    const uint32_t incw = block_incl_scan<kResThreads>(cnt, sm.wsum);
+    const uint32_t incw = block_incl_scan<NT>(cnt, sm.wsum);
     uint32_t pos = written + incw - cnt;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -1237,15 +1236,17 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
         ++pos;
       }
     }
-    if (tid == kResThreads - 1) sm.seg_total = incw;
+    if (tid == NT - 1) sm.seg_total = incw;
     __syncthreads();
     written += sm.seg_total;
     __syncthreads();
   }
 }
 
-// grid: B*Hq blocks of kResThreads.
-__global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
+// grid: B*Hq blocks of NT threads (1024; 512 for batches of more heads than
+// CUs, whose 16-wave workgroups took the dispatcher about 8 us to start).
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_resolve_kernel(
     int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
     int sink, int window, int Hq, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ counters,
@@ -1257,15 +1258,15 @@ __global__ __launch_bounds__(kResThreads) void topk_resolve_kernel(
   const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
   int32_t* out = idx + (int64_t)bg * k_max;
   if (z.total == 0) {
-    for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
+    for (int t = tid; t < k_max; t += NT) out[t] = -1;
     return;
   }
-  __shared__ ResolveSmem sm;
-  resolve_head(bg, n_cap, z, hist, counters, bitmap, words, cand, sm,
+  __shared__ ResolveSmem<NT> sm;
+  resolve_head<NT>(bg, n_cap, z, hist, counters, bitmap, words, cand, sm,
                [&](uint32_t pos, int32_t key) {
                  if (pos < (uint32_t)k_max) out[pos] = key;
                });
-  for (int64_t t = z.total + tid; t < k_max; t += kResThreads) out[t] = -1;
+  for (int64_t t = z.total + tid; t < k_max; t += NT) out[t] = -1;
 }
 
 // ---------------------------------------------------------------- one-pass top-k
@@ -1655,9 +1656,14 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
         ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  topk_resolve_kernel<<<(unsigned)(B * Hq), kResThreads, 0, s>>>(
-      n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, ws.hist, ws.counters, ws.bitmap, ws.words,
-      ws.cand, idx);
+  if (B * Hq <= device_cus())
+    topk_resolve_kernel<kResThreads><<<(unsigned)(B * Hq), kResThreads, 0, s>>>(
+        n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, ws.hist, ws.counters, ws.bitmap, ws.words,
+        ws.cand, idx);
+  else
+    topk_resolve_kernel<512><<<(unsigned)(B * Hq), 512, 0, s>>>(
+        n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, ws.hist, ws.counters, ws.bitmap, ws.words,
+        ws.cand, idx);
   return hipGetLastError();
 }
 

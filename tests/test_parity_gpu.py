@@ -239,13 +239,15 @@ def test_topk_ties_lower_index_wins(n):
         assert (idx[0, g, 100:] == -1).all()
 
 
-def test_topk_ties_small_scan_workgroups():
-    """Equal scores in a batch large enough (4 sequences x 32 heads x 5 chunks
-    of 40000 keys) for the scan's small workgroups: every key is a boundary
+@pytest.mark.parametrize("B,Hq,Hkv,n", [(4, 32, 8, 40000), (1, 264, 66, 140000)],
+                         ids=["4x32-heads-40000", "264-heads-140000"])
+def test_topk_ties_large_batches(B, Hq, Hkv, n):
+    """Equal scores in launches large enough for the scan's small workgroups
+    (more than two 768-thread workgroups a CU): every key is a boundary
     candidate, so each wave's LDS candidate region overflows into the global
-    list, and the lower indices must still win."""
-    n = 40000
-    w = make_workload("c4", n=(64, 64), B=4, Hq=32, Hkv=8, k=100)  # q and W; the keys are set below
+    list, and the lower indices must still win.  264 heads (more than CUs)
+    take the 512-thread resolve, whose 140000-key rows span two segments."""
+    w = make_workload("c4", n=(64, 64), B=B, Hq=Hq, Hkv=Hkv, k=100)  # q and W; keys set below
     w.n_cap = n + 1
     w.lens = np.full(w.B, n, np.int32)
     w.ks = np.full(w.B, 100, np.int32)
