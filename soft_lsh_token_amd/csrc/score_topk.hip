@@ -953,7 +953,7 @@ __global__ __launch_bounds__(NT) void topk_scan_kernel(
   if (c0 >= n) return;
 
   // the head's histogram slice, then every score of this workgroup: load r
-  // covers keys c0 + r*4*kScanThreads + 256*wave + 4*lane .. +3
+  // covers keys c0 + r*4*NT + 256*wave + 4*lane .. +3
   constexpr int NW = NT / 64;                  // waves
   constexpr int NL = kScanKeys / (NT * 4);     // 16-byte loads per thread
   static_assert(kScanKeys % (NT * 4) == 0, "whole load rounds of four keys a thread");
