@@ -132,6 +132,7 @@ SCORE_CASES = [
     dict(name="c2", n=2500, L=100, Hq=8, Hkv=2),   # 8 tables a word: 1 full + 7 factored
     dict(name="c2", n=2000, L=128, Hq=8, Hkv=4),   # the same at two query heads per KV head
     dict(name="c4", n=(1000, 9000), B=4, k=0.02),  # ragged batch
+    dict(name="c2", n=600, Hq=384, Hkv=96),        # 96 KV rows: more table blocks than fit at once
     # two-byte IDs (P = 9, 10): every table kept as two 32-entry halves
     dict(name="c2", n=5000, L=60, P=10),
     dict(name="c2", n=3000, L=60, P=10, Hq=8, Hkv=8),
