@@ -164,6 +164,22 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
 
 
+def _temp_workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace for one call when the caller passes none.  It is freed when
+    the call returns, while its kernels may still be queued, so it is recorded
+    on the stream they run on: torch's caching allocator then hands the block
+    to no other stream before that work has finished."""
+    ws = alloc_workspace(nbytes, device)
+    if stream is not None:
+        if isinstance(stream, torch.cuda.Stream):
+            s = stream
+        else:
+            handle = int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+            s = torch.cuda.ExternalStream(handle, device=device)
+        ws.record_stream(s)
+    return ws
+
+
 def score_stride(n_cap: int) -> int:
     """Row stride of the score rows: n_cap rounded up to 64."""
     return (n_cap + 63) // 64 * 64
@@ -186,7 +202,7 @@ def socket_score_topk(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor, vnorm
     Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
     need = socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
     if ws is None:
-        ws = alloc_workspace(need, q.device)
+        ws = _temp_workspace(need, q.device, stream)
     wptr, wbytes = _ws_ptr(ws, need)
     sptr = None if scores is None else _dev(scores, "scores", torch.float32,
                                             (B, Hq, score_stride(n_cap)))
@@ -251,7 +267,7 @@ def socket_sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx:
     k_max = idx.shape[-1]
     need = socket_sparse_decode_workspace(B, Hq, d, k_max)
     if ws is None:
-        ws = alloc_workspace(need, q.device)
+        ws = _temp_workspace(need, q.device, stream)
     wptr, wbytes = _ws_ptr(ws, need)
     rc = lib().socket_sparse_decode(
         _dev(q, "q"), _dev(K, "K", q.dtype), _dev(V, "V", q.dtype, K.shape), _dtype_code(q), B, Hq,
@@ -272,7 +288,7 @@ def socket_dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, lens:
     _, Hkv, n_cap, _ = K.shape
     need = socket_dense_decode_workspace(B, Hq, Hkv, d, n_cap)
     if ws is None:
-        ws = alloc_workspace(need, q.device)
+        ws = _temp_workspace(need, q.device, stream)
     wptr, wbytes = _ws_ptr(ws, need)
     rc = lib().socket_dense_decode(
         _dev(q, "q"), _dev(K, "K", q.dtype), _dev(V, "V", q.dtype, K.shape), _dtype_code(q), B, Hq,
@@ -326,7 +342,7 @@ def socket_hard_score_topk(q: torch.Tensor, W: torch.Tensor, codes: torch.Tensor
     Hkv, n_cap = vnorm.shape[1], vnorm.shape[2]
     need = socket_hard_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
     if ws is None:
-        ws = alloc_workspace(need, q.device)
+        ws = _temp_workspace(need, q.device, stream)
     wptr, wbytes = _ws_ptr(ws, need)
     sptr = None if scores is None else _dev(scores, "scores", torch.float32,
                                             (B, Hq, score_stride(n_cap)))
@@ -354,7 +370,7 @@ def socket_sample_estimate(q: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
     M = u.shape[-1]
     need = socket_score_topk_workspace(B, Hq, Hkv, n_cap, L, P, 1)
     if ws is None:
-        ws = alloc_workspace(need, q.device)
+        ws = _temp_workspace(need, q.device, stream)
     wptr, wbytes = _ws_ptr(ws, need)
     dptr = None if draws is None else _dev(draws, "draws", torch.int32, (B, Hq, M))
     sptr = None if scores is None else _dev(scores, "scores", torch.float32,
@@ -387,7 +403,7 @@ def socket_decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: tor
     _, Hkv, n_cap, _ = K.shape
     need = socket_decode_step_workspace(B, Hq, Hkv, n_cap, L, P, k_max)
     if ws is None:
-        ws = alloc_workspace(need, q.device)
+        ws = _temp_workspace(need, q.device, stream)
     wptr, wbytes = _ws_ptr(ws, need)
     sptr = None if scores is None else _dev(scores, "scores", torch.float32,
                                             (B, Hq, score_stride(n_cap)))
@@ -399,3 +415,4 @@ def socket_decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: tor
         _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr,
         _dev(out, "out", torch.float32, (B, Hq, d)), wptr, wbytes, _stream(q, stream))
     _check("socket_decode_step", rc)
+

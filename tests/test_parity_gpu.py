@@ -757,3 +757,58 @@ def test_stage_entry_points_match_fused_call():
     sync()
     assert torch.equal(sc3, sc4)
     assert torch.equal(idx3, idx4)
+
+
+def test_side_stream_temporary_workspace():
+    """Calls on a side stream with ws=None: the temporary workspace is freed when
+    the call returns, while its kernels still wait behind other work on that
+    stream.  Blocks that the current stream then allocates and overwrites must
+    not be that workspace; results equal the default-stream calls bit for bit."""
+    w = make_workload("c2", n=20000, n_cap=20064)
+    d = GC.upload(w)
+    ids, vn = GC.gpu_hash(w, d)
+    idx1, sc1 = GC.gpu_score_topk(w, d, ids, vn)
+    out1 = GC.gpu_decode(w, d, idx1)
+    k_max = idx1.shape[-1]
+    lens1 = d["lens"] + 1   # the step appends key 20000
+    idx3 = torch.full_like(idx1, -7)
+    out3 = torch.full_like(out1, float("nan"))
+    S.socket_decode_step(d["q"], d["K"], d["V"], d["W"], ids.clone(), vn.clone(), lens1, d["ks"],
+                         k_max, w.tau, w.L, w.P, w.scale, idx3, out3)
+    sync()
+    # the exact sizes of the three temporary workspaces (what the binding allocates)
+    sizes = [S.socket_score_topk_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, k_max),
+             S.socket_sparse_decode_workspace(w.B, w.Hq, w.d, k_max),
+             S.socket_decode_step_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P, k_max)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    a = torch.randn(4096, 4096, device=DEV)
+    idx2 = torch.full_like(idx1, -7)
+    sc2 = torch.zeros_like(sc1)
+    out2 = torch.full_like(out1, float("nan"))
+    idx4 = torch.full_like(idx1, -7)
+    out4 = torch.full_like(out1, float("nan"))
+    ids4, vn4 = ids.clone(), vn.clone()
+    sync()
+    with torch.cuda.stream(side):
+        for _ in range(20):  # keep the side stream busy so the calls below queue up
+            a = a @ a
+            a = a / a.abs().max()
+    junk = []
+
+    def scribble(v):
+        junk.extend(torch.full((n + 256,), v, dtype=torch.uint8, device=DEV) for n in sizes)
+
+    S.socket_score_topk(d["q"], d["W"], ids, vn, d["lens"], d["ks"], k_max, w.tau, w.L, w.P, idx2,
+                        sc2, stream=side)
+    scribble(0xFF)
+    S.socket_sparse_decode(d["q"], d["K"], d["V"], idx2, w.scale, out2, stream=side)
+    scribble(0x7F)
+    S.socket_decode_step(d["q"], d["K"], d["V"], d["W"], ids4, vn4, lens1, d["ks"], k_max, w.tau,
+                         w.L, w.P, w.scale, idx4, out4, stream=side)
+    scribble(0x3F)
+    side.synchronize()
+    sync()
+    del junk
+    assert torch.equal(idx1, idx2) and torch.equal(sc1, sc2) and torch.equal(out1, out2)
+    assert torch.equal(idx3, idx4) and torch.equal(out3, out4)
