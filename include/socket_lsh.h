@@ -197,6 +197,32 @@ int socket_decode_step(const void* q, const void* K, const void* V, int dtype, i
                        int k_max, int sink, int window, float scale, int32_t* idx, float* scores,
                        float* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * socket_decode_step_noalloc -- socket_decode_step without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * allocates nothing and calls no allocating routine; its scratch memory is
+ * one static device array of SOCKET_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the first call on that GPU until the process ends.
+ *
+ * Arguments, results and status codes are those of socket_decode_step.
+ * Sizes whose socket_decode_step_workspace() exceeds
+ * SOCKET_NOALLOC_SCRATCH_BYTES are rejected with SOCKET_ENOSPC before
+ * anything is enqueued (the 32K and 128K single-sequence steps fit; a batch
+ * of 16 sequences of 32K keys does not).  Every call on one GPU shares that
+ * GPU's array, and the array keeps the last call's contents (each call
+ * clears what it needs cleared inside its own kernels): calls that can
+ * overlap on one GPU -- on different streams, or from different host
+ * threads without ordering -- race on it and must not be issued.
+ */
+#define SOCKET_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int socket_decode_step_noalloc(const void* q, const void* K, const void* V, int dtype, int B,
+                               int Hq, int Hkv, int d, const void* W, int L, int P, float tau,
+                               uint8_t* ids, float* vnorm, const int32_t* lens, int64_t n_cap,
+                               const int32_t* ks, int k_max, int sink, int window, float scale,
+                               int32_t* idx, float* scores, float* out, void* stream);
+
 /* Workspace bytes needed by socket_sparse_decode for these sizes. */
 size_t socket_sparse_decode_workspace(int B, int Hq, int d, int k_max);
 

@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     socket_sparse_decode_workspace, socket_topk, score_stride,
     alloc_codes, codes_words, socket_codes_bytes, socket_hash_codes, socket_hard_score_topk,
     socket_hard_score_topk_workspace, socket_sample_estimate, socket_decode_step,
-    socket_decode_step_workspace,
+    socket_decode_step_workspace, socket_decode_step_noalloc, NOALLOC_SCRATCH_BYTES,
 )
 
 __version__ = "0.1.0"

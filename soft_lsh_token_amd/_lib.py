@@ -42,6 +42,8 @@ _SIGS = {
     "socket_decode_step_workspace": (_sz, [_i, _i, _i, _i64, _i, _i, _i]),
     "socket_decode_step": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp,
                                 _i64, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "socket_decode_step_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp,
+                                        _vp, _vp, _i64, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp]),
     "socket_sample_estimate": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _vp, _vp, _vp,
                                     _i64, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "socket_hash_codes": (_i, [_vp, _vp, _i, _i, _i, _i, _i64, _vp, _i, _vp, _i, _i, _vp, _vp,
@@ -416,3 +418,28 @@ def socket_decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: tor
         _dev(out, "out", torch.float32, (B, Hq, d)), wptr, wbytes, _stream(q, stream))
     _check("socket_decode_step", rc)
 
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SOCKET_NOALLOC_SCRATCH_BYTES
+
+
+def socket_decode_step_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                               W: torch.Tensor, ids: torch.Tensor, vnorm: torch.Tensor,
+                               lens: torch.Tensor, ks: torch.Tensor, k_max: int, tau: float, L: int,
+                               P: int, scale: float, idx: torch.Tensor, out: torch.Tensor,
+                               scores: torch.Tensor | None = None, stream=None, sink: int = 0,
+                               window: int = 0) -> None:
+    """socket_decode_step with the library's static scratch memory instead of a
+    workspace: no device memory is allocated (see the header for the size limit
+    and the rule that calls on one GPU must not overlap)."""
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = K.shape
+    sptr = None if scores is None else _dev(scores, "scores", torch.float32,
+                                            (B, Hq, score_stride(n_cap)))
+    rc = lib().socket_decode_step_noalloc(
+        _dev(q, "q"), _dev(K, "K", q.dtype), _dev(V, "V", q.dtype, K.shape), _dtype_code(q), B, Hq,
+        Hkv, d, _dev(W, "W", q.dtype, (L * P, d)), L, P, float(tau), _ids(ids, B, Hkv, n_cap, L, P),
+        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _dev(lens, "lens", torch.int32, (B,)),
+        n_cap, _dev(ks, "ks", torch.int32, (B,)), int(k_max), int(sink), int(window), float(scale),
+        _dev(idx, "idx", torch.int32, (B, Hq, k_max)), sptr,
+        _dev(out, "out", torch.float32, (B, Hq, d)), _stream(q, stream))
+    _check("socket_decode_step_noalloc", rc)

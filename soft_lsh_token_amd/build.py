@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsocket_lsh.so")
 SOURCES = ["api.hip", "hash.hip", "score_topk.hip", "sparse_decode.hip", "dense_decode.hip",
-           "hard_lsh.hip", "sample_estimate.hip"]
+           "hard_lsh.hip", "sample_estimate.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 
