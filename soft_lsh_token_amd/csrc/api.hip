@@ -216,8 +216,12 @@ int socket_decode_step(const void* q, const void* K, const void* V, int dtype, i
   hipError_t e = launch_soft_tables(q, dtype, B, Hq, Hkv, W, L, P, tau, w, s, ak);
   if (e == hipSuccess)
     e = launch_score(B, Hq, Hkv, L, P, ids, vnorm, lens, n_cap, sw, sc, false, w, s);
-  if (e == hipSuccess) e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s);
+  // the selecting workgroups attend too when the sizes allow it
+  const AttendSpec att{q, K, V, dtype, Hkv, scale, out};
+  bool attended = false;
   if (e == hipSuccess)
+    e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s, &att, &attended);
+  if (e == hipSuccess && !attended)
     e = launch_sparse_decode(q, K, V, dtype, B, Hq, Hkv, n_cap, idx, k_max, scale, out, dw, s);
   return from_hip(e);
 }

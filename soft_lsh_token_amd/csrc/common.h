@@ -61,6 +61,56 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* f) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
+// Load 8 consecutive head elements [8*j, 8*j+8) of a row as floats (bf16
+// rows are passed as uint16_t).
+template <typename T>
+__device__ __forceinline__ void load_row8(const T* row, int j, float* f);
+template <>
+__device__ __forceinline__ void load_row8<uint16_t>(const uint16_t* row, int j, float* f) {
+  const uint4 v = reinterpret_cast<const uint4*>(row)[j];
+  unpack_bf16x8(v, f);
+}
+template <>
+__device__ __forceinline__ void load_row8<float>(const float* row, int j, float* f) {
+  const float4 a = reinterpret_cast<const float4*>(row)[2 * j];
+  const float4 b = reinterpret_cast<const float4*>(row)[2 * j + 1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// The same 8 elements kept packed (bf16: one 16-byte vector; fp32: two) so
+// that many rows can be in flight in few registers; unpack when used.
+template <typename T>
+struct Row8 {
+  uint4 a, b;  // fp32: a, b = elements 0..3, 4..7
+};
+template <>
+struct Row8<uint16_t> {
+  uint4 a;
+};
+template <typename T>
+__device__ __forceinline__ Row8<T> fetch_row8(const T* row, int j) {
+  Row8<T> r;
+  if constexpr (sizeof(T) == 2) {
+    r.a = reinterpret_cast<const uint4*>(row)[j];
+  } else {
+    r.a = reinterpret_cast<const uint4*>(row)[2 * j];
+    r.b = reinterpret_cast<const uint4*>(row)[2 * j + 1];
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void unpack_row8(const Row8<T>& r, float* f) {
+  if constexpr (sizeof(T) == 2) {
+    unpack_bf16x8(r.a, f);
+  } else {
+    f[0] = __uint_as_float(r.a.x); f[1] = __uint_as_float(r.a.y);
+    f[2] = __uint_as_float(r.a.z); f[3] = __uint_as_float(r.a.w);
+    f[4] = __uint_as_float(r.b.x); f[5] = __uint_as_float(r.b.y);
+    f[6] = __uint_as_float(r.b.z); f[7] = __uint_as_float(r.b.w);
+  }
+}
+
 // DPP move within rows of 16 lanes (row_ror:n is control 0x120 + n).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {

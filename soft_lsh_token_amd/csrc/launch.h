@@ -67,11 +67,26 @@ hipError_t launch_estimate(const float* scores, const float* vnorm, const void* 
                            const float* u, int M, float* out, int32_t* draws, const ScoreWs& ws,
                            hipStream_t s);
 
+// The attention a selection may be followed by (socket_decode_step): query,
+// K and V of the step, their dtype, KV heads, scale and output.
+struct AttendSpec {
+  const void* q;
+  const void* K;
+  const void* V;
+  int dtype;
+  int Hkv;
+  float scale;
+  float* out;
+};
+
 // Algorithm 3: top-k selection from the scores and their histogram, united
-// with the sink and window keys.
+// with the sink and window keys.  With att, the selecting workgroups also run
+// each head's attention over its selection when the sizes allow it; then
+// *attended is set and no separate attention launch is needed.
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx,
-                       const ScoreWs& ws, hipStream_t s);
+                       const ScoreWs& ws, hipStream_t s, const AttendSpec* att = nullptr,
+                       bool* attended = nullptr);
 
 // Hard-LSH comparison mode: packed sign codes of the L*P planes per key,
 // stored word-major: codes[(b*Hkv + h) * words + w][n_cap].

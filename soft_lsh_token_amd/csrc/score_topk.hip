@@ -1083,6 +1083,104 @@ __device__ Pick radix_pick(const uint2* cands, uint32_t C, uint32_t vmask, uint3
   return r;
 }
 
+// ---------------------------------------------------------------- attention in the selecting workgroup
+
+// Exact softmax attention (SOCKET Sec. 2 and Sec. 4.1, Algorithm 3) of one
+// query over the S keys listed in LDS `sel`, run by the NT threads of the
+// workgroup that selected them, so a decode step needs no separate attention
+// launches.  16 lanes share a key row (8 head elements each); the R = NT/16
+// rows take keys t = row, row + R, ... in batches of AB, every K and V load of
+// a batch issued before any is used, and keep an online softmax (m, l, o).
+// The R rows are then merged in row order (fixed order, so results repeat bit
+// for bit): M = max m_r, w_r = exp(m_r - M), out = sum w_r o_r / sum w_r l_r.
+// mo: R*kHead floats of LDS, mml: 2*R floats of LDS.
+template <typename T, int NT, int AB>
+__device__ __forceinline__ void attend_selected(const T* __restrict__ qrow, const T* __restrict__ Kh,
+                                const T* __restrict__ Vh, const int32_t* sel, int S, float scale,
+                                float* mo, float* mml, float* __restrict__ out) {
+  constexpr int R = NT / 16;
+  const int tid = threadIdx.x, j = tid & 15, row = tid >> 4;
+  float qf[8];
+  load_row8<T>(qrow, j, qf);
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int t0 = row; t0 < S; t0 += R * AB) {  // the 16 lanes of a row agree
+    int32_t ki[AB];
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      const int t = t0 + a * R;
+      ki[a] = t < S ? sel[t] : -1;
+    }
+    Row8<T> kr[AB], vr[AB];
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      const int64_t r = ki[a] >= 0 ? ki[a] : 0;
+      kr[a] = fetch_row8<T>(Kh + r * kHead, j);
+      vr[a] = fetch_row8<T>(Vh + r * kHead, j);
+    }
+    float lg[AB], mx = m;
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      float kf[8];
+      unpack_row8<T>(kr[a], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[e], dot);
+      dot = row16_sum(dot);
+      lg[a] = ki[a] >= 0 ? dot * scale : -INFINITY;
+      mx = fmaxf(mx, lg[a]);
+    }
+    // t0 < S, so the batch's first key is a real one and mx is finite
+    const float c = m == -INFINITY ? 0.f : __expf(m - mx);
+    l *= c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= c;
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      const float p = lg[a] == -INFINITY ? 0.f : __expf(lg[a] - mx);
+      float vf[8];
+      unpack_row8<T>(vr[a], vf);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mo[row * kHead + 8 * j + e] = o[e];
+  if (j == 0) {
+    mml[2 * row] = m;
+    mml[2 * row + 1] = l;
+  }
+  __syncthreads();
+  if (tid < kHead) {
+    float M = -INFINITY;
+    for (int r = 0; r < R; ++r)
+      if (mml[2 * r + 1] > 0.f) M = fmaxf(M, mml[2 * r]);
+    float L = 0.f, O = 0.f;
+    for (int r = 0; r < R; ++r) {
+      const float lr = mml[2 * r + 1];
+      const float w = lr > 0.f ? __expf(mml[2 * r] - M) : 0.f;
+      L = fmaf(lr, w, L);
+      O = fmaf(mo[r * kHead + tid], w, O);
+    }
+    out[tid] = L > 0.f ? O / L : 0.f;
+  }
+}
+
+// Where a selecting workgroup attends: its query row, the K and V rows of its
+// KV head, the scale, and its output row.
+template <typename T>
+struct AttendArgs {
+  const T* q;
+  const T* K;
+  const T* V;
+  float* out;
+  int Hkv;
+  float scale;
+};
+
 // LDS of one resolve by NT threads.
 template <int NT>
 struct ResolveSmem {
@@ -1245,13 +1343,16 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
 
 // grid: B*Hq blocks of NT threads (1024; 512 for batches of more heads than
 // CUs, whose 16-wave workgroups took the dispatcher about 8 us to start).
-template <int NT>
+// With ATT the workgroup then runs the head's attention over its selection
+// (attend_selected), which it keeps in the candidate list's LDS: rows of at
+// most one emit segment (NT 256-key blocks) and k_max <= 2*kCandCap.
+template <int NT, bool ATT, typename T>
 __global__ __launch_bounds__(NT) void topk_resolve_kernel(
     int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
     int sink, int window, int Hq, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ counters,
     const uint32_t* __restrict__ bitmap, int64_t words, const uint2* __restrict__ cand,
-    int32_t* __restrict__ idx) {
+    int32_t* __restrict__ idx, AttendArgs<T> at) {
   const int bg = blockIdx.x;
   const int b = bg / Hq;
   const int tid = threadIdx.x;
@@ -1259,274 +1360,340 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(
   int32_t* out = idx + (int64_t)bg * k_max;
   if (z.total == 0) {
     for (int t = tid; t < k_max; t += NT) out[t] = -1;
+    if (ATT && tid < kHead) at.out[(int64_t)bg * kHead + tid] = 0.f;
     return;
   }
   __shared__ ResolveSmem<NT> sm;
+  __shared__ float mml[ATT ? 2 * (NT / 16) : 1];
+  static_assert(NT * 8 >= (NT / 16) * kHead, "the segment bitmap LDS holds the attention merge");
+  int32_t* lsel = reinterpret_cast<int32_t*>(sm.lcand);
   resolve_head<NT>(bg, n_cap, z, hist, counters, bitmap, words, cand, sm,
                [&](uint32_t pos, int32_t key) {
-                 if (pos < (uint32_t)k_max) out[pos] = key;
+                 if (pos < (uint32_t)k_max) {
+                   out[pos] = key;
+                   if (ATT) lsel[pos] = key;
+                 }
                });
   for (int64_t t = z.total + tid; t < k_max; t += NT) out[t] = -1;
-}
-
-// ---------------------------------------------------------------- one-pass top-k
-
-// For n_cap <= kResThreads * 4 * kOneMaxRounds: one workgroup per query head
-// does the scan and the resolve above on its own, with the head's scores in
-// registers and the selection bitmap and candidates in LDS.  This saves the
-// second launch for short rows; for longer ones the per-key passes of a single
-// CU per head cost more than the launch, and the scan spreads them over
-// several workgroups per head.  Round r of
-// thread t holds keys r*4096 + 4t .. +3 (coalesced 16-byte loads); the
-// bitmap has the global bitmap's layout (wave ballots per 256-key block).
-// Candidates beyond the LDS capacity are settled from the registers instead.
-// Workgroups are remapped as in the scorer (logical head lid = (blockIdx mod
-// 8) * (grid / 8) + blockIdx / 8), so a head is selected on the XCD whose L2
-// received its scores.
-constexpr int kOneMaxRounds = 2;
-constexpr int kOneKeys = kResThreads * 4;  // keys per round
-
-// The boundary-bin candidates of this thread's keys in round r (4 bits).
-template <int NR>
-__device__ __forceinline__ uint32_t cand_bits(const uint4 (&v)[NR], int r, uint32_t key,
-                                              uint32_t n, uint32_t flo, uint32_t fhi,
-                                              uint32_t lo, uint32_t hi) {
-  const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-  uint32_t m = 0u;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t kk = key + (uint32_t)e;
-    m |= (uint32_t)(kk < n && kk >= flo && kk < fhi && sb[e] <= hi && sb[e] >= lo) << e;
+  if constexpr (ATT) {
+    const int g = bg % Hq, h = g / (Hq / at.Hkv);
+    const int64_t kv = ((int64_t)b * at.Hkv + h) * n_cap * kHead;
+    const int S = (int)(z.total < k_max ? z.total : k_max);
+    attend_selected<T, NT, 4>(
+        at.q + (int64_t)bg * kHead, at.K + kv, at.V + kv, lsel, S, at.scale,
+        reinterpret_cast<float*>(sm.lbm), mml, at.out + (int64_t)bg * kHead);
   }
-  return m;
 }
 
-// radix_pick over the candidates held in registers (overflow path).
-template <int NR, bool BY_INDEX>
-__device__ Pick radix_regs(const uint4 (&v)[NR], uint32_t n, uint32_t flo, uint32_t fhi,
-                           uint32_t lo, uint32_t hi, uint32_t vmask, uint32_t vval,
-                           uint32_t imask, uint32_t ival, int shift, uint32_t need,
-                           uint32_t* h128, Pick* shpick) {
-  const int tid = threadIdx.x;
-  if (tid < 128) h128[tid] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint32_t key = (uint32_t)(r * kOneKeys + 4 * tid);
-    const uint32_t m = cand_bits<NR>(v, r, key, n, flo, fhi, lo, hi);
-    const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t low = sb[e] & 0x1FFFFFu, kk = key + (uint32_t)e;
-      if (((m >> e) & 1u) && (low & vmask) == vval && (!BY_INDEX || (kk & imask) == ival))
-        atomicAdd(&h128[((BY_INDEX ? kk : low) >> shift) & 127u], 1u);
+// ---------------------------------------------------------------- streaming top-k
+
+// The score-bit threshold vval and key threshold imax that complete a top-k
+// of `need` among C candidates (all with the same top digit): a candidate is
+// chosen iff its low 21 bits exceed vval, or equal it with key <= imax.
+// All NT threads call it.
+template <int NT>
+__device__ void settle_candidates(const uint2* cl, uint32_t C, uint32_t need, uint32_t n,
+                                  uint32_t* h128, Pick* shpick, uint32_t& vval, uint32_t& imax) {
+  auto pick = [&](auto by_index, uint32_t vm, uint32_t vv, uint32_t im, uint32_t iv, int shift) {
+    constexpr bool BI = decltype(by_index)::value;
+    return radix_pick<BI, NT>(cl, C, vm, vv, im, iv, shift, need, h128, shpick);
+  };
+  uint32_t vmask = 0u, ties = 0u;
+  vval = 0u;
+  imax = 0xFFFFFFFFu;
+  for (int shift = 14; shift >= 0; shift -= 7) {
+    const Pick pk = pick(std::false_type{}, vmask, vval, 0u, 0u, shift);
+    need -= pk.before;
+    vval |= pk.digit << shift;
+    vmask |= 127u << shift;
+    ties = pk.inbin;
+  }
+  if (ties > need) {  // among keys with exactly that score, the lower indices win
+    uint32_t imask = 0u, ival = 0u;
+    int top = 0;
+    while (((uint64_t)1 << top) < (uint64_t)n) ++top;
+    int shift = top > 7 ? top - 7 : 0;
+    for (;;) {
+      const Pick pk = pick(std::true_type{}, vmask, vval, imask, ival, shift);
+      need -= pk.before;
+      ival |= pk.digit << shift;
+      imask |= 127u << shift;
+      if (shift == 0) break;
+      shift = shift > 7 ? shift - 7 : 0;
     }
+    imax = ival;
   }
-  __syncthreads();
-  if (tid < 64) {
-    const int b0 = BY_INDEX ? 2 * tid : 127 - 2 * tid;
-    const int b1 = BY_INDEX ? 2 * tid + 1 : 126 - 2 * tid;
-    const uint32_t c0 = h128[b0], c1 = h128[b1];
-    const uint32_t inc = wave_incl_scan(c0 + c1);
-    const uint32_t prev = inc - c0 - c1;
-    if (prev < need && need <= prev + c0) *shpick = Pick{(uint32_t)b0, prev, c0};
-    else if (prev + c0 < need && need <= inc) *shpick = Pick{(uint32_t)b1, prev + c0, c1};
-  }
-  __syncthreads();
-  const Pick r = *shpick;
-  __syncthreads();
-  return r;
 }
 
-// grid: B*Hq blocks of kResThreads.
-template <int NR>
-__global__ __launch_bounds__(kResThreads) void topk_onepass_kernel(
+// One workgroup of NT threads per query head does the whole selection in one
+// launch and one read of the head's scores (rows of up to 32*BMW keys):
+//  1. the bin d1 of the first digit that holds the k-th largest score, from
+//     the head's histogram (built by the scorer);
+//  2. one pass over the score row, D loads of 16 bytes per thread in flight:
+//     wave ballots of "above d1" (and of the sink and window keys) go to an
+//     LDS bitmap, and the keys of bin d1 are gathered as candidates (score
+//     bits, key) in LDS;
+//  3. the candidates that complete the top-k are settled by radix select on
+//     the remaining 21 score bits, then on the key (the lower index wins a
+//     tie), and join the bitmap;
+//  4. the bitmap becomes ascending indices (a block scan of word counts).
+// Bitmap layout: 256-key block j (keys 256j + 4i + e, lane i < 64, e < 4) is
+// 8 words; words 8j + 2e and 8j + 2e + 1 hold bit i = key 256j + 4i + e, the
+// ballot over the wave that loaded 4 consecutive keys per lane.  Blocks
+// clear of the row's ends (no sink, window or past-the-end key) cost two
+// compares and two ballots per key.
+// More candidates than the LDS holds (many equal scores) take a second pass
+// that writes them all to the workspace's global list, and step 3 reads them
+// there.  Workgroups are remapped as in the scorer
+// (logical head (blockIdx mod 8) * (grid / 8) + blockIdx / 8), so a head is
+// selected on the XCD whose L2 received its scores.
+// With ATT the workgroup then runs the head's attention over its selection
+// (attend_selected; the selection is kept in the candidate list's LDS, so
+// k_max <= 2*CAP).
+template <int NT, int BMW, int CAP, int D, bool ATT, typename T>
+__global__ __launch_bounds__(NT) void topk_stream_kernel(
     const float* __restrict__ scores, int64_t n_cap, int64_t sstride,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max, int sink,
-    int window, int Hq, int heads, const uint32_t* __restrict__ hist,
-    int32_t* __restrict__ idx) {
+    int window, int Hq, int heads, const uint32_t* __restrict__ hist, uint2* __restrict__ cand,
+    int32_t* __restrict__ idx, AttendArgs<T> at) {
+  constexpr int NW = NT / 64;
+  constexpr int RK = 4 * NT;  // keys per round (one 16-byte load per thread)
   const int bg = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
   if (bg >= heads) return;
   const int b = bg / Hq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
   const int64_t k = z.k;
   int32_t* out = idx + (int64_t)bg * k_max;
   if (z.total == 0) {
-    for (int t = tid; t < k_max; t += kResThreads) out[t] = -1;
+    for (int t = tid; t < k_max; t += NT) out[t] = -1;
+    if (ATT && tid < kHead) at.out[(int64_t)bg * kHead + tid] = 0.f;
     return;
   }
-  // every score load first (past the row: re-read its end, masked below)
-  const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
-  uint4 v[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    int64_t kk = (int64_t)r * kOneKeys + 4 * tid;
-    if (kk > sstride - 4) kk = sstride - 4;
-    v[r] = *reinterpret_cast<const uint4*>(srow + kk);
-  }
-  __shared__ uint32_t wsum[kResWaves];
+  static_assert(!ATT || BMW >= (NT / 16) * kHead, "the bitmap LDS holds the attention merge");
+  __shared__ uint32_t bm[BMW];
+  __shared__ uint2 lc[CAP];
+  __shared__ float mml[ATT ? 2 * (NT / 16) : 1];
+  int32_t* lsel = reinterpret_cast<int32_t*>(lc);  // the selection, once lc is free
+  __shared__ uint32_t wsum[NW];
   __shared__ Boundary shb;
   __shared__ uint32_t h128[128];
   __shared__ Pick shpick;
-  __shared__ uint32_t wcount[kResWaves];
-  __shared__ uint2 lcand[kCandCap];
-  __shared__ uint32_t lbm[NR * kOneKeys / 32];
-  Boundary bd{0u, 0u};
-  if (k > 0)  // uniform
-    bd = find_boundary<kResThreads>(hist + (int64_t)bg * kHistBins, (uint32_t)k, wsum, &shb);
+  __shared__ uint32_t ccount, seg_total;
+
+  // 1. the histogram slice (one bin a thread) and the first D rounds of
+  // scores, then the boundary while the scores are in flight
   const uint32_t n = (uint32_t)z.n, flo = (uint32_t)z.f_lo, fhi = (uint32_t)z.f_hi;
-  // candidates: lo <= bits <= hi; selected outright: bits > hi (nothing when k == 0)
-  const uint32_t lo = k > 0 ? bd.d1 << kHistShift : 1u;
-  const uint32_t hi = k > 0 ? (bd.d1 < (uint32_t)(kHistBins - 1)
-                                   ? ((bd.d1 + 1) << kHistShift) - 1u : 0xFFFFFFFFu)
-                            : 0u;
-  const bool above_ok = k > 0 && hi != 0xFFFFFFFFu;
-  // pass 1: selection ballots into the bitmap, candidates counted per wave
-  const uint64_t lt = lanemask_lt64();
-  uint32_t wc = 0u;
+  const int rounds = (int)((n + RK - 1) / RK);
+  const bool by_score = k > 0;
+  const HistSlice<NT> hs = load_hist_slice<NT>(hist + (int64_t)bg * kHistBins);
+  const uint32_t* srow = reinterpret_cast<const uint32_t*>(scores) + (int64_t)bg * sstride;
+  const uint32_t last = (uint32_t)sstride - 4u;
+  const uint32_t lkey = (uint32_t)wave * 256u + 4u * (uint32_t)lane;  // this lane's first key in a round
+  auto load = [&](int r) {
+    uint32_t key = (uint32_t)r * RK + lkey;
+    if (key > last) key = last;  // past the row: re-read its end (masked below)
+    return *reinterpret_cast<const uint4*>(srow + key);
+  };
+  uint4 ring[D];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint32_t base = (uint32_t)(r * kOneKeys + wave * 256);  // this wave's 256-key block
-    const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-    uint64_t ms[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = base + 4 * lane + e;
-      const bool valid = key < n;
-      const bool forced = key < flo || key >= fhi;
-      ms[e] = __ballot(valid && (forced || (above_ok && sb[e] > hi)));
-      wc += (uint32_t)__popcll(__ballot(valid && !forced && sb[e] <= hi && sb[e] >= lo));
-    }
-    // block j = base / 256: words 8j + 2e (+1) = the ballot of the lanes' e-th keys
-    if (lane < 8) {
-      const uint64_t a = ms[lane >> 1];
-      lbm[(base >> 5) + lane] = (lane & 1) ? (uint32_t)(a >> 32) : (uint32_t)a;
-    }
-  }
-  if (lane == 0) wcount[wave] = wc;
-  __syncthreads();
-  uint32_t cpos = 0u, C = 0u;
-#pragma unroll
-  for (int w = 0; w < kResWaves; ++w) {
-    const uint32_t c = wcount[w];
-    cpos += w < wave ? c : 0u;
-    C += c;
-  }
-  const bool in_lds = C <= (uint32_t)kCandCap;
-  // pass 2: this wave's candidates in key order from its base position
-  if (in_lds && wc) {  // uniform per wave
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint32_t base = (uint32_t)(r * kOneKeys + wave * 256);
-      const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+  for (int d = 0; d < D; ++d) ring[d] = load(d);
+  if (tid == 0) ccount = 0u;
+  Boundary bd{0u, 0u};
+  if (by_score) bd = boundary_of<NT>(hs, (uint32_t)k, wsum, &shb);  // uniform; has barriers
+  else __syncthreads();  // ccount
+  // candidates: lo <= bits <= hi; selected outright: bits > hi.  Without a
+  // top-k part (k = 0) nothing is above and nothing is a candidate.
+  const uint32_t lo = by_score ? bd.d1 << kHistShift : 0xFFFFFFFFu;
+  const uint32_t hi = by_score ? (bd.d1 < (uint32_t)(kHistBins - 1)
+                                      ? ((bd.d1 + 1) << kHistShift) - 1u : 0xFFFFFFFFu)
+                               : 0xFFFFFFFFu;
+
+  // Ballots of round r: sel[e] (selected outright) and cnd[e] (candidates),
+  // bit i = key r*RK + 256*wave + 4i + e; c[e]: this lane's key e is one.
+  auto classify = [&](const uint4& v, int r, uint64_t (&sel)[4], uint64_t (&cnd)[4],
+                      bool (&c)[4]) {
+    const uint32_t sb[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t kb = (uint32_t)r * RK + (uint32_t)wave * 256u;  // the wave's block
+    if (kb >= flo && kb + 256u <= fhi) {  // uniform: every key valid, none forced
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = base + 4 * lane + e;
-        const bool c = key < n && key >= flo && key < fhi && sb[e] <= hi && sb[e] >= lo;
-        const uint64_t mc = __ballot(c);
-        if (c) lcand[cpos + (uint32_t)__popcll(mc & lt)] = make_uint2(sb[e], key);
-        cpos += (uint32_t)__popcll(mc);
+        const bool above = sb[e] > hi;
+        c[e] = by_score && !above && sb[e] >= lo;
+        sel[e] = __ballot(above);
+        cnd[e] = __ballot(c[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = kb + 4u * (uint32_t)lane + (uint32_t)e;
+        const bool valid = key < n;
+        const bool forced = key < flo || key >= fhi;
+        const bool above = sb[e] > hi;
+        c[e] = valid && !forced && by_score && !above && sb[e] >= lo;
+        sel[e] = __ballot(valid && (forced || above));
+        cnd[e] = __ballot(c[e]);
       }
     }
+  };
+  // This wave's candidates of round r from position base on: LDS slots below
+  // CAP (dst == nullptr), or the global list (dst).
+  auto place = [&](auto to_global, const uint4& v, int r, const uint64_t (&cnd)[4],
+                   const bool (&c)[4], uint32_t base, uint2* dst) {
+    const uint32_t sb[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t key0 = (uint32_t)r * RK + lkey;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (cnd[e]) {  // uniform
+        const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(cnd[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cnd[e], 0u));
+        if (c[e]) {
+          const uint2 ent = make_uint2(sb[e], key0 + (uint32_t)e);
+          if constexpr (decltype(to_global)::value) dst[pos] = ent;
+          else lc[pos] = ent;
+        }
+        base += (uint32_t)__popcll(cnd[e]);
+      }
+    }
+  };
+
+  // 2. the streaming pass.  Whole blocks of D rounds run unconditionally, each
+  // round refilling its ring slot, once used, with the round D ahead (clamped
+  // loads), so no branch sits between a load and its use and every slot is
+  // reloaded in place; the last rounds, already in the ring, are then
+  // processed without further loads.
+  auto process = [&](const uint4& v, int r) {
+    uint64_t sel[4], cnd[4];
+    bool c[4];
+    classify(v, r, sel, cnd, c);
+    const uint32_t j = (uint32_t)r * NW + (uint32_t)wave;  // 256-key block
+    if (lane == 0) {
+      uint4* dst = reinterpret_cast<uint4*>(bm + j * 8);
+      dst[0] = make_uint4((uint32_t)sel[0], (uint32_t)(sel[0] >> 32), (uint32_t)sel[1],
+                          (uint32_t)(sel[1] >> 32));
+      dst[1] = make_uint4((uint32_t)sel[2], (uint32_t)(sel[2] >> 32), (uint32_t)sel[3],
+                          (uint32_t)(sel[3] >> 32));
+    }
+    const uint32_t cnt =
+        (uint32_t)(__popcll(cnd[0]) + __popcll(cnd[1]) + __popcll(cnd[2]) + __popcll(cnd[3]));
+    if (cnt) {  // uniform per wave
+      uint32_t base = 0u;
+      if (lane == 0) base = atomicAdd(&ccount, cnt);
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+      // past the LDS list: counted only (the overflow pass rewrites them all)
+      if (base + cnt <= (uint32_t)CAP) place(std::false_type{}, v, r, cnd, c, base, nullptr);
+    }
+  };
+  int r0 = 0;
+  for (; r0 + D <= rounds; r0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      process(ring[d], r0 + d);
+      ring[d] = load(r0 + d + D);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (r0 + d < rounds) process(ring[d], r0 + d);  // uniform
+  __syncthreads();
+  const uint32_t C = ccount;
+  const uint32_t need = by_score ? (uint32_t)k - bd.above : 0u;  // 1 <= need <= C when k > 0
+
+  // 3. the candidates that complete the top-k join the bitmap
+  auto mark = [&](const uint2* cl, uint32_t i0, uint32_t step, uint32_t vval, uint32_t imax) {
+    for (uint32_t i = i0; i < C; i += step) {
+      const uint2 e = cl[i];
+      const uint32_t v = e.x & 0x1FFFFFu;
+      if (v > vval || (v == vval && e.y <= imax)) {
+        const uint32_t t = e.y & 255u, ln = t >> 2;
+        atomicOr(&bm[(e.y >> 8) * 8 + (t & 3u) * 2 + (ln >> 5)], 1u << (ln & 31));
+      }
+    }
+  };
+  if (C <= (uint32_t)CAP) {  // uniform
+    uint32_t vval = 0u, imax = 0xFFFFFFFFu;
+    if (by_score && need < C) settle_candidates<NT>(lc, C, need, n, h128, &shpick, vval, imax);
+    mark(lc, (uint32_t)tid, (uint32_t)NT, vval, imax);
+  } else {  // all candidates to the global list (a second pass), settled by the workgroup
+    uint2* gc = cand + (int64_t)bg * n_cap;
+    __syncthreads();  // every thread has read ccount
+    if (tid == 0) ccount = 0u;
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+      const uint4 v = load(r);
+      uint64_t sel[4], cnd[4];
+      bool c[4];
+      classify(v, r, sel, cnd, c);
+      const uint32_t cnt = (uint32_t)(__popcll(cnd[0]) + __popcll(cnd[1]) + __popcll(cnd[2]) +
+                                      __popcll(cnd[3]));
+      if (cnt) {
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&ccount, cnt);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        place(std::true_type{}, v, r, cnd, c, base, gc);
+      }
+    }
+    __syncthreads();  // the list is complete and visible to the workgroup
+    uint32_t vval = 0u, imax = 0xFFFFFFFFu;
+    if (by_score && need < C) settle_candidates<NT>(gc, C, need, n, h128, &shpick, vval, imax);
+    mark(gc, (uint32_t)tid, (uint32_t)NT, vval, imax);
   }
   __syncthreads();
 
-  // the candidates that complete the top-k
-  uint32_t need = k > 0 ? (uint32_t)k - bd.above : 0u;  // 1 <= need <= C when k > 0
-  uint32_t vmask = 0u, vval = 0u, imax = 0xFFFFFFFFu;
-  if (k > 0 && need < C) {  // uniform
-    uint32_t ties = 0u;
-    for (int shift = 14; shift >= 0; shift -= 7) {
-      const Pick pk = in_lds
-          ? radix_pick<false>(lcand, C, vmask, vval, 0u, 0u, shift, need, h128, &shpick)
-          : radix_regs<NR, false>(v, n, flo, fhi, lo, hi, vmask, vval, 0u, 0u, shift, need,
-                                  h128, &shpick);
-      need -= pk.before;
-      vval |= pk.digit << shift;
-      vmask |= 127u << shift;
-      ties = pk.inbin;
-    }
-    if (ties > need) {  // among keys with exactly that score, the lower indices win
-      uint32_t imask = 0u, ival = 0u;
-      int top = 0;
-      while (((uint64_t)1 << top) < (uint64_t)n) ++top;
-      int shift = top > 7 ? top - 7 : 0;
-      for (;;) {
-        const Pick pk = in_lds
-            ? radix_pick<true>(lcand, C, vmask, vval, imask, ival, shift, need, h128, &shpick)
-            : radix_regs<NR, true>(v, n, flo, fhi, lo, hi, vmask, vval, imask, ival, shift,
-                                   need, h128, &shpick);
-        need -= pk.before;
-        ival |= pk.digit << shift;
-        imask |= 127u << shift;
-        if (shift == 0) break;
-        shift = shift > 7 ? shift - 7 : 0;
-      }
-      imax = ival;
-    }
-  }
-  // the chosen candidates join the bitmap
-  if (in_lds) {
-    for (uint32_t i = tid; i < C; i += kResThreads) {
-      const uint2 e = lcand[i];
-      const uint32_t low = e.x & 0x1FFFFFu;
-      if (low > vval || (low == vval && e.y <= imax)) {
-        const uint32_t i4 = (e.y >> 2) & 63u, ee = e.y & 3u;
-        atomicOr(&lbm[(e.y >> 8) * 8 + ee * 2 + (i4 >> 5)], 1u << (i4 & 31));
-      }
-    }
-  } else {
+  // 4. ascending indices: segments of NT*SW key-order words (SW consecutive
+  // words a thread), each rebuilt from the 8-bit slices of its block's four
+  // ballots
+  constexpr int SW = 4;
+  const uint32_t nwords = (n + 31) >> 5;
+  uint32_t written = 0u;
+  for (uint32_t w0 = 0; w0 < nwords; w0 += NT * SW) {
+    uint32_t kw[SW], cnt = 0u;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint32_t key = (uint32_t)(r * kOneKeys + 4 * tid);
-      const uint32_t m = cand_bits<NR>(v, r, key, n, flo, fhi, lo, hi);
-      const uint32_t sb[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+    for (int q = 0; q < SW; ++q) {
+      const uint32_t wi = w0 + (uint32_t)tid * SW + q;
+      uint32_t x = 0u;
+      if (wi < nwords) {
+        const uint32_t blk = wi >> 3, sub = wi & 7;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t low = sb[e] & 0x1FFFFFu, kk = key + (uint32_t)e;
-        if (((m >> e) & 1u) && (low > vval || (low == vval && kk <= imax))) {
-          const uint32_t i4 = (kk >> 2) & 63u;
-          atomicOr(&lbm[(kk >> 8) * 8 + (uint32_t)e * 2 + (i4 >> 5)], 1u << (i4 & 31));
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t b8 = (bm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
+          x |= spread4(b8) << e;  // key 4i + e of the word at bit 4i + e
         }
       }
+      kw[q] = x;
+      cnt += (uint32_t)__popc(x);
     }
-  }
-  __syncthreads();
-  // key-order 32-bit words from the block masks (W consecutive words a thread)
-  constexpr int W = (NR * kOneKeys / 32 + kResThreads - 1) / kResThreads;
-  const int64_t segw = ((int64_t)n + 31) >> 5;
-  uint32_t kw[W];
-  uint32_t cnt = 0u;
+    const uint32_t inc = block_incl_scan<NT>(cnt, wsum);
+    uint32_t pos = written + inc - cnt;
 #pragma unroll
-  for (int q = 0; q < W; ++q) {
-    const int64_t wi = (int64_t)tid * W + q;
-    uint32_t x = 0u;
-    if (wi < segw) {
-      const int blk = (int)(wi >> 3), sub = (int)(wi & 7);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t b8 = (lbm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
-        x |= spread4(b8) << e;  // key 4i + e of the word at bit 4i + e
+    for (int q = 0; q < SW; ++q) {
+      uint32_t x = kw[q];
+      const uint32_t kbase = (w0 + (uint32_t)tid * SW + q) * 32u;
+      while (x) {
+        const int bit = __ffs(x) - 1;
+        x &= x - 1;
+        if (pos < (uint32_t)k_max) {
+          out[pos] = (int32_t)(kbase + bit);
+          if (ATT) lsel[pos] = (int32_t)(kbase + bit);
+        }
+        ++pos;
       }
     }
-    kw[q] = x;
-    cnt += __popc(x);
+    if (tid == NT - 1) seg_total = inc;
+    __syncthreads();
+    written += seg_total;
+    __syncthreads();
   }
-  const uint32_t incw = block_incl_scan<kResThreads>(cnt, wsum);
-  uint32_t pos = incw - cnt;
-#pragma unroll
-  for (int q = 0; q < W; ++q) {
-    uint32_t x = kw[q];
-    const uint32_t kbase = (uint32_t)(((int64_t)tid * W + q) * 32);
-    while (x) {
-      const int bit = __ffs(x) - 1;
-      x &= x - 1;
-      if (pos < (uint32_t)k_max) out[pos] = (int32_t)(kbase + bit);
-      ++pos;
-    }
+  for (int64_t t = z.total + tid; t < k_max; t += NT) out[t] = -1;
+  if constexpr (ATT) {
+    const int g = bg % Hq, h = g / (Hq / at.Hkv);
+    const int64_t kv = ((int64_t)b * at.Hkv + h) * n_cap * kHead;
+    const int S = (int)(z.total < k_max ? z.total : k_max);
+    attend_selected<T, NT, 4>(at.q + (int64_t)bg * kHead, at.K + kv, at.V + kv, lsel, S,
+                              at.scale, reinterpret_cast<float*>(bm), mml,
+                              at.out + (int64_t)bg * kHead);
   }
-  for (int64_t t = z.total + tid; t < k_max; t += kResThreads) out[t] = -1;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1627,43 +1794,107 @@ hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids
   return hipGetLastError();
 }
 
+// Rows of up to kStreamKeys keys take the streaming top-k (one workgroup per
+// head); longer rows spread the classification over many scan workgroups per
+// head before one resolve workgroup per head (a single workgroup's compare
+// and ballot work grows with the row: at 128K keys it cost 29 us against
+// 18 us for scan + resolve).
+constexpr int64_t kStreamKeys = 40960;
+
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx, const ScoreWs& ws,
-                       hipStream_t s) {
-  if (n_cap <= (int64_t)kOneKeys * kOneMaxRounds) {  // every score of a head in one workgroup
-    const int rounds = (int)((n_cap + kOneKeys - 1) / kOneKeys);
-    auto go = [&](auto rt) {
-      constexpr int NR = decltype(rt)::value;
-      topk_onepass_kernel<NR><<<(unsigned)((B * Hq + kXcds - 1) / kXcds * kXcds), kResThreads, 0,
-                                s>>>(scores, n_cap, score_stride(n_cap), lens, ks, k_max,
-                                     sw.sink, sw.window, Hq, B * Hq, ws.hist, idx);
+                       hipStream_t s, const AttendSpec* att, bool* attended) {
+  if (attended) *attended = false;
+  const int64_t heads = (int64_t)B * Hq;
+  const bool many = heads > device_cus();
+  const int64_t sst = score_stride(n_cap);
+  // the attention arguments of the fused kernels, in K's element type
+  auto with_att = [&](auto tag, auto&& go) {
+    using T = decltype(tag);
+    AttendArgs<T> a{static_cast<const T*>(att->q), static_cast<const T*>(att->K),
+                    static_cast<const T*>(att->V), att->out, att->Hkv, att->scale};
+    go(a);
+  };
+  const AttendArgs<uint16_t> none{};
+  if (n_cap <= kStreamKeys) {
+    // 512-thread form (33 KiB of LDS, several a CU) for batches with more
+    // heads than CUs, else the 1024-thread form (one a CU)
+    const unsigned hgrid = (unsigned)((heads + kXcds - 1) / kXcds * kXcds);
+    constexpr int kSmallCap = 2048, kBigCap = 8192;
+    // Attending in the selecting workgroup (one CU per head) pays only when
+    // there are more heads than CUs: with 32 heads one CU gathering a head's
+    // 656 K and V rows took ~15 us, against ~10 us for the split-k kernels.
+    const bool fuse = att && many && k_max <= 2 * kSmallCap;
+    auto run = [&](auto ntag, auto atag, auto a) {
+      constexpr int NT = decltype(ntag)::value;
+      constexpr bool ATT = decltype(atag)::value;
+      using T = typename std::remove_pointer<decltype(a.q)>::type;
+      using TT = typename std::remove_const<T>::type;
+      if constexpr (NT == 512)
+        topk_stream_kernel<512, 4096, kSmallCap, 8, ATT, TT><<<hgrid, 512, 0, s>>>(
+            scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, (int)heads, ws.hist,
+            ws.cand, idx, a);
+      else
+        topk_stream_kernel<1024, 16384, kBigCap, 8, ATT, TT><<<hgrid, 1024, 0, s>>>(
+            scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, (int)heads, ws.hist,
+            ws.cand, idx, a);
     };
-    if (rounds <= 1) go(std::integral_constant<int, 1>{});
-    else go(std::integral_constant<int, 2>{});
+    using N5 = std::integral_constant<int, 512>;
+    using N10 = std::integral_constant<int, 1024>;
+    if (fuse) {
+      auto go = [&](auto a) {
+        if (many) run(N5{}, std::true_type{}, a);
+        else run(N10{}, std::true_type{}, a);
+      };
+      if (att->dtype == 1) with_att(uint16_t{}, go);
+      else with_att(float{}, go);
+      if (attended) *attended = true;
+    } else if (many) {
+      run(N5{}, std::false_type{}, none);
+    } else {
+      run(N10{}, std::false_type{}, none);
+    }
     return hipGetLastError();
   }
   const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
-  const int64_t nscan = (int64_t)B * Hq * CH;
+  const int64_t nscan = heads * CH;
   const unsigned sgrid = (unsigned)((nscan + kXcds - 1) / kXcds * kXcds);
   // two kScanThreads workgroups fit a CU; beyond that, the small ones
   if (nscan <= 2 * (int64_t)device_cus())
     topk_scan_kernel<kScanThreads, kScanKeys / (kScanThreads / 64)><<<sgrid, kScanThreads, 0, s>>>(
-        scores, n_cap, score_stride(n_cap), lens, ks, k_max, sw.sink, sw.window, Hq, CH, B * Hq,
+        scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, CH, (int)heads,
         ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
   else
     topk_scan_kernel<256, 256><<<sgrid, 256, 0, s>>>(
-        scores, n_cap, score_stride(n_cap), lens, ks, k_max, sw.sink, sw.window, Hq, CH, B * Hq,
+        scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, CH, (int)heads,
         ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (B * Hq <= device_cus())
-    topk_resolve_kernel<kResThreads><<<(unsigned)(B * Hq), kResThreads, 0, s>>>(
+  const int rnt = many ? 512 : kResThreads;
+  const bool fuse = att && many && (n_cap + 255) / 256 <= rnt && k_max <= 2 * kCandCap;
+  auto run = [&](auto ntag, auto atag, auto a) {
+    constexpr int NT = decltype(ntag)::value;
+    constexpr bool ATT = decltype(atag)::value;
+    using T = typename std::remove_const<typename std::remove_pointer<decltype(a.q)>::type>::type;
+    topk_resolve_kernel<NT, ATT, T><<<(unsigned)heads, NT, 0, s>>>(
         n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, ws.hist, ws.counters, ws.bitmap, ws.words,
-        ws.cand, idx);
-  else
-    topk_resolve_kernel<512><<<(unsigned)(B * Hq), 512, 0, s>>>(
-        n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, ws.hist, ws.counters, ws.bitmap, ws.words,
-        ws.cand, idx);
+        ws.cand, idx, a);
+  };
+  using R5 = std::integral_constant<int, 512>;
+  using R10 = std::integral_constant<int, kResThreads>;
+  if (fuse) {
+    auto go = [&](auto a) {
+      if (many) run(R5{}, std::true_type{}, a);
+      else run(R10{}, std::true_type{}, a);
+    };
+    if (att->dtype == 1) with_att(uint16_t{}, go);
+    else with_att(float{}, go);
+    if (attended) *attended = true;
+  } else if (many) {
+    run(R5{}, std::false_type{}, none);
+  } else {
+    run(R10{}, std::false_type{}, none);
+  }
   return hipGetLastError();
 }
 

@@ -32,22 +32,6 @@ size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base) {
   return off;
 }
 
-// Load 8 consecutive head elements [8*j, 8*j+8) of a row as floats.
-template <typename T>
-__device__ __forceinline__ void load_row8(const T* row, int j, float* f);
-template <>
-__device__ __forceinline__ void load_row8<uint16_t>(const uint16_t* row, int j, float* f) {
-  const uint4 v = reinterpret_cast<const uint4*>(row)[j];
-  unpack_bf16x8(v, f);
-}
-template <>
-__device__ __forceinline__ void load_row8<float>(const float* row, int j, float* f) {
-  const float4 a = reinterpret_cast<const float4*>(row)[2 * j];
-  const float4 b = reinterpret_cast<const float4*>(row)[2 * j + 1];
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
 // grid: B*Hq*splits blocks of kDecThreads.
 template <typename T>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(

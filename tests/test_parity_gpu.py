@@ -220,9 +220,9 @@ def test_select_sink_window_parity(sw):
 @pytest.mark.parametrize("n", [3000, 8000, 20000, 70000])
 def test_topk_ties_lower_index_wins(n):
     """All keys of a head share one bucket pattern and norm -> equal scores.
-    3000 and 8000 keys take the one-pass kernel (8000 equal keys overflow its
-    LDS candidate list), 20000 and 70000 the scan + resolve kernels (70000
-    with the candidates left in global memory)."""
+    3000 and 8000 equal keys fit the streaming top-k's LDS candidate list;
+    20000 and 70000 overflow it and take its second pass through the global
+    candidate list."""
     w = make_workload("c2", n=n, Hq=8, Hkv=2, k=100)
     d = GC.upload(w)
     ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
@@ -243,11 +243,11 @@ def test_topk_ties_lower_index_wins(n):
 @pytest.mark.parametrize("B,Hq,Hkv,n", [(4, 32, 8, 40000), (1, 264, 66, 140000)],
                          ids=["4x32-heads-40000", "264-heads-140000"])
 def test_topk_ties_large_batches(B, Hq, Hkv, n):
-    """Equal scores in launches large enough for the scan's small workgroups
-    (more than two 768-thread workgroups a CU): every key is a boundary
-    candidate, so each wave's LDS candidate region overflows into the global
-    list, and the lower indices must still win.  264 heads (more than CUs)
-    take the 512-thread resolve, whose 140000-key rows span two segments."""
+    """Equal scores in large launches: every key is a boundary candidate, so
+    the streaming top-k's LDS candidate list overflows into the global list,
+    and the lower indices must still win.  264 heads (more than CUs) of
+    140000 keys take the 1024-thread form (rows too long for the 512-thread
+    one), whose bitmap spans several emit segments."""
     w = make_workload("c4", n=(64, 64), B=B, Hq=Hq, Hkv=Hkv, k=100)  # q and W; keys set below
     w.n_cap = n + 1
     w.lens = np.full(w.B, n, np.int32)
@@ -265,6 +265,40 @@ def test_topk_ties_large_batches(B, Hq, Hkv, n):
             h = g // (w.Hq // w.Hkv)
             expect = np.arange(half, half + 100) if h == 1 else np.arange(100)
             assert idx[b, g].tolist() == expect.tolist(), (b, g)
+
+
+@pytest.mark.parametrize("ties", [False, True], ids=["scores", "ties"])
+def test_topk_long_rows_scan_resolve(ties):
+    """Rows longer than the streaming top-k's LDS bitmap (512K keys) take the
+    scan + resolve kernels: 600000 keys for two query heads, on the oracle's
+    scores, or with every score equal (all keys boundary candidates, kept in
+    the global list; the lower indices win)."""
+    w = make_workload("c2", n=600000, Hq=2, Hkv=1, L=16, k=1200)
+    d = GC.upload(w)
+    if ties:
+        ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
+        vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+        idx, _ = GC.gpu_score_topk(w, d, ids, vn, sink=5, window=7)
+        sync()
+        idx = idx.cpu().numpy()
+        n = int(w.lens[0])
+        expect = list(range(5 + 1200)) + list(range(n - 7, n))
+        for g in range(w.Hq):
+            assert idx[0, g].tolist() == expect
+        return
+    ids_np, vn_np = _oracle_ids(w)
+    ids = GC.ids_dev(ids_np, w.n_cap, w.P)
+    vn = torch.from_numpy(vn_np).to(DEV)
+    idx, sc = GC.gpu_score_topk(w, d, ids, vn)
+    sync()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    tables = SO.soft_tables(w.q, w.W, w.L, w.P, w.tau)
+    s_ref = SO.scores(tables, ids_np, vn_np.astype(np.float64), w.lens)
+    n, k = int(w.lens[0]), int(w.ks[0])
+    for g in range(w.Hq):
+        GC.check_scores(sc[0, g, :n], s_ref[0, g, :n])
+        GC.check_exact_topk(idx[0, g], sc[0, g], k, n)
+        GC.check_set(idx[0, g], s_ref[0, g, :n], k)
 
 
 def test_topk_edge_lengths():
@@ -681,10 +715,19 @@ def test_run_twice_bitwise():
     (dict(name="c2", n=20000, k=300), (64, 128)),          # k_max 492: 8 splits
     (dict(name="c4", n=(9000, 30000), B=3, Hq=8, Hkv=2, lens=[30000, 9000, 12345]), (16, 16)),
     (dict(name="c1", n=10000, k=200), (0, 0)),              # float32
+    # attention inside the selecting workgroups: the resolve form (rows past
+    # the streaming top-k's length), the 512-thread streaming form (more heads
+    # than CUs), and a selection too long to be kept in LDS (separate attention)
+    (dict(name="c2", n=50000, Hq=8, Hkv=2), (0, 0)),
+    (dict(name="c4", n=(1000, 3000), B=9, k=0.02), (16, 16)),
+    (dict(name="c2", n=30000, Hq=8, Hkv=2, k=17000), (0, 0)),
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else f"sw{c}")
 def test_decode_step_matches_three_calls(case, sw):
-    """socket_decode_step (append hashed inside the table kernel) equals
-    socket_hash_keys + socket_score_topk + socket_sparse_decode, bit for bit."""
+    """socket_decode_step (append hashed inside the table kernel, attention
+    inside the selecting workgroups where it fits) equals socket_hash_keys +
+    socket_score_topk + socket_sparse_decode: IDs, norms, scores and indices
+    bit for bit; the attention output, summed in another order, to 1e-5, and
+    within the oracle's bar on its own."""
     print("case", case, sw, flush=True)
     sink, window = sw
     w = make_workload(**case)
@@ -726,7 +769,14 @@ def test_decode_step_matches_three_calls(case, sw):
     assert torch.equal(vn1, vn2)
     assert torch.equal(idx1, idx2)
     assert torch.equal(sc1, sc2)
-    assert torch.equal(out1, out2)
+    assert not torch.isnan(out2).any()
+    torch.testing.assert_close(out2, out1, rtol=0, atol=1e-5)
+    idx_np, out_np = idx2.cpu().numpy(), out2.cpu().numpy()
+    group = w.Hq // w.Hkv
+    for b in range(w.B):
+        for g in range(0, w.Hq, 5):
+            GC.check_out(out_np[b, g], w.q[b, g], w.K[b, g // group], w.V[b, g // group],
+                         idx_np[b, g], w.scale)
 
 
 def test_stage_entry_points_match_fused_call():
