@@ -1,13 +1,13 @@
 """Benchmark of the SOCKET decode hot path on one MI355X.
 
 One step = one decode step of the GQA 32/8 workload at n = 32768 cached keys
-(d = 128, L = 64 tables x P = 8 planes, tau = 0.5, k = 656 = ceil(2% of n)),
-issued as a caller would, through three C calls:
-
-  socket_hash_keys     append: hash the new key of every KV head, store its norm
-  socket_score_topk    soft tables, soft-count scores of all n + 1 keys for the
-                       32 query heads, top-656 per query head
-  socket_sparse_decode exact attention of each query head over its keys
+(d = 128, L = 64 tables x P = 8 planes, tau = 0.5, k = 656 = ceil(2% of n)):
+the new key of every KV head is hashed and its value norm stored, then soft
+tables, soft-count scores of all n + 1 keys for the 32 query heads, the
+top-656 per query head and exact attention over them -- one
+socket_decode_step call (the same step through the three calls
+socket_hash_keys, socket_score_topk and socket_sparse_decode is reported
+beside it).
 
 `value` is keys scored+selected per second: 32 query heads x (n + 1) keys per
 step, divided by the wall time of K steps bracketed by device syncs.  Inputs
@@ -15,12 +15,23 @@ are resident in HBM.  The cache is replicated `--replicas` times (one replica
 per step, round robin, like successive layers) so the 256 MiB Infinity Cache
 cannot serve a step from the previous one.
 
+`roofline` is the selection stage (soft tables + scores + top-k, one
+socket_score_topk call) at 32K: its algorithmic bytes (per KV-key the L*P-bit
+IDs and the float32 norm read and G float32 scores written; per query-key the
+score read back by the top-k) over its average GPU time in a batch of calls
+timed with HIP events on the library's stream.
+
 Also reported: per-stage GPU time (batches of steps cut after each stage,
 timed with one pair of HIP events per batch while the launches queue behind a
 long matrix product, so host launch gaps stay out; a stage's time includes
-its dispatch), the scorer's average launch time (a batch of scorer launches
-alone) for the roofline, the 128K-key step, the prefill hashing rate against
-the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
+its dispatch), the scorer alone, the 128K-key step, the 128K prefill hashing
+(fused with the norms; IDs only against the bf16 MFMA peak; norms only against
+HBM), the prefill + 256-step decode loop at 128K, the comparison modes, and
+the CPU oracle on bounded samples.
+
+`--only NAME` runs a few launches of one kernel group and exits (for
+rocprofv3 counter runs): prefill128k (IDs only), prefill128k-fused,
+norms128k, stage32k, stage128k, step32k.
 """
 from __future__ import annotations
 
@@ -30,7 +41,6 @@ import hashlib
 import json
 import math
 import os
-import resource
 import sys
 import time
 
@@ -41,8 +51,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-SCORER_SRC = os.path.join(ROOT, "soft_lsh_token_amd", "csrc", "score_topk.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "scorer_c2_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
 def log(*a):
@@ -65,6 +74,11 @@ def parse():
                    help="skip the 10-plane, 60-table measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--loop-steps", type=int, default=256,
+                   help="decode steps of the 128K prefill + decode loop")
+    p.add_argument("--only", default=None, metavar="NAME",
+                   help="run a few launches of one kernel group and exit (counter runs): "
+                        "prefill128k, prefill128k-fused, norms128k, stage32k, stage128k, step32k")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="also run one device-to-device copy of this many MiB (a known-size "
                         "reference kernel for hardware byte counters)")
@@ -134,12 +148,20 @@ class Case:
             [], [], [], [], []
         self.c_dense = []
         self.c_fused = []
+        self.c_prefill_ids, self.c_prefill_norms = [], []
         for r in range(self.replicas):
             K, V, ids, vn = self.K[r].data_ptr(), self.V[r].data_ptr(), self.ids[r].data_ptr(), \
                 self.vn[r].data_ptr()
             common = (vp(K), vp(V), 1, w.B, w.Hkv, w.d, i64(w.n_cap))
             self.c_prefill.append(common + (vp(self.pos_prefill.data_ptr()), self.n,
                                              vp(self.W.data_ptr()), w.L, w.P, vp(ids), vp(vn), st))
+            # the same prefill split in two: bucket IDs only, value norms only
+            self.c_prefill_ids.append((vp(K), None, 1, w.B, w.Hkv, w.d, i64(w.n_cap),
+                                       vp(self.pos_prefill.data_ptr()), self.n,
+                                       vp(self.W.data_ptr()), w.L, w.P, vp(ids), None, st))
+            self.c_prefill_norms.append((None, vp(V), 1, w.B, w.Hkv, w.d, i64(w.n_cap),
+                                         vp(self.pos_prefill.data_ptr()), self.n, None, w.L, w.P,
+                                         None, vp(vn), st))
             self.c_append.append(common + (vp(self.pos_append.data_ptr()), 1,
                                             vp(self.W.data_ptr()), w.L, w.P, vp(ids), vp(vn), st))
             self.c_score.append((w.B, w.Hq, w.Hkv, w.L, w.P, vp(ids), vp(vn),
@@ -181,8 +203,13 @@ class Case:
         if rc != 0:
             raise RuntimeError(f"{what} returned status {rc}")
 
-    def prefill(self, r):
-        self._ok(self.lib.socket_hash_keys(*self.c_prefill[r]), "socket_hash_keys")
+    def prefill(self, r, mode="fused"):
+        c = {"fused": self.c_prefill, "ids": self.c_prefill_ids, "norms": self.c_prefill_norms}[mode]
+        self._ok(self.lib.socket_hash_keys(*c[r]), "socket_hash_keys")
+
+    def score_topk(self, r):
+        """The selection stage alone: soft tables, scores, top-k."""
+        self._ok(self.lib.socket_score_topk(*self.c_score_topk[r]), "socket_score_topk")
 
     def step(self, r):
         """One decode step on replica r through socket_decode_step (the new key
@@ -352,20 +379,28 @@ def hard_mode(lib, torch, S, L, P, replicas):
                 code_gbs=code_bytes / (us * 1e-6) / 1e9)
 
 
-def prefill_rate(case, torch):
-    """GPU time of one prefill hash launch (all n keys of every KV head): a batch
-    of launches on the replicas in turn, queued behind the busy prologue."""
-    case.prefill(0)
+def prefill_rate(case, torch, mode="fused"):
+    """GPU time of one prefill launch (all n keys of every KV head): a batch of
+    launches on the replicas in turn, queued behind the busy prologue.  mode
+    'fused' hashes and stores the norms, 'ids' hashes only (the bf16 MFMA
+    GEMM, against the MFMA peak), 'norms' stores the norms only (against HBM)."""
+    case.prefill(0, mode)
     torch.cuda.synchronize()
-    us, _ = gpu_batch_us(torch, lambda i: case.prefill(i % case.replicas),
+    us, _ = gpu_batch_us(torch, lambda i: case.prefill(i % case.replicas, mode),
                          max(8, 2 * case.replicas))
     t = us * 1e-6
     w = case.w
     keys = w.B * w.Hkv * case.n
     flops = 2.0 * keys * w.d * w.L * w.P
-    hbm = keys * (2 * w.d * 2 + w.L + 4)   # K and V rows read, ids and norm written
-    return dict(keys=keys, seconds=t, tflops=flops / t / 1e12,
-                mfma_frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, hbm_gbs=hbm / t / 1e9)
+    from soft_lsh_token_amd import layout
+    id_bytes = layout.key_bytes(w.L, w.P)
+    k_bytes = w.d * 2
+    hbm = {"fused": keys * (2 * k_bytes + id_bytes + 4), "ids": keys * (k_bytes + id_bytes),
+           "norms": keys * (k_bytes + 4)}[mode]
+    r = dict(mode=mode, keys=keys, us=us, hbm_gbs=hbm / t / 1e9, hbm_frac=hbm / t / 1e9 / HBM_PEAK_GBS)
+    if mode != "norms":
+        r.update(tflops=flops / t / 1e12, mfma_frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS)
+    return r
 
 
 def scorer_bytes(case):
@@ -377,6 +412,15 @@ def scorer_bytes(case):
     return kv_keys * ((w.L * w.P + 7) // 8 + 4 + 4 * G), kv_keys
 
 
+def stage_bytes(case):
+    """Algorithmic bytes of one selection stage (soft tables + scores + top-k):
+    the scorer's, plus every query-key's score read back by the top-k (the
+    tables' and indices' few kilobytes are left out)."""
+    launch, kv_keys = scorer_bytes(case)
+    w = case.w
+    return launch + 4 * kv_keys * (w.Hq // w.Hkv), kv_keys
+
+
 def scorer_stored_bytes(case):
     """Bytes one scorer launch moves in the cache's own layout (cells of one or
     two bytes, tables padded to 16 words per key)."""
@@ -386,58 +430,240 @@ def scorer_stored_bytes(case):
     return case.kv_keys * (layout.key_bytes(w.L, w.P) + 4 + 4 * G)
 
 
-def counters_traffic(launch_bytes):
-    """HBM traffic of the scorer from committed rocprofv3 counters, if they were
-    taken on the current scorer source."""
+def stage_launch_us(case, torch, calls):
+    """Average GPU time of one socket_score_topk call (its three launches back
+    to back on the replicas, after a warm call)."""
+    case.score_topk(0)
+    torch.cuda.synchronize()
+    us, _ = gpu_batch_us(torch, lambda i: case.score_topk(i % case.replicas), calls)
+    return us
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counters_traffic(name):
+    """HBM bytes per call of a kernel group from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters, if they were taken on the current sources (else None)."""
     try:
         with open(COUNTERS) as f:
-            c = json.load(f)
-        with open(SCORER_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if c.get("source_sha256") != sha:
-            return None
-        return float(c["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+            c = json.load(f)[name]
+        for rel, sha in c["sources"].items():
+            if _sha(os.path.join(ROOT, rel)) != sha:
+                return None
+        return float(c["hbm_bytes_per_call"])
+    except (OSError, KeyError, ValueError, TypeError):
+        return None
+
+
+def roofline_entry(name, bytes_, us, kernel, extra=None):
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    r = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": gbs / HBM_PEAK_GBS, "traffic": counters_traffic(name), "kernel": kernel,
+         "bytes_per_call": bytes_, "us_per_call": us}
+    r.update(extra or {})
+    return r
+
+
+def decode_loop_c5(lib, torch, S, steps):
+    """Prefill 131072 keys x 8 KV heads, then `steps` decode steps, each
+    appending one key and value per KV head (socket_decode_step), with a fresh
+    query per step.  Per-step GPU times from HIP events around each step on
+    the library's stream (the host enqueues faster than the GPU runs, so the
+    events see GPU time)."""
+    from soft_lsh_token_amd.inputs import make_workload
+    t0 = time.time()
+    w = make_workload("c5", steps=steps)
+    log(f"[bench] c5: inputs drawn in {time.time() - t0:.1f}s (n={int(w.lens[0])}, "
+        f"n_cap={w.n_cap}, steps={steps})")
+    dev, bf = "cuda:0", torch.bfloat16
+    K = torch.from_numpy(w.K).to(dev).to(bf)
+    V = torch.from_numpy(w.V).to(dev).to(bf)
+    W = torch.from_numpy(w.W).to(dev).to(bf)
+    qs = torch.from_numpy(w.q_steps).to(dev).to(bf)
+    n0 = int(w.lens[0])
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, dev)
+    vn = torch.zeros(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    lens_all = torch.arange(n0 + 1, n0 + steps + 1, dtype=torch.int32, device=dev).view(steps, 1)
+    ks = torch.from_numpy(w.ks).to(dev)
+    k_max = int(w.ks.max())
+    idx = torch.empty(w.B, w.Hq, k_max, dtype=torch.int32, device=dev)
+    out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+    ws = S.alloc_workspace(S.socket_decode_step_workspace(w.B, w.Hq, w.Hkv, w.n_cap, w.L, w.P,
+                                                          k_max), dev)
+    stream = torch.cuda.current_stream()
+
+    def run_once():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 2)]
+        torch.cuda.synchronize()
+        t_host = time.perf_counter()
+        ev[0].record(stream)
+        S.socket_hash_keys(K, V, W, ids, vn, pos0, n0, w.L, w.P)
+        ev[1].record(stream)
+        for t in range(steps):
+            S.socket_decode_step(qs[t], K, V, W, ids, vn, lens_all[t], ks, k_max, w.tau, w.L, w.P,
+                                 w.scale, idx, out, ws=ws)
+            ev[t + 2].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_host
+        return ev, wall
+
+    run_once()  # warm (the first launches of each kernel)
+    ev, wall = run_once()
+    pre_us = ev[0].elapsed_time(ev[1]) * 1e3
+    st = np.array([ev[t + 1].elapsed_time(ev[t + 2]) * 1e3 for t in range(steps)])
+    total_ms = ev[0].elapsed_time(ev[-1])
+    keys = sum(w.Hq * (n0 + t + 1) for t in range(steps))
+    r = dict(prefill_keys=w.B * w.Hkv * n0, steps=steps, prefill_us=pre_us,
+             step_us_median=float(np.median(st)), step_us_p95=float(np.percentile(st, 95)),
+             step_us_mean=float(st.mean()), step_us_first=float(st[0]), step_us_last=float(st[-1]),
+             total_ms=total_ms, wall_ms=wall * 1e3,
+             decode_keys_per_s=keys / (st.sum() * 1e-6))
+    del K, V, ids, vn, ws
+    torch.cuda.empty_cache()
+    return r
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:
         return None
 
 
 def cpu_baseline(seconds):
-    """The CPU oracle, as it stands, on a bounded sample of the 32K decode step."""
+    """The CPU oracle, as it stands, on bounded samples: (1) query heads of the
+    32K decode step, one after another, each with the append hash of its KV
+    head's new key, its soft tables, scores, top-k and attention, timed per
+    stage (the rate is `value`); (2) the prefill + decode loop at 128K: the
+    oracle hashes all 131072 x 8 keys, then runs decode steps 0, 1, 2, 127 and
+    255 for the four query heads of KV head 0 (with every KV head's appended
+    key), timed per stage.  numpy runs the prefill's matrix products on its
+    BLAS threads and everything else on one thread."""
     from oracle import socket_oracle as SO
     from soft_lsh_token_amd.inputs import make_workload
+    blas = _blas_threads()
+    aff = len(os.sched_getaffinity(0))
     w = make_workload("c2", steps=1)
     n = int(w.lens[0])
-    log("[bench] cpu baseline: oracle prefill hash (untimed)")
+    log("[bench] cpu baseline: oracle prefill hash of the 32K cache (untimed)")
     ids = np.empty((w.B, w.Hkv, w.n_cap, w.L), dtype=np.int64)
     for h in range(w.Hkv):
         ids[0, h, :n] = SO.hash_keys(w.K[0, h, :n], w.W, w.L, w.P)[0]
     vn = np.zeros((w.B, w.Hkv, w.n_cap))
     vn[0, :, :n] = SO.value_norms(w.V[0, :, :n])
     lens = np.array([n + 1], dtype=np.int32)
-    # one step = append hash of the new key of every KV head + the decode step
-    # (tables, scores, top-k, attention); the sample is as many query heads of
-    # successive steps as fit in the time budget
-    heads_done, t_used, c_used = 0, 0.0, 0.0
+    stage = dict(append=0.0, tables=0.0, scores=0.0, topk=0.0, attend=0.0)
+    heads_done, t_used = 0, 0.0
     group = w.Hq // w.Hkv
-    while t_used < seconds and heads_done < 64 * w.Hq:
+    budget = 0.6 * seconds
+    while t_used < budget and heads_done < 64 * w.Hq:
         g = heads_done % w.Hq
         h = g // group
-        c0, t0 = time.process_time(), time.perf_counter()
+        t0 = time.perf_counter()
         ids[0, h, n] = SO.hash_keys(w.K[0, h, n:n + 1], w.W, w.L, w.P)[0][0]
         vn[0, h, n] = SO.value_norms(w.V[0, h, n])
+        t1 = time.perf_counter()
         tab = SO.soft_tables(w.q[0, g], w.W, w.L, w.P, w.tau)
+        t2 = time.perf_counter()
         s = SO.scores(tab[None, None], ids[:, h:h + 1], vn[:, h:h + 1], lens)[0, 0]
+        t3 = time.perf_counter()
         sel = SO.topk(s, int(w.ks[0]), n + 1)
+        t4 = time.perf_counter()
         SO.sparse_attention(w.q[0, g], w.K[0, h], w.V[0, h], sel, w.scale)
-        t_used += time.perf_counter() - t0
-        c_used += time.process_time() - c0
+        t5 = time.perf_counter()
+        for key, a, b in (("append", t0, t1), ("tables", t1, t2), ("scores", t2, t3),
+                          ("topk", t3, t4), ("attend", t4, t5)):
+            stage[key] += b - a
+        t_used += t5 - t0
         heads_done += 1
     keys = heads_done * (n + 1)
-    cores = max(1, int(round(c_used / max(t_used, 1e-9))))
-    return dict(value=keys / t_used, unit="keys/s", cores=cores, kind="oracle",
-                sample=f"{heads_done} query heads x {n + 1} keys of the 32K decode step "
-                       f"(append hash + tables + scores + top-k + attention per head), "
-                       f"{t_used:.1f}s wall; host affinity {len(os.sched_getaffinity(0))} cpus")
+    per_head_ms = {k: v / heads_done * 1e3 for k, v in stage.items()}
+
+    # the 128K prefill + decode loop, steps {0, 1, 2, 127, 255} of KV head 0's query heads
+    w5 = make_workload("c5")
+    n0 = int(w5.lens[0])
+    t0 = time.perf_counter()
+    ids5 = np.empty((w5.Hkv, w5.n_cap, w5.L), dtype=np.int64)
+    vn5 = np.zeros((w5.Hkv, w5.n_cap))
+    for h in range(w5.Hkv):
+        ids5[h, :n0] = SO.hash_keys(w5.K[0, h, :n0], w5.W, w5.L, w5.P)[0]
+    t1 = time.perf_counter()
+    vn5[:, :n0] = SO.value_norms(w5.V[0, :, :n0])
+    t2 = time.perf_counter()
+    loop = dict(append=0.0, tables=0.0, scores=0.0, topk=0.0, attend=0.0)
+    check = [0, 1, 2, 127, 255]
+    # keys appended at steps the sample skips are hashed untimed
+    for t in range(w5.steps):
+        if t in check:
+            continue
+        for h in range(w5.Hkv):
+            ids5[h, n0 + t] = SO.hash_keys(w5.K[0, h, n0 + t:n0 + t + 1], w5.W, w5.L, w5.P)[0][0]
+            vn5[h, n0 + t] = SO.value_norms(w5.V[0, h, n0 + t])
+    for t in check:
+        nt = n0 + t + 1
+        a0 = time.perf_counter()
+        for h in range(w5.Hkv):
+            ids5[h, n0 + t] = SO.hash_keys(w5.K[0, h, n0 + t:n0 + t + 1], w5.W, w5.L, w5.P)[0][0]
+            vn5[h, n0 + t] = SO.value_norms(w5.V[0, h, n0 + t])
+        a1 = time.perf_counter()
+        tab = SO.soft_tables(w5.q_steps[t][0, :group], w5.W, w5.L, w5.P, w5.tau)
+        a2 = time.perf_counter()
+        s5 = SO.scores(tab[None], ids5[None, :1], vn5[None, :1], np.array([nt]))[0]
+        a3 = time.perf_counter()
+        sels = [SO.topk(s5[g], int(w5.ks[0]), nt) for g in range(group)]
+        a4 = time.perf_counter()
+        for g in range(group):
+            SO.sparse_attention(w5.q_steps[t][0, g], w5.K[0, 0], w5.V[0, 0], sels[g], w5.scale)
+        a5 = time.perf_counter()
+        for key, a, b in (("append", a0, a1), ("tables", a1, a2), ("scores", a2, a3),
+                          ("topk", a3, a4), ("attend", a4, a5)):
+            loop[key] += b - a
+    loop_s = sum(loop.values())
+    c5 = dict(prefill_hash_s=t1 - t0, prefill_norms_s=t2 - t1, prefill_keys=w5.Hkv * n0,
+              steps=check, heads_per_step=group,
+              step_stage_ms={k: v / len(check) * 1e3 for k, v in loop.items()},
+              step_ms_4_heads=loop_s / len(check) * 1e3,
+              step_ms_all_heads_scaled=loop_s / len(check) * 1e3 * w5.Hq / group)
+    return dict(value=keys / t_used, unit="keys/s", cores=blas or 1, kind="oracle",
+                sample=f"{heads_done} query heads x {n + 1} keys of the 32K decode step, one "
+                       f"after another (append hash + tables + scores + top-k + attention per "
+                       f"head; numpy, one thread), {t_used:.1f}s; then the 128K prefill "
+                       f"(matrix products on {blas} BLAS threads) and decode steps "
+                       f"0/1/2/127/255 for 4 query heads; host affinity {aff} cpus",
+                blas_threads=blas, affinity_cpus=aff, per_head_stage_ms_32k=per_head_ms,
+                decode_loop_128k=c5)
+
+
+def only(args, lib, torch, S):
+    """A few launches of one kernel group, for counter runs; prints what ran."""
+    name = args.only
+    reps = 4
+    if name in ("prefill128k", "prefill128k-fused", "norms128k"):
+        case = Case("c3", reps, lib, torch, S)
+        mode = {"prefill128k": "ids", "prefill128k-fused": "fused", "norms128k": "norms"}[name]
+        for i in range(2 * reps):
+            case.prefill(i % reps, mode)
+    elif name in ("stage32k", "stage128k", "step32k"):
+        case = Case("c2" if name != "stage128k" else "c3", reps, lib, torch, S)
+        for r in range(reps):
+            case.prefill(r)
+        torch.cuda.synchronize()
+        for i in range(4 * reps):
+            if name == "step32k":
+                case.step(i % reps)
+            else:
+                case.score_topk(i % reps)
+    else:
+        raise SystemExit(f"unknown --only {name}")
+    torch.cuda.synchronize()
+    print(json.dumps({"only": name, "calls": 4 * reps if name.startswith(("stage", "step"))
+                      else 2 * reps}), flush=True)
 
 
 def main():
@@ -461,7 +687,11 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.copy_calibration} MiB done")
         del src, dst
+    if args.only:
+        only(args, lib, torch, S)
+        return
 
+    # ---- 32K: the timed step, its stages, the selection stage's roofline
     case = Case("c2", args.replicas, lib, torch, S)
     for r in range(case.replicas):
         case.prefill(r)
@@ -472,60 +702,77 @@ def main():
     log(f"[bench] 32K step wall {sec * 1e6:.1f} us")
     sec3 = timed_steps(case, torch, args.steps, args.warmup, case.step3)
     log(f"[bench] 32K step wall through the three calls {sec3 * 1e6:.1f} us")
-    stages, gpu_step_us, host_step_us = per_stage(case, torch, min(args.steps, 200))
+    stages, gpu_step_us, host_step_us = per_stage(case, torch, min(max(args.steps, 50), 200))
     log(f"[bench] 32K per-stage GPU us {stages}; full step GPU {gpu_step_us:.1f} us; "
         f"host enqueue {host_step_us:.1f} us/step")
+    stage_us = stage_launch_us(case, torch, 4 * case.replicas)
     score_us = scorer_launch_us(case, torch, 4 * case.replicas)
-    log(f"[bench] 32K scorer launch {score_us:.2f} us")
+    log(f"[bench] 32K selection stage {stage_us:.2f} us, scorer launch {score_us:.2f} us")
     dense32 = dense_decode(case, torch, 2 * case.replicas)
     dense32["socket_speedup"] = dense32["us"] / gpu_step_us
     log(f"[bench] 32K dense decode {dense32}")
     est32 = sample_estimate(case, torch, S)
     log(f"[bench] 32K sampling estimator {est32}")
-    launch_bytes, kv_keys = scorer_bytes(case)
-    achieved = launch_bytes / (score_us * 1e-6) / 1e9
-    traffic = counters_traffic(launch_bytes)
+    sbytes, kv_keys = stage_bytes(case)
+    lbytes, _ = scorer_bytes(case)
     w = case.w
     keys_per_step = case.kv_keys * (w.Hq // w.Hkv)
+    roof = roofline_entry(
+        "stage_c2", sbytes, stage_us,
+        "selection stage at 32K: soft_tables_kernel + scorer_kernel + topk_stream_kernel "
+        "(one socket_score_topk call)", {"kv_keys_per_call": kv_keys})
     extra32 = dict(
         step_us_wall=sec * 1e6, step_us_wall_three_calls=sec3 * 1e6,
         step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
-        stage_us=stages, scorer_launch_us=score_us,
-        score_topk_us=stages["tables"] + stages["score"] + stages["topk"],
+        stage_us=stages, selection_stage_us=stage_us, scorer_launch_us=score_us,
+        scorer_roofline=roofline_entry("scorer_c2", lbytes, score_us, "scorer_kernel at 32K"),
         prefill=pre32, dense_decode=dense32, sampling_estimator=est32)
     case.free()
     del case
     torch.cuda.empty_cache()
 
+    # ---- 128K: the step, its stages, the prefill split into IDs and norms
     extra128 = None
     if not args.no_128k:
         c3 = Case("c3", max(4, args.replicas // 5), lib, torch, S)
         for r in range(c3.replicas):
             c3.prefill(r)
         torch.cuda.synchronize()
-        pre128 = prefill_rate(c3, torch)
-        log(f"[bench] prefill hash 128K (the decode-loop prefill): {pre128}")
+        prefill = {m: prefill_rate(c3, torch, m) for m in ("fused", "ids", "norms")}
+        log(f"[bench] prefill 128K (the decode loop's): {prefill}")
         sec3 = timed_steps(c3, torch, args.steps, args.warmup)
-        st3, gpu3, host3 = per_stage(c3, torch, max(20, args.steps // 4))
+        st3, gpu3, _ = per_stage(c3, torch, max(20, args.steps // 4))
+        stage3 = stage_launch_us(c3, torch, 4 * c3.replicas)
         sc3 = scorer_launch_us(c3, torch, 4 * c3.replicas)
+        sb3, _ = stage_bytes(c3)
         lb3, _ = scorer_bytes(c3)
         dense128 = dense_decode(c3, torch, 4 * c3.replicas)
         dense128["socket_speedup"] = dense128["us"] / gpu3
         extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, stage_us=st3,
-                        scorer_launch_us=sc3,
+                        selection_stage_us=stage3, scorer_launch_us=sc3,
                         keys_per_s=c3.kv_keys * (c3.w.Hq // c3.w.Hkv) / sec3,
-                        scorer_gbs=lb3 / (sc3 * 1e-6) / 1e9,
-                        prefill=pre128, dense_decode=dense128)
+                        selection_roofline=roofline_entry(
+                            "stage_c3", sb3, stage3, "selection stage at 128K (soft_tables_kernel"
+                            " + scorer_kernel + topk_scan_kernel + topk_resolve_kernel)"),
+                        scorer_roofline=roofline_entry("scorer_c3", lb3, sc3,
+                                                       "scorer_kernel at 128K"),
+                        prefill=prefill, dense_decode=dense128)
         log(f"[bench] 128K: {extra128}")
         c3.free()
         del c3
         torch.cuda.empty_cache()
 
+    # ---- the prefill + 256-step decode loop at 128K
+    loop5 = None
+    if not args.no_128k:
+        loop5 = decode_loop_c5(lib, torch, S, args.loop_steps)
+        log(f"[bench] 128K prefill + decode loop: {loop5}")
+
     hard = None
     if not args.no_hard:
         hard = [hard_mode(lib, torch, S, L, 2, 16) for L in (300, 500)]
         for h in hard:
-            h["soft_score_topk_us"] = extra32["score_topk_us"]
+            h["soft_score_topk_us"] = extra32["selection_stage_us"]
         log(f"[bench] 32K hard-LSH mode: {hard}")
         torch.cuda.empty_cache()
     extra32["hard_lsh"] = hard
@@ -541,9 +788,11 @@ def main():
         st10, gpu10, _ = per_stage(c10, torch, max(50, args.steps // 2))
         sc10 = scorer_launch_us(c10, torch, 4 * c10.replicas)
         lb10, _ = scorer_bytes(c10)
+        from soft_lsh_token_amd import layout
         extra_p10 = dict(step_us_wall=sec10 * 1e6, step_us_gpu=gpu10, stage_us=st10,
                          scorer_launch_us=sc10,
                          keys_per_s=c10.kv_keys * (c10.w.Hq // c10.w.Hkv) / sec10,
+                         id_bytes_per_key=layout.key_bytes(60, 10),
                          scorer_gbs_algorithmic=lb10 / (sc10 * 1e-6) / 1e9,
                          scorer_gbs_stored=scorer_stored_bytes(c10) / (sc10 * 1e-6) / 1e9,
                          prefill=pre10)
@@ -599,13 +848,12 @@ def main():
                                "P=8, tau=0.5, k=656, batch 1",
                    "global_batch": 1, "seq_len": 32768, "parallelism": "single GPU",
                    "replicas": args.replicas},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "scorer_kernel (soft-count scores + first-digit histogram)",
-                     "bytes_per_launch": launch_bytes, "kv_keys_per_launch": kv_keys},
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "extra": {"ctx32k": extra32, "ctx128k": extra128, "ctx32k_p10_l60": extra_p10,
-                  "batch16_ragged": extra_b16},
+        "extra": {"hash_mfma_frac_128k": None if extra128 is None
+                  else extra128["prefill"]["ids"]["mfma_frac"],
+                  "ctx32k": extra32, "ctx128k": extra128, "decode_loop_128k": loop5,
+                  "ctx32k_p10_l60": extra_p10, "batch16_ragged": extra_b16},
     }
     print(json.dumps(line), flush=True)
 

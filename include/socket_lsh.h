@@ -99,6 +99,11 @@ size_t socket_ids_bytes(int B, int Hkv, int64_t n_cap, int L, int P);
  * pos0 is a device int32 array [B].  ids (socket_ids_bytes(B, Hkv, n_cap, L, P)
  * bytes) receives all 16 words of every hashed key in the tiled layout;
  * other keys and other rows of vnorm are untouched.
+ *
+ * Either output may be left out: ids = NULL computes the value norms only
+ * (K and W may then be NULL), V = vnorm = NULL computes the bucket IDs only.
+ * A V without a vnorm (or the reverse), or neither output, is SOCKET_EINVAL.
+ * The results do not depend on which outputs are asked for.
  */
 int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, int d,
                      int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,

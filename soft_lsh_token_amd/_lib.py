@@ -138,17 +138,22 @@ def _ids(ids: torch.Tensor, B: int, Hkv: int, n_cap: int, L: int, P: int) -> int
     return _dev(ids, "ids", torch.uint8, ids_shape(B, Hkv, n_cap, L, P))
 
 
-def socket_hash_keys(K: torch.Tensor, V: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
-                     vnorm: torch.Tensor, pos0: torch.Tensor, count: int, L: int, P: int,
-                     stream=None) -> None:
-    """Hash rows [pos0[b], pos0[b]+count) of K into ids and store ||V|| in vnorm."""
-    B, Hkv, n_cap, d = K.shape
-    dt = _dtype_code(K)
+def socket_hash_keys(K: torch.Tensor | None, V: torch.Tensor | None, W: torch.Tensor | None,
+                     ids: torch.Tensor | None, vnorm: torch.Tensor | None, pos0: torch.Tensor,
+                     count: int, L: int, P: int, stream=None) -> None:
+    """Hash rows [pos0[b], pos0[b]+count) of K into ids and store ||V|| in vnorm.
+    ids=None (with K, W None allowed) stores the norms only; V=vnorm=None the IDs only."""
+    ref = K if K is not None else V
+    B, Hkv, n_cap, d = ref.shape
+    dt = _dtype_code(ref)
     rc = lib().socket_hash_keys(
-        _dev(K, "K"), _dev(V, "V", K.dtype, K.shape), dt, B, Hkv, d, n_cap,
-        _dev(pos0, "pos0", torch.int32, (B,)), int(count), _dev(W, "W", K.dtype, (L * P, d)),
-        L, P, _ids(ids, B, Hkv, n_cap, L, P),
-        _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)), _stream(K, stream))
+        None if K is None else _dev(K, "K", ref.dtype, ref.shape),
+        None if V is None else _dev(V, "V", ref.dtype, ref.shape), dt, B, Hkv, d, n_cap,
+        _dev(pos0, "pos0", torch.int32, (B,)), int(count),
+        None if W is None else _dev(W, "W", ref.dtype, (L * P, d)), L, P,
+        None if ids is None else _ids(ids, B, Hkv, n_cap, L, P),
+        None if vnorm is None else _dev(vnorm, "vnorm", torch.float32, (B, Hkv, n_cap)),
+        _stream(ref, stream))
     _check("socket_hash_keys", rc)
 
 

@@ -48,7 +48,10 @@ int socket_version(void) { return 100; }
 int socket_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv, int d,
                      int64_t n_cap, const int32_t* pos0, int count, const void* W, int L, int P,
                      uint8_t* ids, float* vnorm, void* stream) {
-  if (!K || !V || !pos0 || !W || !ids || !vnorm) return SOCKET_EINVAL;
+  // IDs need K and W, norms need V; at least one of the two outputs
+  if (!pos0 || (!ids && !vnorm)) return SOCKET_EINVAL;
+  if (ids && (!K || !W)) return SOCKET_EINVAL;
+  if (!V != !vnorm) return SOCKET_EINVAL;
   if (dtype != SOCKET_F32 && dtype != SOCKET_BF16) return SOCKET_EINVAL;
   if (B <= 0 || Hkv <= 0 || n_cap <= 0 || count < 0 || L <= 0 || P <= 0) return SOCKET_EINVAL;
   if (n_cap >= ((int64_t)1 << 31)) return SOCKET_EUNSUPPORTED;

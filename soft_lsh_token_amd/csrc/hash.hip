@@ -75,8 +75,9 @@ __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
   float vf[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) vf[i] = 0.f;
+  const bool norms = vnorm != nullptr;  // uniform: IDs only when there is no norm cache
   if (lane < 16) load8<T>(K + row * kHead + 8 * lane, kf + 8 * lane);
-  if (s == 0 && lane >= 16 && lane < 32) load8<T>(V + row * kHead + 8 * (lane - 16), vf);
+  if (norms && s == 0 && lane >= 16 && lane < 32) load8<T>(V + row * kHead + 8 * (lane - 16), vf);
   __syncthreads();
   float z = 0.f;
   if (live) {
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
     }
   }
   const uint64_t m = __ballot(live && z > 0.f);
-  if (s == 0) {  // value norm: lanes 16..31 form one DPP row
+  if (norms && s == 0) {  // value norm: lanes 16..31 form one DPP row
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = fmaf(vf[i], vf[i], ss);
@@ -125,6 +126,35 @@ __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
     else *reinterpret_cast<uint4*>(dst) = make_uint4((uint32_t)w[0], (uint32_t)(w[0] >> 32),
                                                      (uint32_t)w[1], (uint32_t)(w[1] >> 32));
   }
+}
+
+// ---------------------------------------------------------------- norms only
+
+// The value norms of rows [pos0[b], pos0[b]+count) without hashing: 16 lanes
+// per row, 8 elements each, summed in the order of the hashing kernels
+// (per-lane fused multiply-adds, then a DPP butterfly over the row), so the
+// norms equal theirs bit for bit.  grid: ceil(B*Hkv*count / 16) blocks of
+// kNormThreads; row r of the launch is position r % count of KV row r / count.
+constexpr int kNormThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void value_norms_kernel(
+    const T* __restrict__ V, int Hkv, int64_t n_cap, const int32_t* __restrict__ pos0, int count,
+    int64_t rows, float* __restrict__ vnorm) {
+  int64_t r = (int64_t)blockIdx.x * (kNormThreads / 16) + (threadIdx.x >> 4);
+  const bool live = r < rows;
+  if (!live) r = rows - 1;  // the row's 16 lanes agree; re-read the last row, store nothing
+  const int j = threadIdx.x & 15;
+  const int64_t bh = r / count;
+  const int64_t pos = (int64_t)pos0[bh / Hkv] + r % count;
+  const bool in = live && pos >= 0 && pos < n_cap;
+  float f[8];
+  load_row8<T>(V + (bh * n_cap + (in ? pos : 0)) * kHead, j, f);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+  ss = row16_sum(ss);
+  if (in && j == 0) vnorm[bh * n_cap + pos] = sqrtf(ss);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -182,7 +212,8 @@ __device__ __forceinline__ void store_wide(uint8_t* ids, int64_t bh, int64_t n_c
 // tile tt in lane half h is accumulator c = 16*tt + r of that half; c < 30
 // is plane c % 10 of table 6w + 3h + c / 10, and c = 30, 31 are zero rows.
 // grid: B*Hkv*nblk blocks; block blk hashes keys [pos0 + blk*kpb, +kpb) of (b, h).
-template <int NW, bool WIDE>
+// NRM false: IDs only (no V loads, no norms).
+template <int NW, bool WIDE, bool NRM>
 __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int Hkv, int64_t n_cap,
     const int32_t* __restrict__ pos0, int count, const uint16_t* __restrict__ W, int Lw,
@@ -215,7 +246,7 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     // stored.
     static_assert(kProdU4 == 8, "eight vectors per producer thread");
     const char* kbase = reinterpret_cast<const char*>(K + (rowbase + start) * kHead);
-    const char* vbase = reinterpret_cast<const char*>(V + (rowbase + start) * kHead);
+    const char* vbase = NRM ? reinterpret_cast<const char*>(V + (rowbase + start) * kHead) : nullptr;
     const uint32_t last = (uint32_t)(end - start - 1);
     const int pt = tid - NW * 64;  // 0 .. kProd*64-1
     auto off_of = [&](int t, int u) -> uint32_t {
@@ -226,7 +257,7 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     };
 #define SOCKET_LD(u) \
     k##u = *reinterpret_cast<const uint4*>(kbase + off_of(tl, u)); \
-    v##u = *reinterpret_cast<const uint4*>(vbase + off_of(tl, u));
+    if constexpr (NRM) v##u = *reinterpret_cast<const uint4*>(vbase + off_of(tl, u));
 #define SOCKET_ST(u) kt[((pt + u * kProd * 64) >> 4) * kRowU4 + (pt & 15)] = k##u;
 #define SOCKET_NRM(u) \
     { float f[8]; unpack_bf16x8(v##u, f); float ss = 0.f; \
@@ -246,12 +277,14 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
         uint4* kt = ktile[ts & 1];
         SOCKET_ST(0) SOCKET_ST(1) SOCKET_ST(2) SOCKET_ST(3)
         SOCKET_ST(4) SOCKET_ST(5) SOCKET_ST(6) SOCKET_ST(7)
-        float n0, n1, n2, n3, n4, n5, n6, n7;
-        SOCKET_NRM(0) SOCKET_NRM(1) SOCKET_NRM(2) SOCKET_NRM(3)
-        SOCKET_NRM(4) SOCKET_NRM(5) SOCKET_NRM(6) SOCKET_NRM(7)
-        if ((pt & 15) == 0) {
-          SOCKET_VN(0) SOCKET_VN(1) SOCKET_VN(2) SOCKET_VN(3)
-          SOCKET_VN(4) SOCKET_VN(5) SOCKET_VN(6) SOCKET_VN(7)
+        if constexpr (NRM) {
+          float n0, n1, n2, n3, n4, n5, n6, n7;
+          SOCKET_NRM(0) SOCKET_NRM(1) SOCKET_NRM(2) SOCKET_NRM(3)
+          SOCKET_NRM(4) SOCKET_NRM(5) SOCKET_NRM(6) SOCKET_NRM(7)
+          if ((pt & 15) == 0) {
+            SOCKET_VN(0) SOCKET_VN(1) SOCKET_VN(2) SOCKET_VN(3)
+            SOCKET_VN(4) SOCKET_VN(5) SOCKET_VN(6) SOCKET_VN(7)
+          }
         }
         const int tl = ts + 1;
         SOCKET_LD(0) SOCKET_LD(1) SOCKET_LD(2) SOCKET_LD(3)
@@ -418,6 +451,16 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
   if (count <= 0 || B <= 0 || Hkv <= 0) return hipSuccess;
   const int64_t rows = (int64_t)B * Hkv * count;
   const bool bf16 = dtype == 1;
+  if (!ids) {  // value norms only
+    const unsigned grid = (unsigned)((rows + kNormThreads / 16 - 1) / (kNormThreads / 16));
+    if (bf16)
+      value_norms_kernel<uint16_t><<<grid, kNormThreads, 0, s>>>(
+          static_cast<const uint16_t*>(V), Hkv, n_cap, pos0, count, rows, vnorm);
+    else
+      value_norms_kernel<float><<<grid, kNormThreads, 0, s>>>(
+          static_cast<const float*>(V), Hkv, n_cap, pos0, count, rows, vnorm);
+    return hipGetLastError();
+  }
   // the MFMA path covers every ID word when L is 16, 32 or 64
   const bool mfma_ok = bf16 && P == 8 && (L == 16 || L == 32 || L == 64) && count >= 64;
   const bool wide_ok = bf16 && P == 10 && L <= 64 && count >= 64;
@@ -432,8 +475,12 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     auto go = [&](auto nw, auto wide) {
       constexpr int NW = decltype(nw)::value;
-      hash_mfma_kernel<NW, decltype(wide)::value><<<grid, (NW + kProd) * 64, 0, s>>>(
-          Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk);
+      if (vnorm)
+        hash_mfma_kernel<NW, decltype(wide)::value, true><<<grid, (NW + kProd) * 64, 0, s>>>(
+            Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk);
+      else
+        hash_mfma_kernel<NW, decltype(wide)::value, false><<<grid, (NW + kProd) * 64, 0, s>>>(
+            Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk);
     };
     using N = std::false_type;
     using Y = std::true_type;

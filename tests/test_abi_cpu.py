@@ -59,7 +59,13 @@ def _hash(**kw):
 
 def test_hash_argument_checks():
     assert _hash(K=None) == EINVAL
-    assert _hash(vnorm=None) == EINVAL
+    assert _hash(W=None) == EINVAL
+    assert _hash(vnorm=None) == EINVAL            # V without vnorm
+    assert _hash(V=None) == EINVAL                # vnorm without V
+    assert _hash(ids=None, vnorm=None, V=None) == EINVAL  # no output
+    assert _hash(pos0=None) == EINVAL
+    assert _hash(ids=None, K=None, W=None, count=0) == 0  # norms only: K and W not needed
+    assert _hash(V=None, vnorm=None, count=0) == 0        # IDs only
     assert _hash(dtype=7) == EINVAL
     assert _hash(B=0) == EINVAL
     assert _hash(count=-1) == EINVAL

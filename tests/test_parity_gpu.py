@@ -77,6 +77,33 @@ def test_hash_full_c2_mfma():
     print("id bits inside the 1e-5 band:", band)
 
 
+@pytest.mark.parametrize("case", [
+    dict(name="c2", n=3000),                          # bf16 MFMA
+    dict(name="c2", n=1000, L=60, P=10),              # two-byte IDs, MFMA
+    dict(name="c1", n=700),                           # fp32, generic
+    dict(name="c4", n=(30, 50), B=3, Hkv=2, Hq=4),    # few keys, generic bf16
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_hash_outputs_apart(case):
+    """IDs only (V = vnorm = None) and norms only (ids = None) give exactly the
+    IDs and norms of the joint call, and leave the other cache untouched."""
+    w = make_workload(**case)
+    d = GC.upload(w)
+    ids1, vn1 = GC.gpu_hash(w, d)
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=DEV)
+    count = int(w.lens.max())
+    ids2 = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
+    S.socket_hash_keys(d["K"], None, d["W"], ids2, None, pos0, count, w.L, w.P)
+    vn2 = torch.full((w.B, w.Hkv, w.n_cap), -3.0, dtype=torch.float32, device=DEV)
+    S.socket_hash_keys(None, d["V"], None, None, vn2, pos0, count, w.L, w.P)
+    sync()
+    assert torch.equal(ids1, ids2)
+    live = torch.zeros_like(vn2, dtype=torch.bool)
+    for b in range(w.B):
+        live[b, :, :min(count, w.n_cap)] = True
+    assert torch.equal(vn1[live], vn2[live])
+    assert (vn2[~live] == -3.0).all()
+
+
 @pytest.mark.parametrize("L,n", [(60, 1000), (20, 333), (5, 200), (37, 64)])
 def test_hash_wide_pads_and_range(L, n):
     """Two-byte IDs: the hashed keys' cells of tables >= L (up to 16 words) are
