@@ -144,6 +144,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// The same inclusive prefix sum for floats, in the same fixed order (so any
+// two waves that scan the same values get the same sums bit for bit).
+__device__ __forceinline__ float wave_incl_scan_f32(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+  return x;
+}
+
 // OR over each group of 8 lanes (quad swaps, then the mirror inside each
 // half row, which pairs lane i with lane 7 - i of the other quad).
 __device__ __forceinline__ uint32_t or8_lanes(uint32_t x) {

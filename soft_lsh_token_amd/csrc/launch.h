@@ -20,8 +20,14 @@ struct ScoreWs {
   uint2* cand;          // [B*Hq][n_cap]  top-k candidates (score bits, key)
   float* scores;        // [B*Hq][ns]  when the caller passes no score buffer
   float* usum;          // [B*Hq]  sums of the soft counts (sampling estimator)
+  float* gsum;          // [B*Hq][ceil(n_cap/64)]  score sums of 64-key groups (estimator)
+  float* epart;         // [B*Hq][kEstSlices][kHead]  estimator partial sums
+  float* esz;           // [B*Hq][2]  estimator totals: score sum S, soft-count sum Z
   int64_t words;
+  int64_t groups;       // ceil(n_cap / 64)
 };
+
+constexpr int kEstSlices = 32;  // at most 32 slices of 256 draws (8192 draws a head)
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base);
 

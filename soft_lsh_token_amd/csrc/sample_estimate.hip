@@ -13,71 +13,59 @@
 // u[b][g][m] in [0, 1) and takes the first key whose running score sum
 // exceeds u * sum_j s_j (keys without mass are never drawn).
 //
-// One workgroup per query head: thread t sums the scores of keys
-// [t*C, (t+1)*C) in key order, a block scan turns those into chunk starts,
-// and each draw finds its chunk by binary search over the starts and its key
-// by walking the chunk in order.  The drawn value rows are then summed in a
-// fixed order: 16 lanes per row, 64 row slots (slot r takes draws r, r + 64,
-// ...), the slots added up in LDS.
+// Spread over the chip: the scorer leaves, besides the scores, each head's
+// score sum over every 64-key group.  Workgroup (head, slice) of
+// estimate_draw_kernel takes draws [256*slice, 256*slice + 256):
+//  * thread t sums the groups of its run [t*R, (t+1)*R) (R = ceil(groups /
+//    256)) in group order, and a block scan of the run totals gives the run
+//    starts (the same in every slice of the head);
+//  * thread t's draw finds its run by binary search over the run starts, its
+//    group by walking the run's group sums, its key by walking the group's
+//    64 scores in key order;
+//  * the slice's drawn value rows are summed in a fixed order (16 lanes per
+//    row, 16 row slots, slot r taking draws r, r + 16, ...).
+// estimate_merge_kernel adds the slices of each head in slice order.  The
+// fp32 group sums and the in-group walk need not agree to the last bit: a
+// draw whose running sum falls in the rounding gap at the end of a group takes
+// the group's last key with mass.
 #include "common.h"
 #include "launch.h"
 
 namespace socketlsh {
 
-constexpr int kEstThreads = 1024;
-constexpr int kEstWaves = kEstThreads / 64;
-constexpr int kEstMaxDraws = 8192;
-constexpr int kEstSlots = kEstThreads / 16;  // value rows gathered at once (16 lanes a row)
-constexpr int kEstBatch = 8;   // scores loaded together along a chunk
-constexpr int kEstRowBatch = 4;  // value rows per lane in flight
+constexpr int kDrawThreads = 256;  // draws per slice, one a thread
+constexpr int kEstMaxDraws = kEstSlices * kDrawThreads;
+constexpr int kEstRowSlots = kDrawThreads / 16;
 
-// Elements 8j .. 8j+7 of a value row as float32.
+// grid: B*Hq*slices blocks of kDrawThreads, slices = ceil(M / kDrawThreads).
 template <typename T>
-__device__ __forceinline__ void elems8(const T* row, int j, float* f);
-template <>
-__device__ __forceinline__ void elems8<uint16_t>(const uint16_t* row, int j, float* f) {
-  unpack_bf16x8(reinterpret_cast<const uint4*>(row)[j], f);
-}
-template <>
-__device__ __forceinline__ void elems8<float>(const float* row, int j, float* f) {
-  const float4 a = reinterpret_cast<const float4*>(row)[2 * j];
-  const float4 b = reinterpret_cast<const float4*>(row)[2 * j + 1];
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
-// grid: B*Hq blocks of kEstThreads.
-template <typename T>
-__global__ __launch_bounds__(kEstThreads) void estimate_kernel(
-    const float* __restrict__ scores, int64_t sstride, const float* __restrict__ vnorm,
-    const T* __restrict__ V, const int32_t* __restrict__ lens, int Hq, int Hkv, int64_t n_cap,
-    const float* __restrict__ usum, const float* __restrict__ u, int M, float* __restrict__ out,
-    int32_t* __restrict__ draws) {
-  const int bg = blockIdx.x;
+__global__ __launch_bounds__(kDrawThreads) void estimate_draw_kernel(
+    const float* __restrict__ scores, int64_t sstride, const float* __restrict__ gsum,
+    int64_t gstride, const float* __restrict__ vnorm, const T* __restrict__ V,
+    const int32_t* __restrict__ lens, int Hq, int Hkv, int64_t n_cap,
+    const float* __restrict__ usum, const float* __restrict__ u, int M, int slices,
+    float* __restrict__ epart, float* __restrict__ esz, int32_t* __restrict__ draws) {
+  const int bg = blockIdx.x / slices, sl = blockIdx.x % slices;
   const int b = bg / Hq, h = (bg % Hq) / (Hq / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t n = lens[b];
   if (n < 0) n = 0;
   if (n > n_cap) n = n_cap;
-  __shared__ float cstart[kEstThreads + 1];
-  __shared__ float wtot[kEstWaves];
-  __shared__ int32_t J[kEstMaxDraws];
-  __shared__ float part[kEstSlots][kHead];
-
-  // chunk sums in key order, then an exclusive scan of them
+  const int64_t G = (n + 63) >> 6;
+  const int64_t R = (G + kDrawThreads - 1) / kDrawThreads;
+  __shared__ float rstart[kDrawThreads + 1];
+  __shared__ float wtot[kDrawThreads / 64];
+  __shared__ int32_t J[kDrawThreads];
+  __shared__ float part[kEstRowSlots][kHead];
+  const float* gs = gsum + (int64_t)bg * gstride;
   const float* srow = scores + (int64_t)bg * sstride;
-  const int64_t C = (n + kEstThreads - 1) / kEstThreads;
-  const int64_t j0 = (int64_t)tid * C;
-  const int64_t j1 = j0 + C < n ? j0 + C : n;
-  float cs = 0.f;
-  for (int64_t j = j0; j < j1; j += kEstBatch) {
-    float v[kEstBatch];
-#pragma unroll
-    for (int i = 0; i < kEstBatch; ++i) v[i] = srow[j + i < j1 ? j + i : j1 - 1];
-#pragma unroll
-    for (int i = 0; i < kEstBatch; ++i) cs += j + i < j1 ? v[i] : 0.f;
-  }
-  float inc = cs;
+
+  // run totals in group order, then their exclusive scan
+  const int64_t g0 = (int64_t)tid * R;
+  const int64_t g1 = g0 + R < G ? g0 + R : G;
+  float tot = 0.f;
+  for (int64_t g = g0; g < g1; ++g) tot += gs[g];
+  float inc = tot;
   for (int o = 1; o < 64; o <<= 1) {
     const float y = __shfl_up(inc, o, 64);
     if (lane >= o) inc += y;
@@ -86,110 +74,155 @@ __global__ __launch_bounds__(kEstThreads) void estimate_kernel(
   __syncthreads();
   float before = 0.f;
   for (int w = 0; w < wave; ++w) before += wtot[w];
-  cstart[tid] = before + inc - cs;
-  if (tid == kEstThreads - 1) cstart[kEstThreads] = before + inc;
+  rstart[tid] = before + inc - tot;
+  if (tid == kDrawThreads - 1) rstart[kDrawThreads] = before + inc;
   __syncthreads();
-  const float S = cstart[kEstThreads];
+  const float S = rstart[kDrawThreads];
   const float Z = usum[bg];
-  float* o = out + (int64_t)bg * kHead;
-  if (n == 0 || !(S > 0.f) || !(Z > 0.f)) {
-    if (tid < kHead) o[tid] = 0.f;
-    if (draws)
-      for (int m = tid; m < M; m += kEstThreads) draws[(int64_t)bg * M + m] = -1;
+  if (sl == 0 && tid == 0) {
+    esz[2 * bg] = S;
+    esz[2 * bg + 1] = Z;
+  }
+  float* pout = epart + ((int64_t)bg * kEstSlices + sl) * kHead;
+  const int m = sl * kDrawThreads + tid;
+  if (n == 0 || !(S > 0.f) || !(Z > 0.f)) {  // uniform: nothing to draw
+    if (draws && m < M) draws[(int64_t)bg * M + m] = -1;
+    if (tid < kHead) pout[tid] = 0.f;
     return;
   }
 
-  // draws
-  const float top = __uint_as_float(__float_as_uint(S) - 1u);  // the float below S (> 0)
-  for (int m = tid; m < M; m += kEstThreads) {
+  // this thread's draw: run, then group, then key
+  int32_t pick = -1;
+  if (m < M) {
+    const float top = __uint_as_float(__float_as_uint(S) - 1u);  // the float below S (> 0)
     float t = u[(int64_t)bg * M + m] * S;
     if (t > top) t = top;
-    int lo = 0, hi = kEstThreads - 1;  // last chunk whose start is <= t
+    int lo = 0, hi = kDrawThreads - 1;  // last run whose start is <= t
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (cstart[mid] <= t) lo = mid;
+      if (rstart[mid] <= t) lo = mid;
       else hi = mid - 1;
     }
-    int64_t pick = -1, last = -1;
-    float acc = cstart[lo];
-    const int64_t c1 = (int64_t)(lo + 1) * C < n ? (int64_t)(lo + 1) * C : n;
-    for (int64_t j = (int64_t)lo * C; j < c1 && pick < 0; j += kEstBatch) {
-      float v[kEstBatch];
+    const int64_t r0 = (int64_t)lo * R;
+    const int64_t r1 = r0 + R < G ? r0 + R : G;
+    float acc = rstart[lo];
+    int64_t g = r1 - 1;  // rounding past the run's end: its last group
+    for (int64_t x = r0; x < r1; ++x) {
+      const float gv = gs[x];
+      if (acc + gv > t) {
+        g = x;
+        break;
+      }
+      acc += gv;
+    }
+    // the group's keys in order
+    const int64_t k0 = g * 64;
+    float v[64];
+    const uint4* src = reinterpret_cast<const uint4*>(srow + k0);
 #pragma unroll
-      for (int i = 0; i < kEstBatch; ++i) v[i] = srow[j + i < c1 ? j + i : c1 - 1];
+    for (int q = 0; q < 16; ++q) {
+      const uint4 w4 = src[q];  // the score row is padded to whole groups
+      v[4 * q] = __uint_as_float(w4.x); v[4 * q + 1] = __uint_as_float(w4.y);
+      v[4 * q + 2] = __uint_as_float(w4.z); v[4 * q + 3] = __uint_as_float(w4.w);
+    }
+    int64_t last = -1;
+    bool done = false;
 #pragma unroll
-      for (int i = 0; i < kEstBatch; ++i) {
-        if (pick < 0 && j + i < c1) {
-          if (v[i] > 0.f) last = j + i;
-          acc += v[i];
-          if (acc > t) pick = j + i;
+    for (int i = 0; i < 64; ++i) {
+      if (!done && k0 + i < n) {
+        if (v[i] > 0.f) last = k0 + i;
+        acc += v[i];
+        if (acc > t && v[i] > 0.f) {
+          pick = (int32_t)(k0 + i);
+          done = true;
         }
       }
     }
-    // rounding between the scan and the walk: take the last key with mass
-    // at or before the chunk end (some key has mass, since S > 0)
-    if (pick < 0 || !(srow[pick] > 0.f)) {
-      pick = last;
-      const int64_t from = (int64_t)lo * C < n ? (int64_t)lo * C : n;
-      for (int64_t j = from - 1; pick < 0 && j >= 0; --j)
-        if (srow[j] > 0.f) pick = j;
-      for (int64_t j = from; pick < 0 && j < n; ++j)
-        if (srow[j] > 0.f) pick = j;
-    }
-    J[m] = (int32_t)pick;
-    if (draws) draws[(int64_t)bg * M + m] = (int32_t)pick;
+    // rounding between the sums and the walk: the group's last key with mass,
+    // else the nearest key with mass before the group, else after it
+    if (pick < 0) pick = (int32_t)last;
+    for (int64_t j = k0 - 1; pick < 0 && j >= 0; --j)
+      if (srow[j] > 0.f) pick = (int32_t)j;
+    for (int64_t j = k0 + 64; pick < 0 && j < n; ++j)
+      if (srow[j] > 0.f) pick = (int32_t)j;
+    if (draws) draws[(int64_t)bg * M + m] = pick;
   }
+  J[tid] = pick;
   __syncthreads();
 
-  // sum of v_J / ||v_J||: slot r takes draws r, r + 64, ...; lane j of the
-  // slot's 16 owns elements 8j .. 8j+7
+  // sum of v_J / ||v_J|| over the slice's draws: slot r takes draws r, r + 16, ...;
+  // lane j of the slot's 16 owns elements 8j .. 8j+7
+  const int nd = M - sl * kDrawThreads < kDrawThreads ? M - sl * kDrawThreads : kDrawThreads;
   const int r = tid >> 4, j = tid & 15;
   const int64_t rowbase = ((int64_t)b * Hkv + h) * n_cap;
-  float acc[8];
+  float a8[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int m0 = r; m0 < M; m0 += kEstSlots * kEstRowBatch) {
-    float x[kEstRowBatch][8], nv[kEstRowBatch];
+  for (int e = 0; e < 8; ++e) a8[e] = 0.f;
+  // value rows in flight per lane: a slot's whole share of a full slice for bf16
+  constexpr int RB = sizeof(T) == 2 ? kDrawThreads / kEstRowSlots : kDrawThreads / kEstRowSlots / 2;
+  for (int d0 = r; d0 < nd; d0 += kEstRowSlots * RB) {
+    Row8<T> x[RB];
+    float nv[RB];
+    bool use[RB];
 #pragma unroll
-    for (int i = 0; i < kEstRowBatch; ++i) {  // past the last draw: re-read it, add nothing
-      const int m = m0 + i * kEstSlots;
-      const int64_t row = rowbase + J[m < M ? m : r];
-      elems8<T>(V + row * kHead, j, x[i]);
+    for (int i = 0; i < RB; ++i) {  // past the last draw: read row 0, add nothing
+      const int d = d0 + i * kEstRowSlots;
+      const int32_t jd = d < nd ? J[d] : -1;
+      use[i] = jd >= 0;
+      const int64_t row = rowbase + (jd >= 0 ? jd : 0);
+      x[i] = fetch_row8<T>(V + row * kHead, j);
       nv[i] = vnorm[row];
     }
 #pragma unroll
-    for (int i = 0; i < kEstRowBatch; ++i) {
-      if (m0 + i * kEstSlots < M) {
+    for (int i = 0; i < RB; ++i) {
+      if (use[i]) {
+        float f[8];
+        unpack_row8<T>(x[i], f);
         const float inv = 1.f / nv[i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(x[i][e], inv, acc[e]);
+        for (int e = 0; e < 8; ++e) a8[e] = fmaf(f[e], inv, a8[e]);
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[r][8 * j + e] = acc[e];
+  for (int e = 0; e < 8; ++e) part[r][8 * j + e] = a8[e];
   __syncthreads();
   if (tid < kHead) {
     float t = 0.f;
-    for (int g = 0; g < kEstSlots; ++g) t += part[g][tid];
-    o[tid] = (S / Z) / (float)M * t;
+    for (int g = 0; g < kEstRowSlots; ++g) t += part[g][tid];
+    pout[tid] = t;
   }
+}
+
+// grid: B*Hq blocks of kHead threads: out = (S / Z) / M * (sum of the slices).
+__global__ __launch_bounds__(kHead) void estimate_merge_kernel(
+    const float* __restrict__ epart, const float* __restrict__ esz, int M, int slices,
+    float* __restrict__ out) {
+  const int bg = blockIdx.x, d = threadIdx.x;
+  const float S = esz[2 * bg], Z = esz[2 * bg + 1];
+  float t = 0.f;
+  for (int sl = 0; sl < slices; ++sl) t += epart[((int64_t)bg * kEstSlices + sl) * kHead + d];
+  out[(int64_t)bg * kHead + d] = (S > 0.f && Z > 0.f) ? (S / Z) / (float)M * t : 0.f;
 }
 
 hipError_t launch_estimate(const float* scores, const float* vnorm, const void* V, int dtype,
                            int B, int Hq, int Hkv, const int32_t* lens, int64_t n_cap,
                            const float* u, int M, float* out, int32_t* draws, const ScoreWs& ws,
                            hipStream_t s) {
-  if (M > kEstMaxDraws) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)(B * Hq);
+  if (M <= 0 || M > kEstMaxDraws) return hipErrorInvalidValue;
+  const int slices = (M + kDrawThreads - 1) / kDrawThreads;
+  const unsigned grid = (unsigned)(B * Hq * slices);
   if (dtype == 1)
-    estimate_kernel<uint16_t><<<grid, kEstThreads, 0, s>>>(
-        scores, score_stride(n_cap), vnorm, static_cast<const uint16_t*>(V), lens, Hq, Hkv, n_cap,
-        ws.usum, u, M, out, draws);
+    estimate_draw_kernel<uint16_t><<<grid, kDrawThreads, 0, s>>>(
+        scores, score_stride(n_cap), ws.gsum, ws.groups, vnorm, static_cast<const uint16_t*>(V),
+        lens, Hq, Hkv, n_cap, ws.usum, u, M, slices, ws.epart, ws.esz, draws);
   else
-    estimate_kernel<float><<<grid, kEstThreads, 0, s>>>(
-        scores, score_stride(n_cap), vnorm, static_cast<const float*>(V), lens, Hq, Hkv, n_cap,
-        ws.usum, u, M, out, draws);
+    estimate_draw_kernel<float><<<grid, kDrawThreads, 0, s>>>(
+        scores, score_stride(n_cap), ws.gsum, ws.groups, vnorm, static_cast<const float*>(V),
+        lens, Hq, Hkv, n_cap, ws.usum, u, M, slices, ws.epart, ws.esz, draws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  estimate_merge_kernel<<<(unsigned)(B * Hq), kHead, 0, s>>>(ws.epart, ws.esz, M, slices, out);
   return hipGetLastError();
 }
 

@@ -159,6 +159,9 @@ size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreW
   const size_t o_cand = off; off = align256(off + heads * (size_t)n_cap * sizeof(uint2));
   const size_t o_sc = off; off = align256(off + heads * (size_t)score_stride(n_cap) * sizeof(float));
   const size_t o_us = off; off = align256(off + heads * sizeof(float));
+  const size_t o_gs = off; off = align256(off + heads * (size_t)ids_groups(n_cap) * sizeof(float));
+  const size_t o_ep = off; off = align256(off + heads * kEstSlices * kHead * sizeof(float));
+  const size_t o_ez = off; off = align256(off + heads * 2 * sizeof(float));
   if (ws) {
     char* p = static_cast<char*>(base);
     ws->img = reinterpret_cast<float*>(p + o_img);
@@ -170,6 +173,10 @@ size_t select_ws_layout(size_t first_bytes, int B, int Hq, int64_t n_cap, ScoreW
     ws->cand = reinterpret_cast<uint2*>(p + o_cand);
     ws->scores = reinterpret_cast<float*>(p + o_sc);
     ws->usum = reinterpret_cast<float*>(p + o_us);
+    ws->gsum = reinterpret_cast<float*>(p + o_gs);
+    ws->epart = reinterpret_cast<float*>(p + o_ep);
+    ws->esz = reinterpret_cast<float*>(p + o_ez);
+    ws->groups = ids_groups(n_cap);
     ws->words = words;
   }
   return off;
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     const float* __restrict__ img, int img_floats, const uint8_t* __restrict__ ids,
     const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
     int64_t n_cap, int sink, int window, int rows, int nblk, int gpb, float* __restrict__ scores,
-    uint32_t* __restrict__ hist, float* __restrict__ usum) {
+    uint32_t* __restrict__ hist, float* __restrict__ usum, float* __restrict__ gsum) {
   using Sh = ImageShape<G, TL, WIDE>;
   constexpr int NF = Sh::NF, NS = Sh::NS, HE = Sh::HE;
   constexpr int C = WIDE ? 2 : 1;  // bytes per ID
@@ -695,6 +702,13 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
             for (int gg = 0; gg < G; ++gg) {
               scores[(int64_t)(bg0 + gg) * sst + key] = vb[s] * u[0][gg];
               us[gg] += u[0][gg];
+            }
+          }
+          if (gsum) {  // uniform: each head's score sum over the group (estimator)
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) {
+              const float t = wave_incl_scan_f32(valid ? vb[s] * u[0][gg] : 0.f);
+              if (lane == 63) gsum[(int64_t)(bg0 + gg) * ids_groups(n_cap) + gi] = t;
             }
           }
           gi += kScoreWaves;
@@ -1725,7 +1739,7 @@ static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, SinkWind
   const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
   scorer_kernel<G, TL, WIDE><<<(unsigned)grid, kScoreThreads, 0, s>>>(
       ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, P, n_cap, sw.sink, sw.window, (int)rows,
-      (int)nblk, (int)gpb, scores, ws.hist, usum);
+      (int)nblk, (int)gpb, scores, ws.hist, usum, usum ? ws.gsum : nullptr);
 }
 
 template <int G>
