@@ -358,8 +358,13 @@ def hard_mode(lib, torch, S, L, P, replicas):
     q = torch.from_numpy(w.q).to(dev).to(bf)
     codes = S.alloc_codes(w.B, w.Hkv, w.n_cap, L, P, dev)
     vn = torch.zeros(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=dev)
-    S.socket_hash_codes(K, V, Wt, codes, vn, torch.zeros(w.B, dtype=torch.int32, device=dev),
-                        n + 1, L, P)
+    zeros = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    S.socket_hash_codes(K, V, Wt, codes, vn, zeros, n + 1, L, P)
+    torch.cuda.synchronize()
+    # prefill: codes and norms of all n + 1 keys of every KV head
+    hash_us, _ = gpu_batch_us(torch, lambda i: S.socket_hash_codes(
+        K, V, Wt, codes, vn, zeros, n + 1, L, P), 8)
+    keys = w.B * w.Hkv * (n + 1)
     del K, V
     reps = [codes] + [codes.clone() for _ in range(replicas - 1)]
     lens = torch.full((w.B,), n + 1, dtype=torch.int32, device=dev)
@@ -374,9 +379,13 @@ def hard_mode(lib, torch, S, L, P, replicas):
     torch.cuda.synchronize()
     us, _ = gpu_batch_us(torch, lambda i: S.socket_hard_score_topk(
         q, Wt, reps[i % replicas], vn, lens, ks, k, L, P, idx, sc, ws), 4 * replicas)
-    code_bytes = w.B * w.Hkv * (n + 1) * (4 * S.codes_words(L, P) + 4)
-    return dict(L=L, P=P, bits_per_key=L * P, score_topk_us=us,
-                code_gbs=code_bytes / (us * 1e-6) / 1e9)
+    key_bytes = 4 * S.codes_words(L, P) + 4  # code words + value norm
+    code_bytes = keys * key_bytes
+    flops = 2.0 * keys * w.d * L * P
+    return dict(L=L, P=P, bits_per_key=L * P, cache_bytes_per_key=key_bytes,
+                score_topk_us=us, code_gbs=code_bytes / (us * 1e-6) / 1e9,
+                hash_prefill=dict(keys=keys, us=hash_us, tflops=flops / (hash_us * 1e-6) / 1e12,
+                                  mfma_frac=flops / (hash_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS))
 
 
 def prefill_rate(case, torch, mode="fused"):
@@ -726,7 +735,8 @@ def main():
         step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
         stage_us=stages, selection_stage_us=stage_us, scorer_launch_us=score_us,
         scorer_roofline=roofline_entry("scorer_c2", lbytes, score_us, "scorer_kernel at 32K"),
-        prefill=pre32, dense_decode=dense32, sampling_estimator=est32)
+        prefill=pre32, dense_decode=dense32, sampling_estimator=est32,
+        id_bytes_per_key=S.layout.key_bytes(w.L, w.P))
     case.free()
     del case
     torch.cuda.empty_cache()
@@ -771,8 +781,10 @@ def main():
     hard = None
     if not args.no_hard:
         hard = [hard_mode(lib, torch, S, L, 2, 16) for L in (300, 500)]
-        for h in hard:
+        for h in hard:  # the soft path beside it, as SOCKET Table 3 sets them side by side
             h["soft_score_topk_us"] = extra32["selection_stage_us"]
+            h["soft_cache_bytes_per_key"] = extra32["id_bytes_per_key"] + 4
+            h["soft_hash_prefill_us"] = extra32["prefill"]["us"]
         log(f"[bench] 32K hard-LSH mode: {hard}")
         torch.cuda.empty_cache()
     extra32["hard_lsh"] = hard

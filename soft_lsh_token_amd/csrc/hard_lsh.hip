@@ -116,6 +116,10 @@ hipError_t launch_hash_codes(const void* K, const void* V, int dtype, int B, int
                              int P, uint32_t* codes, float* vnorm, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   const int LP = L * P, WPK = codes_words(L, P), S = (LP + 63) / 64;
+  if (dtype == 1 && pos0 && V && vnorm && count >= 64)  // bf16 prefill: the MFMA GEMM
+    return launch_hash_codes_mfma(static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                                  B, Hkv, n_cap, pos0, count, static_cast<const uint16_t*>(W), LP,
+                                  WPK, codes, vnorm, s);
   const dim3 grid((unsigned)((int64_t)B * Hkv * count * S));
   if (dtype == 1)
     hash_codes_kernel<uint16_t><<<grid, 64, 0, s>>>(

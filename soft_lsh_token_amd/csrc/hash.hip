@@ -13,6 +13,10 @@
 //    consumers multiply the previous tile.  The planes of each tile are
 //    ordered so that every lane's accumulators hold complete tables, which
 //    turns the sign test + bit packing into lane-local work.
+//    The same kernel also writes the packed sign codes of the hard-LSH mode
+//    (any number of planes L*P): every 32-plane A tile pair of a consumer
+//    wave then gives one 32-bit code word per key half-wave, and workgroups
+//    split the planes into chunks of at most 16 words.
 //  * hash_generic_kernel: any dtype, P <= 10, any L; one-wave workgroups,
 //    each projecting one slice of a key's planes, one plane per lane.  Used
 //    for float32 keys, for odd shapes and for the decode-time append of a
@@ -211,17 +215,30 @@ __device__ __forceinline__ void store_wide(uint8_t* ids, int64_t bh, int64_t n_c
 // 8*(r/4) + 4*(l/32) + r%4) lane l holds whole tables.  WIDE: register r of
 // tile tt in lane half h is accumulator c = 16*tt + r of that half; c < 30
 // is plane c % 10 of table 6w + 3h + c / 10, and c = 30, 31 are zero rows.
-// grid: B*Hkv*nblk blocks; block blk hashes keys [pos0 + blk*kpb, +kpb) of (b, h).
-// NRM false: IDs only (no V loads, no norms).
-template <int NW, bool WIDE, bool NRM>
+// CODES (hard-LSH sign codes, LP = L*P planes, WPK words a key): the
+// one-byte pipeline with plane 64*(NW*chunk + w) + 32*h + c as accumulator c
+// of lane half h, so that the lane's packed word is code word
+// 2*(NW*chunk + w) + h, bit c; planes >= LP are zero rows and masked out.
+// grid: chunks*B*Hkv*nblk blocks; block blk hashes keys [pos0 + blk*kpb,
+// +kpb) of (b, h) (for plane chunk `chunk` in CODES mode, the norms with
+// chunk 0).  NRM false: no V loads, no norms.
+constexpr int kModeIds8 = 0;   // one-byte IDs, P = 8
+constexpr int kModeIds10 = 1;  // two-byte IDs, P = 10
+constexpr int kModeCodes = 2;  // packed sign codes
+template <int NW, int MODE, bool NRM>
 __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int Hkv, int64_t n_cap,
     const int32_t* __restrict__ pos0, int count, const uint16_t* __restrict__ W, int Lw,
-    uint8_t* __restrict__ ids, float* __restrict__ vnorm, int kpb, int nblk) {
+    uint8_t* __restrict__ ids, float* __restrict__ vnorm, int kpb, int nblk,
+    uint32_t* __restrict__ codes, int LP, int WPK, int chunks) {
+  constexpr bool WIDE = MODE == kModeIds10;
   constexpr int L8 = NW * 8;  // tables of the one-byte layout
   constexpr int NB = kTK / kBTile;
-  const int blk = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
+  const int per_chunk = (int)(gridDim.x / (unsigned)chunks);
+  const int chunk = (int)blockIdx.x / per_chunk;
+  const int blk = ((int)blockIdx.x % per_chunk) % nblk;
+  const int bh = ((int)blockIdx.x % per_chunk) / nblk;
+  const bool nrm = NRM && chunk == 0;  // uniform
   const int b = bh / Hkv;
   const int64_t first = (int64_t)pos0[b];
   const int64_t start = first + (int64_t)blk * kpb;
@@ -246,7 +263,7 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     // stored.
     static_assert(kProdU4 == 8, "eight vectors per producer thread");
     const char* kbase = reinterpret_cast<const char*>(K + (rowbase + start) * kHead);
-    const char* vbase = NRM ? reinterpret_cast<const char*>(V + (rowbase + start) * kHead) : nullptr;
+    const char* vbase = nrm ? reinterpret_cast<const char*>(V + (rowbase + start) * kHead) : nullptr;
     const uint32_t last = (uint32_t)(end - start - 1);
     const int pt = tid - NW * 64;  // 0 .. kProd*64-1
     auto off_of = [&](int t, int u) -> uint32_t {
@@ -257,7 +274,7 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     };
 #define SOCKET_LD(u) \
     k##u = *reinterpret_cast<const uint4*>(kbase + off_of(tl, u)); \
-    if constexpr (NRM) v##u = *reinterpret_cast<const uint4*>(vbase + off_of(tl, u));
+    if (nrm) v##u = *reinterpret_cast<const uint4*>(vbase + off_of(tl, u));
 #define SOCKET_ST(u) kt[((pt + u * kProd * 64) >> 4) * kRowU4 + (pt & 15)] = k##u;
 #define SOCKET_NRM(u) \
     { float f[8]; unpack_bf16x8(v##u, f); float ss = 0.f; \
@@ -277,7 +294,7 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
         uint4* kt = ktile[ts & 1];
         SOCKET_ST(0) SOCKET_ST(1) SOCKET_ST(2) SOCKET_ST(3)
         SOCKET_ST(4) SOCKET_ST(5) SOCKET_ST(6) SOCKET_ST(7)
-        if constexpr (NRM) {
+        if (nrm) {
           float n0, n1, n2, n3, n4, n5, n6, n7;
           SOCKET_NRM(0) SOCKET_NRM(1) SOCKET_NRM(2) SOCKET_NRM(3)
           SOCKET_NRM(4) SOCKET_NRM(5) SOCKET_NRM(6) SOCKET_NRM(7)
@@ -324,14 +341,21 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
         // stored negated: the accumulator of a plane is then -(W k), rounded as
         // W k with the sign flipped, so the plane's bit (W k > 0) is its sign
         // bit (an exact zero sums to +0 from the +0 start and gives 0)
-        const int table = 8 * wave + 4 * hout + 2 * tt + (r >> 3);
-        const uint16_t* wr = W + ((int64_t)(table * 8 + (r & 7))) * kHead + 64 * half;
+        // plane 64*wave + 32*hout + 16*tt + r (of the chunk, for codes)
+        int plane = 64 * wave + 32 * hout + 16 * tt + r;
+        bool live = true;
+        if constexpr (MODE == kModeCodes) {
+          plane += 64 * NW * chunk;
+          live = plane < LP;
+        }
+        const uint16_t* wr = W + (int64_t)(live ? plane : 0) * kHead + 64 * half;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const uint4 v = *reinterpret_cast<const uint4*>(wr + 8 * kk);
-          a[tt][kk] = __builtin_bit_cast(
-              bf16x8_t, make_uint4(v.x ^ 0x80008000u, v.y ^ 0x80008000u, v.z ^ 0x80008000u,
-                                   v.w ^ 0x80008000u));
+          a[tt][kk] = live ? __builtin_bit_cast(
+                                 bf16x8_t, make_uint4(v.x ^ 0x80008000u, v.y ^ 0x80008000u,
+                                                      v.z ^ 0x80008000u, v.w ^ 0x80008000u))
+                           : bf16x8_t{};
         }
       }
     }
@@ -356,8 +380,15 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     };
     // register r of tile tt = plane r & 7 of table 8w + 4*half + 2*tt + (r >> 3):
     // the word holds the 4 tables 8w + 4*half .. +3 as ID bytes of the tiled layout
+    // code word of the lane (CODES): its index, and the mask of its planes < LP
+    const int cw = 2 * (NW * chunk + wave) + half;
+    const int cbits = LP - 32 * cw;
+    const uint32_t cmask = cbits >= 32 ? ~0u : cbits > 0 ? (1u << cbits) - 1u : 0u;
+    uint32_t* crow = codes + ((int64_t)bh * WPK + (cw < WPK ? cw : 0)) * n_cap;
     auto store = [&](int64_t pos, uint32_t word) {
-      if constexpr (TL == 4) {
+      if constexpr (MODE == kModeCodes) {
+        if (cw < WPK) crow[pos] = word & cmask;
+      } else if constexpr (TL == 4) {
         *reinterpret_cast<uint32_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) = word;
       } else if constexpr (TL == 2) {
         *reinterpret_cast<uint16_t*>(ids + ids_word_offset(bh, n_cap, TL, pos, t0w)) =
@@ -370,7 +401,13 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
           ids[ids_word_offset(bh, n_cap, TL, pos, t0w + b8)] = (uint8_t)(word >> (8 * b8));
       }
     };
+    // a codes wave whose planes are all past LP only keeps the barriers
+    const bool idle = MODE == kModeCodes && 2 * (NW * chunk + wave) >= WPK;
     for (int t = 0; t < ntiles; ++t) {
+      if (idle) {
+        lds_barrier();
+        continue;
+      }
       const int64_t t0 = start + (int64_t)t * kTK;
       const uint4* kt = ktile[t & 1] + col * kRowU4 + 8 * half;
       const bool full = t0 + kTK <= end;
@@ -475,12 +512,15 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     auto go = [&](auto nw, auto wide) {
       constexpr int NW = decltype(nw)::value;
+      constexpr int MODE = decltype(wide)::value ? kModeIds10 : kModeIds8;
       if (vnorm)
-        hash_mfma_kernel<NW, decltype(wide)::value, true><<<grid, (NW + kProd) * 64, 0, s>>>(
-            Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk);
+        hash_mfma_kernel<NW, MODE, true><<<grid, (NW + kProd) * 64, 0, s>>>(
+            Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk, nullptr, 0,
+            0, 1);
       else
-        hash_mfma_kernel<NW, decltype(wide)::value, false><<<grid, (NW + kProd) * 64, 0, s>>>(
-            Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk);
+        hash_mfma_kernel<NW, MODE, false><<<grid, (NW + kProd) * 64, 0, s>>>(
+            Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk, nullptr, 0,
+            0, 1);
     };
     using N = std::false_type;
     using Y = std::true_type;
@@ -516,6 +556,34 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     hash_generic_kernel<float><<<grid, kGenThreads, 0, s>>>(
         static_cast<const float*>(K), static_cast<const float*>(V), Hkv, n_cap, pos0, count,
         static_cast<const float*>(W), L, P, TL, C, WPB, S, ids, vnorm);
+  return hipGetLastError();
+}
+
+// Hard-LSH sign codes of bf16 keys on the MFMA path: plane chunks of at most
+// 16 code words (8 consumer waves), about one workgroup per CU in all.
+hipError_t launch_hash_codes_mfma(const uint16_t* K, const uint16_t* V, int B, int Hkv,
+                                  int64_t n_cap, const int32_t* pos0, int count,
+                                  const uint16_t* W, int LP, int WPK, uint32_t* codes,
+                                  float* vnorm, hipStream_t s) {
+  const int waves = (WPK + 1) / 2;  // consumer waves over all chunks
+  const int chunks = (waves + 7) / 8;
+  const int per = (waves + chunks - 1) / chunks;
+  const int64_t heads = (int64_t)B * Hkv;
+  int64_t nblk = (256 + heads * chunks - 1) / (heads * chunks);
+  int64_t kpb = ((count + nblk - 1) / nblk + 127) / 128 * 128;
+  nblk = (count + kpb - 1) / kpb;
+  const dim3 grid((unsigned)(chunks * heads * nblk));
+  auto go = [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    hash_mfma_kernel<NW, kModeCodes, true><<<grid, (NW + kProd) * 64, 0, s>>>(
+        K, V, Hkv, n_cap, pos0, count, W, 0, nullptr, vnorm, (int)kpb, (int)nblk, codes, LP, WPK,
+        chunks);
+  };
+  if (per <= 2) go(std::integral_constant<int, 2>{});
+  else if (per <= 4) go(std::integral_constant<int, 4>{});
+  else if (per <= 5) go(std::integral_constant<int, 5>{});
+  else if (per <= 6) go(std::integral_constant<int, 6>{});
+  else go(std::integral_constant<int, 8>{});
   return hipGetLastError();
 }
 

@@ -98,6 +98,10 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
 // stored word-major: codes[(b*Hkv + h) * words + w][n_cap].
 int codes_words(int L, int P);  // 32-bit words per code: ceil(L*P / 32)
 
+hipError_t launch_hash_codes_mfma(const uint16_t* K, const uint16_t* V, int B, int Hkv,
+                                  int64_t n_cap, const int32_t* pos0, int count,
+                                  const uint16_t* W, int LP, int WPK, uint32_t* codes,
+                                  float* vnorm, hipStream_t s);
 hipError_t launch_hash_codes(const void* K, const void* V, int dtype, int B, int Hkv,
                              int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
                              int P, uint32_t* codes, float* vnorm, hipStream_t s);

@@ -472,6 +472,37 @@ HARD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("L,P,n,off", [
+    (300, 2, 1000, 0),     # 600 bits: two chunks of five waves
+    (500, 2, 777, 0),      # 1000 bits: two chunks of eight waves, ragged tail
+    (64, 1, 300, 0),       # 64 bits: one chunk with an idle wave
+    (1024, 4, 200, 0),     # 4096 bits, the largest code: eight chunks
+    (300, 2, 500, 123),    # a key range that starts past 0
+], ids=lambda v: str(v))
+def test_hash_codes_mfma(L, P, n, off):
+    """bf16 sign codes from the MFMA path: the hashed keys' code bits (within
+    the float32 band) and value norms against the oracle, bits past L*P
+    cleared, and cells outside [off, off + n) untouched."""
+    w = make_workload("c2", n=off + n, L=L, P=P, Hkv=2, Hq=4, n_cap=off + n + 70)
+    d = GC.upload(w)
+    codes = S.alloc_codes(w.B, w.Hkv, w.n_cap, L, P, DEV).fill_(0x5A5A5A5A)
+    vn = torch.full((w.B, w.Hkv, w.n_cap), -1.0, dtype=torch.float32, device=DEV)
+    pos0 = torch.full((w.B,), off, dtype=torch.int32, device=DEV)
+    S.socket_hash_codes(d["K"], d["V"], d["W"], codes, vn, pos0, n, L, P)
+    sync()
+    c = codes.cpu().numpy().view(np.uint32)
+    vn = vn.cpu().numpy()
+    ids = S.layout.codes_to_ids(c[:, :, :, off:off + n], L, P)
+    for h in range(w.Hkv):
+        GC.check_ids(ids[0, h], w.K[0, h, off:off + n], w.W, L, P, n)
+        np.testing.assert_allclose(vn[0, h, off:off + n], SO.value_norms(w.V[0, h, off:off + n]),
+                                   rtol=2e-6)
+    if (L * P) % 32:
+        assert (c[:, :, -1, off:off + n] >> np.uint32((L * P) % 32) == 0).all()
+    assert (c[:, :, :, :off] == 0x5A5A5A5A).all() and (c[:, :, :, off + n:] == 0x5A5A5A5A).all()
+    assert (vn[:, :, :off] == -1.0).all() and (vn[:, :, off + n:] == -1.0).all()
+
+
 def _hard_run(w, d, sink, window, heads=None):
     """Hard mode on the GPU (codes, query codes, scores, selection, attention)
     against the oracle; IDs are float-decided integers, so the scores are
