@@ -39,7 +39,8 @@
  * Bucket-ID cache layout
  * ----------------------
  * The bucket ID of table l (bit j = sign of plane j) is a cell of C bytes:
- * C = 1 for P <= 8, C = 2 (little-endian) for P = 9 or 10.  The IDs of a key
+ * C = 1 for P <= 8, C = 2 (little-endian) for P = 9 or 10 and L <= 32
+ * (packed ten-bit cells for larger L, below).  The IDs of a key
  * are cut into 16 words of TL tables, TL = 1, 2, 4 or 8 the smallest power of
  * two with 16*TL >= L; word w holds tables w*TL .. w*TL+TL-1 (cell b of the
  * word = table w*TL + b; tables >= L read as 0) and is WB = TL*C bytes long.
@@ -49,6 +50,14 @@
  *   ((r * ceil(n_cap/64) + i/64) * 1024 + (u/R)*64*R + (16*kg + w)*R + u%R) * WB.
  * This order lets the scorer read its words with 16-byte loads, 1 KiB per
  * wave and load.
+ * Packed words (P = 9 or 10 with 33 <= L <= 64, TL = 4): the four IDs of a
+ * word are ten-bit fields, table w*4 + m at bits 10m .. 10m+9 of a 40-bit
+ * value, and a key takes 80 bytes (SOCKET Sec. 1 puts the footprint at about
+ * 600 bits a token with P = 10 and L = 60).  With the same t, kg, x, u and
+ * lane c = 16*kg + w, the low 32 bits (little-endian) of word w start at
+ *   (r * ceil(n_cap/64) + i/64) * 5120 + (u/4)*1024 + 16*c + 4*(u%4)
+ * and its high byte lies at
+ *   (r * ceil(n_cap/64) + i/64) * 5120 + 4096 + 16*c + u.
  * - Errors are reported as negative return codes before anything is
  *   enqueued (argument checks), or as SOCKET_EHIP when a launch fails.
  *   Nothing throws or aborts.  socket_status_string() names a code.

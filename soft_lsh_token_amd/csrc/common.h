@@ -25,6 +25,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 //   (r / R) * 64 * R + (16*kg + j) * R + r % R,   R = 16 / WB,
 // so that a lane's words of R consecutive rounds form one 16-byte vector and
 // a wave's 16-byte loads read 1 KiB contiguously.
+//
+// Packed words (P = 9 or 10 with 33 <= L <= 64, so T = 4): ten-bit cells,
+// cell m of word j at bits 10m .. 10m+9 of a 40-bit value, 80 bytes a key.
+// A lane's 16 words are five 16-byte vectors of the group's 5 KiB slab,
+// vector v at byte v*1024 + 16*lane: vectors 0..3 hold the low 32 bits of
+// rounds 4v .. 4v+3, vector 4 the high byte of round r at byte r.
 __host__ __device__ constexpr int ids_tables_per_word(int L) {
   return L <= 16 ? 1 : L <= 32 ? 2 : L <= 64 ? 4 : 8;
 }
@@ -32,7 +38,19 @@ __host__ __device__ constexpr int ids_cell_bytes(int P) { return P > 8 ? 2 : 1; 
 __host__ __device__ constexpr int ids_word_bytes(int L, int P) {
   return ids_tables_per_word(L) * ids_cell_bytes(P);
 }
-__host__ __device__ constexpr int ids_key_bytes(int L, int P) { return 16 * ids_word_bytes(L, P); }
+__host__ __device__ constexpr bool ids_packed(int L, int P) {
+  return P > 8 && ids_tables_per_word(L) == 4;
+}
+// bit offset of cell m inside a word is m * ids_cell_bits
+__host__ __device__ constexpr int ids_cell_bits(int L, int P) {
+  return ids_packed(L, P) ? 10 : 8 * ids_cell_bytes(P);
+}
+__host__ __device__ constexpr int ids_key_bytes(int L, int P) {
+  return ids_packed(L, P) ? 80 : 16 * ids_word_bytes(L, P);
+}
+// 16-byte vectors of one scorer lane per 64-key group (the group's slab is
+// 1024 * this many bytes)
+__host__ __device__ constexpr int ids_lane_vectors(int L, int P) { return ids_key_bytes(L, P) / 16; }
 __host__ __device__ inline int64_t ids_groups(int64_t n_cap) { return (n_cap + 63) / 64; }
 
 // Byte offset of word j of key `key` of KV row bh, for WB-byte words.
@@ -44,6 +62,37 @@ __host__ __device__ inline int64_t ids_word_offset(int64_t bh, int64_t n_cap, in
   const int r = (x - j) & 15;
   const int slot = (r / R) * 64 * R + ((kg << 4) | j) * R + (r % R);
   return ((bh * ids_groups(n_cap) + gi) * 1024 + slot) * WB;
+}
+
+// Packed words: byte offsets of the low 32 bits and of the high byte of word
+// j of key `key` of KV row bh.
+__host__ __device__ inline void ids_packed_offsets(int64_t bh, int64_t n_cap, int64_t key, int j,
+                                                   int64_t* lo, int64_t* hi) {
+  const int64_t base = (bh * ids_groups(n_cap) + (key >> 6)) * 5120;
+  const int t = (int)(key & 63), kg = t >> 4, x = t & 15;
+  const int r = (x - j) & 15;
+  const int lane = (kg << 4) | j;
+  *lo = base + (r >> 2) * 1024 + lane * 16 + (r & 3) * 4;
+  *hi = base + 4096 + lane * 16 + r;
+}
+
+// Stores word j of key `key` of KV row bh: cell m of the word at bits
+// m * ids_cell_bits(L, P) of w.
+__device__ inline void ids_store_word(uint8_t* ids, int64_t bh, int64_t n_cap, int L, int P,
+                                      int64_t key, int j, uint64_t w) {
+  if (ids_packed(L, P)) {
+    int64_t lo, hi;
+    ids_packed_offsets(bh, n_cap, key, j, &lo, &hi);
+    *reinterpret_cast<uint32_t*>(ids + lo) = (uint32_t)w;
+    ids[hi] = (uint8_t)(w >> 32);
+    return;
+  }
+  const int WB = ids_word_bytes(L, P);  // at most 8 (T = 8 only with one-byte cells)
+  uint8_t* dst = ids + ids_word_offset(bh, n_cap, WB, key, j);
+  if (WB == 1) *dst = (uint8_t)w;
+  else if (WB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+  else if (WB == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w;
+  else *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w, (uint32_t)(w >> 32));
 }
 
 // Row stride (floats) of the per-head score rows: n_cap rounded up to 64, so

@@ -110,25 +110,18 @@ __global__ __launch_bounds__(kGenThreads) void hash_generic_kernel(
     if (lane == 16) vnorm[row] = sqrtf(ss);
   }
   if (lane < WPB) {
-    // word = TL tables of C-byte cells (WB = TL*C <= 16 bytes)
+    // word = TL tables, cell b8 at bit b8 * CB (at most 64 bits)
     const int word = s * WPB + lane;
-    const int WB = TL * C;
-    uint64_t w[2] = {0ull, 0ull};
+    const int CB = ids_cell_bits(L, P);
+    uint64_t w = 0ull;
     for (int b8 = 0; b8 < TL; ++b8) {
       const int t = word * TL + b8;  // table
       if (t < L) {
         const uint64_t id = (m >> ((lane * TL + b8) * P)) & ((1ull << P) - 1ull);
-        const int bit = 8 * C * b8;
-        w[bit >> 6] |= id << (bit & 63);
+        w |= id << (CB * b8);
       }
     }
-    uint8_t* dst = ids + ids_word_offset(bh, n_cap, WB, pos, word);
-    if (WB == 1) *dst = (uint8_t)w[0];
-    else if (WB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
-    else if (WB == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w[0];
-    else if (WB == 8) *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w[0], (uint32_t)(w[0] >> 32));
-    else *reinterpret_cast<uint4*>(dst) = make_uint4((uint32_t)w[0], (uint32_t)(w[0] >> 32),
-                                                     (uint32_t)w[1], (uint32_t)(w[1] >> 32));
+    ids_store_word(ids, bh, n_cap, L, P, pos, word, w);
   }
 }
 
@@ -168,6 +161,7 @@ constexpr int kTK = 128;       // keys per LDS tile
 constexpr int kProd = 4;       // producer waves
 constexpr int kRowU4 = 17;     // K rows in LDS padded to 272 B: 16 consecutive keys hit 16 bank groups
 constexpr int kProdU4 = kTK * 16 / (kProd * 64);  // K (and V) vectors per producer thread per tile (8)
+constexpr int kStageRow = 68;  // two-byte IDs staged per key (64 tables + pad: 8-byte rows, 2-bank skew)
 
 // Two-byte IDs of tables t0, t0+1, t0+2 of key pos (those < L), in the tiled
 // layout of L tables (TL per word, 2*TL-byte words).  The lane holding table
@@ -222,16 +216,18 @@ __device__ __forceinline__ void store_wide(uint8_t* ids, int64_t bh, int64_t n_c
 // grid: chunks*B*Hkv*nblk blocks; block blk hashes keys [pos0 + blk*kpb,
 // +kpb) of (b, h) (for plane chunk `chunk` in CODES mode, the norms with
 // chunk 0).  NRM false: no V loads, no norms.
-constexpr int kModeIds8 = 0;   // one-byte IDs, P = 8
-constexpr int kModeIds10 = 1;  // two-byte IDs, P = 10
-constexpr int kModeCodes = 2;  // packed sign codes
+constexpr int kModeIds8 = 0;    // one-byte IDs, P = 8
+constexpr int kModeIds10 = 1;   // two-byte IDs, P = 10, L <= 32
+constexpr int kModeCodes = 2;   // packed sign codes
+constexpr int kModeIds10P = 3;  // packed ten-bit IDs, P = 10, 32 < L <= 64
 template <int NW, int MODE, bool NRM>
 __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int Hkv, int64_t n_cap,
     const int32_t* __restrict__ pos0, int count, const uint16_t* __restrict__ W, int Lw,
     uint8_t* __restrict__ ids, float* __restrict__ vnorm, int kpb, int nblk,
     uint32_t* __restrict__ codes, int LP, int WPK, int chunks) {
-  constexpr bool WIDE = MODE == kModeIds10;
+  constexpr bool WIDE = MODE == kModeIds10 || MODE == kModeIds10P;
+  constexpr bool PACKED = MODE == kModeIds10P;
   constexpr int L8 = NW * 8;  // tables of the one-byte layout
   constexpr int NB = kTK / kBTile;
   const int per_chunk = (int)(gridDim.x / (unsigned)chunks);
@@ -254,6 +250,8 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
   const int64_t rowbase = (int64_t)bh * n_cap;
   const int ntiles = (int)((end - start + kTK - 1) / kTK);
   __shared__ uint4 ktile[2][kTK * kRowU4];
+  // two-byte IDs of the last two tiles, for packed words (WIDE with L > 32)
+  __shared__ __attribute__((aligned(16))) uint16_t stage[PACKED ? 2 * kTK * kStageRow : 2];
 
   if (producer) {
     // The next tile's K and V wait in registers (8 named vectors each, one
@@ -360,6 +358,10 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
       }
     }
   }
+  if constexpr (PACKED) {  // tables no wave projects stay 0
+    uint32_t* z = reinterpret_cast<uint32_t*>(stage);
+    for (int i = tid; i < kTK * kStageRow; i += NW * 64) z[i] = 0u;
+  }
   lds_barrier();
   if constexpr (!WIDE) {
     // One-byte IDs: a software pipeline over the tile's four 32-key blocks.
@@ -449,9 +451,29 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
     }
     return;
   }
+  // Packed words: the consumers write their IDs into the tile's stage, and
+  // after the tile's barrier turn the previous tile's stage into whole words
+  // (one word a thread: key kl = i / 16, word j = i % 16).
+  auto pack_tile = [&](int tp) {
+    const uint16_t* st = stage + (tp & 1) * kTK * kStageRow;
+    const int64_t t0p = start + (int64_t)tp * kTK;
+    for (int i = wave * 64 + lane; i < kTK * 16; i += NW * 64) {
+      const int kl = i >> 4, j = i & 15;
+      const int64_t pos = t0p + kl;
+      if (pos < end) {
+        const uint2 c = *reinterpret_cast<const uint2*>(st + kl * kStageRow + 4 * j);
+        const uint64_t w = (uint64_t)(c.x & 0xFFFFu) | ((uint64_t)(c.x >> 16) << 10) |
+                           ((uint64_t)(c.y & 0xFFFFu) << 20) | ((uint64_t)(c.y >> 16) << 30);
+        ids_store_word(ids, bh, n_cap, Lw, 10, pos, j, w);
+      }
+    }
+  };
   for (int t = 0; t < ntiles; ++t) {
     const int64_t t0 = start + (int64_t)t * kTK;
     const uint4* kt = ktile[t & 1];
+    if constexpr (PACKED) {
+      if (t > 0) pack_tile(t - 1);
+    }
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
       f32x16_t acc0 = {0}, acc1 = {0};
@@ -473,11 +495,20 @@ __global__ __launch_bounds__((NW + kProd) * 64) void hash_mfma_kernel(
         else if (c < 20) id1 |= bit;
         else id2 |= bit;
       }
-      if (pos < end) store_wide(ids, bh, n_cap, pos, Lw, 6 * wave + 3 * half, id0, id1, id2,
-                                wave == 0 && half == 0);
+      if constexpr (PACKED) {
+        uint16_t* st = stage + (t & 1) * kTK * kStageRow + (bt * kBTile + col) * kStageRow;
+        const int tb = 6 * wave + 3 * half;
+        if (tb < 64) st[tb] = (uint16_t)id0;
+        if (tb + 1 < 64) st[tb + 1] = (uint16_t)id1;
+        if (tb + 2 < 64) st[tb + 2] = (uint16_t)id2;
+      } else if (pos < end) {
+        store_wide(ids, bh, n_cap, pos, Lw, 6 * wave + 3 * half, id0, id1, id2,
+                   wave == 0 && half == 0);
+      }
     }
     lds_barrier();  // the ID stores stay in flight
   }
+  if constexpr (PACKED) pack_tile(ntiles - 1);  // complete: the loop ended on a barrier
 }
 
 // ---------------------------------------------------------------- launcher
@@ -512,7 +543,8 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     auto go = [&](auto nw, auto wide) {
       constexpr int NW = decltype(nw)::value;
-      constexpr int MODE = decltype(wide)::value ? kModeIds10 : kModeIds8;
+      constexpr int MODE = decltype(wide)::value == 2 ? kModeIds10P
+                           : decltype(wide)::value == 1 ? kModeIds10 : kModeIds8;
       if (vnorm)
         hash_mfma_kernel<NW, MODE, true><<<grid, (NW + kProd) * 64, 0, s>>>(
             Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk, nullptr, 0,
@@ -522,22 +554,26 @@ hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int 
             Kb, Vb, Hkv, n_cap, pos0, count, Wb, L, ids, vnorm, (int)kpb, (int)nblk, nullptr, 0,
             0, 1);
     };
-    using N = std::false_type;
-    using Y = std::true_type;
+    using N = std::integral_constant<int, 0>;  // one-byte IDs
+    using Y = std::integral_constant<int, 1>;  // two-byte IDs
+    using Q = std::integral_constant<int, 2>;  // packed ten-bit IDs
     if (mfma_ok) {
       switch (L) {
         case 16: go(std::integral_constant<int, 2>{}, N{}); break;
         case 32: go(std::integral_constant<int, 4>{}, N{}); break;
         default: go(std::integral_constant<int, 8>{}, N{}); break;
       }
-    } else {  // six 10-plane tables per consumer wave
+    } else if (!ids_packed(L, P)) {  // six 10-plane tables per consumer wave
       const int nw = (L + 5) / 6;
       if (nw <= 2) go(std::integral_constant<int, 2>{}, Y{});
       else if (nw <= 4) go(std::integral_constant<int, 4>{}, Y{});
-      else if (nw <= 6) go(std::integral_constant<int, 6>{}, Y{});
-      else if (nw <= 8) go(std::integral_constant<int, 8>{}, Y{});
-      else if (nw <= 10) go(std::integral_constant<int, 10>{}, Y{});
-      else go(std::integral_constant<int, 11>{}, Y{});
+      else go(std::integral_constant<int, 6>{}, Y{});
+    } else {
+      const int nw = (L + 5) / 6;  // 6 .. 11
+      if (nw <= 6) go(std::integral_constant<int, 6>{}, Q{});
+      else if (nw <= 8) go(std::integral_constant<int, 8>{}, Q{});
+      else if (nw <= 10) go(std::integral_constant<int, 10>{}, Q{});
+      else go(std::integral_constant<int, 11>{}, Q{});
     }
     return hipGetLastError();
   }

@@ -415,22 +415,15 @@ __device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int
   __syncthreads();
   if (tid < WPB && w0 + tid < 16) {
     const int wd = w0 + tid;
-    const int C = P > 8 ? 2 : 1, WB = TL * C;
-    uint64_t w[2] = {0ull, 0ull};
+    const int CB = ids_cell_bits(L, P);
+    uint64_t w = 0ull;
     for (int mm = 0; mm < TL; ++mm) {
       uint64_t id = 0ull;
       if (wd * TL + mm < L)
         for (int p2 = 0; p2 < P; ++p2) id |= (uint64_t)kbit[tid * WP + mm * P + p2] << p2;
-      const int bit = 8 * C * mm;
-      w[bit >> 6] |= id << (bit & 63);
+      w |= id << (CB * mm);
     }
-    uint8_t* dst = ak.ids + ids_word_offset(bh, ak.n_cap, WB, pos, wd);
-    if (WB == 1) *dst = (uint8_t)w[0];
-    else if (WB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
-    else if (WB == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w[0];
-    else if (WB == 8) *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)w[0], (uint32_t)(w[0] >> 32));
-    else *reinterpret_cast<uint4*>(dst) = make_uint4((uint32_t)w[0], (uint32_t)(w[0] >> 32),
-                                                     (uint32_t)w[1], (uint32_t)(w[1] >> 32));
+    ids_store_word(ak.ids, bh, ak.n_cap, L, P, pos, wd, w);
   }
 }
 // ---------------------------------------------------------------- scorer
@@ -457,18 +450,30 @@ constexpr int kScoreWaves = kScoreThreads / 64;
 // the value lane j - d holds for the same key (its slot x + d); row_ror:d
 // gives lane j the register of lane (j - d) mod 16.
 
-// The WB-byte ID word of round x from the lane's WB 16-byte vectors.
-template <int WB>
-__device__ __forceinline__ uint2 round_word(const uint4 (&v)[WB], int x) {
-  constexpr int R = 16 / WB;
-  const uint4 q = v[x / R];
-  const int k = x % R;  // word index inside the vector
-  if constexpr (WB == 8) {
-    return k == 0 ? make_uint2(q.x, q.y) : make_uint2(q.z, q.w);
+// The ID word of round x from the lane's NV 16-byte vectors: WB = NV bytes
+// (w.x, and w.y for WB = 8), or, packed (PK, five vectors), the low 32 bits
+// in w.x and the high byte in w.y.
+template <int NV, bool PK>
+__device__ __forceinline__ uint2 round_word(const uint4 (&v)[NV], int x) {
+  if constexpr (PK) {
+    static_assert(NV == 5, "packed words: four vectors of low words and one of high bytes");
+    const uint4 q = v[x >> 2];
+    const uint32_t lo = (x & 3) == 0 ? q.x : (x & 3) == 1 ? q.y : (x & 3) == 2 ? q.z : q.w;
+    const uint4 h = v[4];
+    const uint32_t hd = (x >> 2) == 0 ? h.x : (x >> 2) == 1 ? h.y : (x >> 2) == 2 ? h.z : h.w;
+    return make_uint2(lo, hd >> (8 * (x & 3)));
   } else {
-    const int byte = k * WB;
-    const uint32_t d = byte < 4 ? q.x : byte < 8 ? q.y : byte < 12 ? q.z : q.w;
-    return make_uint2(WB == 4 ? d : (d >> (8 * (byte & 3))) & (WB == 2 ? 0xFFFFu : 0xFFu), 0u);
+    constexpr int WB = NV;
+    constexpr int R = 16 / WB;
+    const uint4 q = v[x / R];
+    const int k = x % R;  // word index inside the vector
+    if constexpr (WB == 8) {
+      return k == 0 ? make_uint2(q.x, q.y) : make_uint2(q.z, q.w);
+    } else {
+      const int byte = k * WB;
+      const uint32_t d = byte < 4 ? q.x : byte < 8 ? q.y : byte < 12 ? q.z : q.w;
+      return make_uint2(WB == 4 ? d : (d >> (8 * (byte & 3))) & (WB == 2 ? 0xFFFFu : 0xFFu), 0u);
+    }
   }
 }
 
@@ -510,20 +515,34 @@ __device__ __forceinline__ void issue_full(const float* lds, uint2 w, int j, uin
   }
 }
 
-// Half-table lookups of tables NF .. NF+NS-1 (C-byte cells, HE-entry halves).
-template <int NF, int NS, int G, int C, int HE, int M = 0>
+// Half-table lookups of tables NF .. NF+NS-1 (C-byte cells, HE-entry halves;
+// PK: ten-bit cells at bit 10*T of the 40-bit word, five-bit halves).
+template <int NF, int NS, int G, int C, int HE, bool PK, int M = 0>
 __device__ __forceinline__ void issue_half(const float* lds, uint2 w, int j, int plo,
                                            RoundVals<NF, NS, G>& r) {
   if constexpr (M < NS) {
     // the two factors' entries as bit fields of the word (one extract each)
-    constexpr int T = NF + M, PER = 4 / C;  // cells per 32-bit half of the word
-    const uint32_t src = T < PER ? w.x : w.y;
-    constexpr uint32_t off = 8 * C * (T % PER);
-    const uint32_t lo = __builtin_amdgcn_ubfe(src, off, (uint32_t)plo);
-    const uint32_t hi = __builtin_amdgcn_ubfe(src, off + (uint32_t)plo, 8 * C - (uint32_t)plo);
+    constexpr int T = NF + M;
+    uint32_t lo, hi;
+    if constexpr (PK) {
+      static_assert(NF == 0 && NS == 4, "packed words hold four factored tables");
+      if constexpr (T < 3) {
+        lo = __builtin_amdgcn_ubfe(w.x, 10 * T, 5);
+        hi = __builtin_amdgcn_ubfe(w.x, 10 * T + 5, 5);
+      } else {  // bits 30 .. 39 straddle the low word and the high byte
+        lo = __builtin_amdgcn_alignbit(w.y, w.x, 30) & 31u;
+        hi = __builtin_amdgcn_ubfe(w.y, 3, 5);
+      }
+    } else {
+      constexpr int PER = 4 / C;  // cells per 32-bit half of the word
+      const uint32_t src = T < PER ? w.x : w.y;
+      constexpr uint32_t off = 8 * C * (T % PER);
+      lo = __builtin_amdgcn_ubfe(src, off, (uint32_t)plo);
+      hi = __builtin_amdgcn_ubfe(src, off + (uint32_t)plo, 8 * C - (uint32_t)plo);
+    }
     lds_get<G>(lds, ((int)lo * NS + M) * 16 + j, r.lo[M]);
     lds_get<G>(lds, ((HE + (int)hi) * NS + M) * 16 + j, r.hi[M]);
-    issue_half<NF, NS, G, C, HE, M + 1>(lds, w, j, plo, r);
+    issue_half<NF, NS, G, C, HE, PK, M + 1>(lds, w, j, plo, r);
   }
 }
 
@@ -545,23 +564,23 @@ __device__ __forceinline__ void round_sum(const RoundVals<NF, NS, G>& r, float (
 // x + 1 are issued before round x is summed.  The first reduce-scatter stage
 // (row_ror 8) is applied as soon as round x + 8 is summed, so only 8 rounds of
 // partial sums stay live.  On exit u[0] of lane j holds the sums of its key.
-template <int NF, int NS, int G, int C, int HE, int WB>
-__device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[WB], int j,
+template <int NF, int NS, int G, int C, int HE, int NV, bool PK>
+__device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)[NV], int j,
                                             int plo, float (&u)[8][G]) {
   constexpr int FULL = 256 * NF * 16 * G;
   const uint32_t jw = ((uint32_t)j << 4) | 0x100u;
   RoundVals<NF, NS, G> cur, nxt;
   {
-    const uint2 w = round_word<WB>(ids, 0);
+    const uint2 w = round_word<NV, PK>(ids, 0);
     issue_full<NF, NS, G>(lds, w, j, jw, cur);
-    issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, plo, cur);
+    issue_half<NF, NS, G, C, HE, PK>(lds + FULL, w, j, plo, cur);
   }
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     if (x < 15) {
-      const uint2 w = round_word<WB>(ids, x + 1);
+      const uint2 w = round_word<NV, PK>(ids, x + 1);
       issue_full<NF, NS, G>(lds, w, j, jw, nxt);
-      issue_half<NF, NS, G, C, HE>(lds + FULL, w, j, plo, nxt);
+      issue_half<NF, NS, G, C, HE, PK>(lds + FULL, w, j, plo, nxt);
     }
     float acc[G];
     round_sum<NF, NS, G>(cur, acc);
@@ -610,7 +629,9 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   using Sh = ImageShape<G, TL, WIDE>;
   constexpr int NF = Sh::NF, NS = Sh::NS, HE = Sh::HE;
   constexpr int C = WIDE ? 2 : 1;  // bytes per ID
-  constexpr int WB = TL * C;       // bytes per ID word
+  constexpr int WB = TL * C;       // bytes per ID word (unpacked)
+  constexpr bool PK = WIDE && TL == 4;      // packed ten-bit cells
+  constexpr int NV = PK ? 5 : WB;           // 16-byte ID vectors per lane and group
   constexpr int D = kPrefetch;
   __shared__ __attribute__((aligned(16))) float lds[Sh::FLOATS];
   __shared__ uint32_t lhist[G * kHistBins];
@@ -643,17 +664,17 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     // are issued unconditionally (a group past the segment re-reads its last
     // group, keys past n_cap re-read the last norm) so that no branch sits
     // between a load and its use and each wait covers only the group needed.
-    const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * WB;
+    const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * NV;
     const float* vrow = vnorm + (int64_t)bh * n_cap;
-    auto load_group = [&](int64_t gi, uint4 (&v)[WB], float& vn) {
+    auto load_group = [&](int64_t gi, uint4 (&v)[NV], float& vn) {
       const int64_t gl = gi < g_end ? gi : g_end - 1;
-      const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * WB) + lane;
+      const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * NV) + lane;
 #pragma unroll
-      for (int qv = 0; qv < WB; ++qv) v[qv] = src[qv * 64];
+      for (int qv = 0; qv < NV; ++qv) v[qv] = src[qv * 64];
       const int64_t key = gl * 64 + lane;
       vn = vrow[key < n_cap ? key : n_cap - 1];
     };
-    uint4 buf[D + 1][WB];
+    uint4 buf[D + 1][NV];
     float vb[D + 1];
     int64_t gi = g_begin + wave;
 #pragma unroll
@@ -686,7 +707,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
         if (more) {
           load_group(gi + (int64_t)D * kScoreWaves, buf[(s + D) % (D + 1)], vb[(s + D) % (D + 1)]);
           float u[8][G];
-          score_group<NF, NS, G, C, HE, WB>(lds, buf[s], j, plo, u);
+          score_group<NF, NS, G, C, HE, NV, PK>(lds, buf[s], j, plo, u);
           const int64_t key = gi * 64 + lane;
           const bool valid = key < n;
           const uint32_t ranked = valid && key >= f_lo && key < f_hi ? 1u : 0u;

@@ -253,15 +253,36 @@ def test_ids_layout_roundtrip_and_formula(L, P):
     assert layout.word_bytes(L, P) == WB
     flat = tiled.reshape(-1)
     G = (n_cap + 63) // 64
-    for (b, h, i, l) in [(0, 0, 0, 0), (1, 2, 149, L - 1), (0, 1, 77, L // 2), (1, 0, 64, 0)]:
+    packed = P > 8 and L > 32
+    assert layout.packed(L, P) == packed
+    assert layout.key_bytes(L, P) == (80 if packed else 16 * WB)
+    for (b, h, i, l) in [(0, 0, 0, 0), (1, 2, 149, L - 1), (0, 1, 77, L // 2), (1, 0, 64, 0),
+                         (1, 1, 100, min(L - 1, 3)), (0, 2, 15, min(L - 1, 35))]:
         r, w, cell = b * Hkv + h, l // TL, l % TL
         t = i % 64
         kg, x = t // 16, t % 16
-        u, R = (x - w) % 16, 16 // WB
-        off = ((r * G + i // 64) * 1024 + (u // R) * 64 * R + (16 * kg + w) * R + u % R) * WB
-        off += cell * C
-        value = int(flat[off]) | (int(flat[off + 1]) << 8 if C == 2 else 0)
+        u = (x - w) % 16
+        if packed:  # the header's packed formula: 40-bit word = 4 low bytes + 1 high byte
+            base = (r * G + i // 64) * 5120
+            lo = base + (u // 4) * 1024 + 16 * (16 * kg + w) + 4 * (u % 4)
+            hi = base + 4096 + 16 * (16 * kg + w) + u
+            word = int.from_bytes(bytes(flat[lo:lo + 4]), "little") | (int(flat[hi]) << 32)
+            value = (word >> (10 * cell)) & 0x3FF
+        else:
+            R = 16 // WB
+            off = ((r * G + i // 64) * 1024 + (u // R) * 64 * R + (16 * kg + w) * R + u % R) * WB
+            off += cell * C
+            value = int(flat[off]) | (int(flat[off + 1]) << 8 if C == 2 else 0)
         assert value == ids[b, h, i, l]
+
+
+def test_p10_footprint():
+    """At the pages' operating point (P = 10, L = 60: 600 bits a token, SOCKET Sec. 1) the
+    cache stores 80 bytes of IDs and a 4-byte norm per key, 16.4% over bf16 K and V at
+    d = 128 (the pages put it near 15%, Sec. 7)."""
+    per_key = S.socket_ids_bytes(1, 1, 64, 60, 10) // 64
+    assert per_key == 80 and per_key * 8 >= 600
+    assert (per_key + 4) / (2 * 128 * 2) < 0.17
 
 
 def test_ids_bytes_limits():
@@ -269,6 +290,7 @@ def test_ids_bytes_limits():
     assert S.socket_ids_bytes(1, 1, 10, 129, 8) == 0
     assert S.socket_ids_bytes(1, 1, 10, 65, 10) == 0
     assert S.socket_ids_bytes(1, 1, 10, 64, 11) == 0
-    assert S.socket_ids_bytes(1, 1, 10, 64, 10) == 64 * 16 * 8
-    assert S.socket_ids_bytes(1, 1, 10, 60, 9) == 64 * 16 * 8
+    assert S.socket_ids_bytes(1, 1, 10, 64, 10) == 64 * 80     # packed: 80 bytes a key
+    assert S.socket_ids_bytes(1, 1, 10, 60, 9) == 64 * 80
+    assert S.socket_ids_bytes(1, 1, 10, 32, 10) == 64 * 16 * 4  # two-byte cells
     assert S.socket_ids_bytes(1, 1, 10, 128, 8) == 64 * 16 * 8

@@ -41,11 +41,11 @@ def sync():
     dict(name="c2", n=500, L=7, P=5, Hkv=2, Hq=4),     # odd shapes: generic path
     dict(name="c2", n=300, L=3, P=8, Hkv=2, Hq=2),
     dict(name="c4", n=(300, 900), B=3, Hkv=2, Hq=8),   # batch with different lengths
-    dict(name="c2", n=1000, L=60, P=10),               # two-byte IDs, MFMA, 10 consumer waves
-    dict(name="c2", n=700, L=64, P=10, Hkv=4, Hq=8),   # MFMA, 11 consumer waves
+    dict(name="c2", n=1000, L=60, P=10),               # packed IDs, MFMA, 10 consumer waves
+    dict(name="c2", n=700, L=64, P=10, Hkv=4, Hq=8),   # packed IDs, MFMA, 11 consumer waves
     dict(name="c2", n=500, L=20, P=10, Hkv=2, Hq=4),   # MFMA, two tables per word
     dict(name="c2", n=300, L=5, P=10, Hkv=2, Hq=2),    # MFMA, one table per word
-    dict(name="c2", n=40, L=60, P=10),                 # few keys: generic, two-byte IDs
+    dict(name="c2", n=40, L=60, P=10),                 # few keys: generic, packed IDs
     dict(name="c2", n=300, L=5, P=9, Hkv=2, Hq=2),     # generic, one table per word
     dict(name="c1", L=60, P=10),                       # fp32: generic
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
@@ -79,7 +79,7 @@ def test_hash_full_c2_mfma():
 
 @pytest.mark.parametrize("case", [
     dict(name="c2", n=3000),                          # bf16 MFMA
-    dict(name="c2", n=1000, L=60, P=10),              # two-byte IDs, MFMA
+    dict(name="c2", n=1000, L=60, P=10),              # packed IDs, MFMA
     dict(name="c1", n=700),                           # fp32, generic
     dict(name="c4", n=(30, 50), B=3, Hkv=2, Hq=4),    # few keys, generic bf16
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
@@ -106,11 +106,13 @@ def test_hash_outputs_apart(case):
 
 @pytest.mark.parametrize("L,n", [(60, 1000), (20, 333), (5, 200), (37, 64)])
 def test_hash_wide_pads_and_range(L, n):
-    """Two-byte IDs: the hashed keys' cells of tables >= L (up to 16 words) are
-    cleared, and keys past the hashed range keep their bytes."""
+    """P = 10 IDs (two-byte cells for L <= 32, packed ten-bit cells above): the
+    hashed keys' cells of tables >= L (up to 16 words) are cleared, and keys
+    past the hashed range keep their bytes."""
     w = make_workload("c2", n=n, L=L, P=10, Hkv=2, Hq=4, n_cap=n + 100)
     d = GC.upload(w)
     ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV).fill_(0xAB)
+    untouched = GC.ids_np(ids, 16 * S.layout.tables_per_word(L), P=10)  # the fill, as cells
     ids, _ = GC.gpu_hash(w, d, ids=ids)
     sync()
     slots = 16 * S.layout.tables_per_word(L)
@@ -118,7 +120,8 @@ def test_hash_wide_pads_and_range(L, n):
     for h in range(w.Hkv):
         GC.check_ids(full[0, h, :, :L], w.K[0, h], w.W, w.L, w.P, n)
     assert (full[0, :, :n, L:] == 0).all()
-    assert (full[0, :, n:, :] == 0xABAB).all()
+    assert (full[0, :, n:, :] == untouched[0, :, n:, :]).all()
+    assert S.layout.packed(L, 10) or (untouched == 0xABAB).all()
 
 
 @pytest.mark.parametrize("L,P", [(64, 8), (60, 10)])
@@ -127,7 +130,7 @@ def test_hash_append_rows_only(L, P):
     w = make_workload("c4", n=(200, 600), B=2, Hkv=2, Hq=8, L=L, P=P)
     d = GC.upload(w)
     ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV).fill_(0xAB)
-    fill = 0xABAB if P > 8 else 0xAB
+    fill = GC.ids_np(ids, w.L, w.n_cap, w.P)  # the fill byte, as cells of this layout
     vn = torch.full((w.B, w.Hkv, w.n_cap), -1.0, dtype=torch.float32, device=DEV)
     pos0 = d["lens"].clone()
     GC.gpu_hash(w, d, pos0=pos0, count=1, ids=ids, vnorm=vn)
@@ -141,7 +144,7 @@ def test_hash_append_rows_only(L, P):
                 np.testing.assert_allclose(vn[b, h, p], SO.value_norms(w.V[b, h, p]), rtol=2e-6)
             mask = np.ones(w.n_cap, bool)
             mask[p:p + 1] = False
-            assert (ids[b, h, mask] == fill).all()
+            assert (ids[b, h, mask] == fill[b, h, mask]).all()
             assert (vn[b, h, mask] == -1.0).all()
 
 
