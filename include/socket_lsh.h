@@ -31,8 +31,10 @@
  *     scores    [B][Hq][ns]             float32, ns = n_cap rounded up to 64
  *     out       [B][Hq][d]              float32
  * - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
- *   Hq must be a multiple of Hkv; socket_score_topk needs Hq / Hkv in
- *   {1, 2, 4}.
+ *   Hq must be a multiple of Hkv, with G = Hq / Hkv <= 64.  The scorer and
+ *   the dense kernel take the query heads of a KV row four at a time (two
+ *   or one when 4 does not divide G), so with G > 4 a KV row's IDs (or K
+ *   and V) are read G / 4 times per step.
  * - d must be 128.  Either 1 <= P <= 8 and 1 <= L <= 128, or P in {9, 10}
  *   and 1 <= L <= 64.  1 <= k_max <= 65536.
  *
@@ -325,7 +327,7 @@ size_t socket_dense_decode_workspace(int B, int Hq, int Hkv, int d, int64_t n_ca
  * contributions; Sec. 6), computed at the same shapes as the sparse path.
  *   out[b][g] = sum_{i < lens[b]} a_i V_i,
  *   a_i = exp(scale * <q, K_i>) / sum_{i' < lens[b]} exp(scale * <q, K_i'>)
- * with K, V of KV head g / (Hq/Hkv), Hq / Hkv in {1, 2, 4}.  Accumulation is
+ * with K, V of KV head g / (Hq/Hkv).  Accumulation is
  * float32.  lens is a device int32 array [B], 0 <= lens[b] <= n_cap; an
  * empty sequence produces zeros.  ws must hold
  * socket_dense_decode_workspace(B, Hq, Hkv, d, n_cap) bytes, 256-byte aligned;

@@ -12,6 +12,7 @@ constexpr int kMaxL = 128;       // 16 ID words of at most 8 tables each
 constexpr int kMaxScoreL = 128;
 constexpr int kMaxKmax = 1 << 16;  // 1024 attention splits of 64 keys
 constexpr int kMaxCodeBits = 4096;  // hard-LSH mode: L * P
+constexpr int kMaxGroup = 64;       // query heads per KV head
 constexpr int kMaxDraws = 8192;     // sampling estimator: draws per query head
 
 // Table shapes with an ID layout: one-byte IDs (P <= 8) for up to 128
@@ -20,10 +21,11 @@ static bool tables_ok(int L, int P) {
   return P <= 8 ? L <= kMaxL : P <= 10 && L <= 64;
 }
 
+// Any whole number of query heads per KV head (G > 4 runs G / 4 passes of
+// four heads, or of two or one when 4 does not divide G).
 bool group_ok(int Hq, int Hkv) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
-  const int G = Hq / Hkv;
-  return G == 1 || G == 2 || G == 4;
+  return Hq / Hkv <= kMaxGroup;
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? SOCKET_OK : SOCKET_EHIP; }

@@ -43,7 +43,7 @@ int dense_chunk(int B, int Hkv, int64_t n_cap) {
 }
 
 size_t dense_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, DenseWs* ws, void* base) {
-  const int chunk = dense_chunk(B, Hkv, n_cap);
+  const int chunk = dense_chunk(B, Hkv * pass_subs(Hq / Hkv), n_cap);  // over the sub-rows
   const int splits = (int)((n_cap + chunk - 1) / chunk);
   const size_t off = align256x((size_t)B * Hq * splits * kDensePart * sizeof(float));
   if (ws) {
@@ -101,17 +101,20 @@ __device__ __forceinline__ void widen(const uint4 (&r)[KeyRegs<T>::NV], float* f
   }
 }
 
-// grid: B*Hkv*splits blocks of kDenseThreads.
+// grid: B*Hkv*splits blocks of kDenseThreads, Hkv sub-rows per sequence:
+// sub-row bh serves query heads b*Hq + (bh % Hkv)*G + [0, G) and reads the K
+// and V rows of KV row bh / sub.
 template <typename T, int G>
 __global__ __launch_bounds__(kDenseThreads) void dense_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V, int Hq, int Hkv,
-    int64_t n_cap, const int32_t* __restrict__ lens, float scale, int splits, int chunk,
+    int sub, int64_t n_cap, const int32_t* __restrict__ lens, float scale, int splits, int chunk,
     float* __restrict__ part) {
   using Regs = KeyRegs<T>;
   constexpr int NV = Regs::NV;
   const int sp = blockIdx.x % splits;
   const int bh = blockIdx.x / splits;
   const int b = bh / Hkv, h = bh % Hkv;
+  const int kv = bh / sub;  // the KV row of this sub-row
   const int tid = threadIdx.x, row = tid >> 4, j = tid & 15;
   int64_t n = lens[b];
   if (n < 0) n = 0;
@@ -144,8 +147,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_partial_kernel(
   // batch t: keys c0 + (t*kDenseU + u)*kDenseRows + row, u < kDenseU; loads
   // past the split re-read its first key (always present when the split is
   // not empty) and are masked out of the softmax
-  const T* Kr = K + (int64_t)bh * n_cap * kHead;
-  const T* Vr = V + (int64_t)bh * n_cap * kHead;
+  const T* Kr = K + (int64_t)kv * n_cap * kHead;
+  const T* Vr = V + (int64_t)kv * n_cap * kHead;
   const int64_t nk = c1 - c0;
   const int nbatch = nk > 0 ? (int)((nk + kDenseRows * kDenseU - 1) / (kDenseRows * kDenseU)) : 0;
   auto issue = [&](int t, Regs& r) {
@@ -260,25 +263,25 @@ __global__ __launch_bounds__(kDenseThreads) void dense_partial_kernel(
 hipError_t launch_dense_decode(const void* q, const void* K, const void* V, int dtype, int B,
                                int Hq, int Hkv, int64_t n_cap, const int32_t* lens, float scale,
                                float* out, const DenseWs& ws, hipStream_t s) {
-  const int G = Hq / Hkv;
-  const unsigned grid = (unsigned)((int64_t)B * Hkv * ws.splits);
+  const int G = Hq / Hkv, GK = pass_heads(G), sub = pass_subs(G);
+  const unsigned grid = (unsigned)((int64_t)B * Hkv * sub * ws.splits);
   auto go = [&](auto tag, auto gtag) {
     using T = decltype(tag);
     constexpr int GG = decltype(gtag)::value;
     dense_partial_kernel<T, GG><<<grid, kDenseThreads, 0, s>>>(
-        static_cast<const T*>(q), static_cast<const T*>(K), static_cast<const T*>(V), Hq, Hkv,
-        n_cap, lens, scale, ws.splits, ws.chunk, ws.part);
+        static_cast<const T*>(q), static_cast<const T*>(K), static_cast<const T*>(V), Hq,
+        Hkv * sub, sub, n_cap, lens, scale, ws.splits, ws.chunk, ws.part);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   if (dtype == 1) {
-    if (G == 1) go(uint16_t{}, I1{});
-    else if (G == 2) go(uint16_t{}, I2{});
+    if (GK == 1) go(uint16_t{}, I1{});
+    else if (GK == 2) go(uint16_t{}, I2{});
     else go(uint16_t{}, I4{});
   } else {
-    if (G == 1) go(float{}, I1{});
-    else if (G == 2) go(float{}, I2{});
+    if (GK == 1) go(float{}, I1{});
+    else if (GK == 2) go(float{}, I2{});
     else go(float{}, I4{});
   }
   hipError_t e = hipGetLastError();

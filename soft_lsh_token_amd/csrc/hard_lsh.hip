@@ -148,14 +148,16 @@ __device__ __forceinline__ uint32_t group_matches(uint32_t x, uint32_t low) {
   return (uint32_t)__popc(~x & low);
 }
 
-// grid: a multiple of kXcds blocks, at least B*Hkv*nblk; logical block lid
-// (XCD-local as in the soft scorer) takes keys [blk*kpb, (blk+1)*kpb) of KV
-// row lid / nblk, one key per thread at a time, for all G query heads.
+// grid: a multiple of kXcds blocks, at least rows*nblk; logical block lid
+// (XCD-local as in the soft scorer) takes keys [blk*kpb, (blk+1)*kpb) of
+// sub-row lid / nblk, one key per thread at a time, for its G query heads.
+// Sub-rows as in the soft scorer: Hkv of them per sequence, sub-row bh reading
+// the codes and norms of KV row bh / sub.
 template <int G, int P>
 __global__ __launch_bounds__(kHardThreads) void hard_scorer_kernel(
     const uint32_t* __restrict__ qcodes, const uint32_t* __restrict__ codes,
-    const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int LP,
-    int WPK, int64_t n_cap, int sink, int window, int rows, int nblk, int kpb,
+    const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int sub,
+    int LP, int WPK, int64_t n_cap, int sink, int window, int rows, int nblk, int kpb,
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
   const int lid = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
   if (lid >= rows * nblk) return;
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(kHardThreads) void hard_scorer_kernel(
   // low bit of every valid P-bit group of word w
   uint32_t lowpat = 0u;
   for (int t = 0; t < 32; t += P) lowpat |= 1u << t;
-  const uint32_t* crow = codes + (int64_t)bh * WPK * n_cap;
+  const int kv = bh / sub;  // the KV row of this sub-row
+  const uint32_t* crow = codes + (int64_t)kv * WPK * n_cap;
   const uint32_t* qrow = qcodes + (int64_t)bg0 * WPK;  // uniform: scalar loads
   for (int64_t key = k0 + tid; key < k1; key += kHardThreads) {
     uint32_t cnt[G];
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kHardThreads) void hard_scorer_kernel(
         for (int g = 0; g < G; ++g) cnt[g] += group_matches<P>(kw[i] ^ qrow[g * WPK + wq], low);
       }
     }
-    const float vn = vnorm[(int64_t)bh * n_cap + key];
+    const float vn = vnorm[(int64_t)kv * n_cap + key];
     const bool ranked = key >= f_lo && key < f_hi;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -249,19 +252,20 @@ hipError_t launch_hard_score(const void* q, int dtype, int B, int Hq, int Hkv, c
         WPK, S, ws.qcodes, nullptr, ws.hist, ws.counters);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // about four blocks per CU over the KV rows
-  const int64_t rows = (int64_t)B * Hkv;
+  // about four blocks per CU over the sub-rows
+  const int G = Hq / Hkv, GK = pass_heads(G), sub = pass_subs(G);
+  const int Hv = Hkv * sub;
+  const int64_t rows = (int64_t)B * Hv;
   int64_t nblk = (4 * device_cu_count() + rows - 1) / rows;
   int64_t kpb = (n_cap + nblk - 1) / nblk;
   kpb = (kpb + kHardThreads - 1) / kHardThreads * kHardThreads;
   nblk = (n_cap + kpb - 1) / kpb;
   const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
-  const int G = Hq / Hkv;
   auto go = [&](auto gt, auto pt) {
     constexpr int GG = decltype(gt)::value, PP = decltype(pt)::value;
     hard_scorer_kernel<GG, PP><<<(unsigned)grid, kHardThreads, 0, s>>>(
-        ws.qcodes, codes, vnorm, lens, Hq, Hkv, LP, WPK, n_cap, sw.sink, sw.window, (int)rows,
-        (int)nblk, (int)kpb, scores, ws.hist);
+        ws.qcodes, codes, vnorm, lens, Hq, Hv, sub, LP, WPK, n_cap, sw.sink, sw.window,
+        (int)rows, (int)nblk, (int)kpb, scores, ws.hist);
   };
   auto by_p = [&](auto gt) {
     switch (P) {
@@ -272,8 +276,8 @@ hipError_t launch_hard_score(const void* q, int dtype, int B, int Hq, int Hkv, c
       default: go(gt, std::integral_constant<int, 16>{}); break;
     }
   };
-  if (G == 1) by_p(std::integral_constant<int, 1>{});
-  else if (G == 2) by_p(std::integral_constant<int, 2>{});
+  if (GK == 1) by_p(std::integral_constant<int, 1>{});
+  else if (GK == 2) by_p(std::integral_constant<int, 2>{});
   else by_p(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }

@@ -6,6 +6,14 @@
 
 namespace socketlsh {
 
+// Query heads per scorer (and dense) pass: the largest of 4, 2 and 1 that
+// divides G = Hq / Hkv.  A KV row with more query heads is taken in
+// G / pass_heads(G) passes ("sub-rows"): sub-row v of the B*Hkv*sub rows
+// serves query heads b*Hq + (v % (Hkv*sub)) * pass_heads(G) + [0, pass_heads(G))
+// and reads KV row v / sub.
+inline int pass_heads(int G) { return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+inline int pass_subs(int G) { return G / pass_heads(G); }
+
 hipError_t launch_hash_keys(const void* K, const void* V, int dtype, int B, int Hkv,
                             int64_t n_cap, const int32_t* pos0, int count, const void* W, int L,
                             int P, uint8_t* ids, float* vnorm, hipStream_t s);

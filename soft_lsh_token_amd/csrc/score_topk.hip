@@ -140,9 +140,9 @@ constexpr int kScanKeys = 9216;
 
 size_t score_ws_layout(int B, int Hq, int Hkv, int64_t n_cap, int L, ScoreWs* ws, void* base) {
   const int G = Hq / Hkv;
-  const int img_floats = image_stride(G == 1 || G == 2 ? G : 4, L);
-  const size_t n = select_ws_layout((size_t)B * Hkv * img_floats * sizeof(float), B, Hq, n_cap,
-                                    ws, base);
+  const int img_floats = image_stride(pass_heads(G), L);
+  const size_t rows = (size_t)B * Hkv * pass_subs(G);  // one image per sub-row
+  const size_t n = select_ws_layout(rows * img_floats * sizeof(float), B, Hq, n_cap, ws, base);
   if (ws) ws->img_floats = img_floats;
   return n;
 }
@@ -193,14 +193,15 @@ __device__ __forceinline__ void store_slot(float* dst, const float* v) {
   else dst[0] = v[0];
 }
 
-// grid: B*Hkv*16 blocks of kTabThreads.  Block (bh, j) computes the tables
-// j*TL .. j*TL+TL-1 (the tables of scorer lane j) for the G query heads of KV
-// row bh and writes their image slots whole (one slot = the G heads' values
-// of one entry).  It also clears a 1/16 share of those heads' histograms
-// (block j = 0: their candidate counters and soft-count sums).
+// grid: rows*16 blocks of kTabThreads, rows = B*Hkv*sub sub-rows of G query
+// heads each.  Block (bh, j) computes the tables j*TL .. j*TL+TL-1 (the
+// tables of scorer lane j) for the G query heads of sub-row bh and writes
+// their image slots whole (one slot = the G heads' values of one entry).  It
+// also clears a 1/16 share of those heads' histograms (block j = 0: their
+// candidate counters and soft-count sums).
 // Tables l >= L (padding of the last lane word) get all-zero entries.
-// With ak.K set, blocks past the first B*Hkv*16 hash the key appended at
-// position lens[b] - 1 of each KV row (append_block below) alongside.
+// With ak.K set, blocks past the first rows*16 hash the key appended at
+// position lens[b] - 1 of each of the B*Hkv KV rows (append_block below).
 template <typename T>
 __device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int TL, int nab,
                              int rows, const AppendKey& ak);
@@ -210,17 +211,18 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
     int TL, int NF, int NS, int HE, int FULL, int img_floats, float* __restrict__ img,
     uint32_t* __restrict__ hist, uint32_t* __restrict__ counters, float* __restrict__ usum,
-    AppendKey ak, int rows, int nab) {
+    AppendKey ak, int rows, int nab, int sub) {
   if ((int)blockIdx.x >= rows * 16) {  // uniform
     append_block<T>(W, Hkv, L, P, TL, nab, rows, ak);
     return;
   }
+  const int Hv = Hkv * sub;  // sub-rows per sequence (rows = B * Hv)
   // Logical table block lid = (blockIdx mod 8) * (2 rows) + blockIdx / 8: the
   // 16 blocks of a KV row share an XCD (blocks go to the XCDs round robin),
   // so the 16-byte slots they write into each image line meet in one L2.
   const int lid = (int)(blockIdx.x % kXcds) * (rows * 16 / kXcds) + (int)(blockIdx.x / kXcds);
   const int bh = lid >> 4, j = lid & 15;
-  const int b = bh / Hkv, h = bh % Hkv;
+  const int b = bh / Hv, h = bh % Hv;
   const int bg0 = b * Hq + h * G;
   const int tid = threadIdx.x;
   float* im = img + (int64_t)bh * img_floats;
@@ -605,7 +607,10 @@ __device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)
   for (int g = 0; g < G; ++g) u[0][g] += dpp_f32<0x121>(u[1][g]);
 }
 
-// grid: a multiple of kXcds blocks of kScoreThreads, at least B*Hkv*nblk.
+// grid: a multiple of kXcds blocks of kScoreThreads, at least rows*nblk.
+// Rows are sub-rows (Hkv of them per sequence): sub-row bh serves the G query
+// heads b*Hq + (bh % Hkv)*G + [0, G) and reads the IDs and norms of KV row
+// bh / sub (sub = 1 when a KV row has at most 4 query heads).
 // Logical block lid = (blockIdx mod 8) * (grid / 8) + blockIdx / 8 keeps
 // consecutive logical blocks -- the blocks of one KV row -- on one XCD.
 // When every sequence has the same length, logical block blk of KV row bh
@@ -623,8 +628,9 @@ __device__ __forceinline__ void score_group(const float* lds, const uint4 (&ids)
 template <int G, int TL, bool WIDE>
 __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     const float* __restrict__ img, int img_floats, const uint8_t* __restrict__ ids,
-    const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int P,
-    int64_t n_cap, int sink, int window, int rows, int nblk, int gpb, float* __restrict__ scores,
+    const float* __restrict__ vnorm, const int32_t* __restrict__ lens, int Hq, int Hkv, int sub,
+    int P, int64_t n_cap, int sink, int window, int rows, int nblk, int gpb,
+    float* __restrict__ scores,
     uint32_t* __restrict__ hist, float* __restrict__ usum, float* __restrict__ gsum) {
   using Sh = ImageShape<G, TL, WIDE>;
   constexpr int NF = Sh::NF, NS = Sh::NS, HE = Sh::HE;
@@ -648,7 +654,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     return n;
   };
 
-  // Score groups [g_begin, g_end) (g_begin < g_end) of KV row bh; every wave
+  // Score groups [g_begin, g_end) (g_begin < g_end) of sub-row bh; every wave
   // of the block calls it.
   auto segment = [&](int bh, int64_t g_begin, int64_t g_end) {
     const int b = bh / Hkv;
@@ -664,8 +670,9 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     // are issued unconditionally (a group past the segment re-reads its last
     // group, keys past n_cap re-read the last norm) so that no branch sits
     // between a load and its use and each wait covers only the group needed.
-    const uint8_t* idg = ids + (int64_t)bh * ids_groups(n_cap) * 1024 * NV;
-    const float* vrow = vnorm + (int64_t)bh * n_cap;
+    const int kv = bh / sub;  // the KV row of this sub-row
+    const uint8_t* idg = ids + (int64_t)kv * ids_groups(n_cap) * 1024 * NV;
+    const float* vrow = vnorm + (int64_t)kv * n_cap;
     auto load_group = [&](int64_t gi, uint4 (&v)[NV], float& vn) {
       const int64_t gl = gi < g_end ? gi : g_end - 1;
       const uint4* src = reinterpret_cast<const uint4*>(idg + gl * 1024 * NV) + lane;
@@ -1746,7 +1753,7 @@ static int device_cus() {
 }
 
 template <int G, int TL, bool WIDE>
-static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, SinkWindow sw,
+static void launch_scorer(int B, int Hkv, int sub, int Hq, int P, int64_t n_cap, SinkWindow sw,
                           float* usum, const ScoreWs& ws,
                           const uint8_t* ids, const float* vnorm, const int32_t* lens,
                           float* scores, hipStream_t s) {
@@ -1759,58 +1766,58 @@ static void launch_scorer(int B, int Hkv, int Hq, int P, int64_t n_cap, SinkWind
   nblk = (ng + gpb - 1) / gpb;
   const int64_t grid = (rows * nblk + kXcds - 1) / kXcds * kXcds;
   scorer_kernel<G, TL, WIDE><<<(unsigned)grid, kScoreThreads, 0, s>>>(
-      ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, P, n_cap, sw.sink, sw.window, (int)rows,
-      (int)nblk, (int)gpb, scores, ws.hist, usum, usum ? ws.gsum : nullptr);
+      ws.img, ws.img_floats, ids, vnorm, lens, Hq, Hkv, sub, P, n_cap, sw.sink, sw.window,
+      (int)rows, (int)nblk, (int)gpb, scores, ws.hist, usum, usum ? ws.gsum : nullptr);
 }
 
 template <int G>
-static void launch_scorer_g(int B, int Hkv, int Hq, int L, int P, int64_t n_cap, SinkWindow sw,
-                            float* usum,
+static void launch_scorer_g(int B, int Hkv, int sub, int Hq, int L, int P, int64_t n_cap,
+                            SinkWindow sw, float* usum,
                             const ScoreWs& ws, const uint8_t* ids, const float* vnorm,
                             const int32_t* lens, float* scores, hipStream_t s) {
   if (P > 8) {  // two-byte IDs, L <= 64
     switch (ids_tables_per_word(L)) {
-      case 1: launch_scorer<G, 1, true>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-      case 2: launch_scorer<G, 2, true>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-      default: launch_scorer<G, 4, true>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+      case 1: launch_scorer<G, 1, true>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+      case 2: launch_scorer<G, 2, true>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+      default: launch_scorer<G, 4, true>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
     }
     return;
   }
   switch (ids_tables_per_word(L)) {
-    case 1: launch_scorer<G, 1, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer<G, 2, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-    case 4: launch_scorer<G, 4, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer<G, 8, false>(B, Hkv, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 1: launch_scorer<G, 1, false>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer<G, 2, false>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 4: launch_scorer<G, 4, false>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer<G, 8, false>(B, Hkv, sub, Hq, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
   }
 }
 
 hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, const void* W,
                               int L, int P, float tau, const ScoreWs& ws, hipStream_t s,
                               AppendKey ak) {
-  const int G = Hq / Hkv;
-  const ImageDims im = image_dims(G == 1 || G == 2 ? G : 4, L, P);
-  const int rows = B * Hkv;
+  const int G = Hq / Hkv, GK = pass_heads(G), sub = pass_subs(G);
+  const ImageDims im = image_dims(GK, L, P);
+  const int rows = B * Hkv * sub;  // table blocks: 16 per sub-row
   const int TLw = ids_tables_per_word(L);
   const int nab = ak.K ? (16 + kTabThreads / (TLw * P) - 1) / (kTabThreads / (TLw * P)) : 0;
-  const unsigned grid = (unsigned)(rows * (16 + nab));
+  const unsigned grid = (unsigned)(rows * 16 + B * Hkv * nab);
   auto go = [&](auto tag, auto gtag) {
     using T = decltype(tag);
     constexpr int GG = decltype(gtag)::value;
     soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
         static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
         im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum, ak, rows,
-        nab);
+        nab, sub);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   if (dtype == 1) {
-    if (G == 1) go(uint16_t{}, I1{});
-    else if (G == 2) go(uint16_t{}, I2{});
+    if (GK == 1) go(uint16_t{}, I1{});
+    else if (GK == 2) go(uint16_t{}, I2{});
     else go(uint16_t{}, I4{});
   } else {
-    if (G == 1) go(float{}, I1{});
-    else if (G == 2) go(float{}, I2{});
+    if (GK == 1) go(float{}, I1{});
+    else if (GK == 2) go(float{}, I2{});
     else go(float{}, I4{});
   }
   return hipGetLastError();
@@ -1821,10 +1828,12 @@ hipError_t launch_score(int B, int Hq, int Hkv, int L, int P, const uint8_t* ids
                         float* scores, bool soft_sums,
                         const ScoreWs& ws, hipStream_t s) {
   float* usum = soft_sums ? ws.usum : nullptr;
-  switch (Hq / Hkv) {
-    case 1: launch_scorer_g<1>(B, Hkv, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-    case 2: launch_scorer_g<2>(B, Hkv, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
-    default: launch_scorer_g<4>(B, Hkv, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+  const int G = Hq / Hkv, sub = pass_subs(G);
+  const int Hv = Hkv * sub;  // sub-rows per sequence
+  switch (pass_heads(G)) {
+    case 1: launch_scorer_g<1>(B, Hv, sub, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    case 2: launch_scorer_g<2>(B, Hv, sub, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
+    default: launch_scorer_g<4>(B, Hv, sub, Hq, L, P, n_cap, sw, usum, ws, ids, vnorm, lens, scores, s); break;
   }
   return hipGetLastError();
 }

@@ -40,7 +40,8 @@ def test_workspace_sizes():
     assert 0 < a < b
     assert a % 256 == 0
     assert S.socket_score_topk_workspace(0, 32, 8, 32768, 64, 8, 656) == 0
-    assert S.socket_score_topk_workspace(1, 32, 4, 32768, 64, 8, 656) == 0  # 8 heads per KV head
+    assert S.socket_score_topk_workspace(1, 32, 4, 32768, 64, 8, 656) > 0   # 8 heads per KV head
+    assert S.socket_score_topk_workspace(1, 130, 2, 32768, 64, 8, 656) == 0  # 65: too many
     assert S.socket_score_topk_workspace(1, 32, 8, 32768, 129, 8, 656) == 0
     assert S.socket_score_topk_workspace(1, 32, 8, 32768, 65, 10, 656) == 0
     # one workspace size for both ID widths (the stage entries take no P)
@@ -93,7 +94,9 @@ def test_score_argument_checks():
     assert _score(tau=float("nan")) == EINVAL
     assert _score(tau=float("inf")) == EINVAL
     assert _score(Hkv=5) == EINVAL        # 32 % 5
-    assert _score(Hkv=4) == EUNSUP        # 8 query heads per KV head
+    assert _score(Hq=130, Hkv=2) == EUNSUP  # 65 query heads per KV head (at most 64)
+    assert S.socket_score_topk_workspace(1, 64, 8, 1024, 64, 8, 32) > 0   # 8 per KV head
+    assert S.socket_score_topk_workspace(1, 24, 8, 1024, 64, 8, 32) > 0   # 3 per KV head
     assert _score(P=11) == EUNSUP
     assert _score(P=9, L=65) == EUNSUP
     assert _score(d=96) == EUNSUP
@@ -121,7 +124,8 @@ def test_dense_decode_argument_checks():
         return lib.socket_dense_decode(*a.values())
     assert call(lens=None) == EINVAL
     assert call(Hkv=5) == EINVAL
-    assert call(Hkv=4) == EUNSUP               # 8 query heads per KV head
+    assert call(Hq=130, Hkv=2) == EUNSUP       # 65 query heads per KV head (at most 64)
+    assert S.socket_dense_decode_workspace(1, 64, 8, 128, 32768) > 0   # 8 per KV head
     assert call(d=96) == EUNSUP
     assert call(scale=float("nan")) == EINVAL
     assert call(ws=FAKE + 8) == EINVAL
@@ -136,7 +140,8 @@ def test_hard_mode_argument_checks():
     assert S.socket_codes_bytes(1, 8, 1000, 4097, 1) == 0
     need = S.socket_hard_score_topk_workspace(1, 32, 8, 1024, 300, 2, 64)
     assert need > 0
-    assert S.socket_hard_score_topk_workspace(1, 32, 4, 1024, 300, 2, 64) == 0
+    assert S.socket_hard_score_topk_workspace(1, 32, 4, 1024, 300, 2, 64) > 0   # 8 heads per KV head
+    assert S.socket_hard_score_topk_workspace(1, 130, 2, 1024, 300, 2, 64) == 0  # 65: too many
     h = dict(K=FAKE, V=FAKE, dtype=1, B=1, Hkv=8, d=128, n_cap=1024, pos0=FAKE, count=16, W=FAKE,
              L=300, P=2, codes=FAKE, vnorm=FAKE, stream=None)
 

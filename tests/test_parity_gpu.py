@@ -169,6 +169,11 @@ SCORE_CASES = [
     dict(name="c2", n=3000, L=64, P=10, Hq=16, Hkv=8),
     dict(name="c2", n=2000, L=9, P=9, Hq=8, Hkv=2),
     dict(name="c2", n=2000, L=30, P=10, Hq=8, Hkv=2, tau=0.3),
+    # more than four query heads per KV head: passes of four (or two, or one)
+    dict(name="c2", n=3000, Hq=16, Hkv=2),          # 8 a KV head: two passes of four
+    dict(name="c2", n=2000, Hq=6, Hkv=2),           # 3: three passes of one
+    dict(name="c2", n=2500, L=60, P=10, Hq=16, Hkv=2),
+    dict(name="c4", n=(1000, 5000), B=3, Hq=24, Hkv=2, k=0.02),  # 12, ragged
 ]
 
 
@@ -472,6 +477,8 @@ HARD_CASES = [
     dict(case=dict(name="c4", n=(1000, 9000), B=3, L=300, P=2), sink=64, window=128),
     dict(case=dict(name="c4", n=(10, 20), B=4, Hq=8, Hkv=2, L=300, P=2, lens=[0, 1, 150, 900],
                    n_cap=1000, k=5), sink=16, window=16),
+    dict(case=dict(name="c2", n=3000, L=300, P=2, Hq=16, Hkv=2), sink=0, window=0),   # G = 8
+    dict(case=dict(name="c2", n=2000, L=64, P=4, Hq=6, Hkv=2), sink=8, window=8),    # G = 3
 ]
 
 
@@ -576,6 +583,8 @@ DENSE_CASES = [
     dict(name="c4", n=(1000, 9000), B=3),
     dict(name="c2", n=20000, Hq=8, Hkv=2),                      # 157 splits: eight-group merge
     dict(name="c2", n=20000, Hq=4, Hkv=1),                      # 313 splits: general merge
+    dict(name="c2", n=4500, Hq=16, Hkv=2),                      # 8 query heads a KV head
+    dict(name="c2", n=3000, Hq=6, Hkv=2),                       # 3
 ]
 
 
@@ -782,6 +791,9 @@ def test_run_twice_bitwise():
     (dict(name="c2", n=50000, Hq=8, Hkv=2), (0, 0)),
     (dict(name="c4", n=(1000, 3000), B=9, k=0.02), (16, 16)),
     (dict(name="c2", n=30000, Hq=8, Hkv=2, k=17000), (0, 0)),
+    # eight and twelve query heads per KV head
+    (dict(name="c2", n=6000, Hq=16, Hkv=2), (16, 16)),
+    (dict(name="c4", n=(1000, 4000), B=3, Hq=24, Hkv=2, k=0.02), (0, 0)),
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else f"sw{c}")
 def test_decode_step_matches_three_calls(case, sw):
     """socket_decode_step (append hashed inside the table kernel, attention
