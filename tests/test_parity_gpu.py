@@ -47,6 +47,7 @@ def sync():
     dict(name="c2", n=300, L=5, P=10, Hkv=2, Hq=2),    # MFMA, one table per word
     dict(name="c2", n=40, L=60, P=10),                 # few keys: generic, packed IDs
     dict(name="c2", n=300, L=5, P=9, Hkv=2, Hq=2),     # generic, one table per word
+    dict(name="c2", n=700, L=40, P=9, Hkv=2, Hq=4),    # generic, packed nine-bit IDs
     dict(name="c1", L=60, P=10),                       # fp32: generic
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_hash_parity(case):
@@ -174,6 +175,7 @@ SCORE_CASES = [
     dict(name="c2", n=2000, Hq=6, Hkv=2),           # 3: three passes of one
     dict(name="c2", n=2500, L=60, P=10, Hq=16, Hkv=2),
     dict(name="c4", n=(1000, 5000), B=3, Hq=24, Hkv=2, k=0.02),  # 12, ragged
+    dict(name="c2", n=2500, L=45, P=9, Hq=8, Hkv=2),    # packed nine-bit IDs
 ]
 
 
@@ -779,6 +781,7 @@ def test_run_twice_bitwise():
     (dict(name="c4", n=(1000, 9000), B=3, k=0.02), (64, 128)),
     (dict(name="c4", n=(10, 20), B=4, Hq=8, Hkv=2, lens=[0, 1, 300, 999], n_cap=1000, k=5), (8, 8)),
     (dict(name="c2", n=3000, L=60, P=10, Hq=16, Hkv=8), (0, 0)),
+    (dict(name="c2", n=2000, L=40, P=9, Hq=8, Hkv=2), (8, 8)),   # packed, generic append
     (dict(name="c1"), (0, 16)),
     # longer rows: the scan + resolve top-k
     (dict(name="c2", n=20000), (0, 0)),
