@@ -206,7 +206,7 @@ template <typename T>
 __device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int TL, int nab,
                              int rows, const AppendKey& ak);
 
-template <typename T, int G>
+template <typename T, int G, bool TWO>
 __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const T* __restrict__ q, const T* __restrict__ W, int Hq, int Hkv, int L, int P, float tau,
     int TL, int NF, int NS, int HE, int FULL, int img_floats, float* __restrict__ img,
@@ -226,9 +226,15 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   const int bg0 = b * Hq + h * G;
   const int tid = threadIdx.x;
   float* im = img + (int64_t)bh * img_floats;
-  __shared__ float qf[G][kHead];         // the queries (exact in float32)
+  // the queries (exact in float32), row 2g + h = half h of head g, rows
+  // padded to 68 floats so the 2G rows the lanes of a wave read at one time
+  // sit in different bank groups
+  constexpr int kQRow = kHead / 2 + 4;
+  __shared__ float qf[2 * G][kQRow];
   __shared__ double sig[kTabThreads][2];  // [(m*P + plane)*G + g][bit] = sigmoid(+-2u/tau)
-  __shared__ double half[8][G][64];       // [m][g][hf*HE + c]
+  // [(m*G + g)*2HE + hf*HE + c]: TL*G*2*HE <= 256*G entries (TL <= 8 with
+  // HE = 16, TL <= 4 with HE = 32)
+  __shared__ double half[256 * G];
 
   constexpr int kHistShare = G * kHistBins / 16;
   for (int i = tid; i < kHistShare; i += kTabThreads)
@@ -239,35 +245,42 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   }
   for (int i = tid; i < G * kHead; i += kTabThreads) {
     const int64_t src = (int64_t)(bg0 + i / kHead) * kHead + i % kHead;
-    if constexpr (sizeof(T) == 2) qf[i / kHead][i % kHead] = __uint_as_float((uint32_t)q[src] << 16);
-    else qf[i / kHead][i % kHead] = q[src];
+    float* dst = &qf[2 * (i / kHead) + (i % kHead) / (kHead / 2)][(i % kHead) % (kHead / 2)];
+    if constexpr (sizeof(T) == 2) *dst = __uint_as_float((uint32_t)q[src] << 16);
+    else *dst = q[src];
   }
-  // projections: two threads (lanes 2p, 2p+1) per (table member m, plane
-  // pl, head g), each taking half of the 128-element dot product
-  constexpr int NV = kHead * (int)sizeof(T) / 32;  // 16-byte vectors per half row
-  const int nproj = TL * P * G;
-  const int hv = tid & 1;
-  uint4 raw[2][NV];
+  // projections: eight threads per W row (table member m, plane pl); thread
+  // s of the eight takes elements 16s .. 16s+15 of the row's dot products
+  // with all G queries, so each row is read once, and three butterfly steps
+  // add the eight partial sums
+  constexpr int EPT = kHead / 8;                  // elements a thread
+  constexpr int NV = EPT * (int)sizeof(T) / 16;   // 16-byte vectors a thread
+  const int nrows = TL * P;                       // TWO: more than kTabThreads / 8
+  const int s8 = tid & 7;
+  constexpr int NIT = TWO ? 2 : 1;  // rounds of rows
+  uint4 raw[NIT][NV];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int pr = (tid >> 1) + it * (kTabThreads / 2);
-    const int m = pr / (P * G), pl = (pr / G) % P;
-    const int l = j * TL + m;
-    if (pr < nproj && l < L) {
-      const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + pl) * kHead) + hv * NV;
+  for (int it = 0; it < NIT; ++it) {
+    const int row = (tid >> 3) + it * (kTabThreads / 8);
+    const int l = j * TL + row / P;
+    if (row < nrows && l < L) {
+      const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + row % P) * kHead +
+                                                       s8 * EPT);
 #pragma unroll
       for (int v = 0; v < NV; ++v) raw[it][v] = wr[v];
     }
   }
-  __syncthreads();
+  lds_barrier();  // the queries (the W loads and histogram clears stay in flight)
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int pr = (tid >> 1) + it * (kTabThreads / 2);
-    if (it * (kTabThreads / 2) >= nproj) break;  // uniform
-    const int m = pr / (P * G), pl = (pr / G) % P, g = pr % G;
-    const int l = j * TL + m;
-    const bool live = pr < nproj && l < L;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int it = 0; it < NIT; ++it) {
+    const int row = (tid >> 3) + it * (kTabThreads / 8);
+    if (it * (kTabThreads / 8) >= nrows) break;  // uniform
+    const int l = j * TL + row / P;
+    const bool live = row < nrows && l < L;
+    const float* qrow = &qf[s8 / 4][(s8 % 4) * EPT];  // this slice of head 0's query
+    double acc[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = acc[g][2] = acc[g][3] = 0.0;
     if (live) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -281,24 +294,35 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
           f[2] = __uint_as_float(raw[it][v].z); f[3] = __uint_as_float(raw[it][v].w);
           cnt = 4;
         }
-        const int base = hv * (kHead / 2) + v * cnt;
 #pragma unroll
         for (int e = 0; e < cnt; ++e)
-          acc[e & 3] = fma((double)f[e], (double)qf[g][base + e], acc[e & 3]);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            acc[g][e & 3] = fma((double)f[e], (double)qrow[2 * g * kQRow + v * cnt + e],
+                                acc[g][e & 3]);
       }
     }
-    double u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    u += __shfl_xor(u, 1, 64);  // the partner lane's half
-    if (pr < nproj && hv == 0) {
+    // every lane of the eight gets every head's sum; lane g of them takes
+    // head g's sigmoid, so the G exponentials run side by side
+    double ug = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      double u = (acc[g][0] + acc[g][1]) + (acc[g][2] + acc[g][3]);
+      u += __shfl_xor(u, 1, 64);
+      u += __shfl_xor(u, 2, 64);
+      u += __shfl_xor(u, 4, 64);
+      if (s8 == g) ug = u;
+    }
+    if (row < nrows && s8 < G) {
       // sigmoid(x) and sigmoid(-x) from one exponential of -|x|
-      const double x = 2.0 * u / (double)tau;
+      const double x = 2.0 * ug / (double)tau;
       const double e = exp(-fabs(x));
       const double big = 1.0 / (1.0 + e), small = e * big;
-      sig[pr][1] = x >= 0.0 ? big : small;  // bit set: corner sign +1
-      sig[pr][0] = x >= 0.0 ? small : big;  // bit clear: corner sign -1
+      sig[row * G + s8][1] = x >= 0.0 ? big : small;  // bit set: corner sign +1
+      sig[row * G + s8][0] = x >= 0.0 ? small : big;  // bit clear: corner sign -1
     }
   }
-  __syncthreads();
+  lds_barrier();  // the sigmoids (global stores and loads stay in flight)
   // halves: planes 0 .. plo-1 and plo .. P-1, HE entries each
   const int plo = HE == 32 ? 5 : (P < 4 ? P : 4);
   const int phi = P - plo;
@@ -308,13 +332,23 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const int nb = hf ? phi : plo;
     double prod = 0.0;
     if (c < (1 << nb) && j * TL + mm < L) {
-      prod = 1.0;
+      // at most 5 planes a half: all of its sigmoids requested at once (rows
+      // past nb, clamped inside sig, are not multiplied in)
       const int p0 = hf ? plo : 0;
-      for (int jj = 0; jj < nb; ++jj) prod *= sig[(mm * P + p0 + jj) * G + gg][(c >> jj) & 1];
+      double sv[5];
+#pragma unroll
+      for (int jj = 0; jj < 5; ++jj) {
+        const int row = (mm * P + p0 + jj) * G + gg;
+        sv[jj] = sig[row < kTabThreads ? row : kTabThreads - 1][(c >> jj) & 1];
+      }
+      prod = 1.0;
+#pragma unroll
+      for (int jj = 0; jj < 5; ++jj)
+        if (jj < nb) prod *= sv[jj];
     }
-    half[mm][gg][r] = prod;
+    half[(mm * G + gg) * 2 * HE + r] = prod;
   }
-  __syncthreads();
+  lds_barrier();  // the halves
   // full tables, table-major: slot (m*256 + e)*16 + j for entries e < 2^P
   const int nent = 1 << P;
   const int lomask = (1 << plo) - 1;
@@ -323,7 +357,8 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     float v[G];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg)
-      v[gg] = (float)(half[mm][gg][e & lomask] * half[mm][gg][HE + (e >> plo)]);
+      v[gg] = (float)(half[(mm * G + gg) * 2 * HE + (e & lomask)] *
+                      half[(mm * G + gg) * 2 * HE + HE + (e >> plo)]);
     store_slot<G>(im + ((int64_t)(mm * 256 + e) * 16 + j) * G, v);
   }
   // factored tables: slot FULL/G + ((hc*NS + m - NF)*16 + j), hc = hf*HE + c
@@ -331,7 +366,7 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
     const int hc = i / NS, mm = NF + i % NS;
     float v[G];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) v[gg] = (float)half[mm][gg][hc];
+    for (int gg = 0; gg < G; ++gg) v[gg] = (float)half[(mm * G + gg) * 2 * HE + hc];
     store_slot<G>(im + FULL + ((int64_t)i * 16 + j) * G, v);
   }
 }
@@ -354,13 +389,16 @@ __device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int
   const int word = w0 + tid / WP, qq = tid % WP;
   const int m = qq / P, pl = qq % P, l = word * TL + m;
   const bool live = tid < WPB * WP && word < 16 && l < L;
-  // the plane's W row first: it does not depend on the key position
+  // the first half of the plane's W row first: it does not depend on the key
+  // position (the second half comes after it is used, so that the append
+  // path needs no more registers than the table blocks of the same launch)
   constexpr int NV = kHead * (int)sizeof(T) / 16;
-  uint4 wv[NV];
+  constexpr int NH = NV / 2;
+  const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(live ? l * P + pl : 0) * kHead);
+  uint4 wv[NH];
   if (live) {
-    const uint4* wr = reinterpret_cast<const uint4*>(W + (int64_t)(l * P + pl) * kHead);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) wv[v] = wr[v];
+    for (int v = 0; v < NH; ++v) wv[v] = wr[v];
   }
   const int64_t pos = (int64_t)ak.lens[b] - 1;
   if (pos < 0 || pos >= ak.n_cap) return;  // uniform: no key to append
@@ -389,19 +427,26 @@ __device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int
   float z = 0.f;
   if (live) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      float f[8];
-      int cnt;
-      if constexpr (sizeof(T) == 2) {
-        unpack_bf16x8(wv[v], f);
-        cnt = 8;
-      } else {
-        f[0] = __uint_as_float(wv[v].x); f[1] = __uint_as_float(wv[v].y);
-        f[2] = __uint_as_float(wv[v].z); f[3] = __uint_as_float(wv[v].w);
-        cnt = 4;
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1) {
+#pragma unroll
+        for (int v = 0; v < NH; ++v) wv[v] = wr[NH + v];
       }
 #pragma unroll
-      for (int e = 0; e < cnt; ++e) z = fmaf(f[e], kf[v * cnt + e], z);
+      for (int v = 0; v < NH; ++v) {
+        float f[8];
+        int cnt;
+        if constexpr (sizeof(T) == 2) {
+          unpack_bf16x8(wv[v], f);
+          cnt = 8;
+        } else {
+          f[0] = __uint_as_float(wv[v].x); f[1] = __uint_as_float(wv[v].y);
+          f[2] = __uint_as_float(wv[v].z); f[3] = __uint_as_float(wv[v].w);
+          cnt = 4;
+        }
+#pragma unroll
+        for (int e = 0; e < cnt; ++e) z = fmaf(f[e], kf[(hh * NH + v) * cnt + e], z);
+      }
     }
   }
   kbit[tid] = live && z > 0.f ? 1u : 0u;  // z == 0 gives bit 0
@@ -1800,13 +1845,20 @@ hipError_t launch_soft_tables(const void* q, int dtype, int B, int Hq, int Hkv, 
   const int TLw = ids_tables_per_word(L);
   const int nab = ak.K ? (16 + kTabThreads / (TLw * P) - 1) / (kTabThreads / (TLw * P)) : 0;
   const unsigned grid = (unsigned)(rows * 16 + B * Hkv * nab);
+  const bool two = im.TL * P > kTabThreads / 8;  // W rows past one round of eight threads each
   auto go = [&](auto tag, auto gtag) {
     using T = decltype(tag);
     constexpr int GG = decltype(gtag)::value;
-    soft_tables_kernel<T, GG><<<grid, kTabThreads, 0, s>>>(
-        static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
-        im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum, ak, rows,
-        nab, sub);
+    if (two)
+      soft_tables_kernel<T, GG, true><<<grid, kTabThreads, 0, s>>>(
+          static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
+          im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum, ak, rows,
+          nab, sub);
+    else
+      soft_tables_kernel<T, GG, false><<<grid, kTabThreads, 0, s>>>(
+          static_cast<const T*>(q), static_cast<const T*>(W), Hq, Hkv, L, P, tau, im.TL, im.NF,
+          im.NS, im.HE, im.full, ws.img_floats, ws.img, ws.hist, ws.counters, ws.usum, ak, rows,
+          nab, sub);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
