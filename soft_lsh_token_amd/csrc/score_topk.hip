@@ -326,9 +326,10 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   // halves: planes 0 .. plo-1 and plo .. P-1, HE entries each
   const int plo = HE == 32 ? 5 : (P < 4 ? P : 4);
   const int phi = P - plo;
+  const int hs = HE == 32 ? 5 : 4;  // log2 HE (16 or 32): shifts, not divisions
   for (int i = tid; i < TL * G * 2 * HE; i += kTabThreads) {
-    const int mm = i / (G * 2 * HE), gg = (i / (2 * HE)) % G, r = i % (2 * HE);
-    const int hf = r / HE, c = r % HE;
+    const int pair = i >> (hs + 1), mm = pair / G, gg = pair % G, r = i & (2 * HE - 1);
+    const int hf = r >> hs, c = r & (HE - 1);
     const int nb = hf ? phi : plo;
     double prod = 0.0;
     if (c < (1 << nb) && j * TL + mm < L) {
@@ -352,22 +353,25 @@ __global__ __launch_bounds__(kTabThreads) void soft_tables_kernel(
   // full tables, table-major: slot (m*256 + e)*16 + j for entries e < 2^P
   const int nent = 1 << P;
   const int lomask = (1 << plo) - 1;
-  for (int i = tid; i < NF * nent; i += kTabThreads) {
-    const int e = i / NF, mm = i % NF;
-    float v[G];
+  for (int mm = 0; mm < NF; ++mm) {
+    for (int e = tid; e < nent; e += kTabThreads) {
+      float v[G];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg)
-      v[gg] = (float)(half[(mm * G + gg) * 2 * HE + (e & lomask)] *
-                      half[(mm * G + gg) * 2 * HE + HE + (e >> plo)]);
-    store_slot<G>(im + ((int64_t)(mm * 256 + e) * 16 + j) * G, v);
+      for (int gg = 0; gg < G; ++gg)
+        v[gg] = (float)(half[(mm * G + gg) * 2 * HE + (e & lomask)] *
+                        half[(mm * G + gg) * 2 * HE + HE + (e >> plo)]);
+      store_slot<G>(im + ((int64_t)(mm * 256 + e) * 16 + j) * G, v);
+    }
   }
   // factored tables: slot FULL/G + ((hc*NS + m - NF)*16 + j), hc = hf*HE + c
-  for (int i = tid; i < 2 * HE * NS; i += kTabThreads) {
-    const int hc = i / NS, mm = NF + i % NS;
-    float v[G];
+  for (int ms = 0; ms < NS; ++ms) {
+    for (int hc = tid; hc < 2 * HE; hc += kTabThreads) {
+      const int mm = NF + ms, i = hc * NS + ms;
+      float v[G];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) v[gg] = (float)half[(mm * G + gg) * 2 * HE + hc];
-    store_slot<G>(im + FULL + ((int64_t)i * 16 + j) * G, v);
+      for (int gg = 0; gg < G; ++gg) v[gg] = (float)half[(mm * G + gg) * 2 * HE + hc];
+      store_slot<G>(im + FULL + ((int64_t)i * 16 + j) * G, v);
+    }
   }
 }
 
