@@ -536,6 +536,10 @@ __device__ __forceinline__ uint32_t word_cell(uint2 w) {
 }
 
 constexpr int kPrefetch = 1;  // 64-key groups of IDs each wave keeps in flight
+// The fixed cost of a scorer row segment (its image load, barrier and
+// histogram merge, about 4.7 us) in 64-key groups of a 512-thread block
+// (about 0.32 us each), for splitting ragged batches.
+constexpr int kSegGroups = 15;
 
 // The lookups of one round: NF full-table slots and NS lo/hi half slots.
 template <int NF, int NS, int G>
@@ -841,11 +845,19 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
     return;
   }
   // Ragged lengths: share lid of the row-ordered valid groups, row by row.
-  // The totals and offsets are wave-uniform and kept in scalar registers.
+  // Each non-empty row counts kSegGroups groups more than it holds (a row
+  // segment's image load and histogram merge cost about that much), so a
+  // share that spans row starts takes fewer keys; a share inside a row's
+  // extra groups scores nothing there.  The totals and offsets are
+  // wave-uniform and kept in scalar registers.
+  auto padded = [&](int b) {  // a row's groups plus its fixed cost, 0 for an empty row
+    const uint32_t ng = (uint32_t)((seq_len(b) + 63) >> 6);
+    return ng ? ng + (uint32_t)kSegGroups : 0u;
+  };
   uint32_t total = 0u;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + lane;
-    const uint32_t ng = b < B ? (uint32_t)((seq_len(b) + 63) >> 6) : 0u;
+    const uint32_t ng = b < B ? padded(b) : 0u;
     total += (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(wave_incl_scan(ng), 63, 64)) *
              (uint32_t)Hkv;
   }
@@ -854,12 +866,12 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
   uint32_t G0 = (uint32_t)lid * per;
   const uint32_t G1 = G0 + per < total ? G0 + per : total;
   int bcur = 0;
-  uint32_t base = 0u;  // groups of the sequences before bcur (all KV heads)
+  uint32_t base = 0u;  // padded groups of the sequences before bcur (all KV heads)
   while (G0 < G1) {
-    // the sequence whose groups hold G0, by a wave scan over 64 sequences at a time
+    // the sequence whose padded groups hold G0, by a wave scan over 64 sequences at a time
     for (;;) {
       const int b = bcur + lane;
-      const uint32_t ng = b < B ? (uint32_t)((seq_len(b) + 63) >> 6) * (uint32_t)Hkv : 0u;
+      const uint32_t ng = b < B ? padded(b) * (uint32_t)Hkv : 0u;
       const uint32_t inc = wave_incl_scan(ng);
       const uint64_t past = __ballot(b < B && base + inc <= G0);  // sequences ending by G0
       const int skip = __popcll(past);  // a prefix of the lanes
@@ -871,12 +883,15 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
       base += (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(inc, 63, 64));
       bcur += 64;
     }
-    const uint32_t ngb = (uint32_t)((seq_len(bcur) + 63) >> 6);
-    const uint32_t h = (G0 - base) / ngb;
-    const uint32_t row0 = base + h * ngb;  // first group of KV row (bcur, h)
-    const uint32_t row1 = row0 + ngb;
+    const uint32_t ngp = padded(bcur);  // > 0: G0 lies in this sequence's rows
+    const uint32_t h = (G0 - base) / ngp;
+    const uint32_t row0 = base + h * ngp;  // padded start of KV row (bcur, h)
+    const uint32_t row1 = row0 + ngp;
     const uint32_t s1 = G1 < row1 ? G1 : row1;
-    segment(bcur * Hkv + (int)h, (int64_t)(G0 - row0), (int64_t)(s1 - row0));
+    const uint32_t k = (uint32_t)kSegGroups;  // the row's groups start after its fixed cost
+    const uint32_t a = G0 - row0 > k ? G0 - row0 - k : 0u;
+    const uint32_t e = s1 - row0 > k ? s1 - row0 - k : 0u;
+    if (a < e) segment(bcur * Hkv + (int)h, (int64_t)a, (int64_t)e);
     G0 = s1;
   }
 }
