@@ -797,20 +797,20 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();  // the LDS histogram is complete (the score stores stay in flight)
     for (int i = tid; i < G * kHistBins; i += kScoreThreads) {
       const uint32_t v = lhist[i];
       if (v) atomicAdd(&hist[(int64_t)(bg0 + i / kHistBins) * kHistBins + (i % kHistBins)], v);
     }
     if (usum) {  // per-head sums of the soft counts, for the sampling estimator
-      __syncthreads();  // the merge above has read the histogram: reuse its LDS
+      lds_barrier();  // the merge above has read the histogram: reuse its LDS
       float* red = reinterpret_cast<float*>(lhist);  // [kScoreWaves][G]
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
         const float t = wave_sum(us[gg]);
         if (lane == 0) red[wave * G + gg] = t;
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < G) {
         float t = 0.f;
 #pragma unroll
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(kScoreThreads) void scorer_kernel(
         atomicAdd(&usum[bg0 + tid], t);
       }
     }
-    __syncthreads();  // a following segment reuses the image and histogram LDS
+    lds_barrier();  // a following segment reuses the image and histogram LDS
   };
 
   // Whether the sequence lengths differ (in groups), the same in every wave:
@@ -928,14 +928,15 @@ __device__ __forceinline__ uint32_t spread4(uint32_t b) {
   return b;
 }
 
-// Block-wide inclusive scan of one value per thread (NT threads).
+// Block-wide inclusive scan of one value per thread (NT threads).  Its
+// barriers order LDS only: global loads and stores in flight stay in flight.
 template <int NT>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_incl_scan(v);
-  __syncthreads();
+  lds_barrier();
   if (lane == 63) wsum[wave] = v;
-  __syncthreads();
+  lds_barrier();
   uint32_t off = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) off += w < wave ? wsum[w] : 0u;
@@ -1016,9 +1017,9 @@ __device__ Boundary boundary_of(const HistSlice<NT>& h, uint32_t k, uint32_t* ws
     if (bin >= 0 && prev < k && k <= prev + h.c[i]) *sh = Boundary{(uint32_t)bin, prev};
     prev += h.c[i];
   }
-  __syncthreads();
+  lds_barrier();  // LDS only: the caller's bulk loads stay in flight
   const Boundary r = *sh;
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -1441,9 +1442,9 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
       }
     }
     if (tid == NT - 1) sm.seg_total = incw;
-    __syncthreads();
+    lds_barrier();  // the index stores stay in flight
     written += sm.seg_total;
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -1787,9 +1788,9 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
       }
     }
     if (tid == NT - 1) seg_total = inc;
-    __syncthreads();
+    lds_barrier();  // the index stores stay in flight
     written += seg_total;
-    __syncthreads();
+    lds_barrier();
   }
   for (int64_t t = z.total + tid; t < k_max; t += NT) out[t] = -1;
   if constexpr (ATT) {
