@@ -60,11 +60,18 @@ __global__ __launch_bounds__(kDrawThreads) void estimate_draw_kernel(
   const float* gs = gsum + (int64_t)bg * gstride;
   const float* srow = scores + (int64_t)bg * sstride;
 
-  // run totals in group order, then their exclusive scan
+  // run totals in group order (four group sums requested at a time), then
+  // their exclusive scan
   const int64_t g0 = (int64_t)tid * R;
   const int64_t g1 = g0 + R < G ? g0 + R : G;
   float tot = 0.f;
-  for (int64_t g = g0; g < g1; ++g) tot += gs[g];
+  for (int64_t g = g0; g < g1; g += 4) {
+    float x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = gs[g + q < g1 ? g + q : g1 - 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot = g + q < g1 ? tot + x[q] : tot;
+  }
   float inc = tot;
   for (int o = 1; o < 64; o <<= 1) {
     const float y = __shfl_up(inc, o, 64);
@@ -107,13 +114,19 @@ __global__ __launch_bounds__(kDrawThreads) void estimate_draw_kernel(
     const int64_t r1 = r0 + R < G ? r0 + R : G;
     float acc = rstart[lo];
     int64_t g = r1 - 1;  // rounding past the run's end: its last group
-    for (int64_t x = r0; x < r1; ++x) {
-      const float gv = gs[x];
-      if (acc + gv > t) {
-        g = x;
-        break;
+    bool found = false;
+    for (int64_t x0 = r0; x0 < r1 && !found; x0 += 4) {  // four group sums a step
+      float gv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gv[q] = gs[x0 + q < r1 ? x0 + q : r1 - 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = !found && x0 + q < r1;
+        const bool hit = ok && acc + gv[q] > t;
+        g = hit ? x0 + q : g;
+        acc = ok && !hit ? acc + gv[q] : acc;
+        found = found || hit;
       }
-      acc += gv;
     }
     // the group's keys in order
     const int64_t k0 = g * 64;
@@ -125,19 +138,21 @@ __global__ __launch_bounds__(kDrawThreads) void estimate_draw_kernel(
       v[4 * q] = __uint_as_float(w4.x); v[4 * q + 1] = __uint_as_float(w4.y);
       v[4 * q + 2] = __uint_as_float(w4.z); v[4 * q + 3] = __uint_as_float(w4.w);
     }
-    int64_t last = -1;
-    bool done = false;
+    // branch-free: the running sum over the group's valid keys in key order;
+    // the first key with mass whose running sum exceeds t, and the last key
+    // with mass
+    const int lim = n - k0 < 64 ? (int)(n - k0) : 64;
+    int first = -1, lastm = -1;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
-      if (!done && k0 + i < n) {
-        if (v[i] > 0.f) last = k0 + i;
-        acc += v[i];
-        if (acc > t && v[i] > 0.f) {
-          pick = (int32_t)(k0 + i);
-          done = true;
-        }
-      }
+      const float vi = i < lim ? v[i] : 0.f;
+      acc += vi;
+      const bool mass = vi > 0.f;
+      lastm = mass ? i : lastm;
+      first = first < 0 && mass && acc > t ? i : first;
     }
+    if (first >= 0) pick = (int32_t)(k0 + first);
+    const int64_t last = lastm >= 0 ? k0 + lastm : -1;
     // rounding between the sums and the walk: the group's last key with mass,
     // else the nearest key with mass before the group, else after it
     if (pick < 0) pick = (int32_t)last;
