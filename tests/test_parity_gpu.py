@@ -176,6 +176,10 @@ SCORE_CASES = [
     dict(name="c2", n=2500, L=60, P=10, Hq=16, Hkv=2),
     dict(name="c4", n=(1000, 5000), B=3, Hq=24, Hkv=2, k=0.02),  # 12, ragged
     dict(name="c2", n=2500, L=45, P=9, Hq=8, Hkv=2),    # packed nine-bit IDs
+    # many short and empty rows: ragged shares that start or lie inside a row's fixed cost
+    dict(name="c4", n=(10, 20), B=24, Hq=8, Hkv=2, n_cap=3000, k=0.02,
+         lens=[0, 1, 64, 65, 127, 128, 129, 300, 1000, 0, 2, 3000, 17, 640, 641, 960, 5, 2047,
+               2048, 2049, 1, 64, 700, 2999]),
 ]
 
 
