@@ -1313,20 +1313,14 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   const int tid = threadIdx.x;
   const int64_t n = z.n, k = z.k;
 
-  // every independent load at once: candidate count, the first kCandCap
-  // candidates (whatever their count), this thread's first bitmap block,
-  // its histogram bin (inside find_boundary)
+  // every independent load at once: candidate count, the first NT
+  // candidates (one a thread, whatever their count), this thread's first
+  // bitmap block, its histogram bin (inside find_boundary)
   const HistSlice<NT> hs = load_hist_slice<NT>(hist + (int64_t)bg * kHistBins);
   const uint2* gc = cand + (int64_t)bg * n_cap;
   const uint32_t* bm = bitmap + (int64_t)bg * words;
   const uint32_t Cg = counters[bg];
-  uint2 cv[(kCandCap / NT)];
-#pragma unroll
-  for (int i = 0; i < (kCandCap / NT); ++i) {
-    int64_t ci = (int64_t)i * NT + tid;
-    if (ci >= n_cap) ci = n_cap - 1;
-    cv[i] = gc[ci];
-  }
+  const uint2 cv = gc[(int64_t)tid < n_cap ? (int64_t)tid : n_cap - 1];
   const int64_t nblocks = (n + 255) >> 8;
   const int64_t bl0 = tid < nblocks ? tid : 0;
   const uint4 bw0 = reinterpret_cast<const uint4*>(bm)[bl0 * 2];
@@ -1335,11 +1329,9 @@ __device__ __forceinline__ void resolve_head(int bg, int64_t n_cap, const SelSiz
   const uint32_t C = Cg < (uint32_t)n ? Cg : (uint32_t)n;
   const bool in_lds = C <= (uint32_t)kCandCap;
   if (in_lds) {
-#pragma unroll
-    for (int i = 0; i < (kCandCap / NT); ++i) {
-      const uint32_t ci = (uint32_t)(i * NT + tid);
-      if (ci < C) sm.lcand[ci] = cv[i];
-    }
+    if ((uint32_t)tid < C) sm.lcand[tid] = cv;
+    // more than NT candidates (rare): the rest in a second round trip
+    for (uint32_t ci = (uint32_t)(NT + tid); ci < C; ci += NT) sm.lcand[ci] = gc[ci];
   }
   // the first segment's bitmap blocks go to LDS now, while their loads are
   // certainly in (the radix passes below do not touch lbm)

@@ -281,6 +281,27 @@ def test_topk_ties_lower_index_wins(n):
         assert (idx[0, g, 100:] == -1).all()
 
 
+@pytest.mark.parametrize("tied", [900, 3000, 6000])
+def test_topk_resolve_tied_block(tied):
+    """Rows of 45000 keys (scan + resolve) where a block of `tied` keys shares
+    the top score: all of them are boundary candidates of one bin, up to one
+    per resolve thread or past that (the rest loaded in a second round trip),
+    and the lower indices win."""
+    n, k, start = 45000, 100, 20000
+    w = make_workload("c2", n=n, Hq=8, Hkv=2, k=k)
+    d = GC.upload(w)
+    ids = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
+    vn = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+    vn[:, 1, start:start + tied] = 2.0
+    idx, _ = GC.gpu_score_topk(w, d, ids, vn)
+    sync()
+    idx = idx.cpu().numpy()
+    for g in range(w.Hq):
+        h = g // (w.Hq // w.Hkv)
+        expect = np.arange(k) if h == 0 else np.arange(start, start + k)
+        assert idx[0, g, :k].tolist() == expect.tolist(), g
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,n", [(4, 32, 8, 40000), (1, 264, 66, 140000)],
                          ids=["4x32-heads-40000", "264-heads-140000"])
 def test_topk_ties_large_batches(B, Hq, Hkv, n):
