@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--only", default=None, metavar="NAME",
                    help="run a few launches of one kernel group and exit (counter runs): "
                         "prefill128k, prefill128k-fused, norms128k, stage32k, stage128k, step32k")
+    p.add_argument("--crossover", action="store_true",
+                   help="only time the decode step against the dense decode at 32K-128K keys "
+                        "(GQA 32/8, L = 64, P = 8, k = 2%%) and print one JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="also run one device-to-device copy of this many MiB (a known-size "
                         "reference kernel for hardware byte counters)")
@@ -649,6 +652,30 @@ def cpu_baseline(seconds):
                 decode_loop_128k=c5)
 
 
+def crossover(args, lib, torch, S):
+    """Decode step (socket_decode_step) against the dense decode of the same
+    32/8 GQA shape as n grows: GPU us per call over batches of calls on 8
+    replicas (cold caches), and the speedup of the sparse step."""
+    rows = []
+    for n in (32768, 49152, 65536, 98304, 131072):
+        case = Case("c2", 8, lib, torch, S, n=n, k=0.02)
+        for r in range(case.replicas):
+            case.prefill(r)
+        torch.cuda.synchronize()
+        timed_steps(case, torch, 0, 40)  # warm-up: the first steps after a prefill run slow
+        step_us, _ = gpu_batch_us(torch, lambda i: case.step(i % case.replicas), 100)
+        dense_decode(case, torch, case.replicas)
+        dense = dense_decode(case, torch, 2 * case.replicas)
+        row = dict(n=n, k=case.k, step_us=step_us, dense_us=dense["us"],
+                   speedup=dense["us"] / step_us)
+        log(f"[bench] crossover {row}")
+        rows.append(row)
+        case.free()
+        del case
+        torch.cuda.empty_cache()
+    print(json.dumps({"crossover": rows}), flush=True)
+
+
 def only(args, lib, torch, S):
     """A few launches of one kernel group, for counter runs; prints what ran."""
     name = args.only
@@ -698,6 +725,9 @@ def main():
         del src, dst
     if args.only:
         only(args, lib, torch, S)
+        return
+    if args.crossover:
+        crossover(args, lib, torch, S)
         return
 
     # ---- 32K: the timed step, its stages, the selection stage's roofline
