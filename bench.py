@@ -662,7 +662,7 @@ def crossover(args, lib, torch, S):
         for r in range(case.replicas):
             case.prefill(r)
         torch.cuda.synchronize()
-        timed_steps(case, torch, 0, 40)  # warm-up: the first steps after a prefill run slow
+        timed_steps(case, torch, 40, 40)  # warm-up: the first steps after a prefill run slow
         step_us, _ = gpu_batch_us(torch, lambda i: case.step(i % case.replicas), 100)
         dense_decode(case, torch, case.replicas)
         dense = dense_decode(case, torch, 2 * case.replicas)
