@@ -31,7 +31,7 @@ the CPU oracle on bounded samples.
 
 `--only NAME` runs a few launches of one kernel group and exits (for
 rocprofv3 counter runs): prefill128k (IDs only), prefill128k-fused,
-norms128k, stage32k, stage128k, step32k.
+norms128k, stage32k, stage128k, step32k, step128k.
 """
 from __future__ import annotations
 
@@ -78,7 +78,7 @@ def parse():
                    help="decode steps of the 128K prefill + decode loop")
     p.add_argument("--only", default=None, metavar="NAME",
                    help="run a few launches of one kernel group and exit (counter runs): "
-                        "prefill128k, prefill128k-fused, norms128k, stage32k, stage128k, step32k")
+                        "prefill128k, prefill128k-fused, norms128k, stage32k, stage128k, step32k, step128k")
     p.add_argument("--crossover", action="store_true",
                    help="only time the decode step against the dense decode at 32K-128K keys "
                         "(GQA 32/8, L = 64, P = 8, k = 2%%) and print one JSON line")
@@ -685,13 +685,13 @@ def only(args, lib, torch, S):
         mode = {"prefill128k": "ids", "prefill128k-fused": "fused", "norms128k": "norms"}[name]
         for i in range(2 * reps):
             case.prefill(i % reps, mode)
-    elif name in ("stage32k", "stage128k", "step32k"):
-        case = Case("c2" if name != "stage128k" else "c3", reps, lib, torch, S)
+    elif name in ("stage32k", "stage128k", "step32k", "step128k"):
+        case = Case("c3" if name.endswith("128k") else "c2", reps, lib, torch, S)
         for r in range(reps):
             case.prefill(r)
         torch.cuda.synchronize()
         for i in range(4 * reps):
-            if name == "step32k":
+            if name.startswith("step"):
                 case.step(i % reps)
             else:
                 case.score_topk(i % reps)

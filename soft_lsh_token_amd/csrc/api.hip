@@ -11,6 +11,7 @@ namespace {
 constexpr int kMaxL = 128;       // 16 ID words of at most 8 tables each
 constexpr int kMaxScoreL = 128;
 constexpr int kMaxKmax = 1 << 16;  // 1024 attention splits of 64 keys
+constexpr int kMaxRangeSplits = 1024;  // key ranges a row at most (the merge's limit)
 constexpr int kMaxCodeBits = 4096;  // hard-LSH mode: L * P
 constexpr int kMaxGroup = 64;       // query heads per KV head
 constexpr int kMaxDraws = 8192;     // sampling estimator: draws per query head
@@ -176,7 +177,10 @@ static size_t step_ws(int B, int Hq, int Hkv, int64_t n_cap, int L, int k_max, S
                       DecodeWs* dw, void* base) {
   const size_t a = (score_ws_layout(B, Hq, Hkv, n_cap, L, nullptr, nullptr) + 255) & ~(size_t)255;
   if (base) score_ws_layout(B, Hq, Hkv, n_cap, L, sw, base);
-  const size_t d = decode_ws_layout(B, Hq, k_max, dw, base ? static_cast<char*>(base) + a : nullptr);
+  // room for one partial per key range (the selection + attention by range)
+  const int rs = range_splits(n_cap);
+  const size_t d = decode_ws_layout(B, Hq, k_max, dw, base ? static_cast<char*>(base) + a : nullptr,
+                                    rs <= kMaxRangeSplits ? rs : 0);
   return a + d;
 }
 
@@ -225,7 +229,8 @@ int socket_decode_step(const void* q, const void* K, const void* V, int dtype, i
   const AttendSpec att{q, K, V, dtype, Hkv, scale, out};
   bool attended = false;
   if (e == hipSuccess)
-    e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s, &att, &attended);
+    e = launch_topk(B, Hq, sc, lens, n_cap, ks, k_max, sw, idx, w, s, &att, &attended, dw.part,
+                    dw.splits);
   if (e == hipSuccess && !attended)
     e = launch_sparse_decode(q, K, V, dtype, B, Hq, Hkv, n_cap, idx, k_max, scale, out, dw, s);
   return from_hip(e);

@@ -100,7 +100,12 @@ struct AttendSpec {
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx,
                        const ScoreWs& ws, hipStream_t s, const AttendSpec* att = nullptr,
-                       bool* attended = nullptr);
+                       bool* attended = nullptr, float* part = nullptr, int part_splits = 0);
+
+// Key ranges of the decode step's selection + attention by range: 256-key
+// blocks a range, and ranges (attention splits) a row of n_cap keys.
+int range_blocks(int64_t n_cap);
+int range_splits(int64_t n_cap);
 
 // Hard-LSH comparison mode: packed sign codes of the L*P planes per key,
 // stored word-major: codes[(b*Hkv + h) * words + w][n_cap].
@@ -124,7 +129,8 @@ struct DecodeWs {
   int splits;
 };
 
-size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base);
+// min_splits: partials reserved per head beyond ceil(k_max / kSplitKeys).
+size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base, int min_splits = 0);
 
 hipError_t launch_sparse_decode(const void* q, const void* K, const void* V, int dtype, int B,
                                 int Hq, int Hkv, int64_t n_cap, const int32_t* idx, int k_max,

@@ -1795,6 +1795,274 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------- selection + attention by key range
+
+// The decode step's selection and attention for rows that do not outnumber
+// the CUs: after the scan, one workgroup per (query head, key range) settles
+// the head's boundary-bin candidates itself (each range's workgroup repeats
+// the same radix select, which reads a few hundred candidates), lists the
+// selected keys of its range in ascending order, writes them at their place
+// in the head's index row, and runs split-k attention over them (SOCKET
+// Sec. 4.1, Algorithm 3, exact attention over the retrieved subset).  The
+// partials (o, m, l) go to the split-k merge, one split per range.  This
+// takes the place of the per-head resolve and of the split-k partial launch.
+// A range is RB whole 256-key bitmap blocks (at least 8, at most
+// kRangeBlocksMax), about 32 ranges a row.
+constexpr int kRangeBlocksMax = 24;
+constexpr int kSelAttThreads = 256;
+constexpr int kSelAttCandCap = 2048;  // candidates settled in LDS (more: read in place)
+
+int range_blocks(int64_t n_cap) {
+  const int64_t nb = (n_cap + 255) / 256;
+  int64_t rb = (nb + 31) / 32;
+  if (rb < 8) rb = 8;
+  if (rb > kRangeBlocksMax) rb = kRangeBlocksMax;
+  return (int)rb;
+}
+
+int range_splits(int64_t n_cap) {
+  const int64_t nb = (n_cap + 255) / 256;
+  const int rb = range_blocks(n_cap);
+  return (int)((nb + rb - 1) / rb);
+}
+
+// Attention of one query over the S keys key0 + sel[t] (t < S, ascending) by
+// the NT threads of a workgroup, written as an unnormalised split-k partial
+// pp = (o, m, l) with m the largest logit, l = sum exp(logit - m) and
+// o = sum exp(logit - m) v.  16 lanes share a key row; the R = NT/16 rows take
+// keys t = row, row + R, ... in batches of AB (every K and V load of a batch
+// issued before any is used) with an online softmax, then merge in row order.
+// No key: o = 0, m = -inf, l = 0 (a split the merge skips).
+template <typename T, int NT, int AB>
+__device__ __forceinline__ void attend_partial(const T* __restrict__ qrow,
+                                               const T* __restrict__ Kh,
+                                               const T* __restrict__ Vh, const uint16_t* sel,
+                                               int64_t key0, int S, float scale, float* mo,
+                                               float* mml, float* __restrict__ pp) {
+  constexpr int R = NT / 16;
+  const int tid = threadIdx.x, j = tid & 15, row = tid >> 4;
+  float qf[8];
+  load_row8<T>(qrow, j, qf);
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int t0 = row; t0 < S; t0 += R * AB) {  // the 16 lanes of a row agree
+    int64_t ki[AB];
+    bool live[AB];
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      const int t = t0 + a * R;
+      live[a] = t < S;
+      ki[a] = key0 + (live[a] ? (int64_t)sel[t] : 0);
+    }
+    Row8<T> kr[AB], vr[AB];
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      kr[a] = fetch_row8<T>(Kh + ki[a] * kHead, j);
+      vr[a] = fetch_row8<T>(Vh + ki[a] * kHead, j);
+    }
+    float lg[AB], mx = m;
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      float kf[8];
+      unpack_row8<T>(kr[a], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[e], dot);
+      dot = row16_sum(dot);
+      lg[a] = live[a] ? dot * scale : -INFINITY;
+      mx = fmaxf(mx, lg[a]);
+    }
+    // t0 < S, so the batch's first key is a real one and mx is finite
+    const float c = m == -INFINITY ? 0.f : __expf(m - mx);
+    l *= c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= c;
+#pragma unroll
+    for (int a = 0; a < AB; ++a) {
+      const float p = lg[a] == -INFINITY ? 0.f : __expf(lg[a] - mx);
+      float vf[8];
+      unpack_row8<T>(vr[a], vf);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mo[row * kHead + 8 * j + e] = o[e];
+  if (j == 0) {
+    mml[2 * row] = m;
+    mml[2 * row + 1] = l;
+  }
+  __syncthreads();
+  if (tid < kHead) {
+    float M = -INFINITY;
+    for (int r = 0; r < R; ++r)
+      if (mml[2 * r + 1] > 0.f) M = fmaxf(M, mml[2 * r]);
+    float L = 0.f, O = 0.f;
+    for (int r = 0; r < R; ++r) {
+      const float lr = mml[2 * r + 1];
+      const float w = lr > 0.f ? __expf(mml[2 * r] - M) : 0.f;
+      L = fmaf(lr, w, L);
+      O = fmaf(mo[r * kHead + tid], w, O);
+    }
+    pp[tid] = O;
+    if (tid == 0) {
+      pp[kHead] = M;
+      pp[kHead + 1] = L;
+    }
+  }
+}
+
+// grid: B*Hq*S blocks of NT threads; block (bg, s) = (blockIdx / S, blockIdx mod S)
+// takes bitmap blocks [s*RB, (s+1)*RB) of head bg.
+template <int NT, typename T>
+__global__ __launch_bounds__(NT) void select_attend_kernel(
+    int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
+    int sink, int window, int Hq, int S, int RB, const uint32_t* __restrict__ hist,
+    const uint32_t* __restrict__ counters, const uint32_t* __restrict__ bitmap, int64_t words,
+    const uint2* __restrict__ cand, int32_t* __restrict__ idx, AttendArgs<T> at,
+    float* __restrict__ part) {
+  constexpr int NW = NT / 64;
+  constexpr int CPT = 4;  // candidates a thread requests with the first loads
+  static_assert(kSelAttCandCap >= CPT * NT, "the first loads fit the LDS list");
+  static_assert(kRangeBlocksMax * 8 <= NT, "one key-order word of the range a thread");
+  const int bg = (int)blockIdx.x / S, s = (int)blockIdx.x % S;
+  const int b = bg / Hq;
+  const int tid = threadIdx.x;
+  const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
+  const int64_t n = z.n, k = z.k;
+  int32_t* out = idx + (int64_t)bg * k_max;
+  float* pp = part + ((int64_t)bg * S + s) * kPartStride;
+  if (s == 0)
+    for (int64_t t = z.total + tid; t < k_max; t += NT) out[t] = -1;
+  const int64_t nblocks = (n + 255) >> 8;
+  const int64_t blk0 = (int64_t)s * RB;
+  const int64_t blk1 = blk0 + RB < nblocks ? blk0 + RB : nblocks;
+  if (z.total == 0 || blk0 >= nblocks) {  // uniform: an empty split
+    if (tid < kHead) pp[tid] = 0.f;
+    if (tid == 0) {
+      pp[kHead] = -INFINITY;
+      pp[kHead + 1] = 0.f;
+    }
+    return;
+  }
+
+  __shared__ uint32_t wsum[NW];
+  __shared__ Boundary shb;
+  __shared__ uint32_t h128[128];
+  __shared__ Pick shpick;
+  __shared__ uint32_t lbm[kRangeBlocksMax * 8];
+  __shared__ uint16_t lsel[kRangeBlocksMax * 256];
+  __shared__ float mml[2 * (NT / 16)];
+  __shared__ uint2 lcand[kSelAttCandCap];  // later the attention's row partials
+  static_assert(kSelAttCandCap * 2 >= (NT / 16) * kHead, "the candidate LDS holds the merge");
+
+  // every independent load at once: the histogram slice, the candidate
+  // count, the first CPT*NT candidates, the range's bitmap words and the
+  // bitmap before the range (for the number of selected keys ahead of it)
+  const HistSlice<NT> hs = load_hist_slice<NT>(hist + (int64_t)bg * kHistBins);
+  const uint2* gc = cand + (int64_t)bg * n_cap;
+  const uint32_t* bm = bitmap + (int64_t)bg * words;
+  const uint32_t Cg = counters[bg];
+  uint2 cv[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int64_t ci = (int64_t)tid + i * NT;
+    cv[i] = gc[ci < n_cap ? ci : n_cap - 1];
+  }
+  const int nw = (int)(blk1 - blk0) * 8;  // words of the range
+  const uint32_t rw = bm[blk0 * 8 + (tid < nw ? tid : 0)];
+  const uint4* bm4 = reinterpret_cast<const uint4*>(bm);
+  const int64_t nv = blk0 * 2;  // 16-byte vectors before the range
+  uint32_t pre = 0u;
+  for (int64_t v0 = 0; v0 < nv; v0 += 4 * NT) {
+    uint4 w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t vi = v0 + tid + i * NT;
+      w4[i] = bm4[vi < nv ? vi : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (v0 + tid + i * NT < nv)
+        pre += __popc(w4[i].x) + __popc(w4[i].y) + __popc(w4[i].z) + __popc(w4[i].w);
+  }
+  const Boundary bd = boundary_of<NT>(hs, (uint32_t)k, wsum, &shb);
+  const uint32_t C = Cg < (uint32_t)n ? Cg : (uint32_t)n;
+  const bool in_lds = C <= (uint32_t)kSelAttCandCap;
+  if (in_lds) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if ((uint32_t)(tid + i * NT) < C) lcand[tid + i * NT] = cv[i];
+    for (uint32_t ci = (uint32_t)(CPT * NT + tid); ci < C; ci += NT) lcand[ci] = gc[ci];
+  }
+  if (tid < nw) lbm[tid] = rw;
+  __syncthreads();
+  const uint2* lc = in_lds ? lcand : gc;
+
+  // the candidates that complete the top-k: a candidate is chosen iff its
+  // low 21 score bits exceed vval, or equal it with key <= imax
+  uint32_t vval = 0u, imax = 0xFFFFFFFFu;
+  const uint32_t need = (uint32_t)k - bd.above;  // 1 <= need <= C when k > 0
+  if (k > 0 && need < C) settle_candidates<NT>(lc, C, need, (uint32_t)n, h128, &shpick, vval, imax);
+
+  // chosen candidates: counted when ahead of the range, marked when in it
+  const uint32_t r0 = (uint32_t)(blk0 * 256), r1 = (uint32_t)(blk1 * 256);
+  for (uint32_t i = tid; i < C; i += NT) {
+    const uint2 e = lc[i];
+    const uint32_t v = e.x & 0x1FFFFFu;
+    if (v > vval || (v == vval && e.y <= imax)) {
+      if (e.y < r0) {
+        ++pre;
+      } else if (e.y < r1) {
+        const uint32_t blk = (e.y - r0) >> 8, i4 = (e.y >> 2) & 63u, ee = e.y & 3u;
+        atomicOr(&lbm[blk * 8 + ee * 2 + (i4 >> 5)], 1u << (i4 & 31));
+      }
+    }
+  }
+  __syncthreads();
+  // key-order word t of the range (keys r0 + 32t .. +31), rebuilt from the
+  // 8-bit slices of its block's four ballot masks
+  uint32_t x = 0u;
+  if (tid < nw) {
+    const int blk = tid >> 3, sub = tid & 7;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b8 = (lbm[blk * 8 + 2 * e + (sub >> 2)] >> ((sub & 3) * 8)) & 255u;
+      x |= spread4(b8) << e;
+    }
+  }
+  const uint32_t cnt = (uint32_t)__popc(x);
+  // one scan gives both the selected keys ahead of the range (the sum of
+  // pre, at most k_max <= 2^16) and this word's place in the range (a range
+  // holds at most kRangeBlocksMax*256 < 2^13 keys): pre above bit 13
+  static_assert(kRangeBlocksMax * 256 < (1 << 13), "range counts fit 13 bits");
+  const uint32_t inc = block_incl_scan<NT>((pre << 13) | cnt, wsum);
+  __shared__ uint32_t sh_all;
+  if (tid == NT - 1) sh_all = inc;
+  lds_barrier();
+  const uint32_t all = sh_all;
+  const uint32_t ahead = all >> 13;          // selected keys before the range
+  const uint32_t S_cnt = all & 0x1FFFu;      // selected keys in the range
+  uint32_t p = (inc & 0x1FFFu) - cnt;
+  while (x) {
+    const int bit = __ffs(x) - 1;
+    x &= x - 1;
+    const uint32_t off = (uint32_t)tid * 32u + (uint32_t)bit;
+    lsel[p] = (uint16_t)off;
+    const uint32_t gp = ahead + p;
+    if (gp < (uint32_t)k_max) out[gp] = (int32_t)(r0 + off);
+    ++p;
+  }
+  __syncthreads();
+  const int g = bg % Hq, h = g / (Hq / at.Hkv);
+  const int64_t kv = ((int64_t)b * at.Hkv + h) * n_cap * kHead;
+  attend_partial<T, NT, 4>(at.q + (int64_t)bg * kHead, at.K + kv, at.V + kv, lsel, (int64_t)r0,
+                           (int)S_cnt, at.scale, reinterpret_cast<float*>(lcand), mml, pp);
+}
+
 // ---------------------------------------------------------------- launchers
 
 static int device_cus() {
@@ -1911,7 +2179,8 @@ constexpr int64_t kStreamKeys = 40960;
 
 hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, int64_t n_cap,
                        const int32_t* ks, int k_max, SinkWindow sw, int32_t* idx, const ScoreWs& ws,
-                       hipStream_t s, const AttendSpec* att, bool* attended) {
+                       hipStream_t s, const AttendSpec* att, bool* attended, float* part,
+                       int part_splits) {
   if (attended) *attended = false;
   const int64_t heads = (int64_t)B * Hq;
   const bool many = heads > device_cus();
@@ -1924,6 +2193,43 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
     go(a);
   };
   const AttendArgs<uint16_t> none{};
+  // the scan: bitmap of the keys above the boundary bin, candidates of that bin
+  auto scan = [&]() {
+    const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
+    const int64_t nscan = heads * CH;
+    const unsigned sgrid = (unsigned)((nscan + kXcds - 1) / kXcds * kXcds);
+    // two kScanThreads workgroups fit a CU; beyond that, the small ones
+    if (nscan <= 2 * (int64_t)device_cus())
+      topk_scan_kernel<kScanThreads, kScanKeys / (kScanThreads / 64)><<<sgrid, kScanThreads, 0, s>>>(
+          scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, CH, (int)heads,
+          ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
+    else
+      topk_scan_kernel<256, 256><<<sgrid, 256, 0, s>>>(
+          scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, CH, (int)heads,
+          ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
+    return hipGetLastError();
+  };
+  // A decode step whose heads do not outnumber the CUs: the scan, then the
+  // selection and attention by key range (many workgroups a head instead of
+  // one CU selecting a head), then the split-k merge of the ranges.
+  const int S = range_splits(n_cap);
+  if (att && !many && part && S <= part_splits) {
+    hipError_t e = scan();
+    if (e != hipSuccess) return e;
+    const int RB = range_blocks(n_cap);
+    auto go = [&](auto a) {
+      using T = typename std::remove_const<typename std::remove_pointer<decltype(a.q)>::type>::type;
+      select_attend_kernel<kSelAttThreads, T><<<(unsigned)(heads * S), kSelAttThreads, 0, s>>>(
+          n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, S, RB, ws.hist, ws.counters, ws.bitmap,
+          ws.words, ws.cand, idx, a, part);
+    };
+    if (att->dtype == 1) with_att(uint16_t{}, go);
+    else with_att(float{}, go);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (attended) *attended = true;
+    return launch_decode_combine(part, (int)heads, S, att->out, s);
+  }
   if (n_cap <= kStreamKeys) {
     // 512-thread form (33 KiB of LDS, several a CU) for batches with more
     // heads than CUs, else the 1024-thread form (one a CU)
@@ -1964,19 +2270,7 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
     }
     return hipGetLastError();
   }
-  const int CH = (int)((n_cap + kScanKeys - 1) / kScanKeys);
-  const int64_t nscan = heads * CH;
-  const unsigned sgrid = (unsigned)((nscan + kXcds - 1) / kXcds * kXcds);
-  // two kScanThreads workgroups fit a CU; beyond that, the small ones
-  if (nscan <= 2 * (int64_t)device_cus())
-    topk_scan_kernel<kScanThreads, kScanKeys / (kScanThreads / 64)><<<sgrid, kScanThreads, 0, s>>>(
-        scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, CH, (int)heads,
-        ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
-  else
-    topk_scan_kernel<256, 256><<<sgrid, 256, 0, s>>>(
-        scores, n_cap, sst, lens, ks, k_max, sw.sink, sw.window, Hq, CH, (int)heads,
-        ws.hist, ws.counters, ws.bitmap, ws.words, ws.cand);
-  hipError_t e = hipGetLastError();
+  hipError_t e = scan();
   if (e != hipSuccess) return e;
   const int rnt = many ? 512 : kResThreads;
   const bool fuse = att && many && (n_cap + 255) / 256 <= rnt && k_max <= 2 * kCandCap;

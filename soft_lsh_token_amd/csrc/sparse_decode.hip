@@ -19,8 +19,9 @@ constexpr int kDecWaves = kDecThreads / 64;
 
 static inline size_t align256d(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base) {
-  const int splits = (k_max + kSplitKeys - 1) / kSplitKeys;
+size_t decode_ws_layout(int B, int Hq, int k_max, DecodeWs* ws, void* base, int min_splits) {
+  int splits = (k_max + kSplitKeys - 1) / kSplitKeys;
+  if (splits < min_splits) splits = min_splits;
   const size_t heads = (size_t)B * Hq;
   size_t off = 0;
   const size_t o_part = off; off = align256d(off + heads * splits * kPartStride * sizeof(float));

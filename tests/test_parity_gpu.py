@@ -880,6 +880,44 @@ def test_decode_step_matches_three_calls(case, sw):
                          idx_np[b, g], w.scale)
 
 
+@pytest.mark.parametrize("n,tied", [(20000, 900), (20000, 3000), (45000, 20000)],
+                         ids=["20000-tied900", "20000-tied3000", "45000-tied20000"])
+def test_decode_step_ties_match_three_calls(n, tied):
+    """Equal scores inside socket_decode_step: every cached key has the same
+    bucket IDs and a block of `tied` keys the larger norm, so the boundary bin
+    holds the whole block (900 candidates fit the range workgroups' LDS list;
+    3000 and 20000 are settled in place from the global list).  Indices must
+    equal the three calls' (lower indices win the ties) bit for bit, the
+    output to 1e-5."""
+    print("case", n, tied, flush=True)
+    w = make_workload("c2", n=n, Hq=8, Hkv=2, k=100)
+    d = GC.upload(w)
+    start = 1000
+    ids1 = S.alloc_ids(w.B, w.Hkv, w.n_cap, w.L, w.P, DEV)
+    vn1 = torch.ones(w.B, w.Hkv, w.n_cap, dtype=torch.float32, device=DEV)
+    vn1[:, 1, start:start + tied] = 2.0
+    ids2, vn2 = ids1.clone(), vn1.clone()
+    # three calls: hash the new key (position n - 1), select, attend
+    S.socket_hash_keys(d["K"], d["V"], d["W"], ids1, vn1,
+                       torch.full((1,), n - 1, dtype=torch.int32, device=DEV), 1, w.L, w.P)
+    idx1, sc1 = GC.gpu_score_topk(w, d, ids1, vn1)
+    out1 = GC.gpu_decode(w, d, idx1)
+    idx2 = torch.full_like(idx1, -7)
+    sc2 = torch.zeros_like(sc1)
+    out2 = torch.full_like(out1, float("nan"))
+    S.socket_decode_step(d["q"], d["K"], d["V"], d["W"], ids2, vn2, d["lens"], d["ks"], w.k_max,
+                         w.tau, w.L, w.P, w.scale, idx2, out2, scores=sc2)
+    sync()
+    assert torch.equal(ids1, ids2) and torch.equal(vn1, vn2)
+    assert torch.equal(sc1, sc2)
+    assert torch.equal(idx1, idx2)
+    torch.testing.assert_close(out2, out1, rtol=0, atol=1e-5)
+    idx = idx2.cpu().numpy()
+    for g in range(4, 8):  # KV head 1: the tied block beats the other cached keys
+        sel = [i for i in idx[0, g].tolist() if i != n - 1]
+        assert sel[:99] == list(range(start, start + 99)), g
+
+
 def test_stage_entry_points_match_fused_call():
     """socket_soft_tables + socket_score + socket_topk == socket_score_topk, bit for bit."""
     w = make_workload("c4", n=(3000, 9000), B=3, k=0.02)
