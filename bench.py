@@ -24,7 +24,8 @@ timed with HIP events on the library's stream.
 Also reported: per-stage GPU time (batches of steps cut after each stage,
 timed with one pair of HIP events per batch while the launches queue behind a
 long matrix product, so host launch gaps stay out; a stage's time includes
-its dispatch), the scorer alone, the 128K-key step, the 128K prefill hashing
+its dispatch), the step replayed from a captured HIP graph (one step per
+replica in one graph), the scorer alone, the 128K-key step, the 128K prefill hashing
 (fused with the norms; IDs only against the bf16 MFMA peak; norms only against
 HBM), the prefill + 256-step decode loop at 128K, the comparison modes, and
 the CPU oracle on bounded samples.
@@ -289,6 +290,32 @@ def gpu_batch_us(torch, run, count):
         log(f"[bench] warning: host enqueue {host_ms:.1f} ms exceeded the busy prologue "
             f"{busy_ms:.1f} ms; GPU times may include launch gaps")
     return e0.elapsed_time(e1) * 1e3 / count, host_ms * 1e3 / count
+
+
+def graph_steps(case, torch, replays=50):
+    """GPU us per decode step when the steps run from a captured HIP graph: one
+    graph holds one socket_decode_step per replica (successive layers of a
+    serving loop), captured on a side stream with the case's workspace (the
+    step allocates nothing), then replayed behind the busy prologue."""
+    s = torch.cuda.Stream()
+    vp = ctypes.c_void_p
+    args = [tuple(c[:-1]) + (vp(s.cuda_stream),) for c in case.c_fused]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for a in args:  # warm-up on the capture stream
+            case._ok(case.lib.socket_decode_step(*a), "socket_decode_step")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for a in args:
+            case._ok(case.lib.socket_decode_step(*a), "socket_decode_step")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    us, _ = gpu_batch_us(torch, lambda i: g.replay(), replays)
+    del g
+    return us / len(args)
 
 
 def per_stage(case, torch, steps):
@@ -744,6 +771,8 @@ def main():
     stages, gpu_step_us, host_step_us = per_stage(case, torch, min(max(args.steps, 50), 200))
     log(f"[bench] 32K per-stage GPU us {stages}; full step GPU {gpu_step_us:.1f} us; "
         f"host enqueue {host_step_us:.1f} us/step")
+    graph_us = graph_steps(case, torch)
+    log(f"[bench] 32K step from a captured HIP graph {graph_us:.1f} us (GPU)")
     stage_us = stage_launch_us(case, torch, 4 * case.replicas)
     score_us = scorer_launch_us(case, torch, 4 * case.replicas)
     log(f"[bench] 32K selection stage {stage_us:.2f} us, scorer launch {score_us:.2f} us")
@@ -762,7 +791,7 @@ def main():
         "(one socket_score_topk call)", {"kv_keys_per_call": kv_keys})
     extra32 = dict(
         step_us_wall=sec * 1e6, step_us_wall_three_calls=sec3 * 1e6,
-        step_us_gpu=gpu_step_us, host_enqueue_us_per_step=host_step_us,
+        step_us_gpu=gpu_step_us, step_us_graph=graph_us, host_enqueue_us_per_step=host_step_us,
         stage_us=stages, selection_stage_us=stage_us, scorer_launch_us=score_us,
         scorer_roofline=roofline_entry("scorer_c2", lbytes, score_us, "scorer_kernel at 32K"),
         prefill=pre32, dense_decode=dense32, sampling_estimator=est32,
@@ -782,13 +811,15 @@ def main():
         log(f"[bench] prefill 128K (the decode loop's): {prefill}")
         sec3 = timed_steps(c3, torch, args.steps, args.warmup)
         st3, gpu3, _ = per_stage(c3, torch, max(20, args.steps // 4))
+        graph3 = graph_steps(c3, torch, 20)
         stage3 = stage_launch_us(c3, torch, 4 * c3.replicas)
         sc3 = scorer_launch_us(c3, torch, 4 * c3.replicas)
         sb3, _ = stage_bytes(c3)
         lb3, _ = scorer_bytes(c3)
         dense128 = dense_decode(c3, torch, 4 * c3.replicas)
         dense128["socket_speedup"] = dense128["us"] / gpu3
-        extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, stage_us=st3,
+        extra128 = dict(step_us_wall=sec3 * 1e6, step_us_gpu=gpu3, step_us_graph=graph3,
+                        stage_us=st3,
                         selection_stage_us=stage3, scorer_launch_us=sc3,
                         keys_per_s=c3.kv_keys * (c3.w.Hq // c3.w.Hkv) / sec3,
                         selection_roofline=roofline_entry(

@@ -918,6 +918,56 @@ def test_decode_step_ties_match_three_calls(n, tied):
         assert sel[:99] == list(range(start, start + 99)), g
 
 
+def test_decode_step_graph_replays():
+    """socket_decode_step_noalloc captured in a HIP graph on a side stream
+    (it allocates nothing and records no memset) and replayed three times,
+    with eager work on the outputs between replays: every replay equals the
+    eager call bit for bit (IDs, norms, scores, indices, output)."""
+    w = make_workload("c2", n=20000)
+    d = GC.upload(w)
+    n0 = int(w.lens[0]) - 1
+    ids0, vn0 = GC.gpu_hash(w, d, count=n0)
+    shape_sc = (w.B, w.Hq, S.score_stride(w.n_cap))
+
+    def bufs():
+        return (ids0.clone(), vn0.clone(),
+                torch.full((w.B, w.Hq, w.k_max), -7, dtype=torch.int32, device=DEV),
+                torch.zeros(shape_sc, dtype=torch.float32, device=DEV),
+                torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device=DEV))
+
+    def call(b):
+        ids, vn, idx, sc, out = b
+        S.socket_decode_step_noalloc(d["q"], d["K"], d["V"], d["W"], ids, vn, d["lens"], d["ks"],
+                                     w.k_max, w.tau, w.L, w.P, w.scale, idx, out, scores=sc)
+
+    ref = bufs()
+    call(ref)
+    sync()
+    gb = bufs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(gb)  # warm-up on the capture stream
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(gb)
+    sync()
+    for rep in range(3):
+        gb[0].copy_(ids0)
+        gb[1].copy_(vn0)
+        gb[2].fill_(-7)
+        gb[3].zero_()
+        gb[4].fill_(float("nan"))
+        sync()
+        g.replay()
+        sync()
+        for a, b in zip(ref, gb):
+            assert torch.equal(a, b), rep
+    GC.check_out(gb[4][0, 3].cpu().numpy(), w.q[0, 3], w.K[0, 0], w.V[0, 0],
+                 gb[2][0, 3].cpu().numpy(), w.scale)
+
+
 def test_stage_entry_points_match_fused_call():
     """socket_soft_tables + socket_score + socket_topk == socket_score_topk, bit for bit."""
     w = make_workload("c4", n=(3000, 9000), B=3, k=0.02)
