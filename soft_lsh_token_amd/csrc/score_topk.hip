@@ -411,22 +411,18 @@ __device__ void append_block(const T* __restrict__ W, int Hkv, int L, int P, int
   const T* V = static_cast<const T*>(ak.V);
   __shared__ float kf[kHead];
   __shared__ uint32_t kbit[kTabThreads];
+  // the key's elements and the value row's slices requested together, every
+  // thread from an in-range address (one round trip, not two)
+  const T kraw = K[row * kHead + (tid < kHead ? tid : 0)];
+  const int vs = tid & 15;
+  Row8<T> vraw = fetch_row8<T>(V + row * kHead, vs);
   if (tid < kHead) {
-    if constexpr (sizeof(T) == 2) kf[tid] = __uint_as_float((uint32_t)K[row * kHead + tid] << 16);
-    else kf[tid] = K[row * kHead + tid];
+    if constexpr (sizeof(T) == 2) kf[tid] = __uint_as_float((uint32_t)kraw << 16);
+    else kf[tid] = kraw;
   }
   const bool norm = a == 0 && tid < 16;  // lanes 0..15 of wave 0: the value norm
   float vf[8];
-  if (norm) {
-    if constexpr (sizeof(T) == 2) {
-      unpack_bf16x8(reinterpret_cast<const uint4*>(V + row * kHead)[tid], vf);
-    } else {
-      const float4 x = reinterpret_cast<const float4*>(V + row * kHead)[2 * tid];
-      const float4 y = reinterpret_cast<const float4*>(V + row * kHead)[2 * tid + 1];
-      vf[0] = x.x; vf[1] = x.y; vf[2] = x.z; vf[3] = x.w;
-      vf[4] = y.x; vf[5] = y.y; vf[6] = y.z; vf[7] = y.w;
-    }
-  }
+  unpack_row8<T>(vraw, vf);
   __syncthreads();
   float z = 0.f;
   if (live) {
