@@ -1911,12 +1911,12 @@ __device__ __forceinline__ void attend_partial(const T* __restrict__ qrow,
   }
 }
 
-// grid: B*Hq*S blocks of NT threads; block (bg, s) = (blockIdx / S, blockIdx mod S)
-// takes bitmap blocks [s*RB, (s+1)*RB) of head bg.
+// grid: B*Hq*S blocks of NT threads (rounded up to a multiple of kXcds);
+// logical block bg*S + s takes bitmap blocks [s*RB, (s+1)*RB) of head bg.
 template <int NT, typename T>
 __global__ __launch_bounds__(NT) void select_attend_kernel(
     int64_t n_cap, const int32_t* __restrict__ lens, const int32_t* __restrict__ ks, int k_max,
-    int sink, int window, int Hq, int S, int RB, const uint32_t* __restrict__ hist,
+    int sink, int window, int Hq, int heads, int S, int RB, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ counters, const uint32_t* __restrict__ bitmap, int64_t words,
     const uint2* __restrict__ cand, int32_t* __restrict__ idx, AttendArgs<T> at,
     float* __restrict__ part) {
@@ -1924,7 +1924,11 @@ __global__ __launch_bounds__(NT) void select_attend_kernel(
   constexpr int CPT = 4;  // candidates a thread requests with the first loads
   static_assert(kSelAttCandCap >= CPT * NT, "the first loads fit the LDS list");
   static_assert(kRangeBlocksMax * 8 <= NT, "one key-order word of the range a thread");
-  const int bg = (int)blockIdx.x / S, s = (int)blockIdx.x % S;
+  // logical block (blockIdx mod 8) * (grid / 8) + blockIdx / 8, remapped as
+  // in the scan, so a head's ranges run on the XCD that scanned it
+  const int lid = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  const int bg = lid / S, s = lid % S;
+  if (bg >= heads) return;
   const int b = bg / Hq;
   const int tid = threadIdx.x;
   const SelSizes z = sel_sizes(n_cap, lens[b], ks[b], k_max, sink, window);
@@ -2215,8 +2219,9 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
     const int RB = range_blocks(n_cap);
     auto go = [&](auto a) {
       using T = typename std::remove_const<typename std::remove_pointer<decltype(a.q)>::type>::type;
-      select_attend_kernel<kSelAttThreads, T><<<(unsigned)(heads * S), kSelAttThreads, 0, s>>>(
-          n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, S, RB, ws.hist, ws.counters, ws.bitmap,
+      const unsigned grid = (unsigned)((heads * S + kXcds - 1) / kXcds * kXcds);
+      select_attend_kernel<kSelAttThreads, T><<<grid, kSelAttThreads, 0, s>>>(
+          n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, (int)heads, S, RB, ws.hist, ws.counters, ws.bitmap,
           ws.words, ws.cand, idx, a, part);
     };
     if (att->dtype == 1) with_att(uint16_t{}, go);

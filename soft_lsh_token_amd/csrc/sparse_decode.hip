@@ -206,11 +206,17 @@ hipError_t launch_sparse_decode(const void* q, const void* K, const void* V, int
 // registers, in split order, with no LDS and no barrier.
 constexpr int kFewSplits = 32;
 
+// grid: B*Hq blocks rounded up to a multiple of kXcds; head bg = logical block
+// (blockIdx mod 8) * (grid / 8) + blockIdx / 8, so a head is merged on the XCD
+// that ran its splits when the split kernel remaps its blocks the same way
+// (the decode step's range kernel does).
 template <int NS>
 __global__ __launch_bounds__(kHead) void decode_combine_few_kernel(const float* __restrict__ part,
                                                                    int splits,
-                                                                   float* __restrict__ out) {
-  const int bg = blockIdx.x;
+                                                                   float* __restrict__ out,
+                                                                   int heads) {
+  const int bg = (int)(blockIdx.x % kXcds) * (int)(gridDim.x / kXcds) + (int)(blockIdx.x / kXcds);
+  if (bg >= heads) return;
   const int d = threadIdx.x;
   const float* p = part + (int64_t)bg * splits * kPartStride;
   float o[NS], m[NS], l[NS];
@@ -293,10 +299,12 @@ __global__ __launch_bounds__(NG * kHead) void decode_combine_wide_kernel(
 hipError_t launch_decode_combine(const float* part, int heads, int splits, float* out,
                                  hipStream_t s) {
   if (splits > kMaxSplits) return hipErrorInvalidValue;
-  if (splits <= 8) decode_combine_few_kernel<8><<<heads, kHead, 0, s>>>(part, splits, out);
-  else if (splits <= 16) decode_combine_few_kernel<16><<<heads, kHead, 0, s>>>(part, splits, out);
+  const unsigned g8 = (unsigned)((heads + kXcds - 1) / kXcds * kXcds);
+  if (splits <= 8) decode_combine_few_kernel<8><<<g8, kHead, 0, s>>>(part, splits, out, heads);
+  else if (splits <= 16)
+    decode_combine_few_kernel<16><<<g8, kHead, 0, s>>>(part, splits, out, heads);
   else if (splits <= kFewSplits)
-    decode_combine_few_kernel<kFewSplits><<<heads, kHead, 0, s>>>(part, splits, out);
+    decode_combine_few_kernel<kFewSplits><<<g8, kHead, 0, s>>>(part, splits, out, heads);
   else if (splits <= 4 * kFewSplits)
     decode_combine_wide_kernel<4><<<heads, 4 * kHead, 0, s>>>(part, splits, out);
   else if (splits <= 8 * kFewSplits)
