@@ -811,6 +811,9 @@ def test_run_twice_bitwise():
     # longer rows: the scan + resolve top-k
     (dict(name="c2", n=20000), (0, 0)),
     (dict(name="c2", n=20000, k=300), (64, 128)),          # k_max 492: 8 splits
+    # 300000 keys: the range kernel's widest ranges (24 blocks), 49 ranges a
+    # head, merged by the wide combine
+    (dict(name="c2", n=300000, Hq=2, Hkv=1, L=16, k=600), (0, 0)),
     (dict(name="c4", n=(9000, 30000), B=3, Hq=8, Hkv=2, lens=[30000, 9000, 12345]), (16, 16)),
     (dict(name="c1", n=10000, k=200), (0, 0)),              # float32
     # attention inside the selecting workgroups: the resolve form (rows past
