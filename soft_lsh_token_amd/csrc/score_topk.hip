@@ -1803,14 +1803,15 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // partials (o, m, l) go to the split-k merge, one split per range.  This
 // takes the place of the per-head resolve and of the split-k partial launch.
 // A range is RB whole 256-key bitmap blocks (at least 8, at most
-// kRangeBlocksMax), about 32 ranges a row.
+// kRangeBlocksMax), about 16 ranges a row (measured against 12, 32 and, at
+// 128K, 24: 16 was fastest at 32K and within noise of the best at 128K).
 constexpr int kRangeBlocksMax = 24;
 constexpr int kSelAttThreads = 256;
 constexpr int kSelAttCandCap = 2048;  // candidates settled in LDS (more: read in place)
 
 int range_blocks(int64_t n_cap) {
   const int64_t nb = (n_cap + 255) / 256;
-  int64_t rb = (nb + 31) / 32;
+  int64_t rb = (nb + 15) / 16;
   if (rb < 8) rb = 8;
   if (rb > kRangeBlocksMax) rb = kRangeBlocksMax;
   return (int)rb;
