@@ -1803,17 +1803,21 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 // partials (o, m, l) go to the split-k merge, one split per range.  This
 // takes the place of the per-head resolve and of the split-k partial launch.
 // A range is RB whole 256-key bitmap blocks (at least 8, at most
-// kRangeBlocksMax), about 16 ranges a row (measured against 12, 32 and, at
-// 128K, 24: 16 was fastest at 32K and within noise of the best at 128K).
-constexpr int kRangeBlocksMax = 24;
-constexpr int kSelAttThreads = 256;
+// kRangeBlocksMax).  Rows of up to kShortRowBlocks blocks (64K keys) take
+// about 8 ranges of 512-thread workgroups, longer rows about 16 ranges of
+// 256-thread workgroups: in alternating runs these beat 12, 16 and 32 ranges
+// of 256 threads at 32K keys, and 8 ranges of 512 threads at 128K.
+constexpr int kRangeBlocksMax = 31;
+constexpr int kShortRowBlocks = 256;
 constexpr int kSelAttCandCap = 2048;  // candidates settled in LDS (more: read in place)
 
 int range_blocks(int64_t n_cap) {
   const int64_t nb = (n_cap + 255) / 256;
-  int64_t rb = (nb + 15) / 16;
+  const bool short_row = nb <= kShortRowBlocks;
+  int64_t rb = short_row ? (nb + 7) / 8 : (nb + 15) / 16;
   if (rb < 8) rb = 8;
-  if (rb > kRangeBlocksMax) rb = kRangeBlocksMax;
+  const int64_t cap = short_row ? kRangeBlocksMax : 24;  // 24: measured best for long rows
+  if (rb > cap) rb = cap;
   return (int)rb;
 }
 
@@ -1922,7 +1926,7 @@ __global__ __launch_bounds__(NT) void select_attend_kernel(
     const uint2* __restrict__ cand, int32_t* __restrict__ idx, AttendArgs<T> at,
     float* __restrict__ part) {
   constexpr int NW = NT / 64;
-  constexpr int CPT = 4;  // candidates a thread requests with the first loads
+  constexpr int CPT = 1024 / NT;  // candidates a thread requests with the first loads
   static_assert(kSelAttCandCap >= CPT * NT, "the first loads fit the LDS list");
   static_assert(kRangeBlocksMax * 8 <= NT, "one key-order word of the range a thread");
   // logical block (blockIdx mod 8) * (grid / 8) + blockIdx / 8, remapped as
@@ -2218,12 +2222,18 @@ hipError_t launch_topk(int B, int Hq, const float* scores, const int32_t* lens, 
     hipError_t e = scan();
     if (e != hipSuccess) return e;
     const int RB = range_blocks(n_cap);
+    const bool short_row = (n_cap + 255) / 256 <= kShortRowBlocks;
     auto go = [&](auto a) {
       using T = typename std::remove_const<typename std::remove_pointer<decltype(a.q)>::type>::type;
       const unsigned grid = (unsigned)((heads * S + kXcds - 1) / kXcds * kXcds);
-      select_attend_kernel<kSelAttThreads, T><<<grid, kSelAttThreads, 0, s>>>(
-          n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, (int)heads, S, RB, ws.hist, ws.counters, ws.bitmap,
-          ws.words, ws.cand, idx, a, part);
+      if (short_row)
+        select_attend_kernel<512, T><<<grid, 512, 0, s>>>(
+            n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, (int)heads, S, RB, ws.hist, ws.counters,
+            ws.bitmap, ws.words, ws.cand, idx, a, part);
+      else
+        select_attend_kernel<256, T><<<grid, 256, 0, s>>>(
+            n_cap, lens, ks, k_max, sw.sink, sw.window, Hq, (int)heads, S, RB, ws.hist, ws.counters,
+            ws.bitmap, ws.words, ws.cand, idx, a, part);
     };
     if (att->dtype == 1) with_att(uint16_t{}, go);
     else with_att(float{}, go);
