@@ -203,9 +203,13 @@ size_t socket_decode_step_workspace(int B, int Hq, int Hkv, int64_t n_cap, int L
  * socket_hash_keys with pos0 = lens - 1 and count = 1), then selects as
  * socket_score_topk (with sink and window) and attends as
  * socket_sparse_decode, writing idx, scores (may be NULL) and out.  The key is
- * hashed inside the table kernel, so the step takes one launch fewer than the
- * three calls.  ws must hold socket_decode_step_workspace(...) bytes,
- * 256-byte aligned.
+ * hashed inside the table kernel, and when the query heads do not outnumber
+ * the GPU's compute units the selection ends in a kernel that also attends,
+ * one workgroup per (query head, range of keys), so the step takes one launch
+ * fewer than the three calls.  IDs, norms, scores and idx equal the three
+ * calls' bit for bit; out agrees with theirs to rounding (its partial sums
+ * are taken over key ranges instead of runs of 64 selected keys).  ws must
+ * hold socket_decode_step_workspace(...) bytes, 256-byte aligned.
  */
 int socket_decode_step(const void* q, const void* K, const void* V, int dtype, int B, int Hq,
                        int Hkv, int d, const void* W, int L, int P, float tau, uint8_t* ids,

@@ -1793,8 +1793,8 @@ __global__ __launch_bounds__(NT) void topk_stream_kernel(
 
 // ---------------------------------------------------------------- selection + attention by key range
 
-// The decode step's selection and attention for rows that do not outnumber
-// the CUs: after the scan, one workgroup per (query head, key range) settles
+// The decode step's selection and attention when its query heads do not
+// outnumber the CUs: after the scan, one workgroup per (query head, key range) settles
 // the head's boundary-bin candidates itself (each range's workgroup repeats
 // the same radix select, which reads a few hundred candidates), lists the
 // selected keys of its range in ascending order, writes them at their place
