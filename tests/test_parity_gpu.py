@@ -816,6 +816,7 @@ def test_run_twice_bitwise():
     (dict(name="c2", n=300000, Hq=2, Hkv=1, L=16, k=600), (0, 0)),
     (dict(name="c4", n=(9000, 30000), B=3, Hq=8, Hkv=2, lens=[30000, 9000, 12345]), (16, 16)),
     (dict(name="c1", n=10000, k=200), (0, 0)),              # float32
+    (dict(name="c1", n=70000, k=300), (0, 16)),             # float32, 256-thread ranges
     # attention inside the selecting workgroups: the resolve form (rows past
     # the streaming top-k's length), the 512-thread streaming form (more heads
     # than CUs), and a selection too long to be kept in LDS (separate attention)
